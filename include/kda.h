@@ -1,0 +1,241 @@
+/*
+ * kda.h -- C ABI of libkda, the MI355X (gfx950) library for the KDA (Kimi
+ * Delta Attention) gated delta-rule recurrence.
+ *
+ * The recurrence, per (sequence or request slot, layer, head), with key and
+ * value head dimension K = V = 128 and an fp32 state S[K][V] (key channel =
+ * row index):
+ *
+ *   a[c]    = exp(gk[t][c])                        per-key-channel decay, gk <= 0
+ *   u[j]    = sum_c a[c] k[t][c] S[c][j]           prediction of the decayed state
+ *   w[j]    = beta[t] (v[t][j] - u[j])             delta-rule error
+ *   S[c][j] = a[c] S[c][j] + k[t][c] w[j]          decay, then rank-1 update, in place
+ *   o[t][j] = scale * sum_c q[t][c] S[c][j]        readout from the updated state
+ *
+ * Sources (page title, section):
+ *  [LMSYS-MEM] "SGLang and Miles Add Day-0 Support for Kimi K3" (LMSYS
+ *      blog), section "Hybrid KDA Memory Management": one fixed-size
+ *      recurrent state per request, overwritten in place every token;
+ *      subsection "Three state moves on the forward stream": snapshots at
+ *      chunk boundaries into a ping-pong "extra buffer", every state copy
+ *      ordered on the one forward stream.
+ *  [LMSYS-RSSM] same post, section "ReplaySSM: raw-input replay for the KDA
+ *      state": a K x V state (64 KB at K = V = 128); verify reads the
+ *      committed checkpoint and never writes it, and stores each step's raw
+ *      inputs (v, k, gk, beta), about 1 KB; one fold launch over every layer
+ *      and head replays only the accepted prefix in place, using the stored
+ *      gate values, bit-identical to the recurrent commit.
+ *  [B200-FKDA] Kimi K3 B200 deployment notes (zdszero.github.io), FlashKDA
+ *      items of the optimisation timeline: one fused kernel per chunk with
+ *      intermediates on chip; an fp32 [128,128] state per (sequence, head);
+ *      persistent launch and longest-first (LPT) order of sequences; a CPU
+ *      split plan built once per batch from host data and reused by every
+ *      layer, with no device read-back.
+ *  [B200-RING] same notes, section "DSPARK and KDA state" (decode-side
+ *      choices): a small ring per slot holding (v, k, gate, beta); its length
+ *      is a power of two and at least 2 * (gamma + 1).
+ *
+ * Conventions for every entry point:
+ *  - Pointers to tensors are DEVICE pointers unless the name ends in _host.
+ *    The caller owns every buffer; the library never allocates device
+ *    memory. A plan owns pinned host memory only.
+ *  - Layouts are row-major (C order); the last dimension is the head
+ *    dimension 128. bf16 tensors hold IEEE bfloat16 bit patterns.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream). No call synchronises or reads device memory. Device-data
+ *    preconditions (gk <= 0, beta in [0,1], distinct slots, ...) are
+ *    documented, not checked; index-like device values (slots, lengths,
+ *    ring positions) are clamped or skipped in the kernels so that a bad
+ *    value can never address memory outside the buffers described here.
+ *  - Every entry point returns a kda_status; kda_last_error() gives a
+ *    thread-local message for the last non-OK status. No C++ exception
+ *    crosses the ABI. KDA_ERR_DEVICE carries the HIP runtime's error text.
+ *  - Two calls in flight must not write the same state, snapshot, output or
+ *    ring rows (the single forward stream of [LMSYS-MEM] gives this order).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+#define KDA_HEAD_DIM 128 /* K = V = 128, fixed at build time */
+#define KDA_CHUNK 32     /* prefill chunk length; snap_interval must be a multiple */
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = 1, /* NULL required pointer, bad count, forbidden alias, bad ring length */
+  KDA_ERR_UNSUPPORTED = 2, /* a combination this build does not implement (fp32 inputs with a ring) */
+  KDA_ERR_DEVICE = 3,      /* the HIP runtime reported an error while enqueuing work */
+  KDA_ERR_HOST_ALLOC = 4   /* pinned host allocation for a plan failed */
+} kda_status;
+
+typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
+
+/* Returns KDA_ABI_VERSION of the loaded library. */
+int kda_abi_version(void);
+
+/* Thread-local text for the last non-OK status on this thread ("" if none). */
+const char* kda_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Prefill plan [B200-FKDA]: built once per batch from HOST data and reused by
+ * every layer (no device read-back). Work items are (sequence, head) pairs;
+ * the plan orders them longest sequence first (ties: ascending sequence,
+ * then head), or in input order with KDA_PLAN_FIFO.
+ * ------------------------------------------------------------------------- */
+typedef struct kda_plan kda_plan;
+
+#define KDA_PLAN_LPT 0  /* longest-processing-time-first (default) */
+#define KDA_PLAN_FIFO 1 /* (sequence, head) in input order, for comparison */
+
+/*
+ * cu_seqlens_host: int32[n_seq + 1], host memory, non-decreasing, [0] == 0,
+ *   last < 2^31. Read before return; the plan keeps its own copy.
+ * n_seq >= 1, n_heads >= 1.
+ * snap_interval: 0 = no snapshots; else a positive multiple of KDA_CHUNK.
+ * order: KDA_PLAN_LPT or KDA_PLAN_FIFO.
+ * *out receives an immutable plan, shareable across streams and threads.
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_HOST_ALLOC.
+ */
+kda_status kda_plan_create(const int32_t* cu_seqlens_host, int n_seq, int n_heads,
+                           int snap_interval, int order, kda_plan** out);
+
+/* Bytes of device workspace a prefill with this plan needs (256 + 16 per item). */
+size_t kda_plan_workspace_bytes(const kda_plan* plan);
+
+/* Number of work items (n_seq * n_heads). */
+int kda_plan_num_items(const kda_plan* plan);
+
+/* Copy the ordered work list to host memory items_host[n_items][4] =
+ * (sequence, head, first token, length). For inspection and tests. */
+kda_status kda_plan_items(const kda_plan* plan, int32_t* items_host);
+
+/* Enqueue the upload of the work list into `workspace` (device, at least
+ * kda_plan_workspace_bytes) and zero its counters. The copy reads the plan's
+ * pinned host buffer asynchronously: destroy the plan only after the stream
+ * has passed this point. */
+kda_status kda_plan_upload(const kda_plan* plan, void* workspace, void* stream);
+
+/* Free a plan (NULL is a no-op). */
+void kda_plan_destroy(kda_plan* plan);
+
+/* Inputs of one layer. q, k, v: [rows, H, 128] in the call's q/k/v dtype;
+ * gk: fp32 [rows, H, 128], per-token per-key-channel log-decay, gk <= 0;
+ * beta: fp32 [rows, H], in [0, 1] (already passed through its sigmoid). */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* gk;
+  const float* beta;
+} kda_inputs;
+
+/* ---------------------------------------------------------------------------
+ * Chunked prefill [B200-FKDA], [LMSYS-MEM]. THD-packed batch of the plan's
+ * sequences, T = cu_seqlens[n_seq] tokens, H = plan heads.
+ *
+ *  in        : q, k, v bf16 [T, H, 128]; gk fp32 [T, H, 128]; beta fp32 [T, H].
+ *              Chunked-form precondition: gk >= -10 (the intra-chunk
+ *              factorisation keeps exp(+-sum of gk over 8 tokens) in fp32
+ *              range); the recurrent entry points accept any gk <= 0.
+ *  state_in  : fp32 [n_seq, H, 128, 128] or NULL (= zeros).
+ *  state_out : fp32 [n_seq, H, 128, 128]; may equal state_in (in place);
+ *              any other overlap is rejected.
+ *  o         : fp32 [T, H, 128]; must not overlap any input or state.
+ *  snap      : fp32 [n_seq, snap_slots, H, 128, 128] or NULL. With a plan
+ *              snap_interval > 0 and snap != NULL, after the token at
+ *              position p (1-based, within its sequence) with
+ *              p % snap_interval == 0, the state is copied to slot
+ *              (p / snap_interval - 1) % snap_slots (the ping-pong extra
+ *              buffer when snap_slots == 2). snap_slots >= 1.
+ *  snap_count: int32 [n_seq] or NULL; receives floor(L_n / snap_interval)
+ *              (0 without snapshots).
+ *  workspace : device scratch of kda_plan_workspace_bytes(plan) bytes.
+ *  scale     : readout scale.
+ *  flags     : 0, or KDA_PREFILL_PLAN_RESIDENT when `workspace` already holds
+ *              this plan's work list from kda_plan_upload or from an earlier
+ *              completed prefill with the same plan and workspace (the
+ *              pages' "plan reused by every layer"): the call is then a
+ *              single kernel launch. Without the flag the call enqueues the
+ *              upload first.
+ * Sequences of length 0 get state_out = state_in (or zeros) and no outputs.
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_DEVICE.
+ */
+#define KDA_PREFILL_PLAN_RESIDENT 1
+kda_status kda_chunk_prefill(const kda_plan* plan, const kda_inputs* in, const float* state_in,
+                             float* state_out, float* o, float* snap, int snap_slots,
+                             int32_t* snap_count, void* workspace, float scale, int flags,
+                             void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Per-slot raw-input ring [LMSYS-RSSM], [B200-RING]: for each (slot, layer,
+ * head), len entries of (v, k, gk, beta), 1,028 bytes per entry.
+ *   k, v : bf16 [n_slots, L, H, len, 128];  gk : fp32 [n_slots, L, H, len, 128];
+ *   beta : fp32 [n_slots, L, H, len].  len: a power of two >= 2 * n_tok.
+ * Step t of a request with ring start s lives at position (s + t) & (len - 1).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  void* k;
+  void* v;
+  float* gk;
+  float* beta;
+  int len;
+} kda_ring;
+
+/*
+ * Speculative multi-token verify of one layer [LMSYS-RSSM]: one launch per
+ * layer; reads the committed state and never writes it.
+ *
+ *  batch, n_tok        : requests and draft tokens per request (gamma + 1).
+ *  n_heads, n_layers   : H and L of the pools; layer in [0, L).
+ *  n_slots             : first dimension of the pools and the ring.
+ *  qkv_dtype           : KDA_BF16, or KDA_F32 (only with ring == NULL).
+ *  in                  : rows b * n_tok + t of [batch * n_tok, H, 128].
+ *  state_pool          : fp32 [n_slots, L, H, 128, 128], read only.
+ *  slot_idx            : int32 [batch], distinct; a slot outside [0, n_slots)
+ *                        makes the kernel skip that request.
+ *  o                   : fp32 [batch * n_tok, H, 128].
+ *  ring, ring_start    : ring may be NULL (nothing recorded); ring_start int32
+ *                        [batch] or NULL (= 0).
+ *  commit_len          : int32 [batch] or NULL. For request b with
+ *                        c = min(commit_len[b], n_tok) > 0, the state after c
+ *                        steps is written to commit_pool[slot_b, layer, h]
+ *                        (the recurrent commit; a decode step is n_tok = 1,
+ *                        commit_len = 1, commit_pool = state_pool).
+ *  commit_pool         : like state_pool, or NULL; may equal state_pool, may
+ *                        not overlap it otherwise.
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_DEVICE.
+ */
+kda_status kda_verify(int batch, int n_tok, int n_heads, int n_layers, int layer, int n_slots,
+                      kda_dtype qkv_dtype, const kda_inputs* in, const float* state_pool,
+                      const int32_t* slot_idx, float* o, const kda_ring* ring,
+                      const int32_t* ring_start, const int32_t* commit_len, float* commit_pool,
+                      float scale, void* stream);
+
+/*
+ * Replay fold [LMSYS-RSSM]: one launch over every (request, layer, head).
+ * Advances state_pool[slot_b, l, h] in place by the first accepted_len[b]
+ * ring entries (from ring_start[b]) with the same step and reduction order
+ * as kda_verify, so the result is bit-identical to kda_verify's commit after
+ * that many steps. Entries past the accepted prefix are never read.
+ *
+ *  accepted_len : int32 [batch]; 0 leaves the state untouched; values are
+ *                 clamped to [0, ring->len / 2].
+ *  slot_idx, ring_start : as for kda_verify.
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_DEVICE.
+ */
+kda_status kda_replay_fold(int batch, int n_heads, int n_layers, int n_slots, float* state_pool,
+                           const int32_t* slot_idx, const kda_ring* ring,
+                           const int32_t* ring_start, const int32_t* accepted_len, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */
