@@ -1,0 +1,324 @@
+// kda_api.cpp -- host side of libkda: argument validation, the prefill plan
+// (longest-first work list built from host data), and the kernel launches.
+// See include/kda.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+kda_status fail(kda_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+kda_status ok() { return KDA_OK; }
+
+kda_status device_fail(const char* what, hipError_t e) {
+  return fail(KDA_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// [a, a + na) and [b, b + nb) share a byte
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+constexpr size_t kState = (size_t)KDA_HEAD_DIM * KDA_HEAD_DIM * sizeof(float);
+
+}  // namespace
+
+struct kda_plan {
+  int n_seq = 0, n_heads = 0, snap_interval = 0, order = 0, n_items = 0;
+  int64_t total_tokens = 0;
+  std::vector<int32_t> items;  // host copy, 4 ints per item
+  void* upload = nullptr;      // header + items, pinned when the runtime allows
+  bool pinned = false;
+  size_t bytes = 0;
+};
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_last_error(void) { return g_err.c_str(); }
+
+kda_status kda_plan_create(const int32_t* cu_seqlens_host, int n_seq, int n_heads, int snap_interval,
+                           int order, kda_plan** out) {
+  if (!out) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: out is NULL");
+  *out = nullptr;
+  if (!cu_seqlens_host) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: cu_seqlens_host is NULL");
+  if (n_seq < 1 || n_heads < 1) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: n_seq and n_heads must be >= 1");
+  if ((int64_t)n_seq * n_heads > 0x7fffffffLL) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: too many work items");
+  if (snap_interval < 0 || snap_interval % KDA_CHUNK != 0)
+    return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: snap_interval must be 0 or a positive multiple of KDA_CHUNK (32)");
+  if (order != KDA_PLAN_LPT && order != KDA_PLAN_FIFO) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: bad order");
+  if (cu_seqlens_host[0] != 0) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: cu_seqlens[0] must be 0");
+  for (int n = 0; n < n_seq; ++n)
+    if (cu_seqlens_host[n + 1] < cu_seqlens_host[n])
+      return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: cu_seqlens must be non-decreasing");
+
+  kda_plan* p = new (std::nothrow) kda_plan;
+  if (!p) return fail(KDA_ERR_HOST_ALLOC, "kda_plan_create: out of host memory");
+  p->n_seq = n_seq;
+  p->n_heads = n_heads;
+  p->snap_interval = snap_interval;
+  p->order = order;
+  p->n_items = n_seq * n_heads;
+  p->total_tokens = cu_seqlens_host[n_seq];
+  std::vector<int> idx(p->n_items);
+  for (int i = 0; i < p->n_items; ++i) idx[i] = i;  // item i = (n = i / H, h = i % H)
+  if (order == KDA_PLAN_LPT) {
+    // longest sequence first; equal lengths keep (sequence, head) ascending
+    std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) {
+      const int na = a / n_heads, nb = b / n_heads;
+      return (cu_seqlens_host[na + 1] - cu_seqlens_host[na]) > (cu_seqlens_host[nb + 1] - cu_seqlens_host[nb]);
+    });
+  }
+  p->items.resize((size_t)p->n_items * 4);
+  for (int i = 0; i < p->n_items; ++i) {
+    const int n = idx[i] / n_heads, h = idx[i] % n_heads;
+    p->items[4 * i + 0] = n;
+    p->items[4 * i + 1] = h;
+    p->items[4 * i + 2] = cu_seqlens_host[n];
+    p->items[4 * i + 3] = cu_seqlens_host[n + 1] - cu_seqlens_host[n];
+  }
+  p->bytes = sizeof(kda::PrefillWsHeader) + p->items.size() * sizeof(int32_t);
+  if (hipHostMalloc(&p->upload, p->bytes, hipHostMallocDefault) == hipSuccess) {
+    p->pinned = true;
+  } else {
+    (void)hipGetLastError();  // no device here: keep a pageable copy for inspection
+    p->upload = std::malloc(p->bytes);
+    if (!p->upload) {
+      delete p;
+      return fail(KDA_ERR_HOST_ALLOC, "kda_plan_create: out of host memory");
+    }
+  }
+  std::memset(p->upload, 0, sizeof(kda::PrefillWsHeader));
+  std::memcpy(static_cast<char*>(p->upload) + sizeof(kda::PrefillWsHeader), p->items.data(),
+              p->items.size() * sizeof(int32_t));
+  *out = p;
+  return ok();
+}
+
+size_t kda_plan_workspace_bytes(const kda_plan* p) { return p ? p->bytes : 0; }
+
+int kda_plan_num_items(const kda_plan* p) { return p ? p->n_items : 0; }
+
+kda_status kda_plan_items(const kda_plan* p, int32_t* items_host) {
+  if (!p || !items_host) return fail(KDA_ERR_INVALID_ARG, "kda_plan_items: NULL argument");
+  std::memcpy(items_host, p->items.data(), p->items.size() * sizeof(int32_t));
+  return ok();
+}
+
+kda_status kda_plan_upload(const kda_plan* p, void* workspace, void* stream) {
+  if (!p || !workspace) return fail(KDA_ERR_INVALID_ARG, "kda_plan_upload: NULL argument");
+  const hipError_t e = hipMemcpyAsync(workspace, p->upload, p->bytes, hipMemcpyHostToDevice,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail("kda_plan_upload", e);
+  return ok();
+}
+
+void kda_plan_destroy(kda_plan* p) {
+  if (!p) return;
+  if (p->pinned) (void)hipHostFree(p->upload);
+  else std::free(p->upload);
+  delete p;
+}
+
+kda_status kda_chunk_prefill(const kda_plan* p, const kda_inputs* in, const float* state_in, float* state_out,
+                             float* o, float* snap, int snap_slots, int32_t* snap_count, void* workspace,
+                             float scale, int flags, void* stream) {
+  if (!p) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: plan is NULL");
+  if (!in) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: inputs are NULL");
+  if (!state_out) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: state_out is NULL");
+  if (!workspace) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: workspace is NULL");
+  if (flags & ~KDA_PREFILL_PLAN_RESIDENT) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: unknown flags");
+  const int64_t T = p->total_tokens;
+  const int H = p->n_heads;
+  if (T > 0 && (!in->q || !in->k || !in->v || !in->gk || !in->beta || !o))
+    return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: q, k, v, gk, beta and o are required");
+  const bool snaps = p->snap_interval > 0 && snap != nullptr;
+  if (snaps && snap_slots < 1) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: snap_slots must be >= 1");
+  const size_t tok = (size_t)T * H;
+  const size_t qkv_b = tok * KDA_HEAD_DIM * 2, gk_b = tok * KDA_HEAD_DIM * 4, beta_b = tok * 4;
+  const size_t o_b = tok * KDA_HEAD_DIM * 4;
+  const size_t st_b = (size_t)p->n_seq * H * kState;
+  const size_t snap_b = snaps ? (size_t)p->n_seq * snap_slots * H * kState : 0;
+  const void* ins[5] = {in->q, in->k, in->v, in->gk, in->beta};
+  const size_t insz[5] = {qkv_b, qkv_b, qkv_b, gk_b, beta_b};
+  for (int i = 0; i < 5; ++i) {
+    if (overlap(o, o_b, ins[i], insz[i])) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: o overlaps an input");
+    if (overlap(state_out, st_b, ins[i], insz[i]))
+      return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: state_out overlaps an input");
+    if (snaps && overlap(snap, snap_b, ins[i], insz[i]))
+      return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: snap overlaps an input");
+  }
+  if (overlap(o, o_b, state_out, st_b) || overlap(o, o_b, state_in, st_b) || (snaps && overlap(o, o_b, snap, snap_b)))
+    return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: o overlaps a state buffer");
+  if (state_in != state_out && overlap(state_in, st_b, state_out, st_b))
+    return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: state_in and state_out overlap without being equal");
+  if (snaps && (overlap(snap, snap_b, state_out, st_b) || overlap(snap, snap_b, state_in, st_b)))
+    return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: snap overlaps a state buffer");
+  if (overlap(workspace, p->bytes, o, o_b) || overlap(workspace, p->bytes, state_out, st_b))
+    return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: workspace overlaps an output");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!(flags & KDA_PREFILL_PLAN_RESIDENT)) {
+    const kda_status st = kda_plan_upload(p, workspace, stream);
+    if (st != KDA_OK) return st;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_fail("kda_chunk_prefill: hipGetDevice", e);
+  kda::PrefillArgs a{};
+  a.n_seq = p->n_seq;
+  a.n_heads = H;
+  a.n_items = p->n_items;
+  a.total_tokens = T;
+  a.q = static_cast<const uint16_t*>(in->q);
+  a.k = static_cast<const uint16_t*>(in->k);
+  a.v = static_cast<const uint16_t*>(in->v);
+  a.gk = in->gk;
+  a.beta = in->beta;
+  a.state_in = state_in;
+  a.state_out = state_out;
+  a.o = o;
+  a.snap = snaps ? snap : nullptr;
+  a.snap_slots = snaps ? snap_slots : 0;
+  a.snap_interval = snaps ? p->snap_interval : 0;
+  a.snap_count = snap_count;
+  a.ws = static_cast<kda::PrefillWsHeader*>(workspace);
+  a.items = reinterpret_cast<const int4*>(static_cast<char*>(workspace) + sizeof(kda::PrefillWsHeader));
+  a.scale = scale;
+  const int grid = std::min(p->n_items, kda::prefill_max_grid(dev));
+  e = kda::launch_prefill(a, grid, s);
+  if (e != hipSuccess) return device_fail("kda_chunk_prefill: launch", e);
+  return ok();
+}
+
+kda_status kda_verify(int batch, int n_tok, int n_heads, int n_layers, int layer, int n_slots, kda_dtype qkv_dtype,
+                      const kda_inputs* in, const float* state_pool, const int32_t* slot_idx, float* o,
+                      const kda_ring* ring, const int32_t* ring_start, const int32_t* commit_len, float* commit_pool,
+                      float scale, void* stream) {
+  if (batch < 0 || n_tok < 1 || n_heads < 1 || n_layers < 1 || n_slots < 1 || layer < 0 || layer >= n_layers)
+    return fail(KDA_ERR_INVALID_ARG, "kda_verify: bad batch/n_tok/n_heads/n_layers/layer/n_slots");
+  if (qkv_dtype != KDA_BF16 && qkv_dtype != KDA_F32) return fail(KDA_ERR_INVALID_ARG, "kda_verify: bad qkv_dtype");
+  if (qkv_dtype == KDA_F32 && ring)
+    return fail(KDA_ERR_UNSUPPORTED, "kda_verify: the raw-input ring stores bf16 k/v; fp32 inputs need ring == NULL");
+  if ((int64_t)batch * n_heads > 0x7fffffffLL) return fail(KDA_ERR_INVALID_ARG, "kda_verify: grid too large");
+  if (batch == 0) return ok();
+  if (!in || !in->q || !in->k || !in->v || !in->gk || !in->beta)
+    return fail(KDA_ERR_INVALID_ARG, "kda_verify: q, k, v, gk and beta are required");
+  if (!state_pool || !slot_idx || !o) return fail(KDA_ERR_INVALID_ARG, "kda_verify: state_pool, slot_idx and o are required");
+  if ((commit_len == nullptr) != (commit_pool == nullptr))
+    return fail(KDA_ERR_INVALID_ARG, "kda_verify: commit_len and commit_pool go together");
+  if (ring) {
+    if (!ring->k || !ring->v || !ring->gk || !ring->beta) return fail(KDA_ERR_INVALID_ARG, "kda_verify: ring buffers are NULL");
+    if (!pow2(ring->len) || ring->len < 2 * n_tok)
+      return fail(KDA_ERR_INVALID_ARG, "kda_verify: ring length must be a power of two >= 2 * n_tok");
+  }
+  const size_t esz = qkv_dtype == KDA_F32 ? 4 : 2;
+  const size_t rows = (size_t)batch * n_tok * n_heads;
+  const size_t pool_b = (size_t)n_slots * n_layers * n_heads * kState;
+  const size_t o_b = rows * KDA_HEAD_DIM * 4;
+  const size_t ring_units = (size_t)n_slots * n_layers * n_heads * (ring ? ring->len : 0);
+  const void* bufs[] = {in->q, in->k, in->v, in->gk, in->beta, state_pool};
+  const size_t bsz[] = {rows * KDA_HEAD_DIM * esz, rows * KDA_HEAD_DIM * esz, rows * KDA_HEAD_DIM * esz,
+                        rows * KDA_HEAD_DIM * 4, rows * 4, pool_b};
+  for (int i = 0; i < 6; ++i) {
+    if (overlap(o, o_b, bufs[i], bsz[i])) return fail(KDA_ERR_INVALID_ARG, "kda_verify: o overlaps an input");
+    if (commit_pool && commit_pool != state_pool && overlap(commit_pool, pool_b, bufs[i], bsz[i]))
+      return fail(KDA_ERR_INVALID_ARG, "kda_verify: commit_pool overlaps an input or state_pool");
+    if (ring) {
+      const void* rb[] = {ring->k, ring->v, ring->gk, ring->beta};
+      const size_t rs[] = {ring_units * KDA_HEAD_DIM * 2, ring_units * KDA_HEAD_DIM * 2, ring_units * KDA_HEAD_DIM * 4,
+                           ring_units * 4};
+      for (int j = 0; j < 4; ++j)
+        if (overlap(rb[j], rs[j], bufs[i], bsz[i])) return fail(KDA_ERR_INVALID_ARG, "kda_verify: ring overlaps an input");
+    }
+  }
+  if (commit_pool && overlap(commit_pool, pool_b, o, o_b))
+    return fail(KDA_ERR_INVALID_ARG, "kda_verify: commit_pool overlaps o");
+
+  kda::VerifyArgs a{};
+  a.batch = batch;
+  a.n_tok = n_tok;
+  a.n_heads = n_heads;
+  a.n_layers = n_layers;
+  a.layer = layer;
+  a.n_slots = n_slots;
+  a.q = in->q;
+  a.k = in->k;
+  a.v = in->v;
+  a.gk = in->gk;
+  a.beta = in->beta;
+  a.state_pool = state_pool;
+  a.slot_idx = slot_idx;
+  a.o = o;
+  if (ring) {
+    a.ring_k = ring->k;
+    a.ring_v = ring->v;
+    a.ring_gk = ring->gk;
+    a.ring_beta = ring->beta;
+    a.ring_len = ring->len;
+  }
+  a.ring_start = ring_start;
+  a.commit_len = commit_len;
+  a.commit_pool = commit_pool;
+  a.scale = scale;
+  const hipError_t e = kda::launch_verify(a, qkv_dtype == KDA_F32, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail("kda_verify: launch", e);
+  return ok();
+}
+
+kda_status kda_replay_fold(int batch, int n_heads, int n_layers, int n_slots, float* state_pool, const int32_t* slot_idx,
+                           const kda_ring* ring, const int32_t* ring_start, const int32_t* accepted_len, void* stream) {
+  if (batch < 0 || n_heads < 1 || n_layers < 1 || n_slots < 1)
+    return fail(KDA_ERR_INVALID_ARG, "kda_replay_fold: bad batch/n_heads/n_layers/n_slots");
+  if ((int64_t)batch * n_layers * n_heads > 0x7fffffffLL) return fail(KDA_ERR_INVALID_ARG, "kda_replay_fold: grid too large");
+  if (batch == 0) return ok();
+  if (!state_pool || !slot_idx || !accepted_len || !ring)
+    return fail(KDA_ERR_INVALID_ARG, "kda_replay_fold: state_pool, slot_idx, ring and accepted_len are required");
+  if (!ring->k || !ring->v || !ring->gk || !ring->beta) return fail(KDA_ERR_INVALID_ARG, "kda_replay_fold: ring buffers are NULL");
+  if (!pow2(ring->len) || ring->len < 2) return fail(KDA_ERR_INVALID_ARG, "kda_replay_fold: ring length must be a power of two >= 2");
+  const size_t pool_b = (size_t)n_slots * n_layers * n_heads * kState;
+  const size_t ru = (size_t)n_slots * n_layers * n_heads * ring->len;
+  const void* rb[] = {ring->k, ring->v, ring->gk, ring->beta};
+  const size_t rs[] = {ru * KDA_HEAD_DIM * 2, ru * KDA_HEAD_DIM * 2, ru * KDA_HEAD_DIM * 4, ru * 4};
+  for (int j = 0; j < 4; ++j)
+    if (overlap(state_pool, pool_b, rb[j], rs[j])) return fail(KDA_ERR_INVALID_ARG, "kda_replay_fold: state_pool overlaps the ring");
+  kda::FoldArgs a{};
+  a.batch = batch;
+  a.n_heads = n_heads;
+  a.n_layers = n_layers;
+  a.n_slots = n_slots;
+  a.state_pool = state_pool;
+  a.slot_idx = slot_idx;
+  a.ring_k = ring->k;
+  a.ring_v = ring->v;
+  a.ring_gk = ring->gk;
+  a.ring_beta = ring->beta;
+  a.ring_len = ring->len;
+  a.ring_start = ring_start;
+  a.accepted_len = accepted_len;
+  const hipError_t e = kda::launch_fold(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail("kda_replay_fold: launch", e);
+  return ok();
+}
+
+}  // extern "C"

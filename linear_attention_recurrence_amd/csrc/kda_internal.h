@@ -1,0 +1,75 @@
+// kda_internal.h -- argument blocks and launchers shared by the libkda translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct VerifyArgs {
+  int batch, n_tok, n_heads, n_layers, layer, n_slots;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* gk;
+  const float* beta;
+  const float* state_pool;
+  const int32_t* slot_idx;
+  float* o;
+  void* ring_k;  // nullptr: nothing recorded
+  void* ring_v;
+  float* ring_gk;
+  float* ring_beta;
+  int ring_len;
+  const int32_t* ring_start;  // nullptr: 0
+  const int32_t* commit_len;  // nullptr: no commit
+  float* commit_pool;
+  float scale;
+};
+
+struct FoldArgs {
+  int batch, n_heads, n_layers, n_slots;
+  float* state_pool;
+  const int32_t* slot_idx;
+  const void* ring_k;
+  const void* ring_v;
+  const float* ring_gk;
+  const float* ring_beta;
+  int ring_len;
+  const int32_t* ring_start;
+  const int32_t* accepted_len;
+};
+
+// Work list header at the start of the prefill workspace.
+struct PrefillWsHeader {
+  int32_t counter;  // next item to take
+  int32_t done;     // workgroups finished
+  int32_t pad[62];  // items start at byte 256
+};
+
+struct PrefillArgs {
+  int n_seq, n_heads, n_items;
+  int64_t total_tokens;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* gk;
+  const float* beta;
+  const float* state_in;  // nullptr: zeros
+  float* state_out;
+  float* o;
+  float* snap;  // nullptr: none
+  int snap_slots;
+  int snap_interval;  // 0: none
+  int32_t* snap_count;
+  PrefillWsHeader* ws;
+  const int4* items;  // (sequence, head, first token, length)
+  float scale;
+};
+
+hipError_t launch_verify(const VerifyArgs& a, bool f32_inputs, hipStream_t stream);
+hipError_t launch_fold(const FoldArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int grid, hipStream_t stream);
+int prefill_max_grid(int device);
+
+}  // namespace kda

@@ -1,0 +1,254 @@
+"""Thin ctypes binding of libkda (include/kda.h): argument marshalling only.
+
+Every function has the name of the C entry point it wraps and passes device
+pointers of torch tensors plus the current HIP stream. Tensor shapes, dtypes
+and contiguity are checked here against the layouts the header states, so a
+kernel never addresses memory outside the tensors it was given. There is no
+fallback: if libkda.so is missing or the HIP runtime is unavailable, calls
+raise.
+
+torch is imported before the library is loaded, so libkda binds to the HIP
+runtime torch already mapped (both carry the soname libamdhip64.so.7) and
+torch's stream handles are valid in it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_DEVICE, KDA_ERR_HOST_ALLOC = 0, 1, 2, 3, 4
+KDA_BF16, KDA_F32 = 0, 1
+KDA_PLAN_LPT, KDA_PLAN_FIFO = 0, 1
+KDA_PREFILL_PLAN_RESIDENT = 1
+KDA_HEAD_DIM = 128
+KDA_CHUNK = 32
+
+EXPORTS = ("kda_abi_version", "kda_last_error", "kda_plan_create", "kda_plan_workspace_bytes",
+           "kda_plan_num_items", "kda_plan_items", "kda_plan_upload", "kda_plan_destroy",
+           "kda_chunk_prefill", "kda_verify", "kda_replay_fold")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"libkda status {status}: {msg}")
+        self.status = status
+
+
+class _Inputs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("gk", ctypes.c_void_p), ("beta", ctypes.c_void_p)]
+
+
+class _Ring(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("gk", ctypes.c_void_p),
+                ("beta", ctypes.c_void_p), ("len", ctypes.c_int)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        L.kda_abi_version.restype = i32
+        L.kda_last_error.restype = ctypes.c_char_p
+        L.kda_plan_create.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(vp)]
+        L.kda_plan_workspace_bytes.argtypes = [vp]
+        L.kda_plan_workspace_bytes.restype = ctypes.c_size_t
+        L.kda_plan_num_items.argtypes = [vp]
+        L.kda_plan_num_items.restype = i32
+        L.kda_plan_items.argtypes = [vp, vp]
+        L.kda_plan_upload.argtypes = [vp, vp, vp]
+        L.kda_plan_destroy.argtypes = [vp]
+        L.kda_plan_destroy.restype = None
+        L.kda_chunk_prefill.argtypes = [vp, ctypes.POINTER(_Inputs), vp, vp, vp, vp, i32, vp, vp, f32, i32, vp]
+        L.kda_verify.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(_Inputs), vp, vp, vp,
+                                 ctypes.POINTER(_Ring), vp, vp, vp, f32, vp]
+        L.kda_replay_fold.argtypes = [i32, i32, i32, i32, vp, vp, ctypes.POINTER(_Ring), vp, vp, vp]
+        for f in ("kda_plan_create", "kda_plan_items", "kda_plan_upload", "kda_chunk_prefill", "kda_verify",
+                  "kda_replay_fold"):
+            getattr(L, f).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != KDA_OK:
+        raise KdaError(status, lib().kda_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, shape, dtypes, allow_none=False):
+    if t is None:
+        if allow_none:
+            return
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_BF, _F32, _I32 = (torch.bfloat16,), (torch.float32,), (torch.int32,)
+
+
+def kda_abi_version():
+    return lib().kda_abi_version()
+
+
+def kda_last_error():
+    return lib().kda_last_error().decode()
+
+
+class Plan:
+    """Owner of a kda_plan* (host data only); destroyed with the object."""
+
+    def __init__(self, handle, cu_seqlens, n_heads, snap_interval):
+        self.handle = handle
+        self.cu_seqlens = cu_seqlens
+        self.n_seq = len(cu_seqlens) - 1
+        self.n_heads = n_heads
+        self.snap_interval = snap_interval
+        self.total_tokens = int(cu_seqlens[-1])
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.kda_plan_destroy(self.handle)
+            self.handle = None
+
+
+def kda_plan_create(cu_seqlens_host, n_heads, snap_interval=0, order=KDA_PLAN_LPT):
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
+    h = ctypes.c_void_p()
+    _check(lib().kda_plan_create(cu.ctypes.data, len(cu) - 1, n_heads, snap_interval, order, ctypes.byref(h)))
+    return Plan(h, cu.copy(), n_heads, snap_interval)
+
+
+def kda_plan_workspace_bytes(plan):
+    return int(lib().kda_plan_workspace_bytes(plan.handle))
+
+
+def kda_plan_num_items(plan):
+    return int(lib().kda_plan_num_items(plan.handle))
+
+
+def kda_plan_items(plan):
+    out = np.zeros((kda_plan_num_items(plan), 4), dtype=np.int32)
+    _check(lib().kda_plan_items(plan.handle, out.ctypes.data))
+    return out
+
+
+def kda_plan_upload(plan, workspace, stream=None):
+    _need(workspace, "workspace", (kda_plan_workspace_bytes(plan),), (torch.uint8,))
+    _check(lib().kda_plan_upload(plan.handle, _ptr(workspace), _stream(stream)))
+
+
+def kda_chunk_prefill(plan, q, k, v, gk, beta, state_out, o, workspace, state_in=None, snap=None, snap_slots=0,
+                      snap_count=None, scale=1.0, flags=0, stream=None):
+    """Chunked prefill over the plan's THD-packed batch (see kda_chunk_prefill in include/kda.h)."""
+    T, H, N, Dh = plan.total_tokens, plan.n_heads, plan.n_seq, KDA_HEAD_DIM
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (T, H, Dh), _BF)
+    _need(gk, "gk", (T, H, Dh), _F32)
+    _need(beta, "beta", (T, H), _F32)
+    _need(o, "o", (T, H, Dh), _F32)
+    _need(state_out, "state_out", (N, H, Dh, Dh), _F32)
+    _need(state_in, "state_in", (N, H, Dh, Dh), _F32, allow_none=True)
+    if snap is not None:
+        _need(snap, "snap", (N, snap_slots, H, Dh, Dh), _F32)
+    _need(snap_count, "snap_count", (N,), _I32, allow_none=True)
+    _need(workspace, "workspace", (kda_plan_workspace_bytes(plan),), (torch.uint8,))
+    ins = _Inputs(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(), beta.data_ptr())
+    _check(lib().kda_chunk_prefill(plan.handle, ctypes.byref(ins), _ptr(state_in), _ptr(state_out), _ptr(o),
+                                   _ptr(snap), int(snap_slots), _ptr(snap_count), _ptr(workspace), float(scale),
+                                   int(flags), _stream(stream)))
+
+
+class Ring:
+    """Device buffers of the per-slot raw-input ring: k, v bf16 [S, L, H, R, 128]; gk fp32; beta fp32 [S, L, H, R]."""
+
+    def __init__(self, k, v, gk, beta):
+        self.k, self.v, self.gk, self.beta = k, v, gk, beta
+        self.len = k.shape[3]
+
+    @staticmethod
+    def empty(n_slots, n_layers, n_heads, length, device):
+        sh = (n_slots, n_layers, n_heads, length, KDA_HEAD_DIM)
+        return Ring(torch.empty(sh, dtype=torch.bfloat16, device=device),
+                    torch.empty(sh, dtype=torch.bfloat16, device=device),
+                    torch.empty(sh, dtype=torch.float32, device=device),
+                    torch.empty(sh[:4], dtype=torch.float32, device=device))
+
+    def check(self, n_slots, n_layers, n_heads):
+        sh = (n_slots, n_layers, n_heads, self.len, KDA_HEAD_DIM)
+        _need(self.k, "ring.k", sh, _BF)
+        _need(self.v, "ring.v", sh, _BF)
+        _need(self.gk, "ring.gk", sh, _F32)
+        _need(self.beta, "ring.beta", sh[:4], _F32)
+
+    def c(self):
+        return _Ring(self.k.data_ptr(), self.v.data_ptr(), self.gk.data_ptr(), self.beta.data_ptr(), self.len)
+
+
+def kda_verify(q, k, v, gk, beta, state_pool, slot_idx, o, layer, n_tok, ring=None, ring_start=None,
+               commit_len=None, commit_pool=None, scale=1.0, stream=None):
+    """Verify n_tok draft tokens of every request for one layer (see kda_verify in include/kda.h)."""
+    S, L, H, Dh = state_pool.shape[0], state_pool.shape[1], state_pool.shape[2], KDA_HEAD_DIM
+    B = slot_idx.shape[0]
+    f32 = q.dtype == torch.float32
+    qkv = _F32 if f32 else _BF
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (B * n_tok, H, Dh), qkv)
+    _need(gk, "gk", (B * n_tok, H, Dh), _F32)
+    _need(beta, "beta", (B * n_tok, H), _F32)
+    _need(state_pool, "state_pool", (S, L, H, Dh, Dh), _F32)
+    _need(slot_idx, "slot_idx", (B,), _I32)
+    _need(o, "o", (B * n_tok, H, Dh), _F32)
+    _need(ring_start, "ring_start", (B,), _I32, allow_none=True)
+    _need(commit_len, "commit_len", (B,), _I32, allow_none=True)
+    _need(commit_pool, "commit_pool", (S, L, H, Dh, Dh), _F32, allow_none=True)
+    rc = None
+    if ring is not None:
+        ring.check(S, L, H)
+        rc = ctypes.byref(ring.c())
+    ins = _Inputs(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(), beta.data_ptr())
+    _check(lib().kda_verify(B, n_tok, H, L, layer, S, KDA_F32 if f32 else KDA_BF16, ctypes.byref(ins),
+                            _ptr(state_pool), _ptr(slot_idx), _ptr(o), rc, _ptr(ring_start), _ptr(commit_len),
+                            _ptr(commit_pool), float(scale), _stream(stream)))
+
+
+def kda_replay_fold(state_pool, slot_idx, ring, accepted_len, ring_start=None, stream=None):
+    """Fold the accepted prefix of every request into state_pool, in place (see include/kda.h)."""
+    S, L, H, Dh = state_pool.shape[0], state_pool.shape[1], state_pool.shape[2], KDA_HEAD_DIM
+    B = slot_idx.shape[0]
+    _need(state_pool, "state_pool", (S, L, H, Dh, Dh), _F32)
+    _need(slot_idx, "slot_idx", (B,), _I32)
+    _need(accepted_len, "accepted_len", (B,), _I32)
+    _need(ring_start, "ring_start", (B,), _I32, allow_none=True)
+    ring.check(S, L, H)
+    _check(lib().kda_replay_fold(B, H, L, S, _ptr(state_pool), _ptr(slot_idx), ctypes.byref(ring.c()),
+                                 _ptr(ring_start), _ptr(accepted_len), _stream(stream)))

@@ -1,0 +1,151 @@
+"""Host-side checks of libkda: it loads, exports every entry point include/kda.h
+declares, builds longest-first plans, and rejects bad arguments with
+KDA_ERR_INVALID_ARG / KDA_ERR_UNSUPPORTED before touching a device.
+
+Every call below fails validation on the host, so none launches a kernel
+(these tests also run safely on a GPU machine).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import linear_attention_recurrence_amd as kda
+from linear_attention_recurrence_amd import kda as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call here fails validation first
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 11
+    L = kda.lib()
+    for n in names:
+        assert hasattr(L, n), f"libkda.so does not export {n}"
+    assert set(names) == set(K.EXPORTS)
+    assert kda.kda_abi_version() == 1
+
+
+def test_plan_lpt_order_and_ties():
+    cu = [0, 5, 100, 100, 140, 235]  # lengths 5, 95, 0, 40, 95
+    p = kda.kda_plan_create(cu, n_heads=3)
+    it = kda.kda_plan_items(p)
+    lens = it[:, 3]
+    assert list(lens) == sorted(lens, reverse=True)
+    # equal lengths keep (sequence, head) ascending
+    top = [tuple(x[:2]) for x in it if x[3] == 95]
+    assert top == [(1, 0), (1, 1), (1, 2), (4, 0), (4, 1), (4, 2)]
+    for n, h, t0, L in it:
+        assert t0 == cu[n] and L == cu[n + 1] - cu[n] and 0 <= h < 3
+    assert kda.kda_plan_workspace_bytes(p) == 256 + 16 * 15
+    fifo = kda.kda_plan_items(kda.kda_plan_create(cu, n_heads=3, order=kda.KDA_PLAN_FIFO))
+    assert [tuple(x[:2]) for x in fifo] == [(n, h) for n in range(5) for h in range(3)]
+
+
+@pytest.mark.parametrize("cu,H,iv,msg", [
+    ([1, 5], 1, 0, "cu_seqlens[0]"),
+    ([0, 5, 3], 1, 0, "non-decreasing"),
+    ([0, 5], 0, 0, "n_heads"),
+    ([0, 5], 1, 48, "multiple"),
+    ([0, 5], 1, -32, "multiple"),
+])
+def test_plan_rejects(cu, H, iv, msg):
+    with pytest.raises(kda.KdaError) as e:
+        kda.kda_plan_create(cu, n_heads=H, snap_interval=iv)
+    assert e.value.status == kda.KDA_ERR_INVALID_ARG and msg in str(e.value)
+
+
+def _inputs():
+    return K._Inputs(FAKE.value, FAKE.value + 0x100000, FAKE.value + 0x200000, FAKE.value + 0x300000,
+                     FAKE.value + 0x400000)
+
+
+def test_prefill_rejects_bad_arguments():
+    L = kda.lib()
+    p = kda.kda_plan_create([0, 64], n_heads=1, snap_interval=32)
+    ins = _inputs()
+    ws = ctypes.c_void_p(0x9000000)
+    out = ctypes.c_void_p(0x8000000)
+    o = ctypes.c_void_p(0xA000000)
+    # NULL plan, inputs, state_out, workspace
+    assert L.kda_chunk_prefill(None, ctypes.byref(ins), None, out, o, None, 0, None, ws, 1.0, 0, None) == 1
+    assert L.kda_chunk_prefill(p.handle, None, None, out, o, None, 0, None, ws, 1.0, 0, None) == 1
+    assert L.kda_chunk_prefill(p.handle, ctypes.byref(ins), None, None, o, None, 0, None, ws, 1.0, 0, None) == 1
+    assert L.kda_chunk_prefill(p.handle, ctypes.byref(ins), None, out, o, None, 0, None, None, 1.0, 0, None) == 1
+    # o overlapping q
+    assert L.kda_chunk_prefill(p.handle, ctypes.byref(ins), None, out, FAKE, None, 0, None, ws, 1.0, 0, None) == 1
+    assert "o overlaps" in kda.kda_last_error()
+    # snapshots requested with zero slots
+    assert L.kda_chunk_prefill(p.handle, ctypes.byref(ins), None, out, o, ctypes.c_void_p(0xB000000), 0, None, ws,
+                               1.0, 0, None) == 1
+    assert "snap_slots" in kda.kda_last_error()
+    # partial overlap of state_in and state_out
+    assert L.kda_chunk_prefill(p.handle, ctypes.byref(ins), ctypes.c_void_p(0x8000000 + 4096), out, o, None, 0,
+                               None, ws, 1.0, 0, None) == 1
+    assert "state_in and state_out" in kda.kda_last_error()
+    # unknown flag bits
+    assert L.kda_chunk_prefill(p.handle, ctypes.byref(ins), None, out, o, None, 0, None, ws, 1.0, 2, None) == 1
+
+
+def _ring(length, base=0xC000000):
+    return K._Ring(base, base + 0x1000000, base + 0x2000000, base + 0x3000000, length)
+
+
+def test_verify_rejects_bad_arguments():
+    L = kda.lib()
+    ins = _inputs()
+    pool, slots, o = ctypes.c_void_p(0x20000000), ctypes.c_void_p(0x30000000), ctypes.c_void_p(0x40000000)
+    args = lambda **kw: dict(dict(B=2, T=8, H=2, Lyr=3, layer=0, S=4, dt=kda.KDA_BF16, ring=None), **kw)
+
+    def call(B=2, T=8, H=2, Lyr=3, layer=0, S=4, dt=kda.KDA_BF16, ring=None, commit_len=None, commit_pool=None,
+             o_=o):
+        r = ctypes.byref(ring) if ring is not None else None
+        return L.kda_verify(B, T, H, Lyr, layer, S, dt, ctypes.byref(ins), pool, slots, o_, r, None, commit_len,
+                            commit_pool, 1.0, None)
+
+    assert call(T=0) == 1
+    assert call(layer=3) == 1
+    assert call(layer=-1) == 1
+    assert call(S=0) == 1
+    assert call(dt=7) == 1
+    assert call(dt=kda.KDA_F32, ring=_ring(16)) == 2  # fp32 inputs cannot be recorded in the bf16 ring
+    assert call(ring=_ring(12)) == 1  # not a power of two
+    assert call(ring=_ring(8)) == 1   # < 2 * n_tok
+    assert "power of two" in kda.kda_last_error()
+    assert call(commit_len=FAKE) == 1  # commit_len without commit_pool
+    assert call(commit_len=ctypes.c_void_p(0x50000000), commit_pool=ctypes.c_void_p(0x20000000 + 65536)) == 1
+    assert call(o_=ctypes.c_void_p(0x20000000)) == 1  # o overlaps the state pool
+    assert call(B=0) == 0  # nothing to do
+
+
+def test_fold_rejects_bad_arguments():
+    L = kda.lib()
+    pool, slots, acc = ctypes.c_void_p(0x20000000), ctypes.c_void_p(0x30000000), ctypes.c_void_p(0x31000000)
+    r16 = _ring(16)
+    assert L.kda_replay_fold(2, 2, 3, 4, pool, slots, None, None, acc, None) == 1
+    assert L.kda_replay_fold(2, 2, 3, 4, pool, slots, ctypes.byref(_ring(6)), None, acc, None) == 1
+    assert L.kda_replay_fold(2, 2, 3, 4, pool, None, ctypes.byref(r16), None, acc, None) == 1
+    assert L.kda_replay_fold(2, 2, 3, 4, pool, slots, ctypes.byref(r16), None, None, None) == 1
+    assert L.kda_replay_fold(2, 0, 3, 4, pool, slots, ctypes.byref(r16), None, acc, None) == 1
+    # state pool overlapping the ring
+    assert L.kda_replay_fold(2, 2, 3, 4, ctypes.c_void_p(0xC000000), slots, ctypes.byref(r16), None, acc, None) == 1
+    assert L.kda_replay_fold(0, 2, 3, 4, pool, slots, ctypes.byref(r16), None, acc, None) == 0
+
+
+def test_binding_checks_shapes_without_device():
+    import torch
+
+    p = kda.kda_plan_create([0, 64], n_heads=1)
+    x = torch.zeros((64, 1, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        kda.kda_chunk_prefill(p, x, x, x, x.float(), torch.zeros((64, 1)), torch.zeros((1, 1, 128, 128)),
+                              torch.zeros((64, 1, 128)), torch.zeros(kda.kda_plan_workspace_bytes(p), dtype=torch.uint8))

@@ -1,0 +1,291 @@
+"""GPU parity on small shapes that still span several chunks, ragged tails and
+every edge case; all calls go through the C ABI (libkda.so)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import synth.gpu as sg
+import linear_attention_recurrence_amd as kda
+from kda_ref import TOL, block_err, log, oracle_prefill_unit
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def np_(t):
+    return t.detach().cpu().numpy()
+
+
+def bits(t):
+    return t.detach().cpu().contiguous().view(torch.int16 if t.element_size() == 2 else torch.int32).numpy()
+
+
+# ---------------------------------------------------------------- generator
+@pytest.mark.parametrize("kind,dtype,row_len", [
+    (synth.NORMAL, torch.float32, 128), (synth.NORMAL, torch.bfloat16, 128), (synth.UNIT_ROW, torch.bfloat16, 128),
+    (synth.UNIT_ROW, torch.float32, 128), (synth.NEG_SOFTPLUS, torch.float32, 128), (synth.SIGMOID, torch.float32, 1),
+    (synth.NORMAL, torch.float64, 128)])
+def test_generator_device_matches_host(gpu, kind, dtype, row_len):
+    log(f"generator kind={kind} dtype={dtype}")
+    n_rows, start, step = 3000, 17, 3
+    t = torch.empty(n_rows * row_len, dtype=dtype, device=DEV)
+    sg.fill(t, 77, 5, 2, kind, row_start=start, row_step=step, row_len=row_len, scale=0.3)
+    hd = {torch.float32: synth.F32, torch.bfloat16: synth.BF16, torch.float64: synth.F64}[dtype]
+    h = synth.rows(77, 5, 2, kind, hd, start, step, n_rows, row_len, 0.3).ravel()
+    if dtype == torch.bfloat16:
+        assert np.array_equal(bits(t).view(np.uint16), h)
+    else:
+        assert np.array_equal(np_(t).view(np.uint64 if dtype == torch.float64 else np.uint32),
+                              h.view(np.uint64 if dtype == torch.float64 else np.uint32))
+
+
+# ---------------------------------------------------------------- verify and fold
+def make_verify_case(seed, B, T, H, L, S, R):
+    g = torch.Generator().manual_seed(seed)
+    slot_idx = torch.randperm(S, generator=g)[:B].to(torch.int32)
+    pool = sg.states(seed, S * L * H, DEV).view(S, L, H, 128, 128)
+    ins = [sg.prefill_inputs(seed, B * T, H, DEV, sub=l) for l in range(L)]
+    ring_start = torch.randint(0, 4 * R, (B,), generator=g, dtype=torch.int32)
+    return slot_idx, pool, ins, ring_start
+
+
+def host_inputs(seed, B, T, H, l, b, h):
+    q, k, v, gk, beta = synth.prefill_rows(seed, H, b * T, T, h=h, sub=l)
+    return q, k, v, gk, beta
+
+
+def test_verify_and_fold_small(gpu):
+    seed, B, T, H, L, S, R = 31, 3, 5, 2, 2, 6, 16
+    log("verify/fold small")
+    slot_idx, pool, ins, ring_start = make_verify_case(seed, B, T, H, L, S, R)
+    commit_len = torch.tensor([2, 5, 0], dtype=torch.int32)
+    pool0 = pool.clone()
+    ring = kda.Ring.empty(S, L, H, R, DEV)
+    for buf in (ring.k, ring.v):
+        buf.view(torch.int16).fill_(0x7FC1)  # sentinel bit pattern
+    ring.gk.fill_(-7.0)
+    ring.beta.fill_(-7.0)
+    commit = torch.full_like(pool, -3.0)
+    outs = []
+    for l in range(L):
+        q, k, v, gk, beta = ins[l]
+        o = torch.empty((B * T, H, 128), device=DEV)
+        kda.kda_verify(q, k, v, gk, beta, pool, slot_idx.to(DEV), o, layer=l, n_tok=T, ring=ring,
+                       ring_start=ring_start.to(DEV), commit_len=commit_len.to(DEV), commit_pool=commit, scale=0.6)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(pool, pool0), "verify wrote the committed state"
+    rb = {n: np_(x) if x.dtype != torch.bfloat16 else bits(x).view(np.uint16)
+          for n, x in (("k", ring.k), ("v", ring.v), ("gk", ring.gk), ("beta", ring.beta))}
+    worst = 0.0
+    for l in range(L):
+        o = np_(outs[l]).reshape(B, T, H, 128)
+        for b in range(B):
+            s = int(slot_idx[b])
+            for h in range(H):
+                q, k, v, gk, beta = host_inputs(seed, B, T, H, l, b, h)
+                S0 = np_(pool0[s, l, h])
+                c = int(commit_len[b])
+                o_ref, Sc_ref, _ = oracle.verify(q, k, v, gk, beta, S0, scale=0.6, commit_len=c)
+                worst = max(worst, block_err(o[b, :, h], o_ref))
+                if c > 0:
+                    worst = max(worst, block_err(np_(commit[s, l, h]), Sc_ref))
+                # the ring holds the raw inputs, bit for bit, at (start + t) & (R - 1); other slots untouched
+                pos = [(int(ring_start[b]) + t) & (R - 1) for t in range(T)]
+                assert np.array_equal(rb["k"][s, l, h, pos], k) and np.array_equal(rb["v"][s, l, h, pos], v)
+                assert np.array_equal(rb["gk"][s, l, h, pos], gk) and np.array_equal(rb["beta"][s, l, h, pos], beta)
+                other = [p for p in range(R) if p not in pos]
+                assert np.all(rb["gk"][s, l, h, other] == -7.0)
+    unused = [s for s in range(S) if s not in slot_idx.tolist()]
+    assert torch.all(commit[unused] == -3.0)
+    b0 = int((commit_len == 0).nonzero()[0])
+    assert torch.all(commit[int(slot_idx[b0])] == -3.0), "commit_len 0 must not write"
+    log(f"verify small worst err {worst:.2e}")
+    assert worst <= TOL
+
+    # fold with the same accepted lengths == verify's commit, bit for bit
+    acc = commit_len.clone()
+    folded = pool0.clone()
+    # poison every ring entry past the accepted prefix: the fold must never read it
+    for b in range(B):
+        s = int(slot_idx[b])
+        for t in range(int(acc[b]), R):
+            p = (int(ring_start[b]) + t) & (R - 1)
+            ring.gk[s, :, :, p] = float("nan")
+            ring.beta[s, :, :, p] = float("nan")
+    kda.kda_replay_fold(folded, slot_idx.to(DEV), ring, acc.to(DEV), ring_start=ring_start.to(DEV))
+    torch.cuda.synchronize()
+    for b in range(B):
+        s = int(slot_idx[b])
+        if int(acc[b]) > 0:
+            assert torch.equal(folded[s], commit[s]), f"fold differs from verify commit for request {b}"
+        else:
+            assert torch.equal(folded[s], pool0[s])
+    for s in range(S):
+        if s not in slot_idx.tolist():
+            assert torch.equal(folded[s], pool0[s])
+
+
+@pytest.mark.parametrize("T,accs", [(8, [1, 2, 3, 4, 5, 6, 7, 8]), (1, [1, 0, 1, 1, 0, 1, 1, 0])])
+def test_fold_bitexact_every_length(gpu, T, accs):
+    seed, H, L, R = 40 + T, 3, 3, 16
+    B = S = len(accs)
+    log(f"fold bit-exact T={T}")
+    slot_idx, pool, ins, ring_start = make_verify_case(seed, B, T, H, L, S, R)
+    acc = torch.tensor(accs, dtype=torch.int32, device=DEV)
+    ring = kda.Ring.empty(S, L, H, R, DEV)
+    commit = pool.clone()
+    for l in range(L):
+        q, k, v, gk, beta = ins[l]
+        o = torch.empty((B * T, H, 128), device=DEV)
+        kda.kda_verify(q, k, v, gk, beta, pool, slot_idx.to(DEV), o, layer=l, n_tok=T, ring=ring,
+                       ring_start=ring_start.to(DEV), commit_len=acc, commit_pool=commit)
+    folded = pool.clone()
+    kda.kda_replay_fold(folded, slot_idx.to(DEV), ring, acc, ring_start=ring_start.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(folded, commit)
+    # against the oracle on a few units
+    worst = 0.0
+    for b in range(min(B, 3)):
+        s = int(slot_idx[b])
+        for l in range(L):
+            q, k, v, gk, beta = host_inputs(seed, B, T, H, l, b, 1)
+            n = int(acc[b])
+            S_ref = oracle.fold(n, k, v, gk, beta, np.array(np_(pool[s, l, 1]), dtype=np.float64))
+            worst = max(worst, block_err(np_(folded[s, l, 1]), S_ref))
+    assert worst <= TOL
+
+
+def test_verify_fp32_inputs_config0(gpu):
+    """Single sequence, 1 head, T = 64, fp32 everything, zero initial state (token-by-token path)."""
+    log("config 0 verify fp32")
+    T, H = 64, 1
+    q, k, v, gk, beta = sg.prefill_inputs(0, T, H, DEV, qkv_dtype=torch.float32)
+    pool = torch.zeros((1, 1, H, 128, 128), device=DEV)
+    commit = torch.empty_like(pool)
+    o = torch.empty((T, H, 128), device=DEV)
+    kda.kda_verify(q, k, v, gk, beta, pool, torch.zeros(1, dtype=torch.int32, device=DEV), o, layer=0, n_tok=T,
+                   commit_len=torch.tensor([T], dtype=torch.int32, device=DEV), commit_pool=commit)
+    torch.cuda.synchronize()
+    hq, hk, hv, hg, hb = synth.prefill_rows(0, H, 0, T, h=0, qkv_dtype=synth.F32)
+    o_ref, S_ref, _, _ = oracle.recurrent(hq, hk, hv, hg, hb)
+    e_o, e_s = block_err(np_(o[:, 0]), o_ref), block_err(np_(commit[0, 0, 0]), S_ref)
+    log(f"config 0 fp32 verify: o {e_o:.2e} state {e_s:.2e}")
+    assert e_o <= TOL and e_s <= TOL
+
+
+# ---------------------------------------------------------------- chunked prefill
+def run_prefill(plan, ins, state_in=None, snap_slots=0, scale=1.0, flags=0, state_out=None, order_ws=None):
+    q, k, v, gk, beta = ins
+    N, H = plan.n_seq, plan.n_heads
+    o = torch.full((plan.total_tokens, H, 128), float("nan"), device=DEV)
+    if state_out is None:
+        state_out = torch.empty((N, H, 128, 128), device=DEV)
+    snap = torch.full((N, snap_slots, H, 128, 128), -5.0, device=DEV) if snap_slots else None
+    cnt = torch.full((N,), -1, dtype=torch.int32, device=DEV)
+    ws = order_ws if order_ws is not None else torch.empty(kda.kda_plan_workspace_bytes(plan), dtype=torch.uint8,
+                                                           device=DEV)
+    kda.kda_chunk_prefill(plan, q, k, v, gk, beta, state_out, o, ws, state_in=state_in, snap=snap,
+                          snap_slots=snap_slots, snap_count=cnt, scale=scale, flags=flags)
+    return o, state_out, snap, cnt
+
+
+def check_prefill(seed, plan, lens, H, o, st, snap, cnt, S0=None, scale=1.0, snap_slots=0, units=None):
+    cu = plan.cu_seqlens
+    worst = {"o": 0.0, "state": 0.0, "snap": 0.0}
+    units = units if units is not None else [(n, h) for n in range(len(lens)) for h in range(H)]
+    o_np, st_np = np_(o), np_(st)
+    snap_np = np_(snap) if snap is not None else None
+    for n, h in units:
+        L = int(lens[n])
+        s0 = None if S0 is None else S0[n, h]
+        o_ref, S_ref, snaps_ref, c = oracle_prefill_unit(seed, H, int(cu[n]), L, h, S0=s0, scale=scale,
+                                                         snap_interval=plan.snap_interval if snap_slots else 0,
+                                                         snap_slots=snap_slots)
+        if L > 0:
+            worst["o"] = max(worst["o"], block_err(o_np[cu[n]:cu[n + 1], h], o_ref))
+        worst["state"] = max(worst["state"], block_err(st_np[n, h], S_ref))
+        if snap_slots:
+            assert int(cnt[n]) == c
+            for m in range(1, c + 1)[-snap_slots:]:
+                sl = (m - 1) % snap_slots
+                # the slot holds the latest snapshot written to it
+                worst["snap"] = max(worst["snap"], block_err(snap_np[n, sl, h], snaps_ref[sl]))
+    return worst
+
+
+def test_prefill_ragged_small(gpu):
+    seed, H = 11, 3
+    lens = np.array([1, 31, 33, 100, 0, 257, 64])
+    cu = synth.cu_seqlens(lens)
+    log(f"prefill ragged lens={lens.tolist()}")
+    plan = kda.kda_plan_create(cu, n_heads=H, snap_interval=64)
+    ins = sg.prefill_inputs(seed, int(cu[-1]), H, DEV)
+    S0 = sg.states(seed, len(lens) * H, DEV).view(len(lens), H, 128, 128)
+    o, st, snap, cnt = run_prefill(plan, ins, state_in=S0, snap_slots=2, scale=0.75)
+    torch.cuda.synchronize()
+    S0n = np_(S0)
+    w = check_prefill(seed, plan, lens, H, o, st, snap, cnt, S0=S0n, scale=0.75, snap_slots=2)
+    log(f"prefill ragged worst {w}")
+    assert max(w.values()) <= TOL
+    # sequences of length 0 keep their state
+    assert torch.equal(st[4], S0[4])
+    assert not torch.isnan(o).any()
+
+
+def test_prefill_config0_bf16(gpu):
+    """Config 0 through the chunked path on bf16-rounded q/k/v (the same draws)."""
+    lens = np.array([64])
+    plan = kda.kda_plan_create(synth.cu_seqlens(lens), n_heads=1)
+    ins = sg.prefill_inputs(0, 64, 1, DEV)
+    o, st, _, cnt = run_prefill(plan, ins)
+    torch.cuda.synchronize()
+    w = check_prefill(0, plan, lens, 1, o, st, None, cnt)
+    log(f"config 0 chunked: {w}")
+    assert max(w.values()) <= TOL
+
+
+def test_prefill_exactness_properties(gpu):
+    """NULL state_in == zeros; in place; run-to-run and LPT/FIFO determinism; resident
+    work list reuse; a snapshot restores a chunk-aligned continuation bit for bit."""
+    seed, H = 12, 2
+    lens = np.array([96, 160, 7, 128])
+    cu = synth.cu_seqlens(lens)
+    N = len(lens)
+    ins = sg.prefill_inputs(seed, int(cu[-1]), H, DEV)
+    plan = kda.kda_plan_create(cu, n_heads=H, snap_interval=64)
+    o1, st1, sn1, _ = run_prefill(plan, ins, snap_slots=2)
+    zeros = torch.zeros((N, H, 128, 128), device=DEV)
+    o2, st2, _, _ = run_prefill(plan, ins, state_in=zeros, snap_slots=2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(st1, st2)
+    # in place
+    S0 = sg.states(seed, N * H, DEV).view(N, H, 128, 128)
+    o3, st3, _, _ = run_prefill(plan, ins, state_in=S0.clone(), snap_slots=2)
+    inplace = S0.clone()
+    o4, st4, _, _ = run_prefill(plan, ins, state_in=inplace, state_out=inplace, snap_slots=2)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o4) and torch.equal(st3, inplace)
+    # FIFO order and a resident work list give the same bits
+    fifo = kda.kda_plan_create(cu, n_heads=H, snap_interval=64, order=kda.KDA_PLAN_FIFO)
+    o5, st5, _, _ = run_prefill(fifo, ins, snap_slots=2)
+    ws = torch.empty(kda.kda_plan_workspace_bytes(plan), dtype=torch.uint8, device=DEV)
+    kda.kda_plan_upload(plan, ws)
+    for _ in range(3):
+        o6, st6, _, _ = run_prefill(plan, ins, snap_slots=2, flags=kda.KDA_PREFILL_PLAN_RESIDENT, order_ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o6, o1) and torch.equal(st6, st1)
+    assert torch.equal(o5, o1) and torch.equal(st5, st1)
+    # restore: sequence 1 (160 tokens) from its snapshot at 128 continues identically
+    sub_cu = np.array([0, 32], dtype=np.int32)
+    sub = kda.kda_plan_create(sub_cu, n_heads=H)
+    t0 = int(cu[1]) + 128
+    sub_ins = tuple(x[t0:t0 + 32].contiguous() for x in ins)
+    restored = sn1[1, 1].unsqueeze(0).contiguous()  # 128 = 2 * 64 -> slot (2 - 1) % 2 = 1
+    o7, st7, _, _ = run_prefill(sub, sub_ins, state_in=restored)
+    torch.cuda.synchronize()
+    assert torch.equal(st7[0], st1[1]), "restored snapshot did not continue bit for bit"
+    assert torch.equal(o7, o1[t0:t0 + 32])
