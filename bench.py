@@ -1,0 +1,240 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+Headline (``value``): chunked-prefill throughput in tokens*heads/s on the
+workload "4 sequences x 2048 tokens, H = 64, K = V = 128, bf16 q/k/v, fp32
+gk/beta/state, state_in ~ N(0, 0.1^2)". One step = one kda_chunk_prefill call
+with the work list resident (one persistent-kernel launch), timed with HIP
+events on the launch stream. Beside it, in the same JSON line:
+
+* ``verify_fold``: one speculative step of the workload "256 requests x 69
+  layers x 8 heads, gamma + 1 = 8 bf16 draft tokens, ring length 16, accepted
+  lengths geometric (mean 2.7, clipped to [1, 8])" = 69 kda_verify launches +
+  one kda_replay_fold launch, in us/step (committed states restored from a
+  pristine copy outside the timed region before every step);
+* ``roofline``: HBM roofline of the prefill kernel (algorithmic bytes per
+  launch / measured launch time, against 8 TB/s);
+* ``cpu_baseline``: the fp64 oracle (token-by-token) timed on this host's
+  cores over the same prefill workload.
+
+Inputs are synthetic, generated on the device by the seeded generator.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+METRIC = "KDA prefill tokens*heads/s and verify+fold us/step at 1 GPU; % of roofline"
+
+# traffic measured by rocprofv3 PMC (FETCH_SIZE + WRITE_SIZE), per launch, scaled by the copy-kernel
+# calibration; None until measured for the current kernel
+PREFILL_TRAFFIC_BYTES = None
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--vf-steps", type=int, default=5, help="timed verify+fold steps")
+    ap.add_argument("--no-verify-fold", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="time only the prefill (for profilers)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def prefill_bytes(n_seq, L, H, with_state_in=True):
+    """Algorithmic HBM bytes of one prefill launch: per token*head q,k,v bf16 (3*256) + gk fp32 (512)
+    + beta (4) + o fp32 (512) = 1,796 B; per (sequence, head) 64 KiB state out (+ 64 KiB in)."""
+    th = n_seq * L * H
+    st = n_seq * H * 65536 * (2 if with_state_in else 1)
+    return th * 1796 + st
+
+
+def bench_prefill(args, torch, kda, sg, synth):
+    dev = "cuda:0"
+    N, L, H = 4, 2048, 64
+    cfg = synth.PREFILL_CONFIGS[1]
+    seed = cfg["seed"]
+    cu = synth.cu_seqlens([L] * N)
+    T = int(cu[-1])
+    q, k, v, gk, beta = sg.prefill_inputs(seed, T, H, dev)
+    S0 = sg.states(seed, N * H, dev).view(N, H, 128, 128)
+    o = torch.empty((T, H, 128), device=dev)
+    st = torch.empty((N, H, 128, 128), device=dev)
+    plan = kda.kda_plan_create(cu, n_heads=H)
+    ws = torch.empty(kda.kda_plan_workspace_bytes(plan), dtype=torch.uint8, device=dev)
+    kda.kda_plan_upload(plan, ws)
+    flags = kda.KDA_PREFILL_PLAN_RESIDENT
+
+    def step():
+        kda.kda_chunk_prefill(plan, q, k, v, gk, beta, st, o, ws, state_in=S0, flags=flags)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tokens_heads = N * L * H
+    byts = prefill_bytes(N, L, H)
+    achieved = byts / (ms * 1e-3) / 1e9
+    res = dict(ms=ms, value=tokens_heads / (ms * 1e-3), bytes=byts, achieved=achieved, N=N, L=L, H=H)
+    del q, k, v, gk, beta, o, st, S0
+    return res
+
+
+def bench_verify_fold(args, torch, kda, sg, synth):
+    dev = "cuda:0"
+    c = synth.VERIFY_CONFIG
+    seed, B, Lyr, H, T, R = c["seed"], c["B"], c["L"], c["H"], c["T"], c["R"]
+    S = B
+    pool = sg.states(seed, S * Lyr * H, dev).view(S, Lyr, H, 128, 128)
+    pristine = pool.clone()
+    ring = kda.Ring.empty(S, Lyr, H, R, dev)
+    ins = [sg.prefill_inputs(seed, B * T, H, dev, sub=l) for l in range(Lyr)]
+    slot_idx = torch.arange(B, dtype=torch.int32, device=dev)
+    ring_start = torch.zeros(B, dtype=torch.int32, device=dev)
+    acc = torch.from_numpy(synth.geometric_accept(seed, B)).to(torch.int32).to(dev)
+    o = torch.empty((B * T, H, 128), device=dev)
+    stream = torch.cuda.current_stream()
+
+    def one_step(times):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        for l in range(Lyr):
+            q, k, v, gk, beta = ins[l]
+            kda.kda_verify(q, k, v, gk, beta, pool, slot_idx, o, layer=l, n_tok=T, ring=ring, ring_start=ring_start)
+        ev[1].record(stream)
+        kda.kda_replay_fold(pool, slot_idx, ring, acc, ring_start=ring_start)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        if times is not None:
+            times.append((ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])))
+
+    for _ in range(max(1, args.warmup // 2)):
+        pool.copy_(pristine)
+        one_step(None)
+    times = []
+    for _ in range(args.vf_steps):
+        pool.copy_(pristine)  # the fold advances states in place: restore outside the timed region
+        torch.cuda.synchronize()
+        one_step(times)
+    ver = sum(t[0] for t in times) / len(times)
+    fol = sum(t[1] for t in times) / len(times)
+    units = S * Lyr * H
+    acc_mean = float(acc.float().mean())
+    v_bytes = units * (65536 + T * (768 + 512 + 4 + 512 + 1028))  # state + inputs + o + ring entries
+    f_bytes = units * (2 * 65536) + int(round(float(acc.float().sum()) * Lyr * H * 1028))
+    res = dict(verify_ms=ver, fold_ms=fol, accept_mean=acc_mean,
+               verify_gbs=v_bytes / (ver * 1e-3) / 1e9, fold_gbs=f_bytes / (fol * 1e-3) / 1e9,
+               verify_bytes=v_bytes, fold_bytes=f_bytes)
+    del pool, pristine, ring, ins, o
+    return res
+
+
+def cpu_baseline(synth, oracle):
+    """The fp64 oracle, as it is, on this host's cores: every (sequence, head) unit of the
+    prefill workload (4 x 2048 tokens x 64 heads). Input generation is not timed."""
+    N, L, H = 4, 2048, 64
+    seed = synth.PREFILL_CONFIGS[1]["seed"]
+    threads = min(16, os.cpu_count() or 1)
+    units = [(n, h) for n in range(N) for h in range(H)]
+    data = {}
+    for n, h in units:
+        q, k, v, gk, beta = synth.prefill_rows(seed, H, n * L, L, h=h)
+        S0 = synth.state_rows(seed, n * H + h, 1)[0]
+        data[(n, h)] = (oracle.f64(q), oracle.f64(k), oracle.f64(v), oracle.f64(gk), oracle.f64(beta), S0)
+
+    def run(u):
+        q, k, v, gk, beta, S0 = data[u]
+        oracle.recurrent(q, k, v, gk, beta, S0)
+
+    t0 = time.perf_counter()
+    oracle.run_parallel(run, units, threads=threads)
+    dt = time.perf_counter() - t0
+    return dict(value=N * L * H / dt, unit="tokens*heads/s", cores=threads, kind="oracle",
+                sample=f"full workload: {N} x {L} tokens x {H} heads (fp64 token-by-token), {dt:.2f} s wall")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
+              f"(the kernels need no collectives: see the sharding paragraph of DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import linear_attention_recurrence_amd as kda
+    import synth
+    import synth.gpu as sg
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.init()
+    log("prefill: generating inputs and timing")
+    pf = bench_prefill(args, torch, kda, sg, synth)
+    log(f"prefill: {pf['ms'] * 1e3:.1f} us/launch, {pf['achieved']:.0f} GB/s")
+    vf = None
+    if not (args.no_verify_fold or args.prefill_only):
+        log("verify+fold: generating inputs and timing")
+        vf = bench_verify_fold(args, torch, kda, sg, synth)
+        log(f"verify+fold: {vf['verify_ms'] * 1e3:.0f} + {vf['fold_ms'] * 1e3:.0f} us")
+    cpu = None
+    if not (args.no_cpu_baseline or args.prefill_only):
+        import oracle
+
+        log("cpu baseline: fp64 oracle on host cores")
+        cpu = cpu_baseline(synth, oracle)
+    traffic = PREFILL_TRAFFIC_BYTES
+    line = {
+        "metric": METRIC,
+        "value": pf["value"],
+        "unit": "tokens*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pf["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "chunked prefill: 4 sequences x 2048 tokens, H=64, K=V=128, bf16 q/k/v, "
+                               "fp32 gk/beta/state, state_in N(0,0.1^2), chunk 32, one persistent launch",
+                   "n_seq": pf["N"], "seq_len": pf["L"], "heads": pf["H"], "head_dim": 128},
+        "roofline": {"bound": "hbm", "achieved": pf["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": pf["achieved"] / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "kda::prefill_kernel", "algorithmic_bytes_per_launch": pf["bytes"]},
+        "cpu_baseline": cpu,
+    }
+    if vf is not None:
+        line["verify_fold"] = {
+            "us_per_step": (vf["verify_ms"] + vf["fold_ms"]) * 1e3,
+            "verify_us": vf["verify_ms"] * 1e3, "fold_us": vf["fold_ms"] * 1e3,
+            "verify_hbm_frac": vf["verify_gbs"] / HBM_PEAK_GBS, "fold_hbm_frac": vf["fold_gbs"] / HBM_PEAK_GBS,
+            "verify_gbs": vf["verify_gbs"], "fold_gbs": vf["fold_gbs"], "accept_mean": vf["accept_mean"],
+            "workload": "256 requests x 69 layers x 8 heads, gamma+1=8 bf16 draft tokens, fp32 committed state, "
+                        "ring length 16, accepted lengths geometric mean 2.7 clipped to [1,8]; 69 verify + 1 fold",
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
