@@ -11,99 +11,171 @@
 //
 // Algebra (the chunked form of the token recurrence; C = 32 tokens, chunk
 // start state S0, G_t = sum_{tau<=t} gk_tau inside the chunk):
-//   A[i][j] = beta_i sum_c k_ic k_jc e^{G_ic - G_jc}  (j < i)
-//   P[t][i] =        sum_c q_tc k_ic e^{G_tc - G_ic}  (i <= t)
-//   X = (I + A)^-1,  R = diag(beta) (V - Kt S0),  W = X R      (Kt = k e^G)
-//   O = scale (Qt S0 + P W)                                     (Qt = q e^G)
-//   S_end = diag(e^{G_last}) S0 + K'^T W                        (K' = k e^{G_last - G})
-// The chunk is two 16-token blocks. Factors e^{G_t - G_j} are split into a
-// row factor times a column factor around an anchor inside [j, t] so that
-// neither overflows: the anchor is the last token of block 0 for the
-// off-diagonal block (both factors <= 1) and the block's 8th token for a
-// diagonal block (factors span at most 8 tokens; gk >= -10 keeps them finite).
-// All factors are built from prefix/suffix products of a = exp(gk).
+//   A[i][j] = beta_i sum_c Rk_ic Ck_jc     (j < i)   Rk = k e^{G - G_15}, Ck = k e^{G_15 - G}
+//   P[t][i] =        sum_c Rq_tc Ck_ic     (i <= t)  Rq = q e^{G - G_15}
+//   X = (I + A)^-1,   R = diag(beta) (V - Kt S0),   W = X R       Kt = k e^G
+//   O = scale (Qt S0 + P W)                                       Qt = q e^G
+//   S_end = e^{G_31} S0 + K'^T W                                  K' = k e^{G_31 - G}
+// The intra-chunk factors are anchored at token 15 so each spans at most 16
+// tokens of decay; every factor is a product of a = exp(gk) over such a
+// span or its reciprocal, which stays in fp32/bf16 range when gk >= -5 (the
+// documented precondition of this path). The factors of Kt, Qt, K' are <= 1.
 //
-// Precision: MFMA operands are bf16. Products whose operands' rounding shows
-// at the output (the intra-chunk factors of P and A's column side, P, R, W,
-// Qt, K' and the state in Qt S0) use a hi + lo bf16 pair and 2-3 MFMAs;
-// Kt, X and the state in Kt S0 are single bf16.
+// Precision (chosen by measuring each operand's rounding against the fp64
+// oracle): the intra-chunk factors Rq and Ck enter their MFMAs as bf16 hi + lo
+// pairs (Rk single), because their range needs bf16; every product that
+// touches the state uses fp16 operands (11-bit significand), with R and W as
+// fp16 hi + lo pairs. All accumulation is fp32 and the state stays fp32.
 //
 // Work decomposition: one 256-thread workgroup (4 waves) per (sequence, head)
 // item, persistent, pulling items from a longest-first list with an atomic
 // counter. Wave w owns value columns [32w, 32w+32); its 128x32 slice of the
-// fp32 state lives in MFMA accumulator registers for the whole sequence.
-// The accumulator layout (lane holds rows 4*(l/16)+r of a 16x16 tile) is fed
-// straight back as the B operand of the next products by permuting the
-// reduction index the same way in both operands.
+// fp32 state lives in MFMA accumulator registers for the whole sequence and
+// is fed back as the B operand of the next products by permuting the
+// reduction index identically in both operands. Raw inputs of the next chunk
+// stream into LDS with direct global->LDS loads while the current chunk
+// computes; operands that a product needs transposed are read with the
+// transposing LDS load (ds_read_b64_tr_b16) instead of being stored twice.
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
 constexpr int C = 32;     // chunk length
-constexpr int TM = 136;   // token-major row stride in bf16 (128 + 8 pad)
-constexpr int CMS = 40;   // channel-major row stride in bf16 (32 + 8 pad)
-constexpr int SQ = 40;    // 32x32 bf16 matrices
-constexpr int ATS = 36;   // fp32 32x32 matrices
+constexpr int TM = 136;   // token-major row stride (16-bit elements; 128 + 8 pad)
+constexpr int SQ = 40;    // 32x32 16-bit matrices
+constexpr int ATS = 36;   // 32x32 fp32 matrices
+
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct PrefillLds {
-  uint16_t kxd[C][TM];                  // k * X'  (diagonal-block row factor of A)
-  uint16_t kyd_h[C][TM], kyd_l[C][TM];  // k * Y'  (diagonal-block column factor of A and P)
-  uint16_t qxd_h[C][TM], qxd_l[C][TM];  // q * X'  (diagonal-block row factor of P)
-  uint16_t qt_h[C][TM], qt_l[C][TM];    // q * e^G
-  uint16_t kt[C][TM];                   // k * e^G
-  uint16_t kxo[16][TM];                 // block-1 rows: k * e^{G_t - G_15}
-  uint16_t qxo_h[16][TM], qxo_l[16][TM];
-  uint16_t kyo_h[16][TM], kyo_l[16][TM];  // block-0 rows: k * e^{G_15 - G_j}
-  uint16_t kp_h[D][CMS], kp_l[D][CMS];    // K'^T (channel-major)
-  uint16_t vt[D][CMS];                    // V^T (channel-major)
-  float at[C][ATS];                       // A transposed: at[j][i] = A[i][j]
-  float xf[C][ATS];                       // X in fp32 (the (0,1) block is scratch)
-  uint16_t xb[C][SQ];                     // X in bf16, rows t, columns j
-  uint16_t p_h[C][SQ], p_l[C][SQ];        // P hi/lo, rows t, columns i
+  // operands of the current chunk, token-major [t][c]
+  uint16_t qt[C][TM];                  // fp16  q e^G
+  uint16_t kt[C][TM];                  // fp16  k e^G
+  uint16_t kp[C][TM];                  // fp16  k e^{G_31 - G}
+  uint16_t vt[C][TM];                  // bf16  v (copy out of the staging area)
+  float part[4][6][16][20];            // per-wave partial A and P tiles over 32 channels, [col][row] (padded)
+  float at[C][ATS];                    // A transposed: at[j][i] = A[i][j]
+  float xf[C][ATS];                    // diagonal blocks of X, fp32
+  uint16_t xb[C][SQ];                  // fp16 X, rows t, columns j
+  uint16_t pm[C][SQ];                  // fp16 P, rows t, columns i
   float beta[C];
-  float dec[D];     // e^{G_last} per key channel
-  float dex[2][D];  // per-block decay totals
+  float dlast[D];                      // e^{G_31} per key channel
+  float so[C][D];                      // output tile of the previous chunk, flushed as whole rows
   int item;
 };
 
-__device__ __forceinline__ uint4 lds16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 lds8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ uint4 lds16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// B operand from two accumulator tiles (rows 4g+r of tile 0, then of tile 1)
-__device__ __forceinline__ bf16x8 round8(const f32x4& a, const f32x4& b) {
-  bf16x8 r;
-  r[0] = (__bf16)a[0]; r[1] = (__bf16)a[1]; r[2] = (__bf16)a[2]; r[3] = (__bf16)a[3];
-  r[4] = (__bf16)b[0]; r[5] = (__bf16)b[1]; r[6] = (__bf16)b[2]; r[7] = (__bf16)b[3];
+// 16 (or 4) bytes per lane from global memory into LDS at lds_base + size * lane
+// (lds_base wave-uniform). Written as inline assembly on purpose: the compiler
+// would otherwise make every later LDS read wait for these asynchronous
+// writes, which turns the one-chunk-ahead prefetch into a synchronous load.
+// The kernel orders them itself: s_waitcnt vmcnt(0) plus a barrier before the
+// staging area is read. M0 is used by nothing else in this kernel.
+__device__ __forceinline__ void g2l(const void* src, void* lds_base, int bytes) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_base);
+  if (bytes == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(src) : "memory");
+}
+
+// transposing read: within each 16-lane group, lane j gets element r from the
+// 4-element row chunk that lane 4r + j/4 points at, position j % 4
+__device__ __forceinline__ uint2 lds_tr(const uint16_t* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
+}
+
+__device__ __forceinline__ f32x4 mfma_h(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x8 as_f16x8(uint2 a, uint2 b) {
+  return __builtin_bit_cast(f16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+// permuted A operand of a 32-wide reduction step: row elements {4g..4g+3} then {16+4g..16+4g+3}
+__device__ __forceinline__ f16x8 perm_h(const uint16_t* row, int g) { return as_f16x8(lds8(row + 4 * g), lds8(row + 16 + 4 * g)); }
+
+// B operand from two accumulator tiles (rows 4g+r of tile 0, then of tile 1): fp16, and hi/lo
+__device__ __forceinline__ f16x8 to_h8(const f32x4& a, const f32x4& b) {
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { r[i] = (_Float16)a[i]; r[4 + i] = (_Float16)b[i]; }
   return r;
 }
-__device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
-  hi = round8(a, b);
+__device__ __forceinline__ void split_h8(const f32x4& a, const f32x4& b, f16x8& hi, f16x8& lo) {
+  hi = to_h8(a, b);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    lo[i] = (__bf16)(a[i] - (float)hi[i]);
-    lo[4 + i] = (__bf16)(b[i] - (float)hi[4 + i]);
+    lo[i] = (_Float16)(a[i] - (float)hi[i]);
+    lo[4 + i] = (_Float16)(b[i] - (float)hi[4 + i]);
   }
 }
 
-// permuted A operand: row m, reduction positions {4g..4g+3} then {16+4g..16+4g+3} of a 32-wide step
-__device__ __forceinline__ bf16x8 perm_a(const uint16_t* row, int g) { return as_bf16x8(lds8(row + 4 * g), lds8(row + 16 + 4 * g)); }
+#define KDA_ROW_SHR(v, s) __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(v), 0x110 + (s), 0xf, 0xf, false))
+#define KDA_ROW_BCAST15(v) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x15F, 0xf, 0xf, false))
+
+// inclusive prefix product over the 16 lanes of a DPP row (lane order = token order)
+__device__ __forceinline__ float row_scan_mul(float v) {
+  v = v * KDA_ROW_SHR(v, 1);
+  v = v * KDA_ROW_SHR(v, 2);
+  v = v * KDA_ROW_SHR(v, 4);
+  v = v * KDA_ROW_SHR(v, 8);
+  return v;
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4& u, float (&f)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { f[2 * i] = bf2f(w[i] & 0xffffu); f[2 * i + 1] = bf2f(w[i] >> 16); }
+}
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) { return pack2(f2bf(a), f2bf(b)); }
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+  return pack2(__builtin_bit_cast(uint16_t, (_Float16)a), __builtin_bit_cast(uint16_t, (_Float16)b));
+}
+// 8 products written as one 16-byte row chunk: bf16, bf16 hi/lo, or fp16
+__device__ __forceinline__ void put_bf16(uint16_t* dst, const float (&x)[8]) {
+  *reinterpret_cast<uint4*>(dst) = make_uint4(pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3]), pk_bf16(x[4], x[5]), pk_bf16(x[6], x[7]));
+}
+__device__ __forceinline__ void put_bf16_split(uint16_t* hi, uint16_t* lo, const float (&x)[8]) {
+  uint16_t h[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) split_bf16(x[i], h[i], l[i]);
+  *reinterpret_cast<uint4*>(hi) = make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
+  *reinterpret_cast<uint4*>(lo) = make_uint4(pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7]));
+}
+__device__ __forceinline__ void put_f16(uint16_t* dst, const float (&x)[8]) {
+  *reinterpret_cast<uint4*>(dst) = make_uint4(pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]), pk_f16(x[6], x[7]));
+}
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 prefill_kernel(PrefillArgs A) {
   __shared__ PrefillLds L;
+  // raw inputs of the next chunk, written by direct global->LDS loads
+  __shared__ uint16_t Sq[C][D], Sk[C][D], Sv[C][D];
+  __shared__ float Sg[C][D];
+  __shared__ float Sbeta[C];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, lr = lane & 15;  // MFMA lane group and lane row/column
-  const int pc = tid & 127, pb = tid >> 7;  // prep mapping: key channel, 16-token block
+  const int co = 4 * wave + g;              // prep: channel octet 8co..8co+7
+  const int tl = lr;                        // prep: token tl of block 0 and 16+tl of block 1
   const int H = A.n_heads;
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
 
   // constant zero blocks: A, P and X are lower triangular in 16-blocks
   for (int e = tid; e < 16 * 16; e += 256) {
     const int i = e >> 4, j = 16 + (e & 15);
     L.at[j][i] = 0.f;
-    L.p_h[i][j] = 0;
-    L.p_l[i][j] = 0;
+    L.pm[i][j] = 0;
     L.xb[i][j] = 0;
   }
 
@@ -137,278 +209,311 @@ prefill_kernel(PrefillArgs A) {
         for (int nv = 0; nv < 2; ++nv) S[mc][nv] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // raw inputs of one chunk for (channel pc, block pb): prefetched one chunk ahead
-    float rg[16];
-    uint32_t rk[16], rq[16], rv[16];
-    float rbeta = 0.f;
+    // Raw inputs of a chunk are copied into LDS with direct global->LDS loads
+    // issued one chunk ahead; rows past the sequence end re-read its last
+    // token (always in bounds) and are masked in the prep.
     const int nch = (len + C - 1) / C;
-    auto fetch = [&](int ch) {
+    // Staging rows are stored with their 16-byte chunks permuted (physical
+    // chunk = logical chunk ^ (row & 15)) so the prep's column reads across 16
+    // rows hit 16 different LDS banks; each lane fetches the chunk that lands
+    // in its fixed LDS slot.
+    auto issue = [&](int ch) {
       const int nc = min(C, len - C * ch);
+      const int64_t trow0 = tok0 + C * ch;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int t = 16 * pb + i;
-        if (t < nc) {
-          const size_t row = ((size_t)(tok0 + C * ch + t) * H + h);
-          const size_t e = row * D + pc;
-          rg[i] = A.gk[e];
-          rk[i] = A.k[e];
-          rq[i] = A.q[e];
-          rv[i] = A.v[e];
-        } else {
-          rg[i] = 0.f; rk[i] = 0u; rq[i] = 0u; rv[i] = 0u;
-        }
+      for (int r = 0; r < 2; ++r) {  // q, k, v: 256-byte rows (16 chunks), 4 rows per wave
+        const int prow = 16 * r + 4 * wu + (lane >> 4);
+        const int row = min(prow, nc - 1);
+        const size_t e = ((size_t)(trow0 + row) * H + h) * D + 8 * ((lane & 15) ^ (prow & 15));
+        g2l(A.q + e, &Sq[16 * r + 4 * wu][0], 16);
+        g2l(A.k + e, &Sk[16 * r + 4 * wu][0], 16);
+        g2l(A.v + e, &Sv[16 * r + 4 * wu][0], 16);
       }
-      rbeta = (tid < nc) ? A.beta[(size_t)(tok0 + C * ch + tid) * H + h] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {  // gk: 512-byte rows (32 chunks), 2 rows per wave
+        const int prow = 8 * r + 2 * wu + (lane >> 5);
+        const int row = min(prow, nc - 1);
+        const size_t e = ((size_t)(trow0 + row) * H + h) * D + 4 * ((lane & 31) ^ (prow & 15));
+        g2l(A.gk + e, &Sg[8 * r + 2 * wu][0], 16);
+      }
+      if (wu == 0 && lane < C) g2l(A.beta + (size_t)(trow0 + min(lane, nc - 1)) * H + h, &Sbeta[0], 4);
     };
-    if (nch > 0) fetch(0);
+    // whole-row stores of a staged output tile (8 threads x 64 bytes per token row)
+    auto flush = [&](int ch) {
+      const int nc = min(C, len - C * ch);
+      const int row = tid >> 3, c0 = 16 * (tid & 7);
+      if (row < nc) {
+        float* dst = A.o + ((size_t)(tok0 + C * ch + row) * H + h) * D + c0;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<float4*>(dst + 4 * q4) = *reinterpret_cast<const float4*>(&L.so[row][c0 + 4 * q4]);
+      }
+    };
+    if (nch > 0) issue(0);
 
     for (int ch = 0; ch < nch; ++ch) {
       const int nc = min(C, len - C * ch);
-      // ---------------- prep: decay factors and bf16 operand matrices ----------------
-      float a[16], pf[16], sf[16], xd[16], yd[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) a[i] = __expf(rg[i]);
-      pf[0] = a[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) pf[i] = pf[i - 1] * a[i];
-      sf[15] = 1.f;
-#pragma unroll
-      for (int i = 14; i >= 0; --i) sf[i] = sf[i + 1] * a[i + 1];
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's staging loads (and older stores) are complete
+      __syncthreads();
+      if (ch > 0) flush(ch - 1);
+
+      // ---------------- prep: decay factors and operand matrices ----------------
       {
-        // diagonal-block anchor at the block's 8th token (index 7)
-        float pm = 1.f;
-        xd[7] = 1.f; yd[7] = 1.f;
+        const int c8 = 8 * co;
+        const bool ok0 = tl < nc, ok1 = 16 + tl < nc;
+        float a0[8], a1[8];
+        {
+          // logical gk chunks 2co and 2co+1 of rows tl and 16+tl, at their permuted positions
+          const float4 x0 = *reinterpret_cast<const float4*>(&Sg[tl][4 * ((2 * co) ^ tl)]);
+          const float4 x1 = *reinterpret_cast<const float4*>(&Sg[tl][4 * ((2 * co + 1) ^ tl)]);
+          const float4 y0 = *reinterpret_cast<const float4*>(&Sg[16 + tl][4 * ((2 * co) ^ tl)]);
+          const float4 y1 = *reinterpret_cast<const float4*>(&Sg[16 + tl][4 * ((2 * co + 1) ^ tl)]);
+          const float gx[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          const float gy[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
 #pragma unroll
-        for (int i = 8; i < 16; ++i) { pm = pm * a[i]; xd[i] = pm; yd[i] = __builtin_amdgcn_rcpf(pm); }
-        float sm = 1.f;
-#pragma unroll
-        for (int i = 6; i >= 0; --i) { sm = sm * a[i + 1]; yd[i] = sm; xd[i] = __builtin_amdgcn_rcpf(sm); }
-      }
-      L.dex[pb][pc] = pf[15];
-      if (tid < C) L.beta[tid] = rbeta;
-      __syncthreads();
-      const float D0 = L.dex[0][pc], D1 = L.dex[1][pc];
-      if (pb == 0) L.dec[pc] = D0 * D1;
-      uint32_t kph[8], kpl[8], vtp[8];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int t = 16 * pb + i;
-        const float kf = bf2f(rk[i]), qf = bf2f(rq[i]);
-        const float E = pb == 0 ? pf[i] : D0 * pf[i];
-        const float F = pb == 0 ? sf[i] * D1 : sf[i];
-        uint16_t hi, lo;
-        L.kxd[t][pc] = f2bf(kf * xd[i]);
-        split_bf16(kf * yd[i], hi, lo); L.kyd_h[t][pc] = hi; L.kyd_l[t][pc] = lo;
-        split_bf16(qf * xd[i], hi, lo); L.qxd_h[t][pc] = hi; L.qxd_l[t][pc] = lo;
-        split_bf16(qf * E, hi, lo); L.qt_h[t][pc] = hi; L.qt_l[t][pc] = lo;
-        L.kt[t][pc] = f2bf(kf * E);
-        if (pb == 1) {
-          L.kxo[i][pc] = f2bf(kf * pf[i]);
-          split_bf16(qf * pf[i], hi, lo); L.qxo_h[i][pc] = hi; L.qxo_l[i][pc] = lo;
-        } else {
-          split_bf16(kf * sf[i], hi, lo); L.kyo_h[i][pc] = hi; L.kyo_l[i][pc] = lo;
+          for (int i = 0; i < 8; ++i) { a0[i] = ok0 ? __expf(gx[i]) : 1.f; a1[i] = ok1 ? __expf(gy[i]) : 1.f; }
         }
-        split_bf16(kf * F, hi, lo);
-        if (i & 1) { kph[i >> 1] |= (uint32_t)hi << 16; kpl[i >> 1] |= (uint32_t)lo << 16; vtp[i >> 1] |= rv[i] << 16; }
-        else { kph[i >> 1] = hi; kpl[i >> 1] = lo; vtp[i >> 1] = rv[i]; }
+        const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+        const int sc = 8 * (co ^ tl);  // permuted position of logical chunk co (rows tl and 16+tl share row & 15)
+        const uint4 k0u = ok0 ? lds16(&Sk[tl][sc]) : zero4, k1u = ok1 ? lds16(&Sk[16 + tl][sc]) : zero4;
+        const uint4 q0u = ok0 ? lds16(&Sq[tl][sc]) : zero4, q1u = ok1 ? lds16(&Sq[16 + tl][sc]) : zero4;
+        *reinterpret_cast<uint4*>(&L.vt[tl][c8]) = ok0 ? lds16(&Sv[tl][sc]) : zero4;
+        *reinterpret_cast<uint4*>(&L.vt[16 + tl][c8]) = ok1 ? lds16(&Sv[16 + tl][sc]) : zero4;
+        if (tid < C) L.beta[tid] = tid < nc ? Sbeta[tid] : 0.f;
+        float k0[8], k1[8], q0[8], q1[8];
+        unpack_bf16x8(k0u, k0); unpack_bf16x8(k1u, k1);
+        unpack_bf16x8(q0u, q0); unpack_bf16x8(q1u, q1);
+        float xr0[8], xr1[8], yc0[8], yc1[8], e0[8], e1[8], f0[8], f1[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p0 = row_scan_mul(a0[i]), p1 = row_scan_mul(a1[i]);  // e^{G_t - G_-1}, e^{G_t - G_15}
+          const float T0 = KDA_ROW_BCAST15(p0), T1 = KDA_ROW_BCAST15(p1);   // block totals
+          const float r0 = __builtin_amdgcn_rcpf(p0), r1 = __builtin_amdgcn_rcpf(p1);
+          xr0[i] = p0 * __builtin_amdgcn_rcpf(T0);  // e^{G_t - G_15}, block 0
+          xr1[i] = p1;
+          yc0[i] = T0 * r0;                         // e^{G_15 - G_t}, block 0
+          yc1[i] = r1;
+          e0[i] = p0;                               // e^{G_t}
+          e1[i] = T0 * p1;
+          f0[i] = yc0[i] * T1;                      // e^{G_31 - G_t}
+          f1[i] = T1 * r1;
+          if (tl == 0) L.dlast[c8 + i] = T0 * T1;
+        }
+        // fp16 operands of the state products, token-major rows tl and 16+tl
+        float x[8];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int t = 16 * b + tl;
+          const float(&kk)[8] = b ? k1 : k0;
+          const float(&qq)[8] = b ? q1 : q0;
+          const float(&ee)[8] = b ? e1 : e0;
+          const float(&ff)[8] = b ? f1 : f0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] = qq[i] * ee[i];
+          put_f16(&L.qt[t][c8], x);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] = kk[i] * ee[i];
+          put_f16(&L.kt[t][c8], x);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] = kk[i] * ff[i];
+          put_f16(&L.kp[t][c8], x);
+        }
+        // A and P over this wave's 32 channels, straight from registers: lane (g, lr) holds
+        // channels 32w+8g..+7 of tokens lr (block 0) and 16+lr (block 1), which is the
+        // A-operand fragment of row lr and the B-operand fragment of column lr
+        bf16x8 rk0, rk1, rq0h, rq0l, rq1h, rq1l, ck0h, ck0l, ck1h, ck1l;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          rk0[i] = (__bf16)(k0[i] * xr0[i]);
+          rk1[i] = (__bf16)(k1[i] * xr1[i]);
+          float v = q0[i] * xr0[i]; rq0h[i] = (__bf16)v; rq0l[i] = (__bf16)(v - (float)rq0h[i]);
+          v = q1[i] * xr1[i];       rq1h[i] = (__bf16)v; rq1l[i] = (__bf16)(v - (float)rq1h[i]);
+          v = k0[i] * yc0[i];       ck0h[i] = (__bf16)v; ck0l[i] = (__bf16)(v - (float)ck0h[i]);
+          v = k1[i] * yc1[i];       ck1h[i] = (__bf16)v; ck1l[i] = (__bf16)(v - (float)ck1h[i]);
+        }
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[6];
+        acc[0] = mfma16(rk0, ck0l, mfma16(rk0, ck0h, z4));                          // A 00
+        acc[1] = mfma16(rk1, ck1l, mfma16(rk1, ck1h, z4));                          // A 11
+        acc[2] = mfma16(rk1, ck0l, mfma16(rk1, ck0h, z4));                          // A 10
+        acc[3] = mfma16(rq0l, ck0h, mfma16(rq0h, ck0l, mfma16(rq0h, ck0h, z4)));   // P 00
+        acc[4] = mfma16(rq1l, ck1h, mfma16(rq1h, ck1l, mfma16(rq1h, ck1h, z4)));   // P 11
+        acc[5] = mfma16(rq1l, ck0h, mfma16(rq1h, ck0l, mfma16(rq1h, ck0h, z4)));   // P 10
+#pragma unroll
+        for (int tl6 = 0; tl6 < 6; ++tl6)
+          *reinterpret_cast<f32x4*>(&L.part[wave][tl6][lr][4 * g]) = acc[tl6];
       }
-      *reinterpret_cast<uint4*>(&L.kp_h[pc][16 * pb]) = make_uint4(kph[0], kph[1], kph[2], kph[3]);
-      *reinterpret_cast<uint4*>(&L.kp_h[pc][16 * pb + 8]) = make_uint4(kph[4], kph[5], kph[6], kph[7]);
-      *reinterpret_cast<uint4*>(&L.kp_l[pc][16 * pb]) = make_uint4(kpl[0], kpl[1], kpl[2], kpl[3]);
-      *reinterpret_cast<uint4*>(&L.kp_l[pc][16 * pb + 8]) = make_uint4(kpl[4], kpl[5], kpl[6], kpl[7]);
-      *reinterpret_cast<uint4*>(&L.vt[pc][16 * pb]) = make_uint4(vtp[0], vtp[1], vtp[2], vtp[3]);
-      *reinterpret_cast<uint4*>(&L.vt[pc][16 * pb + 8]) = make_uint4(vtp[4], vtp[5], vtp[6], vtp[7]);
       __syncthreads();
-      // next chunk's raw inputs are in flight while this chunk computes
-      if (ch + 1 < nch) fetch(ch + 1);
+      // the staging area is consumed: next chunk's raw inputs stream in while this chunk computes
+      if (ch + 1 < nch) issue(ch + 1);
 
-      // ---------------- A and P: three 16x16 tiles each (waves 0..2) ----------------
-      if (wave < 3) {
-        const int I = wave == 1 ? 1 : (wave == 2 ? 1 : 0);
-        const int J = wave == 1 ? 1 : 0;
-        const bool diag = I == J;
-        const uint16_t* ra = diag ? &L.kxd[16 * I + lr][0] : &L.kxo[lr][0];
-        const uint16_t* rph = diag ? &L.qxd_h[16 * I + lr][0] : &L.qxo_h[lr][0];
-        const uint16_t* rpl = diag ? &L.qxd_l[16 * I + lr][0] : &L.qxo_l[lr][0];
-        const uint16_t* cbh = diag ? &L.kyd_h[16 * J + lr][0] : &L.kyo_h[lr][0];
-        const uint16_t* cbl = diag ? &L.kyd_l[16 * J + lr][0] : &L.kyo_l[lr][0];
-        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+      // reduce the four channel slices of A and P; mask, scale A rows by beta
+      if (tid < 192) {
+        const int tile = tid >> 5, j = (tid >> 1) & 15, i0 = 8 * (tid & 1);
+        const int I = (tile % 3) == 0 ? 0 : 1, J = (tile % 3) == 1 ? 1 : 0;
+        float sum[8];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int off = 32 * s + 8 * g;
-          const bf16x8 xa = as_bf16x8(lds16(ra + off));
-          const bf16x8 xph = as_bf16x8(lds16(rph + off)), xpl = as_bf16x8(lds16(rpl + off));
-          const bf16x8 yh = as_bf16x8(lds16(cbh + off)), yl = as_bf16x8(lds16(cbl + off));
-          accA = mfma16(xa, yh, accA);
-          accA = mfma16(xa, yl, accA);
-          accP = mfma16(xph, yh, accP);
-          accP = mfma16(xph, yl, accP);
-          accP = mfma16(xpl, yh, accP);
-        }
-        const int j = 16 * J + lr;
+        for (int q8 = 0; q8 < 2; ++q8) {
+          f32x4 s4 = *reinterpret_cast<const f32x4*>(&L.part[0][tile][j][i0 + 4 * q8]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * I + 4 * g + r;
-          L.at[j][i] = (j < i) ? accA[r] * L.beta[i] : 0.f;
-          uint16_t hi = 0, lo = 0;
-          if (j <= i) split_bf16(accP[r], hi, lo);
-          L.p_h[i][j] = hi;
-          L.p_l[i][j] = lo;
-        }
-      }
-      __syncthreads();
-
-      // ---------------- diagonal blocks of X = (I + A)^-1 (wave 0, lanes 0..31) ----------------
-      if (wave == 0 && lane < 32) {
-        const int b = lane >> 4, jl = lane & 15;
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = (i == jl) ? 1.f : 0.f;
-#pragma unroll
-        for (int kk = 0; kk < 15; ++kk) {
-          // column kk of the block: A[16b+i][16b+kk] = at[16b+kk][16b+i]
-          const float* col = &L.at[16 * b + kk][16 * b];
-          float av[16];
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 t4 = *reinterpret_cast<const float4*>(col + 4 * q4);
-            av[4 * q4] = t4.x; av[4 * q4 + 1] = t4.y; av[4 * q4 + 2] = t4.z; av[4 * q4 + 3] = t4.w;
+          for (int w = 1; w < 4; ++w) {
+            const f32x4 p4 = *reinterpret_cast<const f32x4*>(&L.part[w][tile][j][i0 + 4 * q8]);
+            s4[0] += p4[0]; s4[1] += p4[1]; s4[2] += p4[2]; s4[3] += p4[3];
           }
-          const float xk = x[kk];
 #pragma unroll
-          for (int i = kk + 1; i < 16; ++i) x[i] = __builtin_fmaf(-av[i], xk, x[i]);
+          for (int r = 0; r < 4; ++r) sum[4 * q8 + r] = s4[r];
         }
+        const int jg = 16 * J + j;
+        if (tile < 3) {
+          float av[8];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          L.xf[16 * b + i][16 * b + jl] = x[i];
-          L.xb[16 * b + i][16 * b + jl] = f2bf(x[i]);
+          for (int r = 0; r < 8; ++r) {
+            const int ig = 16 * I + i0 + r;
+            av[r] = (jg < ig) ? sum[r] * L.beta[ig] : 0.f;
+          }
+          *reinterpret_cast<float4*>(&L.at[jg][16 * I + i0]) = make_float4(av[0], av[1], av[2], av[3]);
+          *reinterpret_cast<float4*>(&L.at[jg][16 * I + i0 + 4]) = make_float4(av[4], av[5], av[6], av[7]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            const int ig = 16 * I + i0 + r;
+            L.pm[ig][jg] = (jg <= ig) ? __builtin_bit_cast(uint16_t, (_Float16)sum[r]) : (uint16_t)0;
+          }
         }
+      }
+      __syncthreads();  // A (transposed, fp32) and P (fp16) are complete
+
+      // ---------------- X = (I + A)^-1 (wave 0) ----------------
+      if (wave == 0) {
+        if (lane < 32) {
+          // diagonal blocks by forward substitution, one column per lane
+          const int b = lane >> 4, jl = lane & 15;
+          float xv[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xv[i] = (i == jl) ? 1.f : 0.f;
+#pragma unroll
+          for (int kk = 0; kk < 15; ++kk) {
+            const float* col = &L.at[16 * b + kk][16 * b];  // A[16b+i][16b+kk], i = 0..15
+            float av[16];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const float4 t4 = *reinterpret_cast<const float4*>(col + 4 * q4);
+              av[4 * q4] = t4.x; av[4 * q4 + 1] = t4.y; av[4 * q4 + 2] = t4.z; av[4 * q4 + 3] = t4.w;
+            }
+            const float xk = xv[kk];
+#pragma unroll
+            for (int i = kk + 1; i < 16; ++i) xv[i] = __builtin_fmaf(-av[i], xk, xv[i]);
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            L.xf[16 * b + i][16 * b + jl] = xv[i];
+            L.xb[16 * b + i][16 * b + jl] = __builtin_bit_cast(uint16_t, (_Float16)xv[i]);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        // X10 = -X11 (A10 X00) with fp32 MFMAs; the reduction index of step s in lane group g is 4g+s
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) y = mfma_f32(L.at[4 * g + s][16 + lr], L.xf[4 * g + s][lr], y);
+        f32x4 x10 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) x10 = mfma_f32(L.xf[16 + lr][16 + 4 * g + s], y[s], x10);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) L.xb[16 + 4 * g + r][lr] = __builtin_bit_cast(uint16_t, (_Float16)(-x10[r]));
       }
 
       // ---------------- Kt S0 and Qt S0 (independent of X) ----------------
-      bf16x8 Sh[4][2], Sl[4][2];
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int nv = 0; nv < 2; ++nv) split8(S[2 * s][nv], S[2 * s + 1][nv], Sh[s][nv], Sl[s][nv]);
       f32x4 KS[2][2], QS[2][2];
+      {
+        f16x8 Sh[4][2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int nv = 0; nv < 2; ++nv) { KS[mt][nv] = f32x4{0.f, 0.f, 0.f, 0.f}; QS[mt][nv] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+          for (int nv = 0; nv < 2; ++nv) Sh[s][nv] = to_h8(S[2 * s][nv], S[2 * s + 1][nv]);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int m = 16 * mt + lr;
-          const bf16x8 kt = perm_a(&L.kt[m][32 * s], g);
-          const bf16x8 qh = perm_a(&L.qt_h[m][32 * s], g);
-          const bf16x8 ql = perm_a(&L.qt_l[m][32 * s], g);
+        for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-          for (int nv = 0; nv < 2; ++nv) {
-            KS[mt][nv] = mfma16(kt, Sh[s][nv], KS[mt][nv]);
-            QS[mt][nv] = mfma16(qh, Sh[s][nv], QS[mt][nv]);
-            QS[mt][nv] = mfma16(qh, Sl[s][nv], QS[mt][nv]);
-            QS[mt][nv] = mfma16(ql, Sh[s][nv], QS[mt][nv]);
+          for (int nv = 0; nv < 2; ++nv) { KS[mt][nv] = f32x4{0.f, 0.f, 0.f, 0.f}; QS[mt][nv] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const int m = 16 * mt + lr;
+            const f16x8 kr = perm_h(&L.kt[m][32 * s], g);
+            const f16x8 qr = perm_h(&L.qt[m][32 * s], g);
+#pragma unroll
+            for (int nv = 0; nv < 2; ++nv) {
+              KS[mt][nv] = mfma_h(kr, Sh[s][nv], KS[mt][nv]);
+              QS[mt][nv] = mfma_h(qr, Sh[s][nv], QS[mt][nv]);
+            }
           }
         }
       }
-      __syncthreads();
-
-      // ---------------- off-diagonal block X10 = -X11 A10 X00 (wave 0) ----------------
-      if (wave == 0) {
-        // Y = A10 X00 into the scratch block xf[0..15][16..31]
-        float y[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int ri = 4 * g + r;
-          float acc = 0.f;
-#pragma unroll
-          for (int kk = 0; kk < 16; ++kk) acc = __builtin_fmaf(L.at[kk][16 + ri], L.xf[kk][lr], acc);
-          y[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) L.xf[4 * g + r][16 + lr] = y[r];
-      }
-      __syncthreads();
-      if (wave == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int ri = 4 * g + r;
-          float acc = 0.f;
-#pragma unroll
-          for (int m = 0; m < 16; ++m) acc = __builtin_fmaf(L.xf[16 + ri][16 + m], L.xf[m][16 + lr], acc);
-          L.xb[16 + ri][lr] = f2bf(-acc);
-        }
-      }
-      __syncthreads();
+      __syncthreads();  // X is complete
 
       // ---------------- R = diag(beta)(V - Kt S0), W = X R ----------------
-      bf16x8 Wh[2], Wl[2];
+      f32x4 W[2][2];
       {
-        bf16x8 Rh[2], Rl[2];
+        f16x8 Rh[2], Rl[2];
 #pragma unroll
         for (int nv = 0; nv < 2; ++nv) {
           f32x4 R[2];
-          const int v = 32 * wave + 16 * nv + lr;
+          const int c0 = 32 * wave + 16 * nv;
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt) {
-            const uint2 vv = lds8(&L.vt[v][16 * mt + 4 * g]);
+            // V[16mt+4g+r][c0+lr] through the transposing read
+            const uint2 vv = lds_tr(&L.vt[16 * mt + 4 * g + (lr >> 2)][c0 + 4 * (lr & 3)]);
             const float4 b4 = *reinterpret_cast<const float4*>(&L.beta[16 * mt + 4 * g]);
             R[mt][0] = b4.x * (bf2f(vv.x & 0xffffu) - KS[mt][nv][0]);
             R[mt][1] = b4.y * (bf2f(vv.x >> 16) - KS[mt][nv][1]);
             R[mt][2] = b4.z * (bf2f(vv.y & 0xffffu) - KS[mt][nv][2]);
             R[mt][3] = b4.w * (bf2f(vv.y >> 16) - KS[mt][nv][3]);
           }
-          split8(R[0], R[1], Rh[nv], Rl[nv]);
+          split_h8(R[0], R[1], Rh[nv], Rl[nv]);
         }
-        f32x4 W[2][2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 xa = perm_a(&L.xb[16 * mt + lr][0], g);
+          const f16x8 xa = perm_h(&L.xb[16 * mt + lr][0], g);
 #pragma unroll
           for (int nv = 0; nv < 2; ++nv) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma16(xa, Rh[nv], acc);
-            acc = mfma16(xa, Rl[nv], acc);
+            acc = mfma_h(xa, Rh[nv], acc);
+            acc = mfma_h(xa, Rl[nv], acc);
             W[mt][nv] = acc;
           }
         }
-#pragma unroll
-        for (int nv = 0; nv < 2; ++nv) split8(W[0][nv], W[1][nv], Wh[nv], Wl[nv]);
       }
+      f16x8 Wh[2], Wl[2];
+#pragma unroll
+      for (int nv = 0; nv < 2; ++nv) split_h8(W[0][nv], W[1][nv], Wh[nv], Wl[nv]);
 
-      // ---------------- O = scale (Qt S0 + P W) ----------------
+      // ---------------- O = scale (Qt S0 + P W) into the output staging tile ----------------
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 ph = perm_a(&L.p_h[16 * mt + lr][0], g);
-        const bf16x8 pl = perm_a(&L.p_l[16 * mt + lr][0], g);
+        const f16x8 pa = perm_h(&L.pm[16 * mt + lr][0], g);
 #pragma unroll
         for (int nv = 0; nv < 2; ++nv) {
           f32x4 acc = QS[mt][nv];
-          acc = mfma16(ph, Wh[nv], acc);
-          acc = mfma16(ph, Wl[nv], acc);
-          acc = mfma16(pl, Wh[nv], acc);
+          acc = mfma_h(pa, Wh[nv], acc);
+          acc = mfma_h(pa, Wl[nv], acc);
           const int v = 32 * wave + 16 * nv + lr;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 16 * mt + 4 * g + r;
-            if (t < nc) A.o[((size_t)(tok0 + C * ch + t) * H + h) * D + v] = A.scale * acc[r];
-          }
+          for (int r = 0; r < 4; ++r) L.so[16 * mt + 4 * g + r][v] = A.scale * acc[r];
         }
       }
 
-      // ---------------- S = diag(e^{G_last}) S0 + K'^T W ----------------
+      // ---------------- S = e^{G_31} S0 + K'^T W ----------------
 #pragma unroll
       for (int mc = 0; mc < 8; ++mc) {
-        const float4 d4 = *reinterpret_cast<const float4*>(&L.dec[16 * mc + 4 * g]);
-        const bf16x8 kh = perm_a(&L.kp_h[16 * mc + lr][0], g);
-        const bf16x8 kl = perm_a(&L.kp_l[16 * mc + lr][0], g);
+        const float4 d4 = *reinterpret_cast<const float4*>(&L.dlast[16 * mc + 4 * g]);
+        // K'^T rows 16mc+lr, reduction positions t = 4g+r and 16+4g+r, via the transposing read
+        const uint16_t* base = &L.kp[4 * g + (lr >> 2)][16 * mc + 4 * (lr & 3)];
+        const f16x8 ka = as_f16x8(lds_tr(base), lds_tr(base + 16 * TM));
 #pragma unroll
         for (int nv = 0; nv < 2; ++nv) {
           f32x4 acc = S[mc][nv];
           acc[0] *= d4.x; acc[1] *= d4.y; acc[2] *= d4.z; acc[3] *= d4.w;
-          acc = mfma16(kh, Wh[nv], acc);
-          acc = mfma16(kh, Wl[nv], acc);
-          acc = mfma16(kl, Wh[nv], acc);
+          acc = mfma_h(ka, Wh[nv], acc);
+          acc = mfma_h(ka, Wl[nv], acc);
           S[mc][nv] = acc;
         }
       }
@@ -425,8 +530,9 @@ prefill_kernel(PrefillArgs A) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) dst[(size_t)(16 * mc + 4 * g + r) * D + 32 * wave + 16 * nv + lr] = S[mc][nv][r];
       }
-      __syncthreads();  // LDS is rewritten by the next chunk's prep
     }
+    __syncthreads();
+    if (nch > 0) flush(nch - 1);
 
     float* dst = A.state_out + unit * D * D;
 #pragma unroll
