@@ -1,0 +1,206 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+bench times, through the C ABI. The oracle covers every unit where it
+finishes in seconds, a stated sample elsewhere (the whole longest and
+shortest sequences plus random units; two full heads of the 1M-token run);
+bit-exact properties are checked on every unit.
+
+Workloads (synthetic, seeded, shapes from the pages; K = V = 128):
+  prefill A: 4 x 2048 tokens, H = 64, state_in ~ N(0, 0.1^2)
+  prefill B: 32 sequences, lengths log-uniform in [64, 24576], H = 96,
+             snapshots every 2048 tokens into 2 ping-pong slots
+  spec step: 256 requests x 69 layers x 8 heads, gamma + 1 = 8, ring 16,
+             accepted lengths geometric (mean 2.7, clipped to [1, 8])
+  long:      1 x 1,048,576 tokens, H = 96, snapshots every 4096 into 2
+             slots, then 128 single-token decode steps
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import synth.gpu as sg
+import linear_attention_recurrence_amd as kda
+from kda_ref import TOL, block_err, log, oracle_prefill_unit, threads
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def np_(t):
+    return t.detach().cpu().numpy()
+
+
+def prefill_run(cfg, lens, H, state_in=None, snap_slots=0, order=kda.KDA_PLAN_LPT):
+    c = synth.PREFILL_CONFIGS[cfg]
+    cu = synth.cu_seqlens(lens)
+    T = int(cu[-1])
+    plan = kda.kda_plan_create(cu, n_heads=H, snap_interval=c["snap_interval"], order=order)
+    ins = sg.prefill_inputs(c["seed"], T, H, DEV)
+    N = len(lens)
+    o = torch.empty((T, H, 128), device=DEV)
+    st = torch.empty((N, H, 128, 128), device=DEV)
+    snap = torch.full((N, snap_slots, H, 128, 128), -5.0, device=DEV) if snap_slots else None
+    cnt = torch.full((N,), -1, dtype=torch.int32, device=DEV)
+    ws = torch.empty(kda.kda_plan_workspace_bytes(plan), dtype=torch.uint8, device=DEV)
+    kda.kda_plan_upload(plan, ws)
+    kda.kda_chunk_prefill(plan, *ins, st, o, ws, state_in=state_in, snap=snap, snap_slots=snap_slots,
+                          snap_count=cnt, flags=kda.KDA_PREFILL_PLAN_RESIDENT)
+    torch.cuda.synchronize()
+    return plan, cu, ins, o, st, snap, cnt
+
+
+def check_units(cfg, cu, H, units, o, st, snap=None, snap_slots=0, S0=None, interval=0):
+    seed = synth.PREFILL_CONFIGS[cfg]["seed"]
+    o_np = {}
+    for n, h in units:  # device -> host slices first (one process, sequential)
+        o_np[(n, h)] = np_(o[int(cu[n]):int(cu[n + 1]), h])
+    st_np = np_(st)
+    sn_np = np_(snap) if snap is not None else None
+
+    def run(u):
+        n, h = u
+        L = int(cu[n + 1] - cu[n])
+        s0 = None if S0 is None else S0[n, h]
+        o_ref, S_ref, sn_ref, c = oracle_prefill_unit(seed, H, int(cu[n]), L, h, S0=s0, snap_interval=interval,
+                                                      snap_slots=snap_slots)
+        e = {"o": block_err(o_np[u], o_ref) if L else 0.0, "state": block_err(st_np[n, h], S_ref), "snap": 0.0,
+             "count": c}
+        for m in range(max(1, c - snap_slots + 1), c + 1):
+            sl = (m - 1) % snap_slots
+            e["snap"] = max(e["snap"], block_err(sn_np[n, sl, h], sn_ref[sl]))
+        return e
+
+    res = oracle.run_parallel(run, units, threads=threads())
+    worst = {k: max(r[k] for r in res) for k in ("o", "state", "snap")}
+    return worst, res
+
+
+def test_prefill_4x2048_h64_all_units(gpu):
+    lens = [2048] * 4
+    H = 64
+    log("prefill 4x2048 H64: GPU run")
+    S0 = sg.states(1, 4 * H, DEV).view(4, H, 128, 128)
+    plan, cu, ins, o, st, _, _ = prefill_run(1, lens, H, state_in=S0)
+    log("prefill 4x2048 H64: oracle on all 256 units")
+    worst, _ = check_units(1, cu, H, [(n, h) for n in range(4) for h in range(H)], o, st, S0=np_(S0))
+    log(f"prefill 4x2048 H64 worst {worst}")
+    assert max(worst.values()) <= TOL
+
+
+def test_prefill_varlen_h96_snapshots(gpu):
+    H = 96
+    lens = synth.prefill_lengths(2)
+    log(f"prefill varlen: {len(lens)} sequences, total {int(lens.sum())} tokens, max {int(lens.max())}")
+    plan, cu, ins, o, st, snap, cnt = prefill_run(2, lens, H, snap_slots=2)
+    # counts are exact integers for every sequence
+    assert np.array_equal(np_(cnt), lens // 2048)
+    # longest-first and input order give the same bits
+    _, _, _, o2, st2, snap2, _ = prefill_run(2, lens, H, snap_slots=2, order=kda.KDA_PLAN_FIFO)
+    assert torch.equal(o, o2) and torch.equal(st, st2) and torch.equal(snap, snap2)
+    del o2, st2, snap2
+    longest, shortest = int(np.argmax(lens)), int(np.argmin(lens))
+    rng = np.random.default_rng(2)
+    units = [(longest, h) for h in range(0, H, 3)] + [(shortest, h) for h in range(0, H, 12)]
+    units += [(int(rng.integers(len(lens))), int(rng.integers(H))) for _ in range(24)]
+    units = sorted(set(units))
+    log(f"prefill varlen: oracle on {len(units)} units")
+    worst, _ = check_units(2, cu, H, units, o, st, snap=snap, snap_slots=2, interval=2048)
+    log(f"prefill varlen worst {worst}")
+    assert max(worst.values()) <= TOL
+
+
+def test_spec_step_256x69x8(gpu):
+    c = synth.VERIFY_CONFIG
+    seed, B, Lyr, H, T, R = c["seed"], c["B"], c["L"], c["H"], c["T"], c["R"]
+    S = B
+    log("spec step: generating the committed pool and inputs")
+    pool = sg.states(seed, S * Lyr * H, DEV).view(S, Lyr, H, 128, 128)
+    acc_np = synth.geometric_accept(seed, B)
+    acc = torch.from_numpy(acc_np).to(torch.int32).to(DEV)
+    slot_idx = torch.arange(B, dtype=torch.int32, device=DEV)
+    ring_start = torch.zeros(B, dtype=torch.int32, device=DEV)
+    ring = kda.Ring.empty(S, Lyr, H, R, DEV)
+    commit = torch.empty_like(pool)
+    rng = np.random.default_rng(3)
+    samples = sorted({(int(rng.integers(B)), int(rng.integers(Lyr)), int(rng.integers(H))) for _ in range(48)})
+    o_s = {}
+    for l in range(Lyr):
+        ins = sg.prefill_inputs(seed, B * T, H, DEV, sub=l)
+        o = torch.empty((B * T, H, 128), device=DEV)
+        kda.kda_verify(*ins, pool, slot_idx, o, layer=l, n_tok=T, ring=ring, ring_start=ring_start, commit_len=acc,
+                       commit_pool=commit)
+        # the ring holds the raw inputs of every request at positions 0..T-1, bit for bit
+        k_in = ins[1].view(B, T, H, 128).permute(0, 2, 1, 3)
+        v_in = ins[2].view(B, T, H, 128).permute(0, 2, 1, 3)
+        g_in = ins[3].view(B, T, H, 128).permute(0, 2, 1, 3)
+        b_in = ins[4].view(B, T, H).permute(0, 2, 1)
+        assert torch.equal(ring.k[:, l, :, :T], k_in) and torch.equal(ring.v[:, l, :, :T], v_in)
+        assert torch.equal(ring.gk[:, l, :, :T], g_in) and torch.equal(ring.beta[:, l, :, :T], b_in)
+        for (b, ll, h) in samples:
+            if ll == l:
+                o_s[(b, ll, h)] = np_(o.view(B, T, H, 128)[b, :, h])
+    torch.cuda.synchronize()
+    # verify never wrote the committed pool
+    fresh = sg.states(seed, S * Lyr * H, DEV).view(S, Lyr, H, 128, 128)
+    assert torch.equal(pool, fresh)
+    del fresh
+    log("spec step: fold")
+    kda.kda_replay_fold(pool, slot_idx, ring, acc, ring_start=ring_start)
+    torch.cuda.synchronize()
+    # bit-identical to verify's recurrent commit on every (request, layer, head)
+    assert torch.equal(pool, commit), "fold differs from the recurrent commit"
+    log(f"spec step: oracle on {len(samples)} units")
+    pool_np = {u: np_(pool[u[0], u[1], u[2]]) for u in samples}
+
+    def run(u):
+        b, l, h = u
+        q, k, v, gk, beta = synth.prefill_rows(seed, H, b * T, T, h=h, sub=l)
+        S0 = synth.state_rows(seed, (b * Lyr + l) * H + h, 1)[0]
+        o_ref, Sc, _ = oracle.verify(q, k, v, gk, beta, S0, commit_len=int(acc_np[b]))
+        return max(block_err(o_s[u], o_ref), block_err(pool_np[u], Sc))
+
+    worst = max(oracle.run_parallel(run, samples, threads=threads()))
+    log(f"spec step worst {worst:.2e}")
+    assert worst <= TOL
+
+
+def test_long_context_1m_then_decode(gpu):
+    H, T = 96, 1048576
+    cfg = synth.PREFILL_CONFIGS[4]
+    seed = cfg["seed"]
+    log("long context: generating 1M x 96 inputs on the device")
+    plan, cu, ins, o, st, snap, cnt = prefill_run(4, [T], H, snap_slots=2)
+    assert int(cnt[0]) == T // 4096
+    heads = [7, 60]
+    o_np = {h: np_(o[:, h]) for h in heads}
+    del ins, o
+    torch.cuda.empty_cache()
+    # 128 single-token decode steps from the final state: verify with n_tok = 1 and an in-place commit
+    pool = st.view(1, 1, H, 128, 128).clone()
+    slot = torch.zeros(1, dtype=torch.int32, device=DEV)
+    one = torch.ones(1, dtype=torch.int32, device=DEV)
+    dec_tids = (synth.T_DEC_Q, synth.T_DEC_K, synth.T_DEC_V, synth.T_DEC_GK, synth.T_DEC_BETA)
+    dq, dk, dv, dg, db = sg.prefill_inputs(seed, synth.DECODE_STEPS, H, DEV, tids=dec_tids)
+    dec_o = torch.empty((synth.DECODE_STEPS, H, 128), device=DEV)
+    for t in range(synth.DECODE_STEPS):
+        kda.kda_verify(dq[t:t + 1], dk[t:t + 1], dv[t:t + 1], dg[t:t + 1], db[t:t + 1], pool, slot,
+                       dec_o[t:t + 1], layer=0, n_tok=1, commit_len=one, commit_pool=pool)
+    torch.cuda.synchronize()
+    st_np, sn_np, dec_np, fin_np = np_(st), np_(snap), np_(dec_o), np_(pool[0, 0])
+    log(f"long context: oracle on heads {heads} (1,048,576 tokens each) and their decode steps")
+
+    def run(h):
+        o_ref, S_ref, sn_ref, c = oracle_prefill_unit(seed, H, 0, T, h, snap_interval=4096, snap_slots=2)
+        e = {"o": block_err(o_np[h], o_ref), "state": block_err(st_np[0, h], S_ref),
+             "snap": max(block_err(sn_np[0, s, h], sn_ref[s]) for s in range(2))}
+        q, k, v, gk, beta = synth.prefill_rows(seed, H, 0, synth.DECODE_STEPS, h=h, tids=dec_tids)
+        do_ref, dS_ref, _, _ = oracle.recurrent(q, k, v, gk, beta, S_ref)
+        e["decode_o"] = block_err(dec_np[:, h], do_ref)
+        e["decode_state"] = block_err(fin_np[h], dS_ref)
+        return e
+
+    res = oracle.run_parallel(run, heads, threads=len(heads))
+    worst = {k: max(r[k] for r in res) for k in res[0]}
+    log(f"long context worst {worst}")
+    assert max(worst.values()) <= TOL
