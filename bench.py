@@ -32,9 +32,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 METRIC = "KDA prefill tokens*heads/s and verify+fold us/step at 1 GPU; % of roofline"
 
-# traffic measured by rocprofv3 PMC (FETCH_SIZE + WRITE_SIZE), per launch, scaled by the copy-kernel
-# calibration; None until measured for the current kernel
-PREFILL_TRAFFIC_BYTES = None
+# HBM bytes per prefill launch measured by rocprofv3 PMC (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, the
+# factors that make a plain 1 GiB copy read 1 GiB and write 1 GiB); set to None whenever the kernel
+# changes until it is measured again
+PREFILL_TRAFFIC_BYTES = 985_047_268
 
 
 def parse():
@@ -46,6 +47,8 @@ def parse():
     ap.add_argument("--no-verify-fold", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill (for profilers)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy, the reference kernel for scaling HBM byte counters")
     return ap.parse_args()
 
 
@@ -196,6 +199,14 @@ def main():
         log("verify+fold: generating inputs and timing")
         vf = bench_verify_fold(args, torch, kda, sg, synth)
         log(f"verify+fold: {vf['verify_ms'] * 1e3:.0f} + {vf['fold_ms'] * 1e3:.0f} us")
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device copies (1 GiB read + 1 GiB written each)")
+        del src, dst
     cpu = None
     if not (args.no_cpu_baseline or args.prefill_only):
         import oracle

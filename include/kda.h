@@ -141,9 +141,13 @@ typedef struct {
  * sequences, T = cu_seqlens[n_seq] tokens, H = plan heads.
  *
  *  in        : q, k, v bf16 [T, H, 128]; gk fp32 [T, H, 128]; beta fp32 [T, H].
- *              Chunked-form precondition: gk >= -10 (the intra-chunk
- *              factorisation keeps exp(+-sum of gk over 8 tokens) in fp32
- *              range); the recurrent entry points accept any gk <= 0.
+ *              Chunked-form precondition: per key channel, the decay
+ *              summed over each half of a 32-token chunk (tokens 32m..32m+15
+ *              and 32m+16..32m+31 of a sequence) satisfies sum(-gk) <= 80,
+ *              which keeps the intra-chunk factors exp(+-partial sums) in
+ *              fp32/bf16 range; gk >= -5 everywhere is sufficient. Inputs
+ *              outside it give non-finite results, not an error code. The
+ *              recurrent entry points accept any gk <= 0.
  *  state_in  : fp32 [n_seq, H, 128, 128] or NULL (= zeros).
  *  state_out : fp32 [n_seq, H, 128, 128]; may equal state_in (in place);
  *              any other overlap is rejected.
