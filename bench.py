@@ -35,14 +35,14 @@ METRIC = "KDA prefill tokens*heads/s and verify+fold us/step at 1 GPU; % of roof
 # HBM bytes per prefill launch measured by rocprofv3 PMC (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, the
 # factors that make a plain 1 GiB copy read 1 GiB and write 1 GiB); set to None whenever the kernel
 # changes until it is measured again
-PREFILL_TRAFFIC_BYTES = 985_047_268
+PREFILL_TRAFFIC_BYTES = None
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--vf-steps", type=int, default=5, help="timed verify+fold steps")
     ap.add_argument("--no-verify-fold", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -64,6 +64,17 @@ def prefill_bytes(n_seq, L, H, with_state_in=True):
     return th * 1796 + st
 
 
+def settle(step, torch, seconds=0.25):
+    """Run the step untimed until `seconds` of wall time have passed: the GPU's clocks ramp up
+    over the first ~100 launches of a short kernel, and the timed region should see the steady
+    state. This precedes the W warm-up steps and is never part of the timed region."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+
+
 def bench_prefill(args, torch, kda, sg, synth):
     dev = "cuda:0"
     N, L, H = 4, 2048, 64
@@ -83,6 +94,7 @@ def bench_prefill(args, torch, kda, sg, synth):
     def step():
         kda.kda_chunk_prefill(plan, q, k, v, gk, beta, st, o, ws, state_in=S0, flags=flags)
 
+    settle(step, torch)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -130,9 +142,13 @@ def bench_verify_fold(args, torch, kda, sg, synth):
         if times is not None:
             times.append((ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])))
 
-    for _ in range(max(1, args.warmup // 2)):
+    def untimed():
         pool.copy_(pristine)
         one_step(None)
+
+    settle(untimed, torch)
+    for _ in range(max(1, args.warmup // 2)):
+        untimed()
     times = []
     for _ in range(args.vf_steps):
         pool.copy_(pristine)  # the fold advances states in place: restore outside the timed region

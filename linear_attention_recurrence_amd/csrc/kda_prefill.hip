@@ -17,9 +17,10 @@
 //   O = scale (Qt S0 + P W)                                       Qt = q e^G
 //   S_end = e^{G_31} S0 + K'^T W                                  K' = k e^{G_31 - G}
 // The intra-chunk factors are anchored at token 15 so each spans at most 16
-// tokens of decay; every factor is a product of a = exp(gk) over such a
-// span or its reciprocal, which stays in fp32/bf16 range when gk >= -5 (the
-// documented precondition of this path). The factors of Kt, Qt, K' are <= 1.
+// tokens of decay; every factor is a product of a = exp(gk) over such a span
+// or its reciprocal, which stays in fp32/bf16 range while the decay summed
+// over each 16-token half chunk is at most 80 (gk >= -5 suffices), the
+// documented precondition of this path. The factors of Kt, Qt, K' are <= 1.
 //
 // Precision (chosen by measuring each operand's rounding against the fp64
 // oracle): the intra-chunk factors Rq and Ck enter their MFMAs as bf16 hi + lo
@@ -27,63 +28,71 @@
 // touches the state uses fp16 operands (11-bit significand), with R and W as
 // fp16 hi + lo pairs. All accumulation is fp32 and the state stays fp32.
 //
-// Work decomposition: one 256-thread workgroup (4 waves) per (sequence, head)
-// item, persistent, pulling items from a longest-first list with an atomic
-// counter. Wave w owns value columns [32w, 32w+32); its 128x32 slice of the
-// fp32 state lives in MFMA accumulator registers for the whole sequence and
-// is fed back as the B operand of the next products by permuting the
-// reduction index identically in both operands. Raw inputs of the next chunk
-// stream into LDS with direct global->LDS loads while the current chunk
-// computes; operands that a product needs transposed are read with the
-// transposing LDS load (ds_read_b64_tr_b16) instead of being stored twice.
+// Work decomposition: one 512-thread workgroup per CU, persistent, pulling
+// (sequence, head) items from a longest-first list with an atomic counter.
+// Inside an item the workgroup is a two-stage pipeline over chunks, one
+// period per chunk, each period cut in two phases by workgroup barriers:
+//   consumer waves 0-3 run the serial state chain of chunk c. Wave w owns
+//     value columns [32w, 32w+32); its 128x32 slice of the fp32 state lives
+//     in MFMA accumulator registers for the whole sequence and is fed back as
+//     the B operand of the next products by permuting the reduction index
+//     identically in both operands. Phase 1: Kt S0, Qt S0, R, W = X R and
+//     O = Qt S0 + P W (stored straight from the accumulators); phase 2: the
+//     state update and the snapshot.
+//   producer waves 4-7 prepare chunk c+1. Phase 1: raw q, k, gk, beta
+//     (prefetched into registers one period earlier) become decay factors,
+//     the fp16 operand rows of the chain and per-wave partial A and P tiles;
+//     raw v goes from global memory straight into LDS (global_load_lds) for
+//     the chain. Phase 2: one wave sums the A partials and inverts I + A, one
+//     sums the P partials.
+// Everything the two stages exchange is double-buffered by chunk parity, so
+// a period needs just its two barriers. Operands that a product needs
+// transposed are read with the transposing LDS load (ds_read_b64_tr_b16)
+// instead of being stored twice.
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
-constexpr int C = 32;     // chunk length
-constexpr int TM = 136;   // token-major row stride (16-bit elements; 128 + 8 pad)
-constexpr int SQ = 40;    // 32x32 16-bit matrices
-constexpr int ATS = 36;   // 32x32 fp32 matrices
+constexpr int C = 32;      // chunk length
+constexpr int TM = 152;    // token-major row stride (16-bit elements; 128 + 24 pad: rows 12 banks apart)
+constexpr int SQ = 40;     // 32x32 16-bit matrices
+constexpr int ATS = 36;    // 32x32 fp32 matrices
+constexpr int NT = 512;    // threads per workgroup: 4 consumer + 4 producer waves
 
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void gbl_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-struct PrefillLds {
-  // operands of the current chunk, token-major [t][c]
-  uint16_t qt[C][TM];                  // fp16  q e^G
-  uint16_t kt[C][TM];                  // fp16  k e^G
-  uint16_t kp[C][TM];                  // fp16  k e^{G_31 - G}
-  uint16_t vt[C][TM];                  // bf16  v (copy out of the staging area)
+struct alignas(16) PrefillLds {
+  // chain operands, double-buffered by chunk parity; token-major [t][c]
+  uint16_t qt[2][C][TM];               // fp16  q e^G
+  uint16_t kt[2][C][TM];               // fp16  k e^G
+  uint16_t kp[2][C][TM];               // fp16  k e^{G_31 - G}
+  uint16_t vr[2][C][D];                // bf16  raw v, 16-byte chunks stored at chunk ^ (2 row & 15)
+  uint16_t xb[2][C][SQ];               // fp16  diagonal 16-blocks of X = (I + A)^-1, rows t, columns j
+  uint16_t an[2][16][SQ];              // fp16  -A[16 + i][j], the off-diagonal block of A
+  uint16_t pm[2][C][SQ];               // fp16  P, rows t, columns i
+  float beta[2][C];
+  float dlast[2][D];                   // e^{G_31} per key channel
+  // producer-only scratch
   float part[4][6][16][20];            // per-wave partial A and P tiles over 32 channels, [col][row] (padded)
-  float at[C][ATS];                    // A transposed: at[j][i] = A[i][j]
-  float xf[C][ATS];                    // diagonal blocks of X, fp32
-  uint16_t xb[C][SQ];                  // fp16 X, rows t, columns j
-  uint16_t pm[C][SQ];                  // fp16 P, rows t, columns i
-  float beta[C];
-  float dlast[D];                      // e^{G_31} per key channel
-  float so[C][D];                      // output tile of the previous chunk, flushed as whole rows
+  float ar[C][ATS];                    // diagonal blocks of A, fp32, rows i
   int item;
 };
 
 __device__ __forceinline__ uint2 lds8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
-__device__ __forceinline__ uint4 lds16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// 16 (or 4) bytes per lane from global memory into LDS at lds_base + size * lane
+// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane
 // (lds_base wave-uniform). Written as inline assembly on purpose: the compiler
 // would otherwise make every later LDS read wait for these asynchronous
-// writes, which turns the one-chunk-ahead prefetch into a synchronous load.
-// The kernel orders them itself: s_waitcnt vmcnt(0) plus a barrier before the
-// staging area is read. M0 is used by nothing else in this kernel.
-__device__ __forceinline__ void g2l(const void* src, void* lds_base, int bytes) {
+// writes. The kernel orders them itself: the issuing wave waits for vmcnt(0)
+// before the barrier that ends the period. M0 is used by nothing else here.
+__device__ __forceinline__ void g2l16(const void* src, void* lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_base);
-  if (bytes == 16)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory");
-  else
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(src) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory");
 }
 
 // transposing read: within each 16-lane group, lane j gets element r from the
@@ -95,8 +104,9 @@ __device__ __forceinline__ uint2 lds_tr(const uint16_t* p) {
 __device__ __forceinline__ f32x4 mfma_h(const f16x8& a, const f16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+// 16x16x16 fp16 MFMA: lane l holds A[l%16][4(l/16)+i], B[4(l/16)+i][l%16] (i < 4)
+__device__ __forceinline__ f32x4 mfma_h16(const f16x4& a, const f16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f16x8 as_f16x8(uint2 a, uint2 b) {
   return __builtin_bit_cast(f16x8, make_uint4(a.x, a.y, b.x, b.y));
@@ -111,6 +121,13 @@ __device__ __forceinline__ f16x8 to_h8(const f32x4& a, const f32x4& b) {
   for (int i = 0; i < 4; ++i) { r[i] = (_Float16)a[i]; r[4 + i] = (_Float16)b[i]; }
   return r;
 }
+__device__ __forceinline__ void split_h4(const f32x4& a, f16x4& hi, f16x4& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = (_Float16)a[i];
+    lo[i] = (_Float16)(a[i] - (float)hi[i]);
+  }
+}
 __device__ __forceinline__ void split_h8(const f32x4& a, const f32x4& b, f16x8& hi, f16x8& lo) {
   hi = to_h8(a, b);
 #pragma unroll
@@ -120,15 +137,16 @@ __device__ __forceinline__ void split_h8(const f32x4& a, const f32x4& b, f16x8& 
   }
 }
 
-#define KDA_ROW_SHR(v, s) __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(v), 0x110 + (s), 0xf, 0xf, false))
-#define KDA_ROW_BCAST15(v) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x15F, 0xf, 0xf, false))
+// row_shr:s with bound_ctrl: lanes shifted in from outside the 16-lane DPP row read 0
+#define KDA_ROW_SHR0(v, s) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x110 + (s), 0xf, 0xf, true))
+#define KDA_ROW_BCAST15(v) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x15F, 0xf, 0xf, true))
 
-// inclusive prefix product over the 16 lanes of a DPP row (lane order = token order)
-__device__ __forceinline__ float row_scan_mul(float v) {
-  v = v * KDA_ROW_SHR(v, 1);
-  v = v * KDA_ROW_SHR(v, 2);
-  v = v * KDA_ROW_SHR(v, 4);
-  v = v * KDA_ROW_SHR(v, 8);
+// inclusive prefix sum over the 16 lanes of a DPP row (lane order = token order)
+__device__ __forceinline__ float row_scan_add(float v) {
+  v = v + KDA_ROW_SHR0(v, 1);
+  v = v + KDA_ROW_SHR0(v, 2);
+  v = v + KDA_ROW_SHR0(v, 4);
+  v = v + KDA_ROW_SHR0(v, 8);
   return v;
 }
 
@@ -137,46 +155,256 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float (&f)[8]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) { f[2 * i] = bf2f(w[i] & 0xffffu); f[2 * i + 1] = bf2f(w[i] >> 16); }
 }
-__device__ __forceinline__ uint32_t pk_bf16(float a, float b) { return pack2(f2bf(a), f2bf(b)); }
 __device__ __forceinline__ uint32_t pk_f16(float a, float b) {
   return pack2(__builtin_bit_cast(uint16_t, (_Float16)a), __builtin_bit_cast(uint16_t, (_Float16)b));
-}
-// 8 products written as one 16-byte row chunk: bf16, bf16 hi/lo, or fp16
-__device__ __forceinline__ void put_bf16(uint16_t* dst, const float (&x)[8]) {
-  *reinterpret_cast<uint4*>(dst) = make_uint4(pk_bf16(x[0], x[1]), pk_bf16(x[2], x[3]), pk_bf16(x[4], x[5]), pk_bf16(x[6], x[7]));
-}
-__device__ __forceinline__ void put_bf16_split(uint16_t* hi, uint16_t* lo, const float (&x)[8]) {
-  uint16_t h[8], l[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) split_bf16(x[i], h[i], l[i]);
-  *reinterpret_cast<uint4*>(hi) = make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
-  *reinterpret_cast<uint4*>(lo) = make_uint4(pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7]));
 }
 __device__ __forceinline__ void put_f16(uint16_t* dst, const float (&x)[8]) {
   *reinterpret_cast<uint4*>(dst) = make_uint4(pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]), pk_f16(x[6], x[7]));
 }
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-prefill_kernel(PrefillArgs A) {
+// Raw inputs of one chunk as one producer lane needs them: channel octet
+// 8co..8co+7 of tokens tl and 16+tl (rows past the sequence end re-read its
+// last token, always in bounds, and are masked where they are used).
+struct Raw {
+  uint4 q0, q1, k0, k1;
+  float4 g0a, g0b, g1a, g1b;
+  float b0, b1;
+};
+
+// row0: (first token of the chunk) * H + h, wave-uniform; per-lane offsets stay 32-bit
+__device__ __forceinline__ void load_raw(Raw& r, const PrefillArgs& A, size_t row0, int nc, int co, int tl) {
+  const uint32_t H = A.n_heads;
+  const uint32_t t0 = min(tl, nc - 1) * H, t1 = min(16 + tl, nc - 1) * H;
+  const uint32_t e0 = t0 * D + 8 * co, e1 = t1 * D + 8 * co;
+  const uint16_t* q = A.q + row0 * D;
+  const uint16_t* k = A.k + row0 * D;
+  const float* gk = A.gk + row0 * D;
+  r.q0 = *reinterpret_cast<const uint4*>(q + e0);
+  r.q1 = *reinterpret_cast<const uint4*>(q + e1);
+  r.k0 = *reinterpret_cast<const uint4*>(k + e0);
+  r.k1 = *reinterpret_cast<const uint4*>(k + e1);
+  r.g0a = *reinterpret_cast<const float4*>(gk + e0);
+  r.g0b = *reinterpret_cast<const float4*>(gk + e0 + 4);
+  r.g1a = *reinterpret_cast<const float4*>(gk + e1);
+  r.g1b = *reinterpret_cast<const float4*>(gk + e1 + 4);
+  r.b0 = A.beta[row0 + t0];
+  r.b1 = A.beta[row0 + t1];
+}
+
+// raw v rows of a chunk straight into LDS: 4 rows of 256 bytes per instruction, rows
+// 16r + 4w .. 16r + 4w + 3 (r < 2) from wave w of a role; 16-byte chunks land at chunk ^ (2 row & 15)
+__device__ __forceinline__ void issue_v(const PrefillArgs& A, uint16_t (&dst)[C][D], size_t row0, int nc, int wu, int lane) {
+  const uint16_t* vsrc = A.v + row0 * D;
+  const uint32_t HD = (uint32_t)A.n_heads * D;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int prow = 16 * r + 4 * wu + (lane >> 4);
+    const uint32_t e = (uint32_t)min(prow, nc - 1) * HD + 8 * ((lane & 15) ^ ((2 * prow) & 15));
+    g2l16(vsrc + e, &dst[16 * r + 4 * wu][0]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// producer, phase 1 of the period before chunk c: decay factors, the chain's
+// operand rows, partial A and P tiles over this wave's 32 channels
+__device__ __forceinline__ void stage1(PrefillLds& L, const Raw& cur, int nc, int b, int pw, int g, int lr) {
+  const int co = 4 * pw + g;  // channel octet 8co..8co+7
+  const int tl = lr;          // tokens tl (block 0) and 16+tl (block 1)
+  const int c8 = 8 * co;
+  const bool ok0 = tl < nc, ok1 = 16 + tl < nc;
+  // gk in log2 units; tokens past the end decay by nothing
+  constexpr float kLog2e = 1.4426950408889634f;
+  float l0[8], l1[8];
+  {
+    const float gx[8] = {cur.g0a.x, cur.g0a.y, cur.g0a.z, cur.g0a.w, cur.g0b.x, cur.g0b.y, cur.g0b.z, cur.g0b.w};
+    const float gy[8] = {cur.g1a.x, cur.g1a.y, cur.g1a.z, cur.g1a.w, cur.g1b.x, cur.g1b.y, cur.g1b.z, cur.g1b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { l0[i] = ok0 ? gx[i] * kLog2e : 0.f; l1[i] = ok1 ? gy[i] * kLog2e : 0.f; }
+  }
+  const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+  if (pw == 0 && g == 0) {
+    L.beta[b][tl] = ok0 ? cur.b0 : 0.f;
+    L.beta[b][16 + tl] = ok1 ? cur.b1 : 0.f;
+  }
+  float k0[8], k1[8], q0[8], q1[8];
+  unpack_bf16x8(ok0 ? cur.k0 : zero4, k0); unpack_bf16x8(ok1 ? cur.k1 : zero4, k1);
+  unpack_bf16x8(ok0 ? cur.q0 : zero4, q0); unpack_bf16x8(ok1 ? cur.q1 : zero4, q1);
+  float xr0[8], xr1[8], yc0[8], yc1[8], e0[8], e1[8], f0[8], f1[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    // prefix sums inside each 16-token block, then the four exponentials
+    const float s0 = row_scan_add(l0[i]), s1 = row_scan_add(l1[i]);  // log2 of e^{G_t - G_-1}, e^{G_t - G_15}
+    const float p0 = __builtin_amdgcn_exp2f(s0), r0 = __builtin_amdgcn_exp2f(-s0);
+    const float p1 = __builtin_amdgcn_exp2f(s1), r1 = __builtin_amdgcn_exp2f(-s1);
+    const float T0 = KDA_ROW_BCAST15(p0), T1 = KDA_ROW_BCAST15(p1);   // block totals
+    xr0[i] = p0 * KDA_ROW_BCAST15(r0);       // e^{G_t - G_15}, block 0 (lane 15's r0 is 1 / T0)
+    xr1[i] = p1;
+    yc0[i] = T0 * r0;                         // e^{G_15 - G_t}, block 0
+    yc1[i] = r1;
+    e0[i] = p0;                               // e^{G_t}
+    e1[i] = T0 * p1;
+    f0[i] = yc0[i] * T1;                      // e^{G_31 - G_t}
+    f1[i] = T1 * r1;
+    if (tl == 0) L.dlast[b][c8 + i] = T0 * T1;
+  }
+  // fp16 operands of the state products, token-major rows tl and 16+tl
+  float x[8];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int t = 16 * blk + tl;
+    const float(&kk)[8] = blk ? k1 : k0;
+    const float(&qq)[8] = blk ? q1 : q0;
+    const float(&ee)[8] = blk ? e1 : e0;
+    const float(&ff)[8] = blk ? f1 : f0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = qq[i] * ee[i];
+    put_f16(&L.qt[b][t][c8], x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = kk[i] * ee[i];
+    put_f16(&L.kt[b][t][c8], x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = kk[i] * ff[i];
+    put_f16(&L.kp[b][t][c8], x);
+  }
+  // A and P over this wave's 32 channels, straight from registers: lane (g, lr) holds
+  // channels 32pw+8g..+7 of tokens lr (block 0) and 16+lr (block 1), which is the
+  // A-operand fragment of row lr and the B-operand fragment of column lr
+  bf16x8 rk0, rk1, rq0h, rq0l, rq1h, rq1l, ck0h, ck0l, ck1h, ck1l;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    rk0[i] = (__bf16)(k0[i] * xr0[i]);
+    rk1[i] = (__bf16)(k1[i] * xr1[i]);
+    float v = q0[i] * xr0[i]; rq0h[i] = (__bf16)v; rq0l[i] = (__bf16)(v - (float)rq0h[i]);
+    v = q1[i] * xr1[i];       rq1h[i] = (__bf16)v; rq1l[i] = (__bf16)(v - (float)rq1h[i]);
+    v = k0[i] * yc0[i];       ck0h[i] = (__bf16)v; ck0l[i] = (__bf16)(v - (float)ck0h[i]);
+    v = k1[i] * yc1[i];       ck1h[i] = (__bf16)v; ck1l[i] = (__bf16)(v - (float)ck1h[i]);
+  }
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[6];
+  acc[0] = mfma16(rk0, ck0l, mfma16(rk0, ck0h, z4));                          // A 00
+  acc[1] = mfma16(rk1, ck1l, mfma16(rk1, ck1h, z4));                          // A 11
+  acc[2] = mfma16(rk1, ck0l, mfma16(rk1, ck0h, z4));                          // A 10
+  acc[3] = mfma16(rq0l, ck0h, mfma16(rq0h, ck0l, mfma16(rq0h, ck0h, z4)));   // P 00
+  acc[4] = mfma16(rq1l, ck1h, mfma16(rq1h, ck1l, mfma16(rq1h, ck1h, z4)));   // P 11
+  acc[5] = mfma16(rq1l, ck0h, mfma16(rq1h, ck0l, mfma16(rq1h, ck0h, z4)));   // P 10
+#pragma unroll
+  for (int tl6 = 0; tl6 < 6; ++tl6)
+    *reinterpret_cast<f32x4*>(&L.part[pw][tl6][lr][4 * g]) = acc[tl6];
+}
+
+// sums of the four channel slices of NTL 16x16 tiles t0..t0+NTL-1: the lane gets rows
+// i0..i0+3 of column j of each. All reads are issued before the first sum.
+template <int NTL>
+__device__ __forceinline__ void reduce_tiles(const PrefillLds& L, int t0, int j, int i0, f32x4 (&s4)[NTL]) {
+  f32x4 pv[NTL][4];
+#pragma unroll
+  for (int tile = 0; tile < NTL; ++tile)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) pv[tile][w] = *reinterpret_cast<const f32x4*>(&L.part[w][t0 + tile][j][i0]);
+#pragma unroll
+  for (int tile = 0; tile < NTL; ++tile) {
+    s4[tile] = pv[tile][0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s4[tile][r] += pv[tile][w][r];
+  }
+}
+
+// producer wave 0, phase 2: the diagonal 16-blocks of A (beta-scaled strict lower parts of the
+// summed tiles) and of X = (I + A)^-1. The off-diagonal block of X is never formed: the chain
+// applies it as W1 = X11 (R1 - A10 W0).
+__device__ __forceinline__ void stage2_solve(PrefillLds& L, int b, int lane) {
+  const int g = lane >> 4, lr = lane & 15;
+  {
+    const int j = lane >> 2, i0 = 4 * (lane & 3);
+    f32x4 sums[2];
+    reduce_tiles<2>(L, 0, j, i0, sums);
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {  // A00, A11
+      const f32x4 s4 = sums[blk];
+      const float4 b4 = *reinterpret_cast<const float4*>(&L.beta[b][16 * blk + i0]);
+      const int jg = 16 * blk + j, ig = 16 * blk + i0;
+      L.ar[ig][jg] = (jg < ig) ? s4[0] * b4.x : 0.f;
+      L.ar[ig + 1][jg] = (jg < ig + 1) ? s4[1] * b4.y : 0.f;
+      L.ar[ig + 2][jg] = (jg < ig + 2) ? s4[2] * b4.z : 0.f;
+      L.ar[ig + 3][jg] = (jg < ig + 3) ? s4[3] * b4.w : 0.f;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  // Forward substitution on rows. DPP row g of the wave (16 lanes) holds block
+  // blk = g & 1, lane lr = row i of it, and the columns of parity par = g >> 1:
+  // x[m] = X[i][2m + par]. Step kk subtracts A[i][kk] times row kk, which
+  // row_newbcast:kk reads from lane kk of the same DPP row; row kk has no
+  // entries right of column kk, so column pairs beyond kk are skipped.
+  const int blk = g & 1, par = g >> 1, i = lr;
+  float arow[16];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const float4 t4 = *reinterpret_cast<const float4*>(&L.ar[16 * blk + i][16 * blk + 4 * q4]);
+    arow[4 * q4] = -t4.x; arow[4 * q4 + 1] = -t4.y; arow[4 * q4 + 2] = -t4.z; arow[4 * q4 + 3] = -t4.w;
+  }
+  float x[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) x[m] = (2 * m + par == i) ? 1.f : 0.f;
+#define KDA_SOLVE_STEP(kk)                                                                                  \
+  _Pragma("unroll") for (int m = 0; 2 * m <= (kk); ++m) {                                                   \
+    const float xk_ = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[m]), 0x150 + (kk), 0xf, 0xf, true)); \
+    x[m] = __builtin_fmaf(arow[kk], xk_, x[m]);                                                             \
+  }
+  KDA_SOLVE_STEP(0) KDA_SOLVE_STEP(1) KDA_SOLVE_STEP(2) KDA_SOLVE_STEP(3) KDA_SOLVE_STEP(4)
+  KDA_SOLVE_STEP(5) KDA_SOLVE_STEP(6) KDA_SOLVE_STEP(7) KDA_SOLVE_STEP(8) KDA_SOLVE_STEP(9)
+  KDA_SOLVE_STEP(10) KDA_SOLVE_STEP(11) KDA_SOLVE_STEP(12) KDA_SOLVE_STEP(13) KDA_SOLVE_STEP(14)
+#undef KDA_SOLVE_STEP
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+    L.xb[b][16 * blk + i][16 * blk + 2 * m + par] = __builtin_bit_cast(uint16_t, (_Float16)x[m]);
+}
+
+// producer wave 2, phase 2: -A10 = -(beta-scaled summed tile), fp16, for the chain's W1
+__device__ __forceinline__ void stage2_a10(PrefillLds& L, int b, int lane) {
+  const int j = lane >> 2, i0 = 4 * (lane & 3);
+  f32x4 sums[1];
+  reduce_tiles<1>(L, 2, j, i0, sums);
+  const float4 b4 = *reinterpret_cast<const float4*>(&L.beta[b][16 + i0]);
+  const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) L.an[b][i0 + r][j] = __builtin_bit_cast(uint16_t, (_Float16)(-sums[0][r] * bv[r]));
+}
+
+// producer wave 1, phase 2: P = lower part (diagonal included) of the summed tiles, fp16
+__device__ __forceinline__ void stage2_p(PrefillLds& L, int b, int lane) {
+  const int j = lane >> 2, i0 = 4 * (lane & 3);
+  f32x4 sums[3];
+  reduce_tiles<3>(L, 3, j, i0, sums);
+#pragma unroll
+  for (int tile = 3; tile < 6; ++tile) {  // P00, P11, P10
+    const int I = tile == 3 ? 0 : 1, J = tile == 4 ? 1 : 0;
+    const f32x4 s4 = sums[tile - 3];
+    const int jg = 16 * J + j;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int ig = 16 * I + i0 + r;
+      L.pm[b][ig][jg] = (jg <= ig) ? __builtin_bit_cast(uint16_t, (_Float16)s4[r]) : (uint16_t)0;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
   __shared__ PrefillLds L;
-  // raw inputs of the next chunk, written by direct global->LDS loads
-  __shared__ uint16_t Sq[C][D], Sk[C][D], Sv[C][D];
-  __shared__ float Sg[C][D];
-  __shared__ float Sbeta[C];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, lr = lane & 15;  // MFMA lane group and lane row/column
-  const int co = 4 * wave + g;              // prep: channel octet 8co..8co+7
-  const int tl = lr;                        // prep: token tl of block 0 and 16+tl of block 1
+  const bool producer = wave >= 4;          // wave-uniform role
+  const int rw = wave & 3;                  // wave index within the role
+  const int rwu = __builtin_amdgcn_readfirstlane(rw);
   const int H = A.n_heads;
-  const int wu = __builtin_amdgcn_readfirstlane(wave);
 
-  // constant zero blocks: A, P and X are lower triangular in 16-blocks
-  for (int e = tid; e < 16 * 16; e += 256) {
-    const int i = e >> 4, j = 16 + (e & 15);
-    L.at[j][i] = 0.f;
-    L.pm[i][j] = 0;
-    L.xb[i][j] = 0;
+  // constant zero blocks: P is lower triangular in 16-blocks
+  for (int e = tid; e < 2 * 16 * 16; e += NT) {
+    const int b = e >> 8, i = (e >> 4) & 15, j = 16 + (e & 15);
+    L.pm[b][i][j] = 0;
   }
 
   for (;;) {
@@ -191,357 +419,221 @@ prefill_kernel(PrefillArgs A) {
     const int len = wi.w;
     if (n < 0 || n >= A.n_seq || h < 0 || h >= H || tok0 < 0 || len < 0 || tok0 + len > A.total_tokens) continue;
     const size_t unit = (size_t)n * H + h;
-
-    // state slice of this wave in accumulator layout: S[mc][nv] holds rows 16mc+4g+r, column 32w+16nv+lr
-    f32x4 S[8][2];
-    if (A.state_in) {
-      const float* src = A.state_in + unit * D * D;
-#pragma unroll
-      for (int mc = 0; mc < 8; ++mc)
-#pragma unroll
-        for (int nv = 0; nv < 2; ++nv)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) S[mc][nv][r] = src[(size_t)(16 * mc + 4 * g + r) * D + 32 * wave + 16 * nv + lr];
-    } else {
-#pragma unroll
-      for (int mc = 0; mc < 8; ++mc)
-#pragma unroll
-        for (int nv = 0; nv < 2; ++nv) S[mc][nv] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    // Raw inputs of a chunk are copied into LDS with direct global->LDS loads
-    // issued one chunk ahead; rows past the sequence end re-read its last
-    // token (always in bounds) and are masked in the prep.
     const int nch = (len + C - 1) / C;
-    // Staging rows are stored with their 16-byte chunks permuted (physical
-    // chunk = logical chunk ^ (row & 15)) so the prep's column reads across 16
-    // rows hit 16 different LDS banks; each lane fetches the chunk that lands
-    // in its fixed LDS slot.
-    auto issue = [&](int ch) {
-      const int nc = min(C, len - C * ch);
-      const int64_t trow0 = tok0 + C * ch;
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {  // q, k, v: 256-byte rows (16 chunks), 4 rows per wave
-        const int prow = 16 * r + 4 * wu + (lane >> 4);
-        const int row = min(prow, nc - 1);
-        const size_t e = ((size_t)(trow0 + row) * H + h) * D + 8 * ((lane & 15) ^ (prow & 15));
-        g2l(A.q + e, &Sq[16 * r + 4 * wu][0], 16);
-        g2l(A.k + e, &Sk[16 * r + 4 * wu][0], 16);
-        g2l(A.v + e, &Sv[16 * r + 4 * wu][0], 16);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {  // gk: 512-byte rows (32 chunks), 2 rows per wave
-        const int prow = 8 * r + 2 * wu + (lane >> 5);
-        const int row = min(prow, nc - 1);
-        const size_t e = ((size_t)(trow0 + row) * H + h) * D + 4 * ((lane & 31) ^ (prow & 15));
-        g2l(A.gk + e, &Sg[8 * r + 2 * wu][0], 16);
-      }
-      if (wu == 0 && lane < C) g2l(A.beta + (size_t)(trow0 + min(lane, nc - 1)) * H + h, &Sbeta[0], 4);
-    };
-    // whole-row stores of a staged output tile (8 threads x 64 bytes per token row)
-    auto flush = [&](int ch) {
-      const int nc = min(C, len - C * ch);
-      const int row = tid >> 3, c0 = 16 * (tid & 7);
-      if (row < nc) {
-        float* dst = A.o + ((size_t)(tok0 + C * ch + row) * H + h) * D + c0;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<float4*>(dst + 4 * q4) = *reinterpret_cast<const float4*>(&L.so[row][c0 + 4 * q4]);
-      }
-    };
-    if (nch > 0) issue(0);
 
-    for (int ch = 0; ch < nch; ++ch) {
-      const int nc = min(C, len - C * ch);
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's staging loads (and older stores) are complete
-      __syncthreads();
-      if (ch > 0) flush(ch - 1);
-
-      // ---------------- prep: decay factors and operand matrices ----------------
-      {
-        const int c8 = 8 * co;
-        const bool ok0 = tl < nc, ok1 = 16 + tl < nc;
-        float a0[8], a1[8];
-        {
-          // logical gk chunks 2co and 2co+1 of rows tl and 16+tl, at their permuted positions
-          const float4 x0 = *reinterpret_cast<const float4*>(&Sg[tl][4 * ((2 * co) ^ tl)]);
-          const float4 x1 = *reinterpret_cast<const float4*>(&Sg[tl][4 * ((2 * co + 1) ^ tl)]);
-          const float4 y0 = *reinterpret_cast<const float4*>(&Sg[16 + tl][4 * ((2 * co) ^ tl)]);
-          const float4 y1 = *reinterpret_cast<const float4*>(&Sg[16 + tl][4 * ((2 * co + 1) ^ tl)]);
-          const float gx[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-          const float gy[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-#pragma unroll
-          for (int i = 0; i < 8; ++i) { a0[i] = ok0 ? __expf(gx[i]) : 1.f; a1[i] = ok1 ? __expf(gy[i]) : 1.f; }
-        }
-        const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
-        const int sc = 8 * (co ^ tl);  // permuted position of logical chunk co (rows tl and 16+tl share row & 15)
-        const uint4 k0u = ok0 ? lds16(&Sk[tl][sc]) : zero4, k1u = ok1 ? lds16(&Sk[16 + tl][sc]) : zero4;
-        const uint4 q0u = ok0 ? lds16(&Sq[tl][sc]) : zero4, q1u = ok1 ? lds16(&Sq[16 + tl][sc]) : zero4;
-        *reinterpret_cast<uint4*>(&L.vt[tl][c8]) = ok0 ? lds16(&Sv[tl][sc]) : zero4;
-        *reinterpret_cast<uint4*>(&L.vt[16 + tl][c8]) = ok1 ? lds16(&Sv[16 + tl][sc]) : zero4;
-        if (tid < C) L.beta[tid] = tid < nc ? Sbeta[tid] : 0.f;
-        float k0[8], k1[8], q0[8], q1[8];
-        unpack_bf16x8(k0u, k0); unpack_bf16x8(k1u, k1);
-        unpack_bf16x8(q0u, q0); unpack_bf16x8(q1u, q1);
-        float xr0[8], xr1[8], yc0[8], yc1[8], e0[8], e1[8], f0[8], f1[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float p0 = row_scan_mul(a0[i]), p1 = row_scan_mul(a1[i]);  // e^{G_t - G_-1}, e^{G_t - G_15}
-          const float T0 = KDA_ROW_BCAST15(p0), T1 = KDA_ROW_BCAST15(p1);   // block totals
-          const float r0 = __builtin_amdgcn_rcpf(p0), r1 = __builtin_amdgcn_rcpf(p1);
-          xr0[i] = p0 * __builtin_amdgcn_rcpf(T0);  // e^{G_t - G_15}, block 0
-          xr1[i] = p1;
-          yc0[i] = T0 * r0;                         // e^{G_15 - G_t}, block 0
-          yc1[i] = r1;
-          e0[i] = p0;                               // e^{G_t}
-          e1[i] = T0 * p1;
-          f0[i] = yc0[i] * T1;                      // e^{G_31 - G_t}
-          f1[i] = T1 * r1;
-          if (tl == 0) L.dlast[c8 + i] = T0 * T1;
-        }
-        // fp16 operands of the state products, token-major rows tl and 16+tl
-        float x[8];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int t = 16 * b + tl;
-          const float(&kk)[8] = b ? k1 : k0;
-          const float(&qq)[8] = b ? q1 : q0;
-          const float(&ee)[8] = b ? e1 : e0;
-          const float(&ff)[8] = b ? f1 : f0;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) x[i] = qq[i] * ee[i];
-          put_f16(&L.qt[t][c8], x);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) x[i] = kk[i] * ee[i];
-          put_f16(&L.kt[t][c8], x);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) x[i] = kk[i] * ff[i];
-          put_f16(&L.kp[t][c8], x);
-        }
-        // A and P over this wave's 32 channels, straight from registers: lane (g, lr) holds
-        // channels 32w+8g..+7 of tokens lr (block 0) and 16+lr (block 1), which is the
-        // A-operand fragment of row lr and the B-operand fragment of column lr
-        bf16x8 rk0, rk1, rq0h, rq0l, rq1h, rq1l, ck0h, ck0l, ck1h, ck1l;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          rk0[i] = (__bf16)(k0[i] * xr0[i]);
-          rk1[i] = (__bf16)(k1[i] * xr1[i]);
-          float v = q0[i] * xr0[i]; rq0h[i] = (__bf16)v; rq0l[i] = (__bf16)(v - (float)rq0h[i]);
-          v = q1[i] * xr1[i];       rq1h[i] = (__bf16)v; rq1l[i] = (__bf16)(v - (float)rq1h[i]);
-          v = k0[i] * yc0[i];       ck0h[i] = (__bf16)v; ck0l[i] = (__bf16)(v - (float)ck0h[i]);
-          v = k1[i] * yc1[i];       ck1h[i] = (__bf16)v; ck1l[i] = (__bf16)(v - (float)ck1h[i]);
-        }
-        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-        f32x4 acc[6];
-        acc[0] = mfma16(rk0, ck0l, mfma16(rk0, ck0h, z4));                          // A 00
-        acc[1] = mfma16(rk1, ck1l, mfma16(rk1, ck1h, z4));                          // A 11
-        acc[2] = mfma16(rk1, ck0l, mfma16(rk1, ck0h, z4));                          // A 10
-        acc[3] = mfma16(rq0l, ck0h, mfma16(rq0h, ck0l, mfma16(rq0h, ck0h, z4)));   // P 00
-        acc[4] = mfma16(rq1l, ck1h, mfma16(rq1h, ck1l, mfma16(rq1h, ck1h, z4)));   // P 11
-        acc[5] = mfma16(rq1l, ck0h, mfma16(rq1h, ck0l, mfma16(rq1h, ck0h, z4)));   // P 10
-#pragma unroll
-        for (int tl6 = 0; tl6 < 6; ++tl6)
-          *reinterpret_cast<f32x4*>(&L.part[wave][tl6][lr][4 * g]) = acc[tl6];
-      }
-      __syncthreads();
-      // the staging area is consumed: next chunk's raw inputs stream in while this chunk computes
-      if (ch + 1 < nch) issue(ch + 1);
-
-      // reduce the four channel slices of A and P; mask, scale A rows by beta
-      if (tid < 192) {
-        const int tile = tid >> 5, j = (tid >> 1) & 15, i0 = 8 * (tid & 1);
-        const int I = (tile % 3) == 0 ? 0 : 1, J = (tile % 3) == 1 ? 1 : 0;
-        float sum[8];
-#pragma unroll
-        for (int q8 = 0; q8 < 2; ++q8) {
-          f32x4 s4 = *reinterpret_cast<const f32x4*>(&L.part[0][tile][j][i0 + 4 * q8]);
-#pragma unroll
-          for (int w = 1; w < 4; ++w) {
-            const f32x4 p4 = *reinterpret_cast<const f32x4*>(&L.part[w][tile][j][i0 + 4 * q8]);
-            s4[0] += p4[0]; s4[1] += p4[1]; s4[2] += p4[2]; s4[3] += p4[3];
+    // Both roles run nch + 1 periods of two barriers each. Period p runs the
+    // chain of chunk p (p >= 0) beside the preparation of chunk p + 1.
+    // Inside each role the lane index is made opaque once per item, so that the compiler
+    // cannot hoist one role's lane-dependent addresses out of the item loop, where they would
+    // stay live (and spill) while the other role runs.
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    const int g_o = lane_o >> 4, lr_o = lane_o & 15;
+    if (producer) {
+      const int pw = rw;
+      const int lane = lane_o, g = g_o, lr = lr_o;
+      // Raw inputs are prefetched into registers two periods ahead, alternating between two
+      // sets: chunk c lives in set c & 1 from the period that issues it (c - 3) until its
+      // stage 1 (period c - 1). Every period issues the same loads (past the last chunk they
+      // re-read it, which the cache serves), so the compiler's own waits before each use can
+      // count exactly and leave the newer set in flight.
+      if (nch == 0) {
+        __syncthreads();
+        __syncthreads();
+      } else {
+        Raw ra, rb;
+        auto issue = [&](Raw& r, int c) {
+          c = min(c, nch - 1);
+          load_raw(r, A, (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), 4 * pw + g, lr);
+        };
+        issue(ra, 0);
+        asm volatile("" ::: "memory");  // keep the issue order: set a, then set b
+        issue(rb, 1);
+        auto period = [&](int p, Raw& use) {
+          const int c1 = p + 1, b1 = c1 & 1;
+          if (c1 < nch) stage1(L, use, min(C, len - C * c1), b1, pw, g, lr);
+          __syncthreads();
+          issue(use, c1 + 2);
+          if (c1 < nch) {
+            if (pw == 1) stage2_p(L, b1, lane);
+            else if (pw == 2) stage2_a10(L, b1, lane);
           }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sum[4 * q8 + r] = s4[r];
+          __syncthreads();
+        };
+        // periods -1 .. nch-1 in pairs, so that both sets' loads are issued on every path
+        // around the loop
+        int p = -1;
+        for (; p + 1 < nch; p += 2) {
+          period(p, ra);
+          period(p + 1, rb);
         }
-        const int jg = 16 * J + j;
-        if (tile < 3) {
-          float av[8];
-#pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            const int ig = 16 * I + i0 + r;
-            av[r] = (jg < ig) ? sum[r] * L.beta[ig] : 0.f;
-          }
-          *reinterpret_cast<float4*>(&L.at[jg][16 * I + i0]) = make_float4(av[0], av[1], av[2], av[3]);
-          *reinterpret_cast<float4*>(&L.at[jg][16 * I + i0 + 4]) = make_float4(av[4], av[5], av[6], av[7]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            const int ig = 16 * I + i0 + r;
-            L.pm[ig][jg] = (jg <= ig) ? __builtin_bit_cast(uint16_t, (_Float16)sum[r]) : (uint16_t)0;
-          }
-        }
+        if (p < nch) period(p, ra);
       }
-      __syncthreads();  // A (transposed, fp32) and P (fp16) are complete
-
-      // ---------------- X = (I + A)^-1 (wave 0) ----------------
-      if (wave == 0) {
-        if (lane < 32) {
-          // diagonal blocks by forward substitution, one column per lane
-          const int b = lane >> 4, jl = lane & 15;
-          float xv[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) xv[i] = (i == jl) ? 1.f : 0.f;
-#pragma unroll
-          for (int kk = 0; kk < 15; ++kk) {
-            const float* col = &L.at[16 * b + kk][16 * b];  // A[16b+i][16b+kk], i = 0..15
-            float av[16];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              const float4 t4 = *reinterpret_cast<const float4*>(col + 4 * q4);
-              av[4 * q4] = t4.x; av[4 * q4 + 1] = t4.y; av[4 * q4 + 2] = t4.z; av[4 * q4 + 3] = t4.w;
-            }
-            const float xk = xv[kk];
-#pragma unroll
-            for (int i = kk + 1; i < 16; ++i) xv[i] = __builtin_fmaf(-av[i], xk, xv[i]);
-          }
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            L.xf[16 * b + i][16 * b + jl] = xv[i];
-            L.xb[16 * b + i][16 * b + jl] = __builtin_bit_cast(uint16_t, (_Float16)xv[i]);
-          }
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-        __builtin_amdgcn_wave_barrier();
-        // X10 = -X11 (A10 X00) with fp32 MFMAs; the reduction index of step s in lane group g is 4g+s
-        f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) y = mfma_f32(L.at[4 * g + s][16 + lr], L.xf[4 * g + s][lr], y);
-        f32x4 x10 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) x10 = mfma_f32(L.xf[16 + lr][16 + 4 * g + s], y[s], x10);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) L.xb[16 + 4 * g + r][lr] = __builtin_bit_cast(uint16_t, (_Float16)(-x10[r]));
-      }
-
-      // ---------------- Kt S0 and Qt S0 (independent of X) ----------------
-      f32x4 KS[2][2], QS[2][2];
-      {
-        f16x8 Sh[4][2];
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int nv = 0; nv < 2; ++nv) Sh[s][nv] = to_h8(S[2 * s][nv], S[2 * s + 1][nv]);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-          for (int nv = 0; nv < 2; ++nv) { KS[mt][nv] = f32x4{0.f, 0.f, 0.f, 0.f}; QS[mt][nv] = f32x4{0.f, 0.f, 0.f, 0.f}; }
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const int m = 16 * mt + lr;
-            const f16x8 kr = perm_h(&L.kt[m][32 * s], g);
-            const f16x8 qr = perm_h(&L.qt[m][32 * s], g);
-#pragma unroll
-            for (int nv = 0; nv < 2; ++nv) {
-              KS[mt][nv] = mfma_h(kr, Sh[s][nv], KS[mt][nv]);
-              QS[mt][nv] = mfma_h(qr, Sh[s][nv], QS[mt][nv]);
-            }
-          }
-        }
-      }
-      __syncthreads();  // X is complete
-
-      // ---------------- R = diag(beta)(V - Kt S0), W = X R ----------------
-      f32x4 W[2][2];
-      {
-        f16x8 Rh[2], Rl[2];
-#pragma unroll
-        for (int nv = 0; nv < 2; ++nv) {
-          f32x4 R[2];
-          const int c0 = 32 * wave + 16 * nv;
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            // V[16mt+4g+r][c0+lr] through the transposing read
-            const uint2 vv = lds_tr(&L.vt[16 * mt + 4 * g + (lr >> 2)][c0 + 4 * (lr & 3)]);
-            const float4 b4 = *reinterpret_cast<const float4*>(&L.beta[16 * mt + 4 * g]);
-            R[mt][0] = b4.x * (bf2f(vv.x & 0xffffu) - KS[mt][nv][0]);
-            R[mt][1] = b4.y * (bf2f(vv.x >> 16) - KS[mt][nv][1]);
-            R[mt][2] = b4.z * (bf2f(vv.y & 0xffffu) - KS[mt][nv][2]);
-            R[mt][3] = b4.w * (bf2f(vv.y >> 16) - KS[mt][nv][3]);
-          }
-          split_h8(R[0], R[1], Rh[nv], Rl[nv]);
-        }
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const f16x8 xa = perm_h(&L.xb[16 * mt + lr][0], g);
-#pragma unroll
-          for (int nv = 0; nv < 2; ++nv) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma_h(xa, Rh[nv], acc);
-            acc = mfma_h(xa, Rl[nv], acc);
-            W[mt][nv] = acc;
-          }
-        }
-      }
-      f16x8 Wh[2], Wl[2];
-#pragma unroll
-      for (int nv = 0; nv < 2; ++nv) split_h8(W[0][nv], W[1][nv], Wh[nv], Wl[nv]);
-
-      // ---------------- O = scale (Qt S0 + P W) into the output staging tile ----------------
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const f16x8 pa = perm_h(&L.pm[16 * mt + lr][0], g);
-#pragma unroll
-        for (int nv = 0; nv < 2; ++nv) {
-          f32x4 acc = QS[mt][nv];
-          acc = mfma_h(pa, Wh[nv], acc);
-          acc = mfma_h(pa, Wl[nv], acc);
-          const int v = 32 * wave + 16 * nv + lr;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) L.so[16 * mt + 4 * g + r][v] = A.scale * acc[r];
-        }
-      }
-
-      // ---------------- S = e^{G_31} S0 + K'^T W ----------------
-#pragma unroll
-      for (int mc = 0; mc < 8; ++mc) {
-        const float4 d4 = *reinterpret_cast<const float4*>(&L.dlast[16 * mc + 4 * g]);
-        // K'^T rows 16mc+lr, reduction positions t = 4g+r and 16+4g+r, via the transposing read
-        const uint16_t* base = &L.kp[4 * g + (lr >> 2)][16 * mc + 4 * (lr & 3)];
-        const f16x8 ka = as_f16x8(lds_tr(base), lds_tr(base + 16 * TM));
-#pragma unroll
-        for (int nv = 0; nv < 2; ++nv) {
-          f32x4 acc = S[mc][nv];
-          acc[0] *= d4.x; acc[1] *= d4.y; acc[2] *= d4.z; acc[3] *= d4.w;
-          acc = mfma_h(ka, Wh[nv], acc);
-          acc = mfma_h(ka, Wl[nv], acc);
-          S[mc][nv] = acc;
-        }
-      }
-
-      // ---------------- snapshot at chunk ends p with p % interval == 0 ----------------
-      const int p = C * ch + nc;
-      if (A.snap_interval > 0 && p % A.snap_interval == 0) {
-        const int m = p / A.snap_interval;
-        float* dst = A.snap + (((size_t)n * A.snap_slots + (m - 1) % A.snap_slots) * H + h) * D * D;
+    } else {
+      const int cw = rw;
+      const int lane = lane_o, g = g_o, lr = lr_o;
+      // This lane's element of a row-major [128][128] state tile is (16mc+4g+r, 32cw+16nv+lr), at
+      // tile + soff + (16mc+r)*D + 16nv. soff is made opaque here so that the compiler keeps one
+      // offset per lane instead of hoisting all 64 element offsets out of the item loop.
+      int soff = 4 * g * D + 32 * cw + lr;
+      asm volatile("" : "+v"(soff));
+      // state slice of this wave in accumulator layout: S[mc][nv] holds rows 16mc+4g+r, column 32cw+16nv+lr
+      f32x4 S[8][2];
+      if (A.state_in) {
+        const float* src = A.state_in + unit * D * D + soff;
 #pragma unroll
         for (int mc = 0; mc < 8; ++mc)
 #pragma unroll
           for (int nv = 0; nv < 2; ++nv)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(size_t)(16 * mc + 4 * g + r) * D + 32 * wave + 16 * nv + lr] = S[mc][nv][r];
+            for (int r = 0; r < 4; ++r) S[mc][nv][r] = src[(16 * mc + r) * D + 16 * nv];
+      } else {
+#pragma unroll
+        for (int mc = 0; mc < 8; ++mc)
+#pragma unroll
+          for (int nv = 0; nv < 2; ++nv) S[mc][nv] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-    }
-    __syncthreads();
-    if (nch > 0) flush(nch - 1);
+      f16x8 Wh[2], Wl[2];
+      // raw v of chunk c is loaded into vr[c & 1] two periods ahead (chunks 0 and 1 here)
+      if (nch > 0) issue_v(A, L.vr[0], (size_t)tok0 * H + h, min(C, len), cw, lane);
+      if (nch > 1) issue_v(A, L.vr[1], (size_t)(tok0 + C) * H + h, min(C, len - C), cw, lane);
 
-    float* dst = A.state_out + unit * D * D;
+      for (int p = -1; p < nch; ++p) {
+        const int b = p & 1;
+        const int nc = min(C, len - C * p);
+        if (p >= 0) {
+          // ---------------- Kt S0 and Qt S0 ----------------
+          // S enters as fp16 B operands: step s reduces over rows {16(2s)+4g+r} then {16(2s+1)+4g+r},
+          // and the A operands read the same permutation of their columns
+          // The same fragments serve as the A operand of S^T, so (Qt S0)^T = S0^T Qt^T comes out
+          // transposed: QT[nv][mt] holds rows = value columns, columns = tokens.
+          f32x4 KS[2][2], QT[2][2];
 #pragma unroll
-    for (int mc = 0; mc < 8; ++mc)
+          for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int nv = 0; nv < 2; ++nv)
+            for (int nv = 0; nv < 2; ++nv) { KS[mt][nv] = f32x4{0.f, 0.f, 0.f, 0.f}; QT[nv][mt] = f32x4{0.f, 0.f, 0.f, 0.f}; }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(size_t)(16 * mc + 4 * g + r) * D + 32 * wave + 16 * nv + lr] = S[mc][nv][r];
-    if (A.snap_count && h == 0 && tid == 0) A.snap_count[n] = A.snap_interval > 0 ? len / A.snap_interval : 0;
+          for (int s = 0; s < 4; ++s) {
+            const f16x8 sh0 = to_h8(S[2 * s][0], S[2 * s + 1][0]), sh1 = to_h8(S[2 * s][1], S[2 * s + 1][1]);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+              const int m = 16 * mt + lr;
+              const f16x8 kr = perm_h(&L.kt[b][m][32 * s], g);
+              const f16x8 qr = perm_h(&L.qt[b][m][32 * s], g);
+              KS[mt][0] = mfma_h(kr, sh0, KS[mt][0]);
+              KS[mt][1] = mfma_h(kr, sh1, KS[mt][1]);
+              QT[0][mt] = mfma_h(sh0, qr, QT[0][mt]);
+              QT[1][mt] = mfma_h(sh1, qr, QT[1][mt]);
+            }
+          }
+          // ---------------- R = diag(beta)(V - Kt S0), W = X R ----------------
+          // by blocks: W0 = X00 R0, W1 = X11 (R1 - A10 W0), 16x16x16 MFMAs with fp16 hi + lo operands
+          f32x4 W[2][2];
+          {
+            const f16x4 x00 = __builtin_bit_cast(f16x4, lds8(&L.xb[b][lr][4 * g]));
+            const f16x4 x11 = __builtin_bit_cast(f16x4, lds8(&L.xb[b][16 + lr][16 + 4 * g]));
+            const f16x4 a10 = __builtin_bit_cast(f16x4, lds8(&L.an[b][lr][4 * g]));
+#pragma unroll
+            for (int nv = 0; nv < 2; ++nv) {
+              f32x4 R[2];
+              const int c0 = 32 * cw + 16 * nv + 4 * (lr & 3);
+#pragma unroll
+              for (int mt = 0; mt < 2; ++mt) {
+                // V[16mt+4g+r][32cw+16nv+lr] through the transposing read of the swizzled raw rows;
+                // the four rows of one read land in four different 8-bank groups
+                const int row = 16 * mt + 4 * g + (lr >> 2);
+                const uint2 vv = lds_tr(&L.vr[b][row][8 * ((c0 >> 3) ^ ((2 * row) & 15)) + (c0 & 7)]);
+                const float4 b4 = *reinterpret_cast<const float4*>(&L.beta[b][16 * mt + 4 * g]);
+                R[mt][0] = b4.x * (bf2f(vv.x & 0xffffu) - KS[mt][nv][0]);
+                R[mt][1] = b4.y * (bf2f(vv.x >> 16) - KS[mt][nv][1]);
+                R[mt][2] = b4.z * (bf2f(vv.y & 0xffffu) - KS[mt][nv][2]);
+                R[mt][3] = b4.w * (bf2f(vv.y >> 16) - KS[mt][nv][3]);
+              }
+              const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+              f16x4 hi, lo;
+              split_h4(R[0], hi, lo);
+              f32x4 w0 = mfma_h16(x00, lo, mfma_h16(x00, hi, z4));
+              split_h4(w0, hi, lo);
+              f32x4 r1 = mfma_h16(a10, lo, mfma_h16(a10, hi, R[1]));
+              split_h4(r1, hi, lo);
+              W[0][nv] = w0;
+              W[1][nv] = mfma_h16(x11, lo, mfma_h16(x11, hi, z4));
+            }
+          }
+#pragma unroll
+          for (int nv = 0; nv < 2; ++nv) split_h8(W[0][nv], W[1][nv], Wh[nv], Wl[nv]);
+
+          // ---------------- O^T = scale (S0^T Qt^T + W^T P^T), stored from the accumulators ----------------
+          // lane (g, lr) holds O[16mt + lr][32cw + 16nv + 4g + r], r < 4: one 16-byte store per tile
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            const f16x8 pa = perm_h(&L.pm[b][16 * mt + lr][0], g);
+            const int t = 16 * mt + lr;
+            float* orow = A.o + ((size_t)(tok0 + C * p) * H + h) * D + ((uint32_t)t * H * D + 32 * cw + 4 * g);
+#pragma unroll
+            for (int nv = 0; nv < 2; ++nv) {
+              f32x4 acc = QT[nv][mt];
+              acc = mfma_h(Wh[nv], pa, acc);
+              acc = mfma_h(Wl[nv], pa, acc);
+              if (t < nc)
+                *reinterpret_cast<float4*>(orow + 16 * nv) = make_float4(A.scale * acc[0], A.scale * acc[1], A.scale * acc[2], A.scale * acc[3]);
+            }
+          }
+        }
+        __syncthreads();
+        if (p >= 0) {
+          // ---------------- S = e^{G_31} S0 + K'^T W ----------------
+#pragma unroll
+          for (int mc = 0; mc < 8; ++mc) {
+            const float4 d4 = *reinterpret_cast<const float4*>(&L.dlast[b][16 * mc + 4 * g]);
+            // K'^T rows 16mc+lr, reduction positions t = 4g+r and 16+4g+r, via the transposing read
+            const uint16_t* base = &L.kp[b][4 * g + (lr >> 2)][16 * mc + 4 * (lr & 3)];
+            const f16x8 ka = as_f16x8(lds_tr(base), lds_tr(base + 16 * TM));
+#pragma unroll
+            for (int nv = 0; nv < 2; ++nv) {
+              f32x4 acc = S[mc][nv];
+              acc[0] *= d4.x; acc[1] *= d4.y; acc[2] *= d4.z; acc[3] *= d4.w;
+              acc = mfma_h(ka, Wh[nv], acc);
+              acc = mfma_h(ka, Wl[nv], acc);
+              S[mc][nv] = acc;
+            }
+          }
+
+          // ---------------- snapshot at chunk ends q with q % interval == 0 ----------------
+          const int q = C * p + nc;
+          if (A.snap_interval > 0 && q % A.snap_interval == 0) {
+            const int m = q / A.snap_interval;
+            float* dst = A.snap + (((size_t)n * A.snap_slots + (m - 1) % A.snap_slots) * H + h) * D * D + soff;
+#pragma unroll
+            for (int mc = 0; mc < 8; ++mc)
+#pragma unroll
+              for (int nv = 0; nv < 2; ++nv)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[(16 * mc + r) * D + 16 * nv] = S[mc][nv][r];
+          }
+        }
+        // X for the next chunk (its A partials were summed by the producers in phase 1)
+        if (cw == 0 && p + 1 < nch) stage2_solve(L, (p + 1) & 1, lane);
+        // v rows two chunks ahead into the buffer this period's chain has finished with; then wait
+        // for everything older (in issue order), which includes the v rows of the next chunk
+        if (p >= 0 && p + 2 < nch) {
+          issue_v(A, L.vr[b], (size_t)(tok0 + C * (p + 2)) * H + h, min(C, len - C * (p + 2)), cw, lane);
+          __builtin_amdgcn_s_waitcnt(0x0f72);  // vmcnt(2)
+        } else {
+          __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+        }
+        __syncthreads();
+      }
+
+      float* dst = A.state_out + unit * D * D + soff;
+#pragma unroll
+      for (int mc = 0; mc < 8; ++mc)
+#pragma unroll
+        for (int nv = 0; nv < 2; ++nv)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[(16 * mc + r) * D + 16 * nv] = S[mc][nv][r];
+      if (A.snap_count && h == 0 && tid == 0) A.snap_count[n] = A.snap_interval > 0 ? len / A.snap_interval : 0;
+    }
   }
 
   // the last workgroup out resets the counters, so a later launch with the
@@ -564,12 +656,12 @@ int prefill_max_grid(int device) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || n <= 0) n = 256;
     cus[device] = n;
   }
-  return cus[device];  // one 256-thread workgroup per CU (LDS-bound)
+  return cus[device];  // one workgroup per CU (LDS-bound)
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int grid, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_kernel, dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(prefill_kernel, dim3(grid), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 
