@@ -204,10 +204,17 @@ __device__ __forceinline__ void issue_v(const PrefillArgs& A, uint16_t (&dst)[C]
   }
 }
 
+// What phase 2 of the producer needs from phase 1 to write the chain's operand rows: the
+// masked raw q and k (bf16) and the decay factors e^{G_t} and e^{G_31 - G_t} of both tokens.
+struct Keep {
+  uint4 q0, q1, k0, k1;
+  float e0[8], e1[8], f0[8], f1[8];
+};
+
 // ---------------------------------------------------------------------------
-// producer, phase 1 of the period before chunk c: decay factors, the chain's
-// operand rows, partial A and P tiles over this wave's 32 channels
-__device__ __forceinline__ void stage1(PrefillLds& L, const Raw& cur, int nc, int b, int pw, int g, int lr) {
+// producer, phase 1 of the period before chunk c: decay factors and partial A
+// and P tiles over this wave's 32 channels
+__device__ __forceinline__ void stage1(PrefillLds& L, const Raw& cur, int nc, int b, int pw, int g, int lr, Keep& kp_) {
   const int co = 4 * pw + g;  // channel octet 8co..8co+7
   const int tl = lr;          // tokens tl (block 0) and 16+tl (block 1)
   const int c8 = 8 * co;
@@ -226,10 +233,13 @@ __device__ __forceinline__ void stage1(PrefillLds& L, const Raw& cur, int nc, in
     L.beta[b][tl] = ok0 ? cur.b0 : 0.f;
     L.beta[b][16 + tl] = ok1 ? cur.b1 : 0.f;
   }
+  kp_.q0 = ok0 ? cur.q0 : zero4; kp_.q1 = ok1 ? cur.q1 : zero4;
+  kp_.k0 = ok0 ? cur.k0 : zero4; kp_.k1 = ok1 ? cur.k1 : zero4;
   float k0[8], k1[8], q0[8], q1[8];
-  unpack_bf16x8(ok0 ? cur.k0 : zero4, k0); unpack_bf16x8(ok1 ? cur.k1 : zero4, k1);
-  unpack_bf16x8(ok0 ? cur.q0 : zero4, q0); unpack_bf16x8(ok1 ? cur.q1 : zero4, q1);
-  float xr0[8], xr1[8], yc0[8], yc1[8], e0[8], e1[8], f0[8], f1[8];
+  unpack_bf16x8(kp_.k0, k0); unpack_bf16x8(kp_.k1, k1);
+  unpack_bf16x8(kp_.q0, q0); unpack_bf16x8(kp_.q1, q1);
+  float xr0[8], xr1[8], yc0[8], yc1[8];
+  float (&e0)[8] = kp_.e0, (&e1)[8] = kp_.e1, (&f0)[8] = kp_.f0, (&f1)[8] = kp_.f1;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     // prefix sums inside each 16-token block, then the four exponentials
@@ -246,25 +256,6 @@ __device__ __forceinline__ void stage1(PrefillLds& L, const Raw& cur, int nc, in
     f0[i] = yc0[i] * T1;                      // e^{G_31 - G_t}
     f1[i] = T1 * r1;
     if (tl == 0) L.dlast[b][c8 + i] = T0 * T1;
-  }
-  // fp16 operands of the state products, token-major rows tl and 16+tl
-  float x[8];
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    const int t = 16 * blk + tl;
-    const float(&kk)[8] = blk ? k1 : k0;
-    const float(&qq)[8] = blk ? q1 : q0;
-    const float(&ee)[8] = blk ? e1 : e0;
-    const float(&ff)[8] = blk ? f1 : f0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = qq[i] * ee[i];
-    put_f16(&L.qt[b][t][c8], x);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = kk[i] * ee[i];
-    put_f16(&L.kt[b][t][c8], x);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = kk[i] * ff[i];
-    put_f16(&L.kp[b][t][c8], x);
   }
   // A and P over this wave's 32 channels, straight from registers: lane (g, lr) holds
   // channels 32pw+8g..+7 of tokens lr (block 0) and 16+lr (block 1), which is the
@@ -290,6 +281,32 @@ __device__ __forceinline__ void stage1(PrefillLds& L, const Raw& cur, int nc, in
 #pragma unroll
   for (int tl6 = 0; tl6 < 6; ++tl6)
     *reinterpret_cast<f32x4*>(&L.part[pw][tl6][lr][4 * g]) = acc[tl6];
+}
+
+// producer, phase 2: fp16 operands of the state products, token-major rows tl and 16+tl
+__device__ __forceinline__ void stage1b(PrefillLds& L, const Keep& kp_, int b, int pw, int g, int lr) {
+  const int c8 = 8 * (4 * pw + g), tl = lr;
+  float k0[8], k1[8], q0[8], q1[8];
+  unpack_bf16x8(kp_.k0, k0); unpack_bf16x8(kp_.k1, k1);
+  unpack_bf16x8(kp_.q0, q0); unpack_bf16x8(kp_.q1, q1);
+  float x[8];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int t = 16 * blk + tl;
+    const float(&kk)[8] = blk ? k1 : k0;
+    const float(&qq)[8] = blk ? q1 : q0;
+    const float(&ee)[8] = blk ? kp_.e1 : kp_.e0;
+    const float(&ff)[8] = blk ? kp_.f1 : kp_.f0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = qq[i] * ee[i];
+    put_f16(&L.qt[b][t][c8], x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = kk[i] * ee[i];
+    put_f16(&L.kt[b][t][c8], x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = kk[i] * ff[i];
+    put_f16(&L.kp[b][t][c8], x);
+  }
 }
 
 // sums of the four channel slices of NTL 16x16 tiles t0..t0+NTL-1: the lane gets rows
@@ -432,11 +449,12 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
     if (producer) {
       const int pw = rw;
       const int lane = lane_o, g = g_o, lr = lr_o;
-      // Raw inputs are prefetched into registers two periods ahead, alternating between two
-      // sets: chunk c lives in set c & 1 from the period that issues it (c - 3) until its
-      // stage 1 (period c - 1). Every period issues the same loads (past the last chunk they
-      // re-read it, which the cache serves), so the compiler's own waits before each use can
-      // count exactly and leave the newer set in flight.
+      // Raw inputs are prefetched two periods ahead: q, k, gk, beta into registers, alternating
+      // between two sets (chunk c lives in set c & 1 from the period that issues it, c - 3,
+      // until its stage 1 in period c - 1), and v straight into vr[c & 1] (issued in period
+      // c - 2, read by the chain in period c). Every period issues the same 12 loads (past the
+      // last chunk they re-read it), so the compiler's waits before each register use count
+      // exactly, and the wait that closes a period can leave just that period's loads in flight.
       if (nch == 0) {
         __syncthreads();
         __syncthreads();
@@ -446,18 +464,32 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
           c = min(c, nch - 1);
           load_raw(r, A, (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), 4 * pw + g, lr);
         };
+        auto issue_vc = [&](int c) {
+          c = min(c, nch - 1);
+          issue_v(A, L.vr[c & 1], (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), pw, lane);
+        };
         issue(ra, 0);
-        asm volatile("" ::: "memory");  // keep the issue order: set a, then set b
+        asm volatile("" ::: "memory");  // keep the issue order: set a, v of chunk 0, set b
+        issue_vc(0);
+        asm volatile("" ::: "memory");
         issue(rb, 1);
+        asm volatile("" ::: "memory");
         auto period = [&](int p, Raw& use) {
           const int c1 = p + 1, b1 = c1 & 1;
-          if (c1 < nch) stage1(L, use, min(C, len - C * c1), b1, pw, g, lr);
+          Keep keep;
+          if (c1 < nch) stage1(L, use, min(C, len - C * c1), b1, pw, g, lr, keep);
           __syncthreads();
           issue(use, c1 + 2);
+          asm volatile("" ::: "memory");
+          issue_vc(c1 + 1);  // into the buffer the chain read in this period's phase 1
           if (c1 < nch) {
+            stage1b(L, keep, b1, pw, g, lr);
             if (pw == 1) stage2_p(L, b1, lane);
             else if (pw == 2) stage2_a10(L, b1, lane);
           }
+          // everything older than this period's 12 loads has landed: the next chunk's
+          // register set and the v rows the chain reads in the next period
+          __builtin_amdgcn_s_waitcnt(0x0f7c);  // vmcnt(12)
           __syncthreads();
         };
         // periods -1 .. nch-1 in pairs, so that both sets' loads are issued on every path
@@ -468,6 +500,7 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
           period(p + 1, rb);
         }
         if (p < nch) period(p, ra);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no LDS write may outlive the item
       }
     } else {
       const int cw = rw;
@@ -494,9 +527,6 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
           for (int nv = 0; nv < 2; ++nv) S[mc][nv] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       f16x8 Wh[2], Wl[2];
-      // raw v of chunk c is loaded into vr[c & 1] two periods ahead (chunks 0 and 1 here)
-      if (nch > 0) issue_v(A, L.vr[0], (size_t)tok0 * H + h, min(C, len), cw, lane);
-      if (nch > 1) issue_v(A, L.vr[1], (size_t)(tok0 + C) * H + h, min(C, len - C), cw, lane);
 
       for (int p = -1; p < nch; ++p) {
         const int b = p & 1;
@@ -612,16 +642,8 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
                 for (int r = 0; r < 4; ++r) dst[(16 * mc + r) * D + 16 * nv] = S[mc][nv][r];
           }
         }
-        // X for the next chunk (its A partials were summed by the producers in phase 1)
+        // X for the next chunk (its A partials were written by the producers in phase 1)
         if (cw == 0 && p + 1 < nch) stage2_solve(L, (p + 1) & 1, lane);
-        // v rows two chunks ahead into the buffer this period's chain has finished with; then wait
-        // for everything older (in issue order), which includes the v rows of the next chunk
-        if (p >= 0 && p + 2 < nch) {
-          issue_v(A, L.vr[b], (size_t)(tok0 + C * (p + 2)) * H + h, min(C, len - C * (p + 2)), cw, lane);
-          __builtin_amdgcn_s_waitcnt(0x0f72);  // vmcnt(2)
-        } else {
-          __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-        }
         __syncthreads();
       }
 
