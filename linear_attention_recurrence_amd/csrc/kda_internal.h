@@ -68,6 +68,9 @@ struct PrefillArgs {
 };
 
 hipError_t launch_verify(const VerifyArgs& a, bool f32_inputs, hipStream_t stream);
+// chunked-form verify on the matrix cores: bf16 inputs, n_tok <= 16, no recurrent commit
+bool verify_chunk_eligible(const VerifyArgs& a, bool f32_inputs);
+hipError_t launch_verify_chunk(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_fold(const FoldArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int grid, hipStream_t stream);
 int prefill_max_grid(int device);

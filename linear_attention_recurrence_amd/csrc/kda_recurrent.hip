@@ -240,6 +240,7 @@ __global__ void __launch_bounds__(256) fold_kernel(FoldArgs A) {
 }
 
 hipError_t launch_verify(const VerifyArgs& a, bool f32, hipStream_t stream) {
+  if (verify_chunk_eligible(a, f32)) return launch_verify_chunk(a, stream);
   const dim3 grid((unsigned)a.batch * (unsigned)a.n_heads), block(256);
   const bool ring = a.ring_k != nullptr;
   if (f32) hipLaunchKernelGGL((verify_kernel<true, false>), grid, block, 0, stream, a);

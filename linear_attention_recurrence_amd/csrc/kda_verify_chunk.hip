@@ -1,0 +1,278 @@
+// kda_verify_chunk.hip -- speculative verify of up to 16 draft tokens in chunked
+// form on the gfx950 matrix cores.
+//
+// Sources: "SGLang and Miles Add Day-0 Support for Kimi K3" (LMSYS blog),
+// section "ReplaySSM: raw-input replay for the KDA state" -- verify reads the
+// committed state without writing it and records each step's raw inputs
+// (v, k, gk, beta) for the fold. Kimi K3 B200 deployment notes
+// (zdszero.github.io), section "DSPARK and KDA state" -- the per-slot ring.
+//
+// Verify needs the outputs of every draft token but never the state after
+// them (the fold produces that later from the ring), so the T tokens are one
+// chunk of the chunked form, with S0 the committed state and
+// G_t = sum_{tau<=t} gk_tau from the first draft token:
+//   A[i][j] = beta_i sum_c (k_ic e^{G_ic}) (k_jc e^{-G_jc})   (j < i)
+//   P[t][i] =        sum_c (q_tc e^{G_tc}) (k_ic e^{-G_ic})   (i <= t)
+//   R = diag(beta) (V - Kt S0),  W = (I + A)^-1 R,  O = scale (Qt S0 + P W)
+// with Kt = k e^G and Qt = q e^G. The factors e^{-G} grow with the decay
+// summed over the window, which stays in fp32/bf16 range while that sum is at
+// most 80 per key channel (gk >= -5 over 16 tokens suffices).
+//
+// Precision follows the prefill kernel: A and P from bf16 MFMAs with the
+// q e^G and k e^{-G} factors split into bf16 hi + lo (k e^G single); the state
+// products on fp16 MFMAs with R and W as fp16 hi + lo; fp32 accumulation.
+// A call that also asks for the recurrent commit takes the token-by-token
+// kernel instead, whose arithmetic the fold replays bit for bit.
+//
+// Work decomposition: one 256-thread workgroup per (request, head). Wave w
+// stages its 128 x 32 column slice of S0 as fp16 in LDS (coalesced 16-byte
+// loads) and reads it back transposed (ds_read_b64_tr_b16) as MFMA operands.
+// Two workgroups fit on a CU.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int VT = 16;   // tokens per call on this path (padded)
+constexpr int TV = 136;  // operand row stride (16-bit elements; 128 + 8 pad)
+constexpr int PS = 24;   // 16x16 fp16 rows (+8 pad)
+
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+struct alignas(16) VerifyLds {
+  uint16_t sh[4][D][32];   // per wave: fp16 S0[c][32w + j]
+  uint16_t kt[VT][TV];     // fp16 k e^G, rows t
+  uint16_t qt[VT][TV];     // fp16 q e^G
+  uint16_t rk[VT][TV];     // bf16 k e^G
+  uint16_t rqh[VT][TV];    // bf16 q e^G, hi
+  uint16_t rql[VT][TV];    //                lo
+  uint16_t ckh[VT][TV];    // bf16 k e^{-G}, hi
+  uint16_t ckl[VT][TV];    //                 lo
+  uint16_t v[VT][D];       // bf16 v rows
+  uint16_t xh[VT][PS];     // fp16 X = (I + A)^-1, rows t
+  uint16_t ph[VT][PS];     // fp16 P, rows t
+  float am[VT][20];        // A rows (fp32) for the solve
+  float beta[VT];
+};
+
+__device__ __forceinline__ uint2 lds8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ uint2 lds_tr(const uint16_t* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
+}
+__device__ __forceinline__ f16x8 as_f16x8(uint2 a, uint2 b) {
+  return __builtin_bit_cast(f16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+// permuted 32-wide reduction step: row elements {4g..4g+3} then {16+4g..16+4g+3}
+__device__ __forceinline__ f16x8 perm_h(const uint16_t* row, int g) { return as_f16x8(lds8(row + 4 * g), lds8(row + 16 + 4 * g)); }
+__device__ __forceinline__ bf16x8 perm_b(const uint16_t* row, int g) { return as_bf16x8(lds8(row + 4 * g), lds8(row + 16 + 4 * g)); }
+__device__ __forceinline__ f32x4 mfma_h(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_h16(const f16x4& a, const f16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ uint16_t h16(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+__device__ __forceinline__ void split_h4(const f32x4& a, f16x4& hi, f16x4& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = (_Float16)a[i];
+    lo[i] = (_Float16)(a[i] - (float)hi[i]);
+  }
+}
+
+}  // namespace
+
+template <bool RING>
+__global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
+  __shared__ VerifyLds L;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, lr = lane & 15;
+  const int H = A.n_heads;
+  const int b = blockIdx.x / H;
+  const int h = blockIdx.x - b * H;
+  const int slot = A.slot_idx[b];
+  if (slot < 0 || slot >= A.n_slots) return;  // whole workgroup skips together
+  const int T = A.n_tok;                      // 1 .. 16 on this path
+  const size_t unit = ((size_t)slot * A.n_layers + A.layer) * H + h;
+  const size_t row0 = (size_t)b * T * H + h;  // input row of token 0: (b * T + t) * H + h
+
+  // ---- committed state: this wave's 128 x 32 column slice, 16-byte loads (8 rows per instruction)
+  float4 sv[16];
+  {
+    const float* sp = A.state_pool + unit * D * D + 32 * wave + 4 * (lane & 7);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sv[i] = *reinterpret_cast<const float4*>(sp + (size_t)(8 * i + (lane >> 3)) * D);
+  }
+
+  // ---- raw inputs: v rows and beta into LDS, the ring copies (raw bits), 4 channels per thread
+  {
+    const int c4 = 4 * (tid & 31);
+#pragma unroll
+    for (int t = tid >> 5; t < VT; t += 8) {
+      uint2 vv = make_uint2(0u, 0u);
+      float bt = 0.f;
+      if (t < T) {
+        const size_t e = (row0 + (size_t)t * H) * D + c4;
+        vv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.v) + e);
+        bt = A.beta[row0 + (size_t)t * H];
+        if constexpr (RING) {
+          const int rstart = A.ring_start ? A.ring_start[b] : 0;
+          const int pos = (rstart + t) & (A.ring_len - 1);
+          const size_t rrow = unit * A.ring_len + pos;
+          const size_t re = rrow * D + c4;
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(A.ring_v) + re) = vv;
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(A.ring_k) + re) =
+              *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.k) + e);
+          *reinterpret_cast<float4*>(A.ring_gk + re) = *reinterpret_cast<const float4*>(A.gk + e);
+          if (c4 == 0) A.ring_beta[rrow] = bt;
+        }
+      }
+      *reinterpret_cast<uint2*>(&L.v[t][c4]) = vv;
+      if (c4 == 0) L.beta[t] = bt;
+    }
+  }
+
+  // ---- decay factors: thread c < 128 walks channel c through the window
+  if (tid < D) {
+    const int c = tid;
+    float gv[VT], kv[VT], qv[VT];
+#pragma unroll
+    for (int t = 0; t < VT; ++t) {
+      const size_t e = (row0 + (size_t)min(t, T - 1) * H) * D + c;
+      gv[t] = A.gk[e];
+      kv[t] = bf2f(static_cast<const uint16_t*>(A.k)[e]);
+      qv[t] = bf2f(static_cast<const uint16_t*>(A.q)[e]);
+    }
+    float gs = 0.f;
+#pragma unroll
+    for (int t = 0; t < VT; ++t) {
+      const bool ok = t < T;
+      gs += ok ? gv[t] : 0.f;
+      const float e = __expf(gs), ie = __expf(-gs);
+      const float ke = ok ? kv[t] * e : 0.f, qe = ok ? qv[t] * e : 0.f, ck = ok ? kv[t] * ie : 0.f;
+      L.kt[t][c] = h16(ke);
+      L.qt[t][c] = h16(qe);
+      L.rk[t][c] = f2bf(ke);
+      uint16_t hi, lo;
+      split_bf16(qe, hi, lo);
+      L.rqh[t][c] = hi; L.rql[t][c] = lo;
+      split_bf16(ck, hi, lo);
+      L.ckh[t][c] = hi; L.ckl[t][c] = lo;
+    }
+  }
+
+  // ---- state slice to fp16 in LDS
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t lo = pack2(h16(sv[i].x), h16(sv[i].y)), hi = pack2(h16(sv[i].z), h16(sv[i].w));
+    *reinterpret_cast<uint2*>(&L.sh[wave][8 * i + (lane >> 3)][4 * (lane & 7)]) = make_uint2(lo, hi);
+  }
+  __syncthreads();
+
+  // ---- A, P and X = (I + A)^-1 (wave 0)
+  if (wave == 0) {
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 am = z4, pm = z4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 rk = perm_b(&L.rk[lr][32 * s], g);
+      const bf16x8 qh = perm_b(&L.rqh[lr][32 * s], g), ql = perm_b(&L.rql[lr][32 * s], g);
+      const bf16x8 ch = perm_b(&L.ckh[lr][32 * s], g), cl = perm_b(&L.ckl[lr][32 * s], g);
+      am = mfma16(rk, cl, mfma16(rk, ch, am));
+      pm = mfma16(ql, ch, mfma16(qh, cl, mfma16(qh, ch, pm)));
+    }
+    // lane (g, lr) holds entries (4g + r, lr)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * g + r, j = lr;
+      L.am[i][j] = (j < i) ? am[r] * L.beta[i] : 0.f;
+      L.ph[i][j] = (j <= i) ? h16(pm[r]) : (uint16_t)0;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    // forward substitution on rows: DPP row g holds columns 4g .. 4g+3 of row i = lr
+    float arow[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 a4 = *reinterpret_cast<const float4*>(&L.am[lr][4 * q4]);
+      arow[4 * q4] = -a4.x; arow[4 * q4 + 1] = -a4.y; arow[4 * q4 + 2] = -a4.z; arow[4 * q4 + 3] = -a4.w;
+    }
+    float x[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) x[m] = (4 * g + m == lr) ? 1.f : 0.f;
+#define KDA_VSOLVE_STEP(kk)                                                                                   \
+    _Pragma("unroll") for (int m = 0; m < 4; ++m) {                                                           \
+      const float xk_ = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[m]), 0x150 + (kk), 0xf, 0xf, true)); \
+      x[m] = __builtin_fmaf(arow[kk], xk_, x[m]);                                                             \
+    }
+    KDA_VSOLVE_STEP(0) KDA_VSOLVE_STEP(1) KDA_VSOLVE_STEP(2) KDA_VSOLVE_STEP(3) KDA_VSOLVE_STEP(4)
+    KDA_VSOLVE_STEP(5) KDA_VSOLVE_STEP(6) KDA_VSOLVE_STEP(7) KDA_VSOLVE_STEP(8) KDA_VSOLVE_STEP(9)
+    KDA_VSOLVE_STEP(10) KDA_VSOLVE_STEP(11) KDA_VSOLVE_STEP(12) KDA_VSOLVE_STEP(13) KDA_VSOLVE_STEP(14)
+#undef KDA_VSOLVE_STEP
+    *reinterpret_cast<uint2*>(&L.xh[lr][4 * g]) = make_uint2(pack2(h16(x[0]), h16(x[1])), pack2(h16(x[2]), h16(x[3])));
+  }
+
+  // ---- Kt S0 (tokens x values) and (Qt S0)^T (values x tokens) on this wave's 32 columns
+  f32x4 KS[2], QT[2];
+  {
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    KS[0] = KS[1] = QT[0] = QT[1] = z4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const f16x8 kr = perm_h(&L.kt[lr][32 * s], g);
+      const f16x8 qr = perm_h(&L.qt[lr][32 * s], g);
+#pragma unroll
+      for (int nv = 0; nv < 2; ++nv) {
+        // S0 rows {32s+4g+r} then {32s+16+4g+r}, column 16nv+lr of the slice, via the transposing read
+        const uint16_t* p = &L.sh[wave][32 * s + 4 * g + (lr >> 2)][16 * nv + 4 * (lr & 3)];
+        const f16x8 sf = as_f16x8(lds_tr(p), lds_tr(p + 16 * 32));
+        KS[nv] = mfma_h(kr, sf, KS[nv]);
+        QT[nv] = mfma_h(sf, qr, QT[nv]);
+      }
+    }
+  }
+  __syncthreads();  // X and P are complete
+
+  // ---- R = diag(beta)(V - Kt S0), W = X R, O^T = scale (QT + W^T P^T)
+  const f16x4 xa = __builtin_bit_cast(f16x4, lds8(&L.xh[lr][4 * g]));
+  const f16x4 pa = __builtin_bit_cast(f16x4, lds8(&L.ph[lr][4 * g]));
+  const float4 b4 = *reinterpret_cast<const float4*>(&L.beta[4 * g]);
+  const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+  for (int nv = 0; nv < 2; ++nv) {
+    const int col = 32 * wave + 16 * nv + lr;
+    f32x4 R;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) R[r] = bv[r] * (bf2f(L.v[4 * g + r][col]) - KS[nv][r]);
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    f16x4 hi, lo;
+    split_h4(R, hi, lo);
+    const f32x4 W = mfma_h16(xa, lo, mfma_h16(xa, hi, z4));
+    split_h4(W, hi, lo);
+    const f32x4 O = mfma_h16(lo, pa, mfma_h16(hi, pa, QT[nv]));
+    // lane (g, lr) holds O[t = lr][32w + 16nv + 4g + r]
+    if (lr < T) {
+      float* orow = A.o + (row0 + (size_t)lr * H) * D + 32 * wave + 16 * nv + 4 * g;
+      *reinterpret_cast<float4*>(orow) = make_float4(A.scale * O[0], A.scale * O[1], A.scale * O[2], A.scale * O[3]);
+    }
+  }
+}
+
+bool verify_chunk_eligible(const VerifyArgs& a, bool f32_inputs) {
+  return !f32_inputs && a.n_tok >= 1 && a.n_tok <= VT && a.commit_len == nullptr;
+}
+
+hipError_t launch_verify_chunk(const VerifyArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.batch * (unsigned)a.n_heads), block(256);
+  if (a.ring_k) hipLaunchKernelGGL((verify_chunk_kernel<true>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((verify_chunk_kernel<false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace kda

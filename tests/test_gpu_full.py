@@ -124,11 +124,15 @@ def test_spec_step_256x69x8(gpu):
     commit = torch.empty_like(pool)
     rng = np.random.default_rng(3)
     samples = sorted({(int(rng.integers(B)), int(rng.integers(Lyr)), int(rng.integers(H))) for _ in range(48)})
-    o_s = {}
+    o_s, o_c = {}, {}
     for l in range(Lyr):
         ins = sg.prefill_inputs(seed, B * T, H, DEV, sub=l)
+        # the speculative step as served: no recurrent commit (the chunked matrix-core path) ...
         o = torch.empty((B * T, H, 128), device=DEV)
-        kda.kda_verify(*ins, pool, slot_idx, o, layer=l, n_tok=T, ring=ring, ring_start=ring_start, commit_len=acc,
+        kda.kda_verify(*ins, pool, slot_idx, o, layer=l, n_tok=T, ring=ring, ring_start=ring_start)
+        # ... and with the recurrent commit the fold is compared against (the token-by-token path)
+        oc = torch.empty((B * T, H, 128), device=DEV)
+        kda.kda_verify(*ins, pool, slot_idx, oc, layer=l, n_tok=T, ring=ring, ring_start=ring_start, commit_len=acc,
                        commit_pool=commit)
         # the ring holds the raw inputs of every request at positions 0..T-1, bit for bit
         k_in = ins[1].view(B, T, H, 128).permute(0, 2, 1, 3)
@@ -140,6 +144,7 @@ def test_spec_step_256x69x8(gpu):
         for (b, ll, h) in samples:
             if ll == l:
                 o_s[(b, ll, h)] = np_(o.view(B, T, H, 128)[b, :, h])
+                o_c[(b, ll, h)] = np_(oc.view(B, T, H, 128)[b, :, h])
     torch.cuda.synchronize()
     # verify never wrote the committed pool
     fresh = sg.states(seed, S * Lyr * H, DEV).view(S, Lyr, H, 128, 128)
@@ -158,7 +163,7 @@ def test_spec_step_256x69x8(gpu):
         q, k, v, gk, beta = synth.prefill_rows(seed, H, b * T, T, h=h, sub=l)
         S0 = synth.state_rows(seed, (b * Lyr + l) * H + h, 1)[0]
         o_ref, Sc, _ = oracle.verify(q, k, v, gk, beta, S0, commit_len=int(acc_np[b]))
-        return max(block_err(o_s[u], o_ref), block_err(pool_np[u], Sc))
+        return max(block_err(o_s[u], o_ref), block_err(o_c[u], o_ref), block_err(pool_np[u], Sc))
 
     worst = max(oracle.run_parallel(run, samples, threads=threads()))
     log(f"spec step worst {worst:.2e}")

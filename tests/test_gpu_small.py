@@ -129,6 +129,48 @@ def test_verify_and_fold_small(gpu):
             assert torch.equal(folded[s], pool0[s])
 
 
+@pytest.mark.parametrize("T,use_ring", [(1, True), (5, True), (8, True), (16, True), (8, False), (17, True)])
+def test_verify_without_commit(gpu, T, use_ring):
+    """The call shape of a speculative step (no recurrent commit): up to 16 tokens take the chunked
+    matrix-core path, longer windows the token-by-token kernel; either way the outputs match the
+    oracle, the ring holds the raw inputs bit for bit and the committed state is untouched."""
+    seed, B, H, L, S = 41 + T, 3, 2, 2, 6
+    R = 32 if T <= 16 else 64
+    log(f"verify without commit T={T} ring={use_ring}")
+    slot_idx, pool, ins, ring_start = make_verify_case(seed, B, T, H, L, S, R)
+    slot_idx[1] = -1  # a request with no slot: skipped, its outputs stay as they were
+    pool0 = pool.clone()
+    ring = kda.Ring.empty(S, L, H, R, DEV) if use_ring else None
+    if ring is not None:
+        ring.gk.fill_(-7.0)
+    worst = 0.0
+    for l in range(L):
+        q, k, v, gk, beta = ins[l]
+        o = torch.full((B * T, H, 128), -9.0, device=DEV)
+        kda.kda_verify(q, k, v, gk, beta, pool, slot_idx.to(DEV), o, layer=l, n_tok=T, ring=ring,
+                       ring_start=ring_start.to(DEV) if use_ring else None, scale=0.6)
+        torch.cuda.synchronize()
+        on = np_(o).reshape(B, T, H, 128)
+        for b in range(B):
+            s = int(slot_idx[b])
+            if s < 0:
+                assert np.all(on[b] == -9.0)
+                continue
+            for h in range(H):
+                q_, k_, v_, gk_, beta_ = host_inputs(seed, B, T, H, l, b, h)
+                o_ref, _, _ = oracle.verify(q_, k_, v_, gk_, beta_, np_(pool0[s, l, h]), scale=0.6)
+                worst = max(worst, block_err(on[b, :, h], o_ref))
+                if ring is not None:
+                    pos = [(int(ring_start[b]) + t) & (R - 1) for t in range(T)]
+                    assert np.array_equal(bits(ring.k[s, l, h, pos]).view(np.uint16), k_)
+                    assert np.array_equal(bits(ring.v[s, l, h, pos]).view(np.uint16), v_)
+                    assert np.array_equal(np_(ring.gk[s, l, h, pos]), gk_)
+                    assert np.array_equal(np_(ring.beta[s, l, h, pos]), beta_)
+    assert torch.equal(pool, pool0), "verify wrote the committed state"
+    log(f"verify without commit T={T} worst err {worst:.2e}")
+    assert worst <= TOL
+
+
 @pytest.mark.parametrize("T,accs", [(8, [1, 2, 3, 4, 5, 6, 7, 8]), (1, [1, 0, 1, 1, 0, 1, 1, 0])])
 def test_fold_bitexact_every_length(gpu, T, accs):
     seed, H, L, R = 40 + T, 3, 3, 16
