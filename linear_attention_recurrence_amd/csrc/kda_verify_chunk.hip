@@ -42,6 +42,8 @@ constexpr int PS = 24;   // 16x16 fp16 rows (+8 pad)
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+constexpr int kBufWord3 = 0x00020000;  // raw buffer, 32-bit data format: range-checked by num_records
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct alignas(16) VerifyLds {
@@ -87,75 +89,130 @@ __device__ __forceinline__ void split_h4(const f32x4& a, f16x4& hi, f16x4& lo) {
 
 }  // namespace
 
-template <bool RING>
+// Persistent: each workgroup walks units u = blockIdx.x, + gridDim.x, ...; the
+// next unit's committed state and raw inputs are loaded into registers while
+// the current one computes. NT is the padded window (8 or 16 tokens). Every
+// global store of a unit is unconditional (the outputs of padded tokens are
+// dropped by the buffer range check), so the compiler's wait before the next
+// unit's first use of its prefetched registers leaves the stores in flight.
+template <bool RING, int NT>
 __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
   __shared__ VerifyLds L;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, lr = lane & 15;
   const int H = A.n_heads;
-  const int b = blockIdx.x / H;
-  const int h = blockIdx.x - b * H;
-  const int slot = A.slot_idx[b];
-  if (slot < 0 || slot >= A.n_slots) return;  // whole workgroup skips together
-  const int T = A.n_tok;                      // 1 .. 16 on this path
-  const size_t unit = ((size_t)slot * A.n_layers + A.layer) * H + h;
-  const size_t row0 = (size_t)b * T * H + h;  // input row of token 0: (b * T + t) * H + h
+  const int T = A.n_tok;  // 1 .. NT
+  const int n_units = A.batch * H;
+  constexpr int NH = NT / 2;              // tokens per input thread
+  const int c = tid & (D - 1);            // input thread: channel c ...
+  const int t0 = NH * (tid >> 7);         // ... of tokens t0 .. t0 + NH - 1
 
-  // ---- committed state: this wave's 128 x 32 column slice, 16-byte loads (8 rows per instruction)
+  // rows NT .. 15 of the operand matrices stay zero for the whole launch (MFMA tiles are 16 tall)
+  if constexpr (NT < VT) {
+    for (int e = tid; e < (VT - NT) * D; e += 256) {
+      const int t = NT + e / D, cc = e % D;
+      L.kt[t][cc] = 0; L.qt[t][cc] = 0; L.rk[t][cc] = 0; L.rqh[t][cc] = 0; L.rql[t][cc] = 0;
+      L.ckh[t][cc] = 0; L.ckl[t][cc] = 0; L.v[t][cc] = 0;
+    }
+    if (tid < VT - NT) L.beta[NT + tid] = 0.f;
+  }
+
+  // unit u = (request b, head h); a request without a valid slot still runs (on state of slot 0)
+  // but every store it makes is dropped by an empty buffer range
+  auto unit_of = [&](int u, int& b, int& h, size_t& unit) -> bool {
+    b = u / H;
+    h = u - b * H;
+    const int slot = A.slot_idx[b];
+    const bool valid = slot >= 0 && slot < A.n_slots;
+    unit = ((size_t)(valid ? slot : 0) * A.n_layers + A.layer) * H + h;
+    return valid;
+  };
+  // prefetched registers of one unit: this wave's 128 x 32 state slice (16-byte loads, 8 rows per
+  // instruction) and this thread's raw inputs (tokens past the window re-read the last one)
   float4 sv[16];
-  {
+  float gv[NH], gp[NH], kv[NH], qv[NH], vv[NH], bv_in;
+  auto prefetch = [&](int b, int h, size_t unit) {
     const float* sp = A.state_pool + unit * D * D + 32 * wave + 4 * (lane & 7);
 #pragma unroll
     for (int i = 0; i < 16; ++i) sv[i] = *reinterpret_cast<const float4*>(sp + (size_t)(8 * i + (lane >> 3)) * D);
+    const size_t row0 = (size_t)b * T * H + h;
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      const size_t e = (row0 + (size_t)min(t0 + j, T - 1) * H) * D + c;
+      gv[j] = A.gk[e];
+      kv[j] = bf2f(static_cast<const uint16_t*>(A.k)[e]);
+      qv[j] = bf2f(static_cast<const uint16_t*>(A.q)[e]);
+      vv[j] = bf2f(static_cast<const uint16_t*>(A.v)[e]);
+      gp[j] = t0 ? A.gk[(row0 + (size_t)min(j, T - 1) * H) * D + c] : 0.f;
+    }
+    bv_in = A.beta[row0 + (size_t)min(t0 + (c & (NH - 1)), T - 1) * H];
+  };
+  if (blockIdx.x < (unsigned)n_units) {
+    int b, h;
+    size_t unit;
+    unit_of(blockIdx.x, b, h, unit);
+    prefetch(b, h, unit);
   }
 
-  // ---- raw inputs: v rows and beta into LDS, the ring copies (raw bits), 4 channels per thread
-  {
-    const int c4 = 4 * (tid & 31);
+  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+    int b, h;
+    size_t unit;
+    const bool ok = unit_of(u, b, h, unit);  // wave-uniform
+    __syncthreads();                         // the previous unit's LDS readers are done
+    // state slice to fp16 in LDS
 #pragma unroll
-    for (int t = tid >> 5; t < VT; t += 8) {
-      uint2 vv = make_uint2(0u, 0u);
-      float bt = 0.f;
-      if (t < T) {
-        const size_t e = (row0 + (size_t)t * H) * D + c4;
-        vv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.v) + e);
-        bt = A.beta[row0 + (size_t)t * H];
-        if constexpr (RING) {
-          const int rstart = A.ring_start ? A.ring_start[b] : 0;
-          const int pos = (rstart + t) & (A.ring_len - 1);
-          const size_t rrow = unit * A.ring_len + pos;
-          const size_t re = rrow * D + c4;
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(A.ring_v) + re) = vv;
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(A.ring_k) + re) =
-              *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.k) + e);
-          *reinterpret_cast<float4*>(A.ring_gk + re) = *reinterpret_cast<const float4*>(A.gk + e);
-          if (c4 == 0) A.ring_beta[rrow] = bt;
-        }
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t lo = pack2(h16(sv[i].x), h16(sv[i].y)), hi = pack2(h16(sv[i].z), h16(sv[i].w));
+      *reinterpret_cast<uint2*>(&L.sh[wave][8 * i + (lane >> 3)][4 * (lane & 7)]) = make_uint2(lo, hi);
+    }
+    // take this unit's inputs out of the prefetch registers
+    float fg[NH], fk[NH], fq[NH], fv[NH], gs = 0.f;
+    if (t0) {
+#pragma unroll
+      for (int j = 0; j < NH; ++j) gs += (j < T) ? gp[j] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < NH; ++j) { fg[j] = gv[j]; fk[j] = kv[j]; fq[j] = qv[j]; fv[j] = vv[j]; }
+    const float fb = bv_in;
+    {
+      // the next unit streams in while this one computes (past the last unit: this one again,
+      // so that every iteration issues the same loads)
+      int bn, hn;
+      size_t unitn;
+      const int un = u + (int)gridDim.x;
+      unit_of(un < n_units ? un : u, bn, hn, unitn);
+      prefetch(bn, hn, unitn);
+    }
+    const size_t row0 = (size_t)b * T * H + h;  // input row of token t: row0 + t * H
+
+    // ---- raw inputs into the ring (bit copies; tokens past the window rewrite the last entry),
+    // v rows and beta into LDS, and the decay factors of channel c over tokens t0 .. t0 + NH - 1
+    const int rstart = (RING && A.ring_start) ? A.ring_start[b] : 0;
+    // ring rows of this unit (an empty range for a request without a slot)
+    __amdgpu_buffer_rsrc_t rk_rs, rv_rs, rg_rs, rb_rs;
+    if constexpr (RING) {
+      const int nrow = ok ? A.ring_len : 0;
+      rk_rs = __builtin_amdgcn_make_buffer_rsrc(static_cast<uint16_t*>(A.ring_k) + unit * A.ring_len * D, 0, nrow * D * 2, kBufWord3);
+      rv_rs = __builtin_amdgcn_make_buffer_rsrc(static_cast<uint16_t*>(A.ring_v) + unit * A.ring_len * D, 0, nrow * D * 2, kBufWord3);
+      rg_rs = __builtin_amdgcn_make_buffer_rsrc(A.ring_gk + unit * A.ring_len * D, 0, nrow * D * 4, kBufWord3);
+      rb_rs = __builtin_amdgcn_make_buffer_rsrc(A.ring_beta + unit * A.ring_len, 0, nrow * 4, kBufWord3);
+    }
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      const int t = t0 + j;
+      const bool ok_t = t < T;
+      if constexpr (RING) {
+        const int pos = (rstart + min(t, T - 1)) & (A.ring_len - 1);
+        const int re = pos * D + c;
+        __builtin_amdgcn_raw_buffer_store_b16(f2bf(fk[j]), rk_rs, 2 * re, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(f2bf(fv[j]), rv_rs, 2 * re, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fg[j]), rg_rs, 4 * re, 0, 0);
       }
-      *reinterpret_cast<uint2*>(&L.v[t][c4]) = vv;
-      if (c4 == 0) L.beta[t] = bt;
-    }
-  }
-
-  // ---- decay factors: thread c < 128 walks channel c through the window
-  if (tid < D) {
-    const int c = tid;
-    float gv[VT], kv[VT], qv[VT];
-#pragma unroll
-    for (int t = 0; t < VT; ++t) {
-      const size_t e = (row0 + (size_t)min(t, T - 1) * H) * D + c;
-      gv[t] = A.gk[e];
-      kv[t] = bf2f(static_cast<const uint16_t*>(A.k)[e]);
-      qv[t] = bf2f(static_cast<const uint16_t*>(A.q)[e]);
-    }
-    float gs = 0.f;
-#pragma unroll
-    for (int t = 0; t < VT; ++t) {
-      const bool ok = t < T;
-      gs += ok ? gv[t] : 0.f;
+      L.v[t][c] = ok_t ? f2bf(fv[j]) : (uint16_t)0;
+      gs += ok_t ? fg[j] : 0.f;
       const float e = __expf(gs), ie = __expf(-gs);
-      const float ke = ok ? kv[t] * e : 0.f, qe = ok ? qv[t] * e : 0.f, ck = ok ? kv[t] * ie : 0.f;
+      const float ke = ok_t ? fk[j] * e : 0.f, qe = ok_t ? fq[j] * e : 0.f, ck = ok_t ? fk[j] * ie : 0.f;
       L.kt[t][c] = h16(ke);
       L.qt[t][c] = h16(qe);
       L.rk[t][c] = f2bf(ke);
@@ -165,101 +222,102 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
       split_bf16(ck, hi, lo);
       L.ckh[t][c] = hi; L.ckl[t][c] = lo;
     }
-  }
+    if constexpr (RING) {
+      // every thread stores; lanes of the same token write the same bits
+      const int pos = (rstart + min(t0 + (c & (NH - 1)), T - 1)) & (A.ring_len - 1);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fb), rb_rs, 4 * pos, 0, 0);
+    }
+    if (c < NH) L.beta[t0 + c] = (t0 + c < T) ? fb : 0.f;
+    __syncthreads();
 
-  // ---- state slice to fp16 in LDS
+    // ---- A, P and X = (I + A)^-1 (wave 0)
+    if (wave == 0) {
+      const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+      f32x4 am = z4, pm = z4;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t lo = pack2(h16(sv[i].x), h16(sv[i].y)), hi = pack2(h16(sv[i].z), h16(sv[i].w));
-    *reinterpret_cast<uint2*>(&L.sh[wave][8 * i + (lane >> 3)][4 * (lane & 7)]) = make_uint2(lo, hi);
-  }
-  __syncthreads();
-
-  // ---- A, P and X = (I + A)^-1 (wave 0)
-  if (wave == 0) {
-    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-    f32x4 am = z4, pm = z4;
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 rk = perm_b(&L.rk[lr][32 * s], g);
+        const bf16x8 qh = perm_b(&L.rqh[lr][32 * s], g), ql = perm_b(&L.rql[lr][32 * s], g);
+        const bf16x8 ch = perm_b(&L.ckh[lr][32 * s], g), cl = perm_b(&L.ckl[lr][32 * s], g);
+        am = mfma16(rk, cl, mfma16(rk, ch, am));
+        pm = mfma16(ql, ch, mfma16(qh, cl, mfma16(qh, ch, pm)));
+      }
+      // lane (g, lr) holds entries (4g + r, lr)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 rk = perm_b(&L.rk[lr][32 * s], g);
-      const bf16x8 qh = perm_b(&L.rqh[lr][32 * s], g), ql = perm_b(&L.rql[lr][32 * s], g);
-      const bf16x8 ch = perm_b(&L.ckh[lr][32 * s], g), cl = perm_b(&L.ckl[lr][32 * s], g);
-      am = mfma16(rk, cl, mfma16(rk, ch, am));
-      pm = mfma16(ql, ch, mfma16(qh, cl, mfma16(qh, ch, pm)));
-    }
-    // lane (g, lr) holds entries (4g + r, lr)
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * g + r, j = lr;
+        L.am[i][j] = (j < i) ? am[r] * L.beta[i] : 0.f;
+        L.ph[i][j] = (j <= i) ? h16(pm[r]) : (uint16_t)0;
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+      __builtin_amdgcn_wave_barrier();
+      // forward substitution on rows: DPP row g holds columns 4g .. 4g+3 of row i = lr
+      float arow[16];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 4 * g + r, j = lr;
-      L.am[i][j] = (j < i) ? am[r] * L.beta[i] : 0.f;
-      L.ph[i][j] = (j <= i) ? h16(pm[r]) : (uint16_t)0;
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-    __builtin_amdgcn_wave_barrier();
-    // forward substitution on rows: DPP row g holds columns 4g .. 4g+3 of row i = lr
-    float arow[16];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(&L.am[lr][4 * q4]);
+        arow[4 * q4] = -a4.x; arow[4 * q4 + 1] = -a4.y; arow[4 * q4 + 2] = -a4.z; arow[4 * q4 + 3] = -a4.w;
+      }
+      float x[4];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 a4 = *reinterpret_cast<const float4*>(&L.am[lr][4 * q4]);
-      arow[4 * q4] = -a4.x; arow[4 * q4 + 1] = -a4.y; arow[4 * q4 + 2] = -a4.z; arow[4 * q4 + 3] = -a4.w;
-    }
-    float x[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) x[m] = (4 * g + m == lr) ? 1.f : 0.f;
+      for (int m = 0; m < 4; ++m) x[m] = (4 * g + m == lr) ? 1.f : 0.f;
 #define KDA_VSOLVE_STEP(kk)                                                                                   \
-    _Pragma("unroll") for (int m = 0; m < 4; ++m) {                                                           \
-      const float xk_ = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[m]), 0x150 + (kk), 0xf, 0xf, true)); \
-      x[m] = __builtin_fmaf(arow[kk], xk_, x[m]);                                                             \
-    }
-    KDA_VSOLVE_STEP(0) KDA_VSOLVE_STEP(1) KDA_VSOLVE_STEP(2) KDA_VSOLVE_STEP(3) KDA_VSOLVE_STEP(4)
-    KDA_VSOLVE_STEP(5) KDA_VSOLVE_STEP(6) KDA_VSOLVE_STEP(7) KDA_VSOLVE_STEP(8) KDA_VSOLVE_STEP(9)
-    KDA_VSOLVE_STEP(10) KDA_VSOLVE_STEP(11) KDA_VSOLVE_STEP(12) KDA_VSOLVE_STEP(13) KDA_VSOLVE_STEP(14)
+      _Pragma("unroll") for (int m = 0; m < 4; ++m) {                                                           \
+        const float xk_ = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[m]), 0x150 + (kk), 0xf, 0xf, true)); \
+        x[m] = __builtin_fmaf(arow[kk], xk_, x[m]);                                                             \
+      }
+      KDA_VSOLVE_STEP(0) KDA_VSOLVE_STEP(1) KDA_VSOLVE_STEP(2) KDA_VSOLVE_STEP(3) KDA_VSOLVE_STEP(4)
+      KDA_VSOLVE_STEP(5) KDA_VSOLVE_STEP(6) KDA_VSOLVE_STEP(7) KDA_VSOLVE_STEP(8) KDA_VSOLVE_STEP(9)
+      KDA_VSOLVE_STEP(10) KDA_VSOLVE_STEP(11) KDA_VSOLVE_STEP(12) KDA_VSOLVE_STEP(13) KDA_VSOLVE_STEP(14)
 #undef KDA_VSOLVE_STEP
-    *reinterpret_cast<uint2*>(&L.xh[lr][4 * g]) = make_uint2(pack2(h16(x[0]), h16(x[1])), pack2(h16(x[2]), h16(x[3])));
-  }
+      *reinterpret_cast<uint2*>(&L.xh[lr][4 * g]) = make_uint2(pack2(h16(x[0]), h16(x[1])), pack2(h16(x[2]), h16(x[3])));
+    }
 
-  // ---- Kt S0 (tokens x values) and (Qt S0)^T (values x tokens) on this wave's 32 columns
-  f32x4 KS[2], QT[2];
-  {
-    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-    KS[0] = KS[1] = QT[0] = QT[1] = z4;
+    // ---- Kt S0 (tokens x values) and (Qt S0)^T (values x tokens) on this wave's 32 columns
+    f32x4 KS[2], QT[2];
+    {
+      const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+      KS[0] = KS[1] = QT[0] = QT[1] = z4;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const f16x8 kr = perm_h(&L.kt[lr][32 * s], g);
-      const f16x8 qr = perm_h(&L.qt[lr][32 * s], g);
+      for (int s = 0; s < 4; ++s) {
+        const f16x8 kr = perm_h(&L.kt[lr][32 * s], g);
+        const f16x8 qr = perm_h(&L.qt[lr][32 * s], g);
 #pragma unroll
-      for (int nv = 0; nv < 2; ++nv) {
-        // S0 rows {32s+4g+r} then {32s+16+4g+r}, column 16nv+lr of the slice, via the transposing read
-        const uint16_t* p = &L.sh[wave][32 * s + 4 * g + (lr >> 2)][16 * nv + 4 * (lr & 3)];
-        const f16x8 sf = as_f16x8(lds_tr(p), lds_tr(p + 16 * 32));
-        KS[nv] = mfma_h(kr, sf, KS[nv]);
-        QT[nv] = mfma_h(sf, qr, QT[nv]);
+        for (int nv = 0; nv < 2; ++nv) {
+          // S0 rows {32s+4g+r} then {32s+16+4g+r}, column 16nv+lr of the slice, via the transposing read
+          const uint16_t* p = &L.sh[wave][32 * s + 4 * g + (lr >> 2)][16 * nv + 4 * (lr & 3)];
+          const f16x8 sf = as_f16x8(lds_tr(p), lds_tr(p + 16 * 32));
+          KS[nv] = mfma_h(kr, sf, KS[nv]);
+          QT[nv] = mfma_h(sf, qr, QT[nv]);
+        }
       }
     }
-  }
-  __syncthreads();  // X and P are complete
+    __syncthreads();  // X and P are complete
 
-  // ---- R = diag(beta)(V - Kt S0), W = X R, O^T = scale (QT + W^T P^T)
-  const f16x4 xa = __builtin_bit_cast(f16x4, lds8(&L.xh[lr][4 * g]));
-  const f16x4 pa = __builtin_bit_cast(f16x4, lds8(&L.ph[lr][4 * g]));
-  const float4 b4 = *reinterpret_cast<const float4*>(&L.beta[4 * g]);
-  const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+    // ---- R = diag(beta)(V - Kt S0), W = X R, O^T = scale (QT + W^T P^T)
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        A.o + row0 * D, 0, ok ? (int)((((uint32_t)T - 1) * H + 1) * D * 4) : 0, kBufWord3);
+    const f16x4 xa = __builtin_bit_cast(f16x4, lds8(&L.xh[lr][4 * g]));
+    const f16x4 pa = __builtin_bit_cast(f16x4, lds8(&L.ph[lr][4 * g]));
+    const float4 b4 = *reinterpret_cast<const float4*>(&L.beta[4 * g]);
+    const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-  for (int nv = 0; nv < 2; ++nv) {
-    const int col = 32 * wave + 16 * nv + lr;
-    f32x4 R;
+    for (int nv = 0; nv < 2; ++nv) {
+      const int col = 32 * wave + 16 * nv + lr;
+      f32x4 R;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) R[r] = bv[r] * (bf2f(L.v[4 * g + r][col]) - KS[nv][r]);
-    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-    f16x4 hi, lo;
-    split_h4(R, hi, lo);
-    const f32x4 W = mfma_h16(xa, lo, mfma_h16(xa, hi, z4));
-    split_h4(W, hi, lo);
-    const f32x4 O = mfma_h16(lo, pa, mfma_h16(hi, pa, QT[nv]));
-    // lane (g, lr) holds O[t = lr][32w + 16nv + 4g + r]
-    if (lr < T) {
-      float* orow = A.o + (row0 + (size_t)lr * H) * D + 32 * wave + 16 * nv + 4 * g;
-      *reinterpret_cast<float4*>(orow) = make_float4(A.scale * O[0], A.scale * O[1], A.scale * O[2], A.scale * O[3]);
+      for (int r = 0; r < 4; ++r) R[r] = bv[r] * (bf2f(L.v[4 * g + r][col]) - KS[nv][r]);
+      const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+      f16x4 hi, lo;
+      split_h4(R, hi, lo);
+      const f32x4 W = mfma_h16(xa, lo, mfma_h16(xa, hi, z4));
+      split_h4(W, hi, lo);
+      const f32x4 O = mfma_h16(lo, pa, mfma_h16(hi, pa, QT[nv]));
+      // lane (g, lr) holds O[t = lr][32w + 16nv + 4g + r]; rows t >= T fall outside the buffer
+      // range and are dropped by the hardware
+      const f32x4 os = {A.scale * O[0], A.scale * O[1], A.scale * O[2], A.scale * O[3]};
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, os), orsrc,
+                                             (int)(((uint32_t)lr * H * D + 32 * wave + 16 * nv + 4 * g) * 4), 0, 0);
     }
   }
 }
@@ -269,9 +327,19 @@ bool verify_chunk_eligible(const VerifyArgs& a, bool f32_inputs) {
 }
 
 hipError_t launch_verify_chunk(const VerifyArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.batch * (unsigned)a.n_heads), block(256);
-  if (a.ring_k) hipLaunchKernelGGL((verify_chunk_kernel<true>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((verify_chunk_kernel<false>), grid, block, 0, stream, a);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const long units = (long)a.batch * a.n_heads;
+  const long slots = 2L * prefill_max_grid(dev);  // two resident workgroups per CU
+  const dim3 grid((unsigned)(units < slots ? units : slots)), block(256);
+  const bool ring = a.ring_k != nullptr;
+  if (a.n_tok <= 8) {
+    if (ring) hipLaunchKernelGGL((verify_chunk_kernel<true, 8>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((verify_chunk_kernel<false, 8>), grid, block, 0, stream, a);
+  } else {
+    if (ring) hipLaunchKernelGGL((verify_chunk_kernel<true, 16>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((verify_chunk_kernel<false, 16>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
