@@ -63,6 +63,14 @@ struct alignas(16) VerifyLds {
 };
 
 __device__ __forceinline__ uint2 lds8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+// A wave-uniform 32-bit read through the scalar data cache. Plain loads of these
+// indices are emitted as vector loads, and waiting for one of those waits for every
+// older vector memory operation of the wave (prefetches and stores included).
+__device__ __forceinline__ int sload_i32(const int32_t* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
 __device__ __forceinline__ uint2 lds_tr(const uint16_t* p) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
 }
@@ -121,9 +129,11 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
   // unit u = (request b, head h); a request without a valid slot still runs (on state of slot 0)
   // but every store it makes is dropped by an empty buffer range
   auto unit_of = [&](int u, int& b, int& h, size_t& unit) -> bool {
-    b = u / H;
-    h = u - b * H;
-    const int slot = A.slot_idx[b];
+    // uniform values kept in scalar registers, so that the index loads are scalar ones and never
+    // wait behind the vector memory queue
+    b = __builtin_amdgcn_readfirstlane(u / H);
+    h = __builtin_amdgcn_readfirstlane(u - b * H);
+    const int slot = sload_i32(A.slot_idx + b);
     const bool valid = slot >= 0 && slot < A.n_slots;
     unit = ((size_t)(valid ? slot : 0) * A.n_layers + A.layer) * H + h;
     return valid;
@@ -144,7 +154,7 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
       kv[j] = bf2f(static_cast<const uint16_t*>(A.k)[e]);
       qv[j] = bf2f(static_cast<const uint16_t*>(A.q)[e]);
       vv[j] = bf2f(static_cast<const uint16_t*>(A.v)[e]);
-      gp[j] = t0 ? A.gk[(row0 + (size_t)min(j, T - 1) * H) * D + c] : 0.f;
+      gp[j] = A.gk[(row0 + (size_t)min(j, T - 1) * H) * D + c];  // used by the second half only
     }
     bv_in = A.beta[row0 + (size_t)min(t0 + (c & (NH - 1)), T - 1) * H];
   };
@@ -153,6 +163,22 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     size_t unit;
     unit_of(blockIdx.x, b, h, unit);
     prefetch(b, h, unit);
+    // The same stores as the end of an iteration, into empty ranges (dropped): the loop is
+    // then entered with the same pattern of outstanding memory operations from both sides,
+    // and the compiler's wait for the prefetched registers need not drain the stores.
+    const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(A.o, 0, 0, kBufWord3);
+    if constexpr (RING) {
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, none, 0, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, none, 0, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0, 0, 0);
+      }
+      __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0, 0, 0);
+    }
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    __builtin_amdgcn_raw_buffer_store_b128(z, none, 0, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(z, none, 0, 0, 0);
   }
 
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
@@ -188,7 +214,7 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
 
     // ---- raw inputs into the ring (bit copies; tokens past the window rewrite the last entry),
     // v rows and beta into LDS, and the decay factors of channel c over tokens t0 .. t0 + NH - 1
-    const int rstart = (RING && A.ring_start) ? A.ring_start[b] : 0;
+    const int rstart = (RING && A.ring_start) ? sload_i32(A.ring_start + b) : 0;
     // ring rows of this unit (an empty range for a request without a slot)
     __amdgpu_buffer_rsrc_t rk_rs, rv_rs, rg_rs, rb_rs;
     if constexpr (RING) {
