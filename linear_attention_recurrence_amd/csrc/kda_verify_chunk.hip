@@ -43,9 +43,11 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 constexpr int kBufWord3 = 0x00020000;  // raw buffer, 32-bit data format: range-checked by num_records
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
+template <int NT>
 struct alignas(16) VerifyLds {
   uint16_t sh[4][D][32];   // per wave: fp16 S0[c][32w + j]
   uint16_t kt[VT][TV];     // fp16 k e^G, rows t
@@ -60,6 +62,9 @@ struct alignas(16) VerifyLds {
   uint16_t ph[VT][PS];     // fp16 P, rows t
   float am[VT][20];        // A rows (fp32) for the solve
   float beta[VT];
+  uint16_t kin[NT][D];     // raw k, q (bf16) and gk rows of the window
+  uint16_t qin[NT][D];
+  float gin[NT][D];
 };
 
 __device__ __forceinline__ uint2 lds8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
@@ -105,7 +110,7 @@ __device__ __forceinline__ void split_h4(const f32x4& a, f16x4& hi, f16x4& lo) {
 // unit's first use of its prefetched registers leaves the stores in flight.
 template <bool RING, int NT>
 __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
-  __shared__ VerifyLds L;
+  __shared__ VerifyLds<NT> L;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, lr = lane & 15;
@@ -139,24 +144,28 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     return valid;
   };
   // prefetched registers of one unit: this wave's 128 x 32 state slice (16-byte loads, 8 rows per
-  // instruction) and this thread's raw inputs (tokens past the window re-read the last one)
+  // instruction) and 4 channels c4 .. c4+3 of tokens ti and ti + 8 (tokens past the window re-read
+  // the last one)
+  constexpr int NI = NT / 8;
+  const int ti = tid >> 5, c4 = 4 * (tid & 31);
   float4 sv[16];
-  float gv[NH], gp[NH], kv[NH], qv[NH], vv[NH], bv_in;
+  uint2 pk[NI], pq[NI], pv[NI];
+  float4 pg[NI];
+  float pb[NI];
   auto prefetch = [&](int b, int h, size_t unit) {
     const float* sp = A.state_pool + unit * D * D + 32 * wave + 4 * (lane & 7);
 #pragma unroll
     for (int i = 0; i < 16; ++i) sv[i] = *reinterpret_cast<const float4*>(sp + (size_t)(8 * i + (lane >> 3)) * D);
     const size_t row0 = (size_t)b * T * H + h;
 #pragma unroll
-    for (int j = 0; j < NH; ++j) {
-      const size_t e = (row0 + (size_t)min(t0 + j, T - 1) * H) * D + c;
-      gv[j] = A.gk[e];
-      kv[j] = bf2f(static_cast<const uint16_t*>(A.k)[e]);
-      qv[j] = bf2f(static_cast<const uint16_t*>(A.q)[e]);
-      vv[j] = bf2f(static_cast<const uint16_t*>(A.v)[e]);
-      gp[j] = A.gk[(row0 + (size_t)min(j, T - 1) * H) * D + c];  // used by the second half only
+    for (int n = 0; n < NI; ++n) {
+      const size_t r = row0 + (size_t)min(ti + 8 * n, T - 1) * H;
+      pk[n] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.k) + r * D + c4);
+      pq[n] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.q) + r * D + c4);
+      pv[n] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.v) + r * D + c4);
+      pg[n] = *reinterpret_cast<const float4*>(A.gk + r * D + c4);
+      pb[n] = A.beta[r];
     }
-    bv_in = A.beta[row0 + (size_t)min(t0 + (c & (NH - 1)), T - 1) * H];
   };
   if (blockIdx.x < (unsigned)n_units) {
     int b, h;
@@ -167,16 +176,16 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     // then entered with the same pattern of outstanding memory operations from both sides,
     // and the compiler's wait for the prefetched registers need not drain the stores.
     const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(A.o, 0, 0, kBufWord3);
+    const u32x4 z = {0u, 0u, 0u, 0u};
     if constexpr (RING) {
 #pragma unroll
-      for (int j = 0; j < NH; ++j) {
-        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, none, 0, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, none, 0, 0, 0);
+      for (int n = 0; n < NI; ++n) {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, none, 0, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, none, 0, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(z, none, 0, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0, 0, 0);
       }
-      __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0, 0, 0);
     }
-    const u32x4 z = {0u, 0u, 0u, 0u};
     __builtin_amdgcn_raw_buffer_store_b128(z, none, 0, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b128(z, none, 0, 0, 0);
   }
@@ -192,15 +201,34 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
       const uint32_t lo = pack2(h16(sv[i].x), h16(sv[i].y)), hi = pack2(h16(sv[i].z), h16(sv[i].w));
       *reinterpret_cast<uint2*>(&L.sh[wave][8 * i + (lane >> 3)][4 * (lane & 7)]) = make_uint2(lo, hi);
     }
-    // take this unit's inputs out of the prefetch registers
-    float fg[NH], fk[NH], fq[NH], fv[NH], gs = 0.f;
-    if (t0) {
-#pragma unroll
-      for (int j = 0; j < NH; ++j) gs += (j < T) ? gp[j] : 0.f;
+    // raw inputs: staging rows, v and beta for the chain, and the ring (bit copies; tokens past
+    // the window rewrite the last entry with the same bits)
+    const int rstart = (RING && A.ring_start) ? sload_i32(A.ring_start + b) : 0;
+    __amdgpu_buffer_rsrc_t rk_rs, rv_rs, rg_rs, rb_rs;  // this unit's ring rows (empty without a slot)
+    if constexpr (RING) {
+      const int nrow = ok ? A.ring_len : 0;
+      rk_rs = __builtin_amdgcn_make_buffer_rsrc(static_cast<uint16_t*>(A.ring_k) + unit * A.ring_len * D, 0, nrow * D * 2, kBufWord3);
+      rv_rs = __builtin_amdgcn_make_buffer_rsrc(static_cast<uint16_t*>(A.ring_v) + unit * A.ring_len * D, 0, nrow * D * 2, kBufWord3);
+      rg_rs = __builtin_amdgcn_make_buffer_rsrc(A.ring_gk + unit * A.ring_len * D, 0, nrow * D * 4, kBufWord3);
+      rb_rs = __builtin_amdgcn_make_buffer_rsrc(A.ring_beta + unit * A.ring_len, 0, nrow * 4, kBufWord3);
     }
 #pragma unroll
-    for (int j = 0; j < NH; ++j) { fg[j] = gv[j]; fk[j] = kv[j]; fq[j] = qv[j]; fv[j] = vv[j]; }
-    const float fb = bv_in;
+    for (int n = 0; n < NI; ++n) {
+      const int t = ti + 8 * n;
+      const bool ok_t = t < T;
+      *reinterpret_cast<uint2*>(&L.kin[t][c4]) = pk[n];
+      *reinterpret_cast<uint2*>(&L.qin[t][c4]) = pq[n];
+      *reinterpret_cast<float4*>(&L.gin[t][c4]) = pg[n];
+      *reinterpret_cast<uint2*>(&L.v[t][c4]) = ok_t ? pv[n] : make_uint2(0u, 0u);
+      if (c4 == 0) L.beta[t] = ok_t ? pb[n] : 0.f;
+      if constexpr (RING) {
+        const int pos = (rstart + min(t, T - 1)) & (A.ring_len - 1);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pk[n]), rk_rs, 2 * (pos * D + c4), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pv[n]), rv_rs, 2 * (pos * D + c4), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pg[n]), rg_rs, 4 * (pos * D + c4), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pb[n]), rb_rs, 4 * pos, 0, 0);
+      }
+    }
     {
       // the next unit streams in while this one computes (past the last unit: this one again,
       // so that every iteration issues the same loads)
@@ -211,49 +239,34 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
       prefetch(bn, hn, unitn);
     }
     const size_t row0 = (size_t)b * T * H + h;  // input row of token t: row0 + t * H
+    __syncthreads();
 
-    // ---- raw inputs into the ring (bit copies; tokens past the window rewrite the last entry),
-    // v rows and beta into LDS, and the decay factors of channel c over tokens t0 .. t0 + NH - 1
-    const int rstart = (RING && A.ring_start) ? sload_i32(A.ring_start + b) : 0;
-    // ring rows of this unit (an empty range for a request without a slot)
-    __amdgpu_buffer_rsrc_t rk_rs, rv_rs, rg_rs, rb_rs;
-    if constexpr (RING) {
-      const int nrow = ok ? A.ring_len : 0;
-      rk_rs = __builtin_amdgcn_make_buffer_rsrc(static_cast<uint16_t*>(A.ring_k) + unit * A.ring_len * D, 0, nrow * D * 2, kBufWord3);
-      rv_rs = __builtin_amdgcn_make_buffer_rsrc(static_cast<uint16_t*>(A.ring_v) + unit * A.ring_len * D, 0, nrow * D * 2, kBufWord3);
-      rg_rs = __builtin_amdgcn_make_buffer_rsrc(A.ring_gk + unit * A.ring_len * D, 0, nrow * D * 4, kBufWord3);
-      rb_rs = __builtin_amdgcn_make_buffer_rsrc(A.ring_beta + unit * A.ring_len, 0, nrow * 4, kBufWord3);
-    }
+    // ---- decay factors of channel c over tokens t0 .. t0 + NH - 1, from the decay summed over
+    // the tokens before them
+    {
+      float gs = 0.f;
+      if (t0) {
 #pragma unroll
-    for (int j = 0; j < NH; ++j) {
-      const int t = t0 + j;
-      const bool ok_t = t < T;
-      if constexpr (RING) {
-        const int pos = (rstart + min(t, T - 1)) & (A.ring_len - 1);
-        const int re = pos * D + c;
-        __builtin_amdgcn_raw_buffer_store_b16(f2bf(fk[j]), rk_rs, 2 * re, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b16(f2bf(fv[j]), rv_rs, 2 * re, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fg[j]), rg_rs, 4 * re, 0, 0);
+        for (int j = 0; j < NH; ++j) gs += (j < T) ? L.gin[j][c] : 0.f;
       }
-      L.v[t][c] = ok_t ? f2bf(fv[j]) : (uint16_t)0;
-      gs += ok_t ? fg[j] : 0.f;
-      const float e = __expf(gs), ie = __expf(-gs);
-      const float ke = ok_t ? fk[j] * e : 0.f, qe = ok_t ? fq[j] * e : 0.f, ck = ok_t ? fk[j] * ie : 0.f;
-      L.kt[t][c] = h16(ke);
-      L.qt[t][c] = h16(qe);
-      L.rk[t][c] = f2bf(ke);
-      uint16_t hi, lo;
-      split_bf16(qe, hi, lo);
-      L.rqh[t][c] = hi; L.rql[t][c] = lo;
-      split_bf16(ck, hi, lo);
-      L.ckh[t][c] = hi; L.ckl[t][c] = lo;
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        const int t = t0 + j;
+        const bool ok_t = t < T;
+        const float kv = bf2f(L.kin[t][c]), qv = bf2f(L.qin[t][c]);
+        gs += ok_t ? L.gin[t][c] : 0.f;
+        const float e = __expf(gs), ie = __expf(-gs);
+        const float ke = ok_t ? kv * e : 0.f, qe = ok_t ? qv * e : 0.f, ck = ok_t ? kv * ie : 0.f;
+        L.kt[t][c] = h16(ke);
+        L.qt[t][c] = h16(qe);
+        L.rk[t][c] = f2bf(ke);
+        uint16_t hi, lo;
+        split_bf16(qe, hi, lo);
+        L.rqh[t][c] = hi; L.rql[t][c] = lo;
+        split_bf16(ck, hi, lo);
+        L.ckh[t][c] = hi; L.ckl[t][c] = lo;
+      }
     }
-    if constexpr (RING) {
-      // every thread stores; lanes of the same token write the same bits
-      const int pos = (rstart + min(t0 + (c & (NH - 1)), T - 1)) & (A.ring_len - 1);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fb), rb_rs, 4 * pos, 0, 0);
-    }
-    if (c < NH) L.beta[t0 + c] = (t0 + c < T) ? fb : 0.f;
     __syncthreads();
 
     // ---- A, P and X = (I + A)^-1 (wave 0)
@@ -356,7 +369,8 @@ hipError_t launch_verify_chunk(const VerifyArgs& a, hipStream_t stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   const long units = (long)a.batch * a.n_heads;
-  const long slots = 2L * prefill_max_grid(dev);  // two resident workgroups per CU
+  const long per_cu = a.n_tok <= 8 ? 2 : 1;  // resident workgroups per CU (LDS-bound)
+  const long slots = per_cu * prefill_max_grid(dev);
   const dim3 grid((unsigned)(units < slots ? units : slots)), block(256);
   const bool ring = a.ring_k != nullptr;
   if (a.n_tok <= 8) {
