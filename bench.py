@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--no-verify-fold", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill (for profilers)")
+    ap.add_argument("--verify-fold-only", action="store_true", help="time only the speculative step (for profilers)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy, the reference kernel for scaling HBM byte counters")
     return ap.parse_args()
@@ -194,8 +195,8 @@ def cpu_baseline(synth, oracle):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
-              f"(the kernels need no collectives: see the sharding paragraph of DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the units of work are "
+              f"independent and need no collectives; one GPU's share is what is measured)", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -207,6 +208,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.init()
+    if args.verify_fold_only:
+        vf = bench_verify_fold(args, torch, kda, sg, synth)
+        print(json.dumps({"verify_us": vf["verify_ms"] * 1e3, "fold_us": vf["fold_ms"] * 1e3,
+                          "verify_gbs": vf["verify_gbs"], "fold_gbs": vf["fold_gbs"]}), flush=True)
+        return
     log("prefill: generating inputs and timing")
     pf = bench_prefill(args, torch, kda, sg, synth)
     log(f"prefill: {pf['ms'] * 1e3:.1f} us/launch, {pf['achieved']:.0f} GB/s")
