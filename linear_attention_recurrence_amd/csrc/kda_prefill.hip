@@ -40,11 +40,12 @@
 //     O = Qt S0 + P W (stored straight from the accumulators); phase 2: the
 //     state update and the snapshot.
 //   producer waves 4-7 prepare chunk c+1. Phase 1: raw q, k, gk, beta
-//     (prefetched into registers one period earlier) become decay factors,
-//     the fp16 operand rows of the chain and per-wave partial A and P tiles;
+//     (prefetched into registers two periods ahead) become decay factors,
+//     per-wave partial A and P tiles and the fp16 operand rows of the chain;
 //     raw v goes from global memory straight into LDS (global_load_lds) for
-//     the chain. Phase 2: one wave sums the A partials and inverts I + A, one
-//     sums the P partials.
+//     the chain. Phase 2: the operand rows go to LDS, one wave sums the P
+//     partials, one sums the off-diagonal A block; at the end of the period
+//     consumer wave 0 inverts the diagonal blocks of I + A.
 // Everything the two stages exchange is double-buffered by chunk parity, so
 // a period needs just its two barriers. Operands that a product needs
 // transposed are read with the transposing LDS load (ds_read_b64_tr_b16)
