@@ -63,6 +63,7 @@ constexpr int NT = 512;    // threads per workgroup: 4 consumer + 4 producer wav
 
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -122,20 +123,34 @@ __device__ __forceinline__ f16x8 to_h8(const f32x4& a, const f32x4& b) {
   for (int i = 0; i < 4; ++i) { r[i] = (_Float16)a[i]; r[4 + i] = (_Float16)b[i]; }
   return r;
 }
-__device__ __forceinline__ void split_h4(const f32x4& a, f16x4& hi, f16x4& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    hi[i] = (_Float16)a[i];
-    lo[i] = (_Float16)(a[i] - (float)hi[i]);
-  }
+// fp16 hi + lo of two fp32 values: hi = f16(x), lo = f16(x - hi). The remainder x - hi is exact
+// in fp32; it is formed by one fused multiply-add that takes the packed fp16 hi as its operand
+// (the mixed-precision FMA), instead of converting hi back to fp32 and subtracting. The empty
+// asm keeps the packed hi as the operand rather than a second scalar conversion of x.
+__device__ __forceinline__ void split_pair(float x, float y, f16x2& hi, f16x2& lo, float mone) {
+  hi = f16x2{(_Float16)x, (_Float16)y};
+  asm("" : "+v"(hi));
+  lo = f16x2{(_Float16)__builtin_fmaf((float)hi[0], mone, x), (_Float16)__builtin_fmaf((float)hi[1], mone, y)};
 }
-__device__ __forceinline__ void split_h8(const f32x4& a, const f32x4& b, f16x8& hi, f16x8& lo) {
-  hi = to_h8(a, b);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lo[i] = (_Float16)(a[i] - (float)hi[i]);
-    lo[4 + i] = (_Float16)(b[i] - (float)hi[4 + i]);
-  }
+// -1.0f in a register: with a literal the compiler folds the FMA back into a subtraction
+__device__ __forceinline__ float minus_one() {
+  float m = -1.0f;
+  asm volatile("" : "+v"(m));
+  return m;
+}
+__device__ __forceinline__ void split_h4(const f32x4& a, f16x4& hi, f16x4& lo, float mone) {
+  f16x2 h0, l0, h1, l1;
+  split_pair(a[0], a[1], h0, l0, mone);
+  split_pair(a[2], a[3], h1, l1, mone);
+  hi = f16x4{h0[0], h0[1], h1[0], h1[1]};
+  lo = f16x4{l0[0], l0[1], l1[0], l1[1]};
+}
+__device__ __forceinline__ void split_h8(const f32x4& a, const f32x4& b, f16x8& hi, f16x8& lo, float mone) {
+  f16x4 ha, la, hb, lb;
+  split_h4(a, ha, la, mone);
+  split_h4(b, hb, lb, mone);
+  hi = f16x8{ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
+  lo = f16x8{la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3]};
 }
 
 // row_shr:s with bound_ctrl: lanes shifted in from outside the 16-lane DPP row read 0
@@ -157,39 +172,40 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float (&f)[8]) {
   for (int i = 0; i < 4; ++i) { f[2 * i] = bf2f(w[i] & 0xffffu); f[2 * i + 1] = bf2f(w[i] >> 16); }
 }
 __device__ __forceinline__ uint32_t pk_f16(float a, float b) {
-  return pack2(__builtin_bit_cast(uint16_t, (_Float16)a), __builtin_bit_cast(uint16_t, (_Float16)b));
-}
-__device__ __forceinline__ void put_f16(uint16_t* dst, const float (&x)[8]) {
-  *reinterpret_cast<uint4*>(dst) = make_uint4(pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]), pk_f16(x[6], x[7]));
+  return __builtin_bit_cast(uint32_t, f16x2{(_Float16)a, (_Float16)b});
 }
 
 // Raw inputs of one chunk as one producer lane needs them: channel octet
 // 8co..8co+7 of tokens tl and 16+tl (rows past the sequence end re-read its
-// last token, always in bounds, and are masked where they are used).
+// last token, always in bounds; gk and beta are masked where they are used).
 struct Raw {
   uint4 q0, q1, k0, k1;
   float4 g0a, g0b, g1a, g1b;
   float b0, b1;
 };
 
-// row0: (first token of the chunk) * H + h, wave-uniform; per-lane offsets stay 32-bit
+// row0: (first token of the chunk) * H + h, wave-uniform. Per-lane offsets are 32-bit byte
+// offsets from wave-uniform bases, so the loads take the scalar-base addressing form.
+// Tokens past the chunk end re-read the last token (finite values; see stage1).
 __device__ __forceinline__ void load_raw(Raw& r, const PrefillArgs& A, size_t row0, int nc, int co, int tl) {
-  const uint32_t H = A.n_heads;
-  const uint32_t t0 = min(tl, nc - 1) * H, t1 = min(16 + tl, nc - 1) * H;
-  const uint32_t e0 = t0 * D + 8 * co, e1 = t1 * D + 8 * co;
-  const uint16_t* q = A.q + row0 * D;
-  const uint16_t* k = A.k + row0 * D;
-  const float* gk = A.gk + row0 * D;
-  r.q0 = *reinterpret_cast<const uint4*>(q + e0);
-  r.q1 = *reinterpret_cast<const uint4*>(q + e1);
-  r.k0 = *reinterpret_cast<const uint4*>(k + e0);
-  r.k1 = *reinterpret_cast<const uint4*>(k + e1);
-  r.g0a = *reinterpret_cast<const float4*>(gk + e0);
-  r.g0b = *reinterpret_cast<const float4*>(gk + e0 + 4);
-  r.g1a = *reinterpret_cast<const float4*>(gk + e1);
-  r.g1b = *reinterpret_cast<const float4*>(gk + e1 + 4);
-  r.b0 = A.beta[row0 + t0];
-  r.b1 = A.beta[row0 + t1];
+  const uint32_t HD2 = (uint32_t)A.n_heads * (D * 2);  // bytes per token of a bf16 [T, H, D] tensor
+  const uint32_t t0 = (uint32_t)min(tl, nc - 1), t1 = (uint32_t)min(16 + tl, nc - 1);
+  const uint32_t b0 = t0 * HD2 + 16u * co, b1 = t1 * HD2 + 16u * co;
+  const char* q = reinterpret_cast<const char*>(A.q + row0 * D);
+  const char* k = reinterpret_cast<const char*>(A.k + row0 * D);
+  const char* gk = reinterpret_cast<const char*>(A.gk + row0 * D);  // fp32: twice the bf16 offsets
+  const char* beta = reinterpret_cast<const char*>(A.beta + row0);
+  const uint32_t H4 = (uint32_t)A.n_heads * 4u;
+  r.q0 = *reinterpret_cast<const uint4*>(q + b0);
+  r.q1 = *reinterpret_cast<const uint4*>(q + b1);
+  r.k0 = *reinterpret_cast<const uint4*>(k + b0);
+  r.k1 = *reinterpret_cast<const uint4*>(k + b1);
+  r.g0a = *reinterpret_cast<const float4*>(gk + 2u * b0);
+  r.g0b = *reinterpret_cast<const float4*>(gk + 2u * b0 + 16u);
+  r.g1a = *reinterpret_cast<const float4*>(gk + 2u * b1);
+  r.g1b = *reinterpret_cast<const float4*>(gk + 2u * b1 + 16u);
+  r.b0 = *reinterpret_cast<const float*>(beta + t0 * H4);
+  r.b1 = *reinterpret_cast<const float*>(beta + t1 * H4);
 }
 
 // raw v rows of a chunk straight into LDS: 4 rows of 256 bytes per instruction, rows
@@ -207,9 +223,13 @@ __device__ __forceinline__ void issue_v(const PrefillArgs& A, uint16_t (&dst)[C]
 
 // What phase 2 of the producer needs from phase 1 to write the chain's operand rows: the
 // masked raw q and k (bf16) and the decay factors e^{G_t} and e^{G_31 - G_t} of both tokens.
+// eight fp16 products x[i] * y[i], packed
+__device__ __forceinline__ uint4 pk8_mul(const float (&x)[8], const float (&y)[8]) {
+  return make_uint4(pk_f16(x[0] * y[0], x[1] * y[1]), pk_f16(x[2] * y[2], x[3] * y[3]), pk_f16(x[4] * y[4], x[5] * y[5]),
+                    pk_f16(x[6] * y[6], x[7] * y[7]));
+}
 struct Keep {
-  uint4 q0, q1, k0, k1;
-  float e0[8], e1[8], f0[8], f1[8];
+  uint4 qt[2], kt[2], kp[2];  // fp16 q e^G, k e^G, k e^{G_31 - G} of tokens lr and 16 + lr
 };
 
 // ---------------------------------------------------------------------------
@@ -229,18 +249,17 @@ __device__ __forceinline__ void stage1(PrefillLds& L, const Raw& cur, int nc, in
 #pragma unroll
     for (int i = 0; i < 8; ++i) { l0[i] = ok0 ? gx[i] * kLog2e : 0.f; l1[i] = ok1 ? gy[i] * kLog2e : 0.f; }
   }
-  const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
   if (pw == 0 && g == 0) {
     L.beta[b][tl] = ok0 ? cur.b0 : 0.f;
     L.beta[b][16 + tl] = ok1 ? cur.b1 : 0.f;
   }
-  kp_.q0 = ok0 ? cur.q0 : zero4; kp_.q1 = ok1 ? cur.q1 : zero4;
-  kp_.k0 = ok0 ? cur.k0 : zero4; kp_.k1 = ok1 ? cur.k1 : zero4;
+  // q and k of tokens past the end are not masked: beta is zero there, so those rows of
+  // R and W are exactly zero and the rows drop out of every product (the loads re-read the
+  // last token, so the values are finite); gk is masked above so that G stops advancing
   float k0[8], k1[8], q0[8], q1[8];
-  unpack_bf16x8(kp_.k0, k0); unpack_bf16x8(kp_.k1, k1);
-  unpack_bf16x8(kp_.q0, q0); unpack_bf16x8(kp_.q1, q1);
-  float xr0[8], xr1[8], yc0[8], yc1[8];
-  float (&e0)[8] = kp_.e0, (&e1)[8] = kp_.e1, (&f0)[8] = kp_.f0, (&f1)[8] = kp_.f1;
+  unpack_bf16x8(cur.k0, k0); unpack_bf16x8(cur.k1, k1);
+  unpack_bf16x8(cur.q0, q0); unpack_bf16x8(cur.q1, q1);
+  float xr0[8], xr1[8], yc0[8], yc1[8], e0[8], e1[8], f0[8], f1[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     // prefix sums inside each 16-token block, then the four exponentials
@@ -258,6 +277,10 @@ __device__ __forceinline__ void stage1(PrefillLds& L, const Raw& cur, int nc, in
     f1[i] = T1 * r1;
     if (tl == 0) L.dlast[b][c8 + i] = T0 * T1;
   }
+  // fp16 operand rows of the chain, written to LDS in phase 2
+  kp_.qt[0] = pk8_mul(q0, e0); kp_.qt[1] = pk8_mul(q1, e1);
+  kp_.kt[0] = pk8_mul(k0, e0); kp_.kt[1] = pk8_mul(k1, e1);
+  kp_.kp[0] = pk8_mul(k0, f0); kp_.kp[1] = pk8_mul(k1, f1);
   // A and P over this wave's 32 channels, straight from registers: lane (g, lr) holds
   // channels 32pw+8g..+7 of tokens lr (block 0) and 16+lr (block 1), which is the
   // A-operand fragment of row lr and the B-operand fragment of column lr
@@ -284,29 +307,15 @@ __device__ __forceinline__ void stage1(PrefillLds& L, const Raw& cur, int nc, in
     *reinterpret_cast<f32x4*>(&L.part[pw][tl6][lr][4 * g]) = acc[tl6];
 }
 
-// producer, phase 2: fp16 operands of the state products, token-major rows tl and 16+tl
+// producer, phase 2: the fp16 operand rows formed in phase 1 go to LDS (token-major rows lr and 16+lr)
 __device__ __forceinline__ void stage1b(PrefillLds& L, const Keep& kp_, int b, int pw, int g, int lr) {
-  const int c8 = 8 * (4 * pw + g), tl = lr;
-  float k0[8], k1[8], q0[8], q1[8];
-  unpack_bf16x8(kp_.k0, k0); unpack_bf16x8(kp_.k1, k1);
-  unpack_bf16x8(kp_.q0, q0); unpack_bf16x8(kp_.q1, q1);
-  float x[8];
+  const int c8 = 8 * (4 * pw + g);
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-    const int t = 16 * blk + tl;
-    const float(&kk)[8] = blk ? k1 : k0;
-    const float(&qq)[8] = blk ? q1 : q0;
-    const float(&ee)[8] = blk ? kp_.e1 : kp_.e0;
-    const float(&ff)[8] = blk ? kp_.f1 : kp_.f0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = qq[i] * ee[i];
-    put_f16(&L.qt[b][t][c8], x);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = kk[i] * ee[i];
-    put_f16(&L.kt[b][t][c8], x);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = kk[i] * ff[i];
-    put_f16(&L.kp[b][t][c8], x);
+    const int t = 16 * blk + lr;
+    *reinterpret_cast<uint4*>(&L.qt[b][t][c8]) = kp_.qt[blk];
+    *reinterpret_cast<uint4*>(&L.kt[b][t][c8]) = kp_.kt[blk];
+    *reinterpret_cast<uint4*>(&L.kp[b][t][c8]) = kp_.kp[blk];
   }
 }
 
@@ -560,6 +569,7 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
           // ---------------- R = diag(beta)(V - Kt S0), W = X R ----------------
           // by blocks: W0 = X00 R0, W1 = X11 (R1 - A10 W0), 16x16x16 MFMAs with fp16 hi + lo operands
           f32x4 W[2][2];
+          const float mone = minus_one();
           {
             const f16x4 x00 = __builtin_bit_cast(f16x4, lds8(&L.xb[b][lr][4 * g]));
             const f16x4 x11 = __builtin_bit_cast(f16x4, lds8(&L.xb[b][16 + lr][16 + 4 * g]));
@@ -582,17 +592,17 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
               }
               const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
               f16x4 hi, lo;
-              split_h4(R[0], hi, lo);
+              split_h4(R[0], hi, lo, mone);
               f32x4 w0 = mfma_h16(x00, lo, mfma_h16(x00, hi, z4));
-              split_h4(w0, hi, lo);
+              split_h4(w0, hi, lo, mone);
               f32x4 r1 = mfma_h16(a10, lo, mfma_h16(a10, hi, R[1]));
-              split_h4(r1, hi, lo);
+              split_h4(r1, hi, lo, mone);
               W[0][nv] = w0;
               W[1][nv] = mfma_h16(x11, lo, mfma_h16(x11, hi, z4));
             }
           }
 #pragma unroll
-          for (int nv = 0; nv < 2; ++nv) split_h8(W[0][nv], W[1][nv], Wh[nv], Wl[nv]);
+          for (int nv = 0; nv < 2; ++nv) split_h8(W[0][nv], W[1][nv], Wh[nv], Wl[nv], mone);
 
           // ---------------- O^T = scale (S0^T Qt^T + W^T P^T), stored from the accumulators ----------------
           // lane (g, lr) holds O[16mt + lr][32cw + 16nv + 4g + r], r < 4: one 16-byte store per tile
