@@ -41,10 +41,12 @@ constexpr int PS = 24;   // 16x16 fp16 rows (+8 pad)
 
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 constexpr int kBufWord3 = 0x00020000;  // raw buffer, 32-bit data format: range-checked by num_records
+constexpr int kStream = 2;             // cache policy of the output stores: non-temporal (written once, read by later launches)
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 template <int NT>
@@ -92,12 +94,15 @@ __device__ __forceinline__ f32x4 mfma_h16(const f16x4& a, const f16x4& b, const 
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ uint16_t h16(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
-__device__ __forceinline__ void split_h4(const f32x4& a, f16x4& hi, f16x4& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    hi[i] = (_Float16)a[i];
-    lo[i] = (_Float16)(a[i] - (float)hi[i]);
-  }
+// fp16 hi + lo: hi = f16(x), lo = f16(x - hi), the exact remainder formed by one mixed-precision
+// FMA that takes the packed fp16 hi as its operand; mone is -1.0f held in a register (with a
+// literal the compiler folds the FMA back into a subtraction)
+__device__ __forceinline__ void split_h4(const f32x4& a, f16x4& hi, f16x4& lo, float mone) {
+  f16x2 h0 = {(_Float16)a[0], (_Float16)a[1]}, h1 = {(_Float16)a[2], (_Float16)a[3]};
+  asm("" : "+v"(h0), "+v"(h1));
+  hi = f16x4{h0[0], h0[1], h1[0], h1[1]};
+  lo = f16x4{(_Float16)__builtin_fmaf((float)h0[0], mone, a[0]), (_Float16)__builtin_fmaf((float)h0[1], mone, a[1]),
+             (_Float16)__builtin_fmaf((float)h1[0], mone, a[2]), (_Float16)__builtin_fmaf((float)h1[1], mone, a[3])};
 }
 
 }  // namespace
@@ -180,14 +185,14 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     if constexpr (RING) {
 #pragma unroll
       for (int n = 0; n < NI; ++n) {
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, none, 0, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, none, 0, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(z, none, 0, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, none, 0, 0, kStream);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, none, 0, 0, kStream);
+        __builtin_amdgcn_raw_buffer_store_b128(z, none, 0, 0, kStream);
+        __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0, 0, kStream);
       }
     }
-    __builtin_amdgcn_raw_buffer_store_b128(z, none, 0, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(z, none, 0, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(z, none, 0, 0, kStream);
+    __builtin_amdgcn_raw_buffer_store_b128(z, none, 0, 0, kStream);
   }
 
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
@@ -223,10 +228,10 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
       if (c4 == 0) L.beta[t] = ok_t ? pb[n] : 0.f;
       if constexpr (RING) {
         const int pos = (rstart + min(t, T - 1)) & (A.ring_len - 1);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pk[n]), rk_rs, 2 * (pos * D + c4), 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pv[n]), rv_rs, 2 * (pos * D + c4), 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pg[n]), rg_rs, 4 * (pos * D + c4), 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pb[n]), rb_rs, 4 * pos, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pk[n]), rk_rs, 2 * (pos * D + c4), 0, kStream);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pv[n]), rv_rs, 2 * (pos * D + c4), 0, kStream);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pg[n]), rg_rs, 4 * (pos * D + c4), 0, kStream);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pb[n]), rb_rs, 4 * pos, 0, kStream);
       }
     }
     {
@@ -340,6 +345,8 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     const f16x4 pa = __builtin_bit_cast(f16x4, lds8(&L.ph[lr][4 * g]));
     const float4 b4 = *reinterpret_cast<const float4*>(&L.beta[4 * g]);
     const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+    float mone = -1.0f;
+    asm volatile("" : "+v"(mone));
 #pragma unroll
     for (int nv = 0; nv < 2; ++nv) {
       const int col = 32 * wave + 16 * nv + lr;
@@ -348,15 +355,15 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
       for (int r = 0; r < 4; ++r) R[r] = bv[r] * (bf2f(L.v[4 * g + r][col]) - KS[nv][r]);
       const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
       f16x4 hi, lo;
-      split_h4(R, hi, lo);
+      split_h4(R, hi, lo, mone);
       const f32x4 W = mfma_h16(xa, lo, mfma_h16(xa, hi, z4));
-      split_h4(W, hi, lo);
+      split_h4(W, hi, lo, mone);
       const f32x4 O = mfma_h16(lo, pa, mfma_h16(hi, pa, QT[nv]));
       // lane (g, lr) holds O[t = lr][32w + 16nv + 4g + r]; rows t >= T fall outside the buffer
       // range and are dropped by the hardware
       const f32x4 os = {A.scale * O[0], A.scale * O[1], A.scale * O[2], A.scale * O[3]};
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, os), orsrc,
-                                             (int)(((uint32_t)lr * H * D + 32 * wave + 16 * nv + 4 * g) * 4), 0, 0);
+                                             (int)(((uint32_t)lr * H * D + 32 * wave + 16 * nv + 4 * g) * 4), 0, kStream);
     }
   }
 }
