@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 #define KDA_HEAD_DIM 128 /* K = V = 128, fixed at build time */
 #define KDA_CHUNK 32     /* prefill chunk length; snap_interval must be a multiple */
 
@@ -85,9 +85,14 @@ const char* kda_last_error(void);
 
 /* ---------------------------------------------------------------------------
  * Prefill plan [B200-FKDA]: built once per batch from HOST data and reused by
- * every layer (no device read-back). Work items are (sequence, head) pairs;
- * the plan orders them longest sequence first (ties: ascending sequence,
- * then head), or in input order with KDA_PLAN_FIFO.
+ * every layer (no device read-back). Work items are (sequence, head, value
+ * block) triples; the plan orders them longest sequence first (ties:
+ * ascending sequence, then head, then value block), or in input order with
+ * KDA_PLAN_FIFO. A value block is a range of the state's value columns: the
+ * columns of S evolve independently given the key-side quantities, so a
+ * (sequence, head) chain can be split into two halves of 64 columns that run
+ * on two workgroups (each recomputes the key side). That doubles the number
+ * of chains when there are fewer (sequence, head) pairs than compute units.
  * ------------------------------------------------------------------------- */
 typedef struct kda_plan kda_plan;
 
@@ -106,14 +111,31 @@ typedef struct kda_plan kda_plan;
 kda_status kda_plan_create(const int32_t* cu_seqlens_host, int n_seq, int n_heads,
                            int snap_interval, int order, kda_plan** out);
 
+/*
+ * kda_plan_create with a choice of value blocks per (sequence, head):
+ *   v_blocks = 1: whole 128-column chains (what kda_plan_create builds);
+ *   v_blocks = 2: two chains of 64 columns each;
+ *   v_blocks = 0: 2 when twice n_seq * n_heads still fits the compute units
+ *                 of the current device, else 1 (1 when no device is visible).
+ * n_heads <= 65535 (the work list packs head and value block in one int).
+ * Results are bitwise the same for every choice.
+ * Errors: as kda_plan_create; KDA_ERR_INVALID_ARG for another v_blocks.
+ */
+kda_status kda_plan_create_ex(const int32_t* cu_seqlens_host, int n_seq, int n_heads,
+                              int snap_interval, int order, int v_blocks, kda_plan** out);
+
+/* Value blocks per (sequence, head) of a plan: 1 or 2 (0 for NULL). */
+int kda_plan_v_blocks(const kda_plan* plan);
+
 /* Bytes of device workspace a prefill with this plan needs (256 + 16 per item). */
 size_t kda_plan_workspace_bytes(const kda_plan* plan);
 
-/* Number of work items (n_seq * n_heads). */
+/* Number of work items (n_seq * n_heads * value blocks). */
 int kda_plan_num_items(const kda_plan* plan);
 
 /* Copy the ordered work list to host memory items_host[n_items][4] =
- * (sequence, head, first token, length). For inspection and tests. */
+ * (sequence, head | value block << 16, first token, length). For inspection
+ * and tests. */
 kda_status kda_plan_items(const kda_plan* plan, int32_t* items_host);
 
 /* Enqueue the upload of the work list into `workspace` (device, at least

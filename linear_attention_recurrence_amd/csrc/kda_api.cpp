@@ -43,7 +43,7 @@ constexpr size_t kState = (size_t)KDA_HEAD_DIM * KDA_HEAD_DIM * sizeof(float);
 }  // namespace
 
 struct kda_plan {
-  int n_seq = 0, n_heads = 0, snap_interval = 0, order = 0, n_items = 0;
+  int n_seq = 0, n_heads = 0, snap_interval = 0, order = 0, v_blocks = 1, n_items = 0;
   int64_t total_tokens = 0;
   std::vector<int32_t> items;  // host copy, 4 ints per item
   void* upload = nullptr;      // header + items, pinned when the runtime allows
@@ -59,11 +59,28 @@ const char* kda_last_error(void) { return g_err.c_str(); }
 
 kda_status kda_plan_create(const int32_t* cu_seqlens_host, int n_seq, int n_heads, int snap_interval,
                            int order, kda_plan** out) {
+  return kda_plan_create_ex(cu_seqlens_host, n_seq, n_heads, snap_interval, order, 1, out);
+}
+
+kda_status kda_plan_create_ex(const int32_t* cu_seqlens_host, int n_seq, int n_heads, int snap_interval,
+                              int order, int v_blocks, kda_plan** out) {
   if (!out) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: out is NULL");
   *out = nullptr;
   if (!cu_seqlens_host) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: cu_seqlens_host is NULL");
   if (n_seq < 1 || n_heads < 1) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: n_seq and n_heads must be >= 1");
-  if ((int64_t)n_seq * n_heads > 0x7fffffffLL) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: too many work items");
+  if (n_heads > 0xffff) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: n_heads must be <= 65535");
+  if (v_blocks < 0 || v_blocks > 2) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: v_blocks must be 0, 1 or 2");
+  if (v_blocks == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        2LL * n_seq * n_heads <= cus)
+      v_blocks = 2;
+    else
+      v_blocks = 1;
+    (void)hipGetLastError();  // no device visible: the choice falls back to 1
+  }
+  if ((int64_t)n_seq * n_heads * v_blocks > 0x7fffffffLL) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: too many work items");
   if (snap_interval < 0 || snap_interval % KDA_CHUNK != 0)
     return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: snap_interval must be 0 or a positive multiple of KDA_CHUNK (32)");
   if (order != KDA_PLAN_LPT && order != KDA_PLAN_FIFO) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: bad order");
@@ -78,22 +95,24 @@ kda_status kda_plan_create(const int32_t* cu_seqlens_host, int n_seq, int n_head
   p->n_heads = n_heads;
   p->snap_interval = snap_interval;
   p->order = order;
-  p->n_items = n_seq * n_heads;
+  p->v_blocks = v_blocks;
+  p->n_items = n_seq * n_heads * v_blocks;
   p->total_tokens = cu_seqlens_host[n_seq];
+  const int per_seq = n_heads * v_blocks;
   std::vector<int> idx(p->n_items);
-  for (int i = 0; i < p->n_items; ++i) idx[i] = i;  // item i = (n = i / H, h = i % H)
+  for (int i = 0; i < p->n_items; ++i) idx[i] = i;  // item i = (n = i / (H vb), h, value block)
   if (order == KDA_PLAN_LPT) {
-    // longest sequence first; equal lengths keep (sequence, head) ascending
+    // longest sequence first; equal lengths keep (sequence, head, value block) ascending
     std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) {
-      const int na = a / n_heads, nb = b / n_heads;
+      const int na = a / per_seq, nb = b / per_seq;
       return (cu_seqlens_host[na + 1] - cu_seqlens_host[na]) > (cu_seqlens_host[nb + 1] - cu_seqlens_host[nb]);
     });
   }
   p->items.resize((size_t)p->n_items * 4);
   for (int i = 0; i < p->n_items; ++i) {
-    const int n = idx[i] / n_heads, h = idx[i] % n_heads;
+    const int n = idx[i] / per_seq, h = (idx[i] % per_seq) / v_blocks, vb = idx[i] % v_blocks;
     p->items[4 * i + 0] = n;
-    p->items[4 * i + 1] = h;
+    p->items[4 * i + 1] = h | (vb << 16);
     p->items[4 * i + 2] = cu_seqlens_host[n];
     p->items[4 * i + 3] = cu_seqlens_host[n + 1] - cu_seqlens_host[n];
   }
@@ -118,6 +137,8 @@ kda_status kda_plan_create(const int32_t* cu_seqlens_host, int n_seq, int n_head
 size_t kda_plan_workspace_bytes(const kda_plan* p) { return p ? p->bytes : 0; }
 
 int kda_plan_num_items(const kda_plan* p) { return p ? p->n_items : 0; }
+
+int kda_plan_v_blocks(const kda_plan* p) { return p ? p->v_blocks : 0; }
 
 kda_status kda_plan_items(const kda_plan* p, int32_t* items_host) {
   if (!p || !items_host) return fail(KDA_ERR_INVALID_ARG, "kda_plan_items: NULL argument");
@@ -204,6 +225,7 @@ kda_status kda_chunk_prefill(const kda_plan* p, const kda_inputs* in, const floa
   a.snap_count = snap_count;
   a.ws = static_cast<kda::PrefillWsHeader*>(workspace);
   a.items = reinterpret_cast<const int4*>(static_cast<char*>(workspace) + sizeof(kda::PrefillWsHeader));
+  a.n_vblk = p->v_blocks;
   a.scale = scale;
   const int grid = std::min(p->n_items, kda::prefill_max_grid(dev));
   e = kda::launch_prefill(a, grid, s);

@@ -63,7 +63,8 @@ struct PrefillArgs {
   int snap_interval;  // 0: none
   int32_t* snap_count;
   PrefillWsHeader* ws;
-  const int4* items;  // (sequence, head, first token, length)
+  const int4* items;  // (sequence, head | value block << 16, first token, length)
+  int n_vblk;         // value blocks per (sequence, head): 1 (all 128 columns) or 2 (halves)
   float scale;
 };
 

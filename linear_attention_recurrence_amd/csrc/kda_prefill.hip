@@ -50,6 +50,8 @@
 // a period needs just its two barriers. Operands that a product needs
 // transposed are read with the transposing LDS load (ds_read_b64_tr_b16)
 // instead of being stored twice.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -441,10 +443,11 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
     const int it = L.item;
     if (it < 0 || it >= A.n_items) break;  // also ends a launch on a stale counter
     const int4 wi = A.items[it];
-    const int n = wi.x, h = wi.y;
+    const int n = wi.x, h = wi.y & 0xffff, vb = wi.y >> 16;  // head, value block
     const int64_t tok0 = wi.z;
     const int len = wi.w;
-    if (n < 0 || n >= A.n_seq || h < 0 || h >= H || tok0 < 0 || len < 0 || tok0 + len > A.total_tokens) continue;
+    if (n < 0 || n >= A.n_seq || h >= H || vb < 0 || vb >= A.n_vblk || tok0 < 0 || len < 0 || tok0 + len > A.total_tokens)
+      continue;
     const size_t unit = (size_t)n * H + h;
     const int nch = (len + C - 1) / C;
 
@@ -513,159 +516,172 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no LDS write may outlive the item
       }
     } else {
-      const int cw = rw;
       const int lane = lane_o, g = g_o, lr = lr_o;
-      // This lane's element of a row-major [128][128] state tile is (16mc+4g+r, 32cw+16nv+lr), at
-      // tile + soff + (16mc+r)*D + 16nv. soff is made opaque here so that the compiler keeps one
-      // offset per lane instead of hoisting all 64 element offsets out of the item loop.
-      int soff = 4 * g * D + 32 * cw + lr;
-      asm volatile("" : "+v"(soff));
-      // state slice of this wave in accumulator layout: S[mc][nv] holds rows 16mc+4g+r, column 32cw+16nv+lr
-      f32x4 S[8][2];
-      if (A.state_in) {
-        const float* src = A.state_in + unit * D * D + soff;
-#pragma unroll
-        for (int mc = 0; mc < 8; ++mc)
-#pragma unroll
-          for (int nv = 0; nv < 2; ++nv)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) S[mc][nv][r] = src[(16 * mc + r) * D + 16 * nv];
-      } else {
-#pragma unroll
-        for (int mc = 0; mc < 8; ++mc)
-#pragma unroll
-          for (int nv = 0; nv < 2; ++nv) S[mc][nv] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      f16x8 Wh[2], Wl[2];
+      // The chain on the item's value columns: all 128 (four waves of 32, NV = 2 tiles of 16), or
+      // one of two halves of 64 (four waves of 16, NV = 1). Each 16-column tile runs the same
+      // instructions either way, so a split item gives the same bits as the whole one.
+      auto chain = [&](auto nv_tiles) {
+        constexpr int NV = decltype(nv_tiles)::value;
+        const int cw = rw;
+        const int cb = vb * (D / 2) * (2 - NV) + 16 * NV * cw;  // first value column of this wave
+        // This lane's element of a row-major [128][128] state tile is (16mc+4g+r, cb+16nv+lr), at
+        // tile + soff + (16mc+r)*D + 16nv. soff is made opaque here so that the compiler keeps one
+        // offset per lane instead of hoisting all the element offsets out of the item loop.
+        int soff = 4 * g * D + cb + lr;
+        asm volatile("" : "+v"(soff));
+        // state slice of this wave in accumulator layout: S[mc][nv] holds rows 16mc+4g+r, column cb+16nv+lr
+        f32x4 S[8][NV];
+        if (A.state_in) {
+          const float* src = A.state_in + unit * D * D + soff;
+  #pragma unroll
+          for (int mc = 0; mc < 8; ++mc)
+  #pragma unroll
+            for (int nv = 0; nv < NV; ++nv)
+  #pragma unroll
+              for (int r = 0; r < 4; ++r) S[mc][nv][r] = src[(16 * mc + r) * D + 16 * nv];
+        } else {
+  #pragma unroll
+          for (int mc = 0; mc < 8; ++mc)
+  #pragma unroll
+            for (int nv = 0; nv < NV; ++nv) S[mc][nv] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        f16x8 Wh[NV], Wl[NV];
 
-      for (int p = -1; p < nch; ++p) {
-        const int b = p & 1;
-        const int nc = min(C, len - C * p);
-        if (p >= 0) {
-          // ---------------- Kt S0 and Qt S0 ----------------
-          // S enters as fp16 B operands: step s reduces over rows {16(2s)+4g+r} then {16(2s+1)+4g+r},
-          // and the A operands read the same permutation of their columns
-          // The same fragments serve as the A operand of S^T, so (Qt S0)^T = S0^T Qt^T comes out
-          // transposed: QT[nv][mt] holds rows = value columns, columns = tokens.
-          f32x4 KS[2][2], QT[2][2];
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int nv = 0; nv < 2; ++nv) { KS[mt][nv] = f32x4{0.f, 0.f, 0.f, 0.f}; QT[nv][mt] = f32x4{0.f, 0.f, 0.f, 0.f}; }
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const f16x8 sh0 = to_h8(S[2 * s][0], S[2 * s + 1][0]), sh1 = to_h8(S[2 * s][1], S[2 * s + 1][1]);
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-              const int m = 16 * mt + lr;
-              const f16x8 kr = perm_h(&L.kt[b][m][32 * s], g);
-              const f16x8 qr = perm_h(&L.qt[b][m][32 * s], g);
-              KS[mt][0] = mfma_h(kr, sh0, KS[mt][0]);
-              KS[mt][1] = mfma_h(kr, sh1, KS[mt][1]);
-              QT[0][mt] = mfma_h(sh0, qr, QT[0][mt]);
-              QT[1][mt] = mfma_h(sh1, qr, QT[1][mt]);
-            }
-          }
-          // ---------------- R = diag(beta)(V - Kt S0), W = X R ----------------
-          // by blocks: W0 = X00 R0, W1 = X11 (R1 - A10 W0), 16x16x16 MFMAs with fp16 hi + lo operands
-          f32x4 W[2][2];
-          const float mone = minus_one();
-          {
-            const f16x4 x00 = __builtin_bit_cast(f16x4, lds8(&L.xb[b][lr][4 * g]));
-            const f16x4 x11 = __builtin_bit_cast(f16x4, lds8(&L.xb[b][16 + lr][16 + 4 * g]));
-            const f16x4 a10 = __builtin_bit_cast(f16x4, lds8(&L.an[b][lr][4 * g]));
-#pragma unroll
-            for (int nv = 0; nv < 2; ++nv) {
-              f32x4 R[2];
-              const int c0 = 32 * cw + 16 * nv + 4 * (lr & 3);
-#pragma unroll
+        for (int p = -1; p < nch; ++p) {
+          const int b = p & 1;
+          const int nc = min(C, len - C * p);
+          if (p >= 0) {
+            // ---------------- Kt S0 and Qt S0 ----------------
+            // S enters as fp16 B operands: step s reduces over rows {16(2s)+4g+r} then {16(2s+1)+4g+r},
+            // and the A operands read the same permutation of their columns
+            // The same fragments serve as the A operand of S^T, so (Qt S0)^T = S0^T Qt^T comes out
+            // transposed: QT[nv][mt] holds rows = value columns, columns = tokens.
+            f32x4 KS[2][NV], QT[NV][2];
+  #pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+  #pragma unroll
+              for (int nv = 0; nv < NV; ++nv) { KS[mt][nv] = f32x4{0.f, 0.f, 0.f, 0.f}; QT[nv][mt] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+  #pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              f16x8 sh[NV];
+  #pragma unroll
+              for (int nv = 0; nv < NV; ++nv) sh[nv] = to_h8(S[2 * s][nv], S[2 * s + 1][nv]);
+  #pragma unroll
               for (int mt = 0; mt < 2; ++mt) {
-                // V[16mt+4g+r][32cw+16nv+lr] through the transposing read of the swizzled raw rows;
-                // the four rows of one read land in four different 8-bank groups
-                const int row = 16 * mt + 4 * g + (lr >> 2);
-                const uint2 vv = lds_tr(&L.vr[b][row][8 * ((c0 >> 3) ^ ((2 * row) & 15)) + (c0 & 7)]);
-                const float4 b4 = *reinterpret_cast<const float4*>(&L.beta[b][16 * mt + 4 * g]);
-                R[mt][0] = b4.x * (bf2f(vv.x & 0xffffu) - KS[mt][nv][0]);
-                R[mt][1] = b4.y * (bf2f(vv.x >> 16) - KS[mt][nv][1]);
-                R[mt][2] = b4.z * (bf2f(vv.y & 0xffffu) - KS[mt][nv][2]);
-                R[mt][3] = b4.w * (bf2f(vv.y >> 16) - KS[mt][nv][3]);
+                const int m = 16 * mt + lr;
+                const f16x8 kr = perm_h(&L.kt[b][m][32 * s], g);
+                const f16x8 qr = perm_h(&L.qt[b][m][32 * s], g);
+  #pragma unroll
+                for (int nv = 0; nv < NV; ++nv) {
+                  KS[mt][nv] = mfma_h(kr, sh[nv], KS[mt][nv]);
+                  QT[nv][mt] = mfma_h(sh[nv], qr, QT[nv][mt]);
+                }
               }
-              const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-              f16x4 hi, lo;
-              split_h4(R[0], hi, lo, mone);
-              f32x4 w0 = mfma_h16(x00, lo, mfma_h16(x00, hi, z4));
-              split_h4(w0, hi, lo, mone);
-              f32x4 r1 = mfma_h16(a10, lo, mfma_h16(a10, hi, R[1]));
-              split_h4(r1, hi, lo, mone);
-              W[0][nv] = w0;
-              W[1][nv] = mfma_h16(x11, lo, mfma_h16(x11, hi, z4));
             }
-          }
-#pragma unroll
-          for (int nv = 0; nv < 2; ++nv) split_h8(W[0][nv], W[1][nv], Wh[nv], Wl[nv], mone);
+            // ---------------- R = diag(beta)(V - Kt S0), W = X R ----------------
+            // by blocks: W0 = X00 R0, W1 = X11 (R1 - A10 W0), 16x16x16 MFMAs with fp16 hi + lo operands
+            f32x4 W[2][NV];
+            const float mone = minus_one();
+            {
+              const f16x4 x00 = __builtin_bit_cast(f16x4, lds8(&L.xb[b][lr][4 * g]));
+              const f16x4 x11 = __builtin_bit_cast(f16x4, lds8(&L.xb[b][16 + lr][16 + 4 * g]));
+              const f16x4 a10 = __builtin_bit_cast(f16x4, lds8(&L.an[b][lr][4 * g]));
+  #pragma unroll
+              for (int nv = 0; nv < NV; ++nv) {
+                f32x4 R[2];
+                const int c0 = cb + 16 * nv + 4 * (lr & 3);
+  #pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                  // V[16mt+4g+r][32cw+16nv+lr] through the transposing read of the swizzled raw rows;
+                  // the four rows of one read land in four different 8-bank groups
+                  const int row = 16 * mt + 4 * g + (lr >> 2);
+                  const uint2 vv = lds_tr(&L.vr[b][row][8 * ((c0 >> 3) ^ ((2 * row) & 15)) + (c0 & 7)]);
+                  const float4 b4 = *reinterpret_cast<const float4*>(&L.beta[b][16 * mt + 4 * g]);
+                  R[mt][0] = b4.x * (bf2f(vv.x & 0xffffu) - KS[mt][nv][0]);
+                  R[mt][1] = b4.y * (bf2f(vv.x >> 16) - KS[mt][nv][1]);
+                  R[mt][2] = b4.z * (bf2f(vv.y & 0xffffu) - KS[mt][nv][2]);
+                  R[mt][3] = b4.w * (bf2f(vv.y >> 16) - KS[mt][nv][3]);
+                }
+                const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+                f16x4 hi, lo;
+                split_h4(R[0], hi, lo, mone);
+                f32x4 w0 = mfma_h16(x00, lo, mfma_h16(x00, hi, z4));
+                split_h4(w0, hi, lo, mone);
+                f32x4 r1 = mfma_h16(a10, lo, mfma_h16(a10, hi, R[1]));
+                split_h4(r1, hi, lo, mone);
+                W[0][nv] = w0;
+                W[1][nv] = mfma_h16(x11, lo, mfma_h16(x11, hi, z4));
+              }
+            }
+  #pragma unroll
+            for (int nv = 0; nv < NV; ++nv) split_h8(W[0][nv], W[1][nv], Wh[nv], Wl[nv], mone);
 
-          // ---------------- O^T = scale (S0^T Qt^T + W^T P^T), stored from the accumulators ----------------
-          // lane (g, lr) holds O[16mt + lr][32cw + 16nv + 4g + r], r < 4: one 16-byte store per tile
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            const f16x8 pa = perm_h(&L.pm[b][16 * mt + lr][0], g);
-            const int t = 16 * mt + lr;
-            float* orow = A.o + ((size_t)(tok0 + C * p) * H + h) * D + ((uint32_t)t * H * D + 32 * cw + 4 * g);
-#pragma unroll
-            for (int nv = 0; nv < 2; ++nv) {
-              f32x4 acc = QT[nv][mt];
-              acc = mfma_h(Wh[nv], pa, acc);
-              acc = mfma_h(Wl[nv], pa, acc);
-              if (t < nc)
-                *reinterpret_cast<float4*>(orow + 16 * nv) = make_float4(A.scale * acc[0], A.scale * acc[1], A.scale * acc[2], A.scale * acc[3]);
+            // ---------------- O^T = scale (S0^T Qt^T + W^T P^T), stored from the accumulators ----------------
+            // lane (g, lr) holds O[16mt + lr][cb + 16nv + 4g + r], r < 4: one 16-byte store per tile
+  #pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+              const f16x8 pa = perm_h(&L.pm[b][16 * mt + lr][0], g);
+              const int t = 16 * mt + lr;
+              float* orow = A.o + ((size_t)(tok0 + C * p) * H + h) * D + ((uint32_t)t * H * D + cb + 4 * g);
+  #pragma unroll
+              for (int nv = 0; nv < NV; ++nv) {
+                f32x4 acc = QT[nv][mt];
+                acc = mfma_h(Wh[nv], pa, acc);
+                acc = mfma_h(Wl[nv], pa, acc);
+                if (t < nc)
+                  *reinterpret_cast<float4*>(orow + 16 * nv) = make_float4(A.scale * acc[0], A.scale * acc[1], A.scale * acc[2], A.scale * acc[3]);
+              }
             }
           }
+          __syncthreads();
+          if (p >= 0) {
+            // ---------------- S = e^{G_31} S0 + K'^T W ----------------
+  #pragma unroll
+            for (int mc = 0; mc < 8; ++mc) {
+              const float4 d4 = *reinterpret_cast<const float4*>(&L.dlast[b][16 * mc + 4 * g]);
+              // K'^T rows 16mc+lr, reduction positions t = 4g+r and 16+4g+r, via the transposing read
+              const uint16_t* base = &L.kp[b][4 * g + (lr >> 2)][16 * mc + 4 * (lr & 3)];
+              const f16x8 ka = as_f16x8(lds_tr(base), lds_tr(base + 16 * TM));
+  #pragma unroll
+              for (int nv = 0; nv < NV; ++nv) {
+                f32x4 acc = S[mc][nv];
+                acc[0] *= d4.x; acc[1] *= d4.y; acc[2] *= d4.z; acc[3] *= d4.w;
+                acc = mfma_h(ka, Wh[nv], acc);
+                acc = mfma_h(ka, Wl[nv], acc);
+                S[mc][nv] = acc;
+              }
+            }
+
+            // ---------------- snapshot at chunk ends q with q % interval == 0 ----------------
+            const int q = C * p + nc;
+            if (A.snap_interval > 0 && q % A.snap_interval == 0) {
+              const int m = q / A.snap_interval;
+              float* dst = A.snap + (((size_t)n * A.snap_slots + (m - 1) % A.snap_slots) * H + h) * D * D + soff;
+  #pragma unroll
+              for (int mc = 0; mc < 8; ++mc)
+  #pragma unroll
+                for (int nv = 0; nv < NV; ++nv)
+  #pragma unroll
+                  for (int r = 0; r < 4; ++r) dst[(16 * mc + r) * D + 16 * nv] = S[mc][nv][r];
+            }
+          }
+          // X for the next chunk (its A partials were written by the producers in phase 1)
+          if (cw == 0 && p + 1 < nch) stage2_solve(L, (p + 1) & 1, lane);
+          __syncthreads();
         }
-        __syncthreads();
-        if (p >= 0) {
-          // ---------------- S = e^{G_31} S0 + K'^T W ----------------
-#pragma unroll
-          for (int mc = 0; mc < 8; ++mc) {
-            const float4 d4 = *reinterpret_cast<const float4*>(&L.dlast[b][16 * mc + 4 * g]);
-            // K'^T rows 16mc+lr, reduction positions t = 4g+r and 16+4g+r, via the transposing read
-            const uint16_t* base = &L.kp[b][4 * g + (lr >> 2)][16 * mc + 4 * (lr & 3)];
-            const f16x8 ka = as_f16x8(lds_tr(base), lds_tr(base + 16 * TM));
-#pragma unroll
-            for (int nv = 0; nv < 2; ++nv) {
-              f32x4 acc = S[mc][nv];
-              acc[0] *= d4.x; acc[1] *= d4.y; acc[2] *= d4.z; acc[3] *= d4.w;
-              acc = mfma_h(ka, Wh[nv], acc);
-              acc = mfma_h(ka, Wl[nv], acc);
-              S[mc][nv] = acc;
-            }
-          }
 
-          // ---------------- snapshot at chunk ends q with q % interval == 0 ----------------
-          const int q = C * p + nc;
-          if (A.snap_interval > 0 && q % A.snap_interval == 0) {
-            const int m = q / A.snap_interval;
-            float* dst = A.snap + (((size_t)n * A.snap_slots + (m - 1) % A.snap_slots) * H + h) * D * D + soff;
-#pragma unroll
-            for (int mc = 0; mc < 8; ++mc)
-#pragma unroll
-              for (int nv = 0; nv < 2; ++nv)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dst[(16 * mc + r) * D + 16 * nv] = S[mc][nv][r];
-          }
-        }
-        // X for the next chunk (its A partials were written by the producers in phase 1)
-        if (cw == 0 && p + 1 < nch) stage2_solve(L, (p + 1) & 1, lane);
-        __syncthreads();
-      }
+        float* dst = A.state_out + unit * D * D + soff;
+  #pragma unroll
+        for (int mc = 0; mc < 8; ++mc)
+  #pragma unroll
+          for (int nv = 0; nv < NV; ++nv)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(16 * mc + r) * D + 16 * nv] = S[mc][nv][r];
 
-      float* dst = A.state_out + unit * D * D + soff;
-#pragma unroll
-      for (int mc = 0; mc < 8; ++mc)
-#pragma unroll
-        for (int nv = 0; nv < 2; ++nv)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dst[(16 * mc + r) * D + 16 * nv] = S[mc][nv][r];
-      if (A.snap_count && h == 0 && tid == 0) A.snap_count[n] = A.snap_interval > 0 ? len / A.snap_interval : 0;
+      };
+      if (A.n_vblk == 1) chain(std::integral_constant<int, 2>{});
+      else chain(std::integral_constant<int, 1>{});
+      if (A.snap_count && h == 0 && vb == 0 && tid == 0) A.snap_count[n] = A.snap_interval > 0 ? len / A.snap_interval : 0;
     }
   }
 

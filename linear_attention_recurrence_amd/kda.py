@@ -29,8 +29,8 @@ KDA_PREFILL_PLAN_RESIDENT = 1
 KDA_HEAD_DIM = 128
 KDA_CHUNK = 32
 
-EXPORTS = ("kda_abi_version", "kda_last_error", "kda_plan_create", "kda_plan_workspace_bytes",
-           "kda_plan_num_items", "kda_plan_items", "kda_plan_upload", "kda_plan_destroy",
+EXPORTS = ("kda_abi_version", "kda_last_error", "kda_plan_create", "kda_plan_create_ex", "kda_plan_v_blocks",
+           "kda_plan_workspace_bytes", "kda_plan_num_items", "kda_plan_items", "kda_plan_upload", "kda_plan_destroy",
            "kda_chunk_prefill", "kda_verify", "kda_replay_fold")
 
 
@@ -64,6 +64,9 @@ def lib():
         L.kda_abi_version.restype = i32
         L.kda_last_error.restype = ctypes.c_char_p
         L.kda_plan_create.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(vp)]
+        L.kda_plan_create_ex.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(vp)]
+        L.kda_plan_v_blocks.argtypes = [vp]
+        L.kda_plan_v_blocks.restype = i32
         L.kda_plan_workspace_bytes.argtypes = [vp]
         L.kda_plan_workspace_bytes.restype = ctypes.c_size_t
         L.kda_plan_num_items.argtypes = [vp]
@@ -76,8 +79,8 @@ def lib():
         L.kda_verify.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(_Inputs), vp, vp, vp,
                                  ctypes.POINTER(_Ring), vp, vp, vp, f32, vp]
         L.kda_replay_fold.argtypes = [i32, i32, i32, i32, vp, vp, ctypes.POINTER(_Ring), vp, vp, vp]
-        for f in ("kda_plan_create", "kda_plan_items", "kda_plan_upload", "kda_chunk_prefill", "kda_verify",
-                  "kda_replay_fold"):
+        for f in ("kda_plan_create", "kda_plan_create_ex", "kda_plan_items", "kda_plan_upload", "kda_chunk_prefill",
+                  "kda_verify", "kda_replay_fold"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -141,11 +144,17 @@ class Plan:
             self.handle = None
 
 
-def kda_plan_create(cu_seqlens_host, n_heads, snap_interval=0, order=KDA_PLAN_LPT):
+def kda_plan_create(cu_seqlens_host, n_heads, snap_interval=0, order=KDA_PLAN_LPT, v_blocks=1):
+    """kda_plan_create_ex: v_blocks = 1 or 2 value blocks per (sequence, head), 0 = by device size."""
     cu = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
     h = ctypes.c_void_p()
-    _check(lib().kda_plan_create(cu.ctypes.data, len(cu) - 1, n_heads, snap_interval, order, ctypes.byref(h)))
+    _check(lib().kda_plan_create_ex(cu.ctypes.data, len(cu) - 1, n_heads, snap_interval, order, v_blocks,
+                                    ctypes.byref(h)))
     return Plan(h, cu.copy(), n_heads, snap_interval)
+
+
+def kda_plan_v_blocks(plan):
+    return int(lib().kda_plan_v_blocks(plan.handle))
 
 
 def kda_plan_workspace_bytes(plan):

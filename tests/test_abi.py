@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), f"libkda.so does not export {n}"
     assert set(names) == set(K.EXPORTS)
-    assert kda.kda_abi_version() == 1
+    assert kda.kda_abi_version() == 2
 
 
 def test_plan_lpt_order_and_ties():
@@ -51,16 +51,44 @@ def test_plan_lpt_order_and_ties():
     assert [tuple(x[:2]) for x in fifo] == [(n, h) for n in range(5) for h in range(3)]
 
 
-@pytest.mark.parametrize("cu,H,iv,msg", [
-    ([1, 5], 1, 0, "cu_seqlens[0]"),
-    ([0, 5, 3], 1, 0, "non-decreasing"),
-    ([0, 5], 0, 0, "n_heads"),
-    ([0, 5], 1, 48, "multiple"),
-    ([0, 5], 1, -32, "multiple"),
+def test_plan_value_blocks():
+    cu = [0, 5, 100, 100, 140, 235]  # lengths 5, 95, 0, 40, 95
+    p = kda.kda_plan_create(cu, n_heads=3, v_blocks=2)
+    assert kda.kda_plan_v_blocks(p) == 2 and kda.kda_plan_num_items(p) == 30
+    assert kda.kda_plan_workspace_bytes(p) == 256 + 16 * 30
+    it = kda.kda_plan_items(p)
+    h, vb = it[:, 1] & 0xffff, it[:, 1] >> 16
+    assert list(it[:, 3]) == sorted(it[:, 3], reverse=True)
+    # equal lengths keep (sequence, head, value block) ascending; every triple appears once
+    top = [(int(a), int(b), int(c)) for a, b, c, L in zip(it[:, 0], h, vb, it[:, 3]) if L == 95]
+    assert top == [(n, hh, v) for n in (1, 4) for hh in range(3) for v in range(2)]
+    assert sorted(zip(it[:, 0], h, vb)) == [(n, hh, v) for n in range(5) for hh in range(3) for v in range(2)]
+    fifo = kda.kda_plan_items(kda.kda_plan_create(cu, n_heads=3, order=kda.KDA_PLAN_FIFO, v_blocks=2))
+    assert [(x[0], x[1] & 0xffff, x[1] >> 16) for x in fifo] == [(n, hh, v) for n in range(5) for hh in range(3)
+                                                                  for v in range(2)]
+    # the one-block plan is kda_plan_create's, with a zero value block in every item
+    one = kda.kda_plan_items(kda.kda_plan_create(cu, n_heads=3, v_blocks=1))
+    assert np.array_equal(one, kda.kda_plan_items(kda.kda_plan_create(cu, n_heads=3)))
+    assert np.all(one[:, 1] >> 16 == 0)
+    # automatic choice: 1 or 2, never more items than the device could need
+    auto = kda.kda_plan_create(cu, n_heads=3, v_blocks=0)
+    assert kda.kda_plan_v_blocks(auto) in (1, 2)
+    assert kda.kda_plan_v_blocks(kda.kda_plan_create([0, 8] * 1, n_heads=4096, v_blocks=0)) == 1
+
+
+@pytest.mark.parametrize("cu,H,iv,vb,msg", [
+    ([1, 5], 1, 0, 1, "cu_seqlens[0]"),
+    ([0, 5, 3], 1, 0, 1, "non-decreasing"),
+    ([0, 5], 0, 0, 1, "n_heads"),
+    ([0, 5], 1, 48, 1, "multiple"),
+    ([0, 5], 1, -32, 1, "multiple"),
+    ([0, 5], 1, 0, 3, "v_blocks"),
+    ([0, 5], 1, 0, -1, "v_blocks"),
+    ([0, 5], 65536, 0, 1, "65535"),
 ])
-def test_plan_rejects(cu, H, iv, msg):
+def test_plan_rejects(cu, H, iv, vb, msg):
     with pytest.raises(kda.KdaError) as e:
-        kda.kda_plan_create(cu, n_heads=H, snap_interval=iv)
+        kda.kda_plan_create(cu, n_heads=H, snap_interval=iv, v_blocks=vb)
     assert e.value.status == kda.KDA_ERR_INVALID_ARG and msg in str(e.value)
 
 

@@ -31,22 +31,33 @@ def np_(t):
     return t.detach().cpu().numpy()
 
 
-def prefill_run(cfg, lens, H, state_in=None, snap_slots=0, order=kda.KDA_PLAN_LPT):
+def prefill_launch(plan, ins, o, st, snap, cnt, snap_slots, state_in=None):
+    """One prefill with a resident work list; returns its time in ms (HIP events)."""
+    ws = torch.empty(kda.kda_plan_workspace_bytes(plan), dtype=torch.uint8, device=DEV)
+    kda.kda_plan_upload(plan, ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    kda.kda_chunk_prefill(plan, *ins, st, o, ws, state_in=state_in, snap=snap, snap_slots=snap_slots,
+                          snap_count=cnt, flags=kda.KDA_PREFILL_PLAN_RESIDENT)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def prefill_run(cfg, lens, H, state_in=None, snap_slots=0, order=kda.KDA_PLAN_LPT, v_blocks=1):
     c = synth.PREFILL_CONFIGS[cfg]
     cu = synth.cu_seqlens(lens)
     T = int(cu[-1])
-    plan = kda.kda_plan_create(cu, n_heads=H, snap_interval=c["snap_interval"], order=order)
+    plan = kda.kda_plan_create(cu, n_heads=H, snap_interval=c["snap_interval"], order=order, v_blocks=v_blocks)
     ins = sg.prefill_inputs(c["seed"], T, H, DEV)
     N = len(lens)
     o = torch.empty((T, H, 128), device=DEV)
     st = torch.empty((N, H, 128, 128), device=DEV)
     snap = torch.full((N, snap_slots, H, 128, 128), -5.0, device=DEV) if snap_slots else None
     cnt = torch.full((N,), -1, dtype=torch.int32, device=DEV)
-    ws = torch.empty(kda.kda_plan_workspace_bytes(plan), dtype=torch.uint8, device=DEV)
-    kda.kda_plan_upload(plan, ws)
-    kda.kda_chunk_prefill(plan, *ins, st, o, ws, state_in=state_in, snap=snap, snap_slots=snap_slots,
-                          snap_count=cnt, flags=kda.KDA_PREFILL_PLAN_RESIDENT)
-    torch.cuda.synchronize()
+    ms = prefill_launch(plan, ins, o, st, snap, cnt, snap_slots, state_in=state_in)
+    log(f"prefill config {cfg}: {kda.kda_plan_num_items(plan)} items ({kda.kda_plan_v_blocks(plan)} value "
+        f"block(s) each), {ms:.2f} ms")
     return plan, cu, ins, o, st, snap, cnt
 
 
@@ -175,11 +186,20 @@ def test_long_context_1m_then_decode(gpu):
     cfg = synth.PREFILL_CONFIGS[4]
     seed = cfg["seed"]
     log("long context: generating 1M x 96 inputs on the device")
-    plan, cu, ins, o, st, snap, cnt = prefill_run(4, [T], H, snap_slots=2)
+    # 96 (sequence, head) chains for 256 compute units: the automatic plan splits each into two
+    # value blocks; the whole-chain plan must give the same bits
+    plan, cu, ins, o, st, snap, cnt = prefill_run(4, [T], H, snap_slots=2, v_blocks=0)
     assert int(cnt[0]) == T // 4096
     heads = [7, 60]
     o_np = {h: np_(o[:, h]) for h in heads}
-    del ins, o
+    st_split, snap_split = st.clone(), snap.clone()
+    whole = kda.kda_plan_create(cu, n_heads=H, snap_interval=4096, v_blocks=1)
+    ms = prefill_launch(whole, ins, o, st, snap, cnt, 2)
+    log(f"long context: whole-chain plan ({kda.kda_plan_num_items(whole)} items) {ms:.2f} ms")
+    assert torch.equal(st, st_split) and torch.equal(snap, snap_split)
+    for h in heads:
+        assert np.array_equal(np_(o[:, h]), o_np[h])
+    del ins, o, st_split, snap_split
     torch.cuda.empty_cache()
     # 128 single-token decode steps from the final state: verify with n_tok = 1 and an in-place commit
     pool = st.view(1, 1, H, 128, 128).clone()

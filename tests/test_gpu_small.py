@@ -278,6 +278,28 @@ def test_prefill_ragged_small(gpu):
     assert not torch.isnan(o).any()
 
 
+@pytest.mark.parametrize("v_blocks", [2, 0])
+def test_prefill_value_blocks_bitwise(gpu, v_blocks):
+    """Items split into two value blocks of 64 columns give the same bits as whole (sequence, head)
+    chains (o, state_out, snapshots, counts), on the ragged case the oracle checks above, with a
+    state_in, snapshots and a scale; an automatic plan (v_blocks = 0) too."""
+    seed, H = 11, 3
+    lens = np.array([1, 31, 33, 100, 0, 257, 64])
+    cu = synth.cu_seqlens(lens)
+    ins = sg.prefill_inputs(seed, int(cu[-1]), H, DEV)
+    S0 = sg.states(seed, len(lens) * H, DEV).view(len(lens), H, 128, 128)
+    whole = kda.kda_plan_create(cu, n_heads=H, snap_interval=64)
+    split = kda.kda_plan_create(cu, n_heads=H, snap_interval=64, v_blocks=v_blocks)
+    log(f"prefill value blocks: plan with {kda.kda_plan_v_blocks(split)} block(s), {kda.kda_plan_num_items(split)} items")
+    a = run_prefill(whole, ins, state_in=S0, snap_slots=2, scale=0.75)
+    b = run_prefill(split, ins, state_in=S0, snap_slots=2, scale=0.75)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    if v_blocks == 2:
+        assert kda.kda_plan_v_blocks(split) == 2
+
+
 def test_prefill_config0_bf16(gpu):
     """Config 0 through the chunked path on bf16-rounded q/k/v (the same draws)."""
     lens = np.array([64])
