@@ -29,11 +29,15 @@
 // fp16 hi + lo pairs. All accumulation is fp32 and the state stays fp32.
 //
 // Work decomposition: one 512-thread workgroup per CU, persistent, pulling
-// (sequence, head) items from a longest-first list with an atomic counter.
+// (sequence, head, value block) items from a longest-first list with an atomic
+// counter. A value block is all 128 value columns of the state, or one half
+// of them when the plan splits chains (the columns evolve independently given
+// the key side, which each half recomputes).
 // Inside an item the workgroup is a two-stage pipeline over chunks, one
 // period per chunk, each period cut in two phases by workgroup barriers:
 //   consumer waves 0-3 run the serial state chain of chunk c. Wave w owns
-//     value columns [32w, 32w+32); its 128x32 slice of the fp32 state lives
+//     value columns [32w, 32w+32) (in a half-chain [64vb + 16w, +16)); its
+//     128x32 (128x16) slice of the fp32 state lives
 //     in MFMA accumulator registers for the whole sequence and is fed back as
 //     the B operand of the next products by permuting the reduction index
 //     identically in both operands. Phase 1: Kt S0, Qt S0, R, W = X R and
