@@ -157,13 +157,43 @@ def bench_verify_fold(args, torch, kda, sg, synth):
         one_step(times)
     ver = sum(t[0] for t in times) / len(times)
     fol = sum(t[1] for t in times) / len(times)
+
+    # The same step through the fused path: one kda_fold_verify per layer folds the window the
+    # verifies above recorded (positions 0..T-1, the accepted lengths) into the committed state and
+    # verifies the next window (positions T..2T-1) from it.
+    ring_next = torch.full((B,), T, dtype=torch.int32, device=dev)
+
+    def fused_step(times):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for l in range(Lyr):
+            q, k, v, gk, beta = ins[l]
+            kda.kda_fold_verify(q, k, v, gk, beta, pool, slot_idx, o, layer=l, n_tok=T, ring=ring, fold_len=acc,
+                                fold_start=ring_start, ring_start=ring_next)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        if times is not None:
+            times.append(ev[0].elapsed_time(ev[1]))
+
+    for _ in range(max(1, args.warmup // 2)):
+        pool.copy_(pristine)
+        fused_step(None)
+    ftimes = []
+    for _ in range(args.vf_steps):
+        pool.copy_(pristine)
+        torch.cuda.synchronize()
+        fused_step(ftimes)
+    fus = sum(ftimes) / len(ftimes)
     units = S * Lyr * H
     acc_mean = float(acc.float().mean())
     v_bytes = units * (65536 + T * (768 + 512 + 4 + 512 + 1028))  # state + inputs + o + ring entries
     f_bytes = units * (2 * 65536) + int(round(float(acc.float().sum()) * Lyr * H * 1028))
+    # fused: the state read once, written back, the folded entries read, the verify's inputs and outputs
+    fv_bytes = units * (2 * 65536 + T * (768 + 512 + 4 + 512 + 1028)) + int(round(float(acc.float().sum()) * Lyr * H * 1028))
     res = dict(verify_ms=ver, fold_ms=fol, accept_mean=acc_mean,
                verify_gbs=v_bytes / (ver * 1e-3) / 1e9, fold_gbs=f_bytes / (fol * 1e-3) / 1e9,
-               verify_bytes=v_bytes, fold_bytes=f_bytes)
+               verify_bytes=v_bytes, fold_bytes=f_bytes, fused_ms=fus, fused_bytes=fv_bytes,
+               fused_gbs=fv_bytes / (fus * 1e-3) / 1e9)
     del pool, pristine, ring, ins, o
     return res
 
@@ -211,7 +241,8 @@ def main():
     if args.verify_fold_only:
         vf = bench_verify_fold(args, torch, kda, sg, synth)
         print(json.dumps({"verify_us": vf["verify_ms"] * 1e3, "fold_us": vf["fold_ms"] * 1e3,
-                          "verify_gbs": vf["verify_gbs"], "fold_gbs": vf["fold_gbs"]}), flush=True)
+                          "verify_gbs": vf["verify_gbs"], "fold_gbs": vf["fold_gbs"],
+                          "fused_us": vf["fused_ms"] * 1e3, "fused_gbs": vf["fused_gbs"]}), flush=True)
         return
     log("prefill: generating inputs and timing")
     pf = bench_prefill(args, torch, kda, sg, synth)
@@ -220,7 +251,7 @@ def main():
     if not (args.no_verify_fold or args.prefill_only):
         log("verify+fold: generating inputs and timing")
         vf = bench_verify_fold(args, torch, kda, sg, synth)
-        log(f"verify+fold: {vf['verify_ms'] * 1e3:.0f} + {vf['fold_ms'] * 1e3:.0f} us")
+        log(f"verify+fold: {vf['verify_ms'] * 1e3:.0f} + {vf['fold_ms'] * 1e3:.0f} us; fused {vf['fused_ms'] * 1e3:.0f} us")
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
         dst = torch.empty_like(src)
@@ -265,6 +296,10 @@ def main():
             "verify_gbs": vf["verify_gbs"], "fold_gbs": vf["fold_gbs"], "accept_mean": vf["accept_mean"],
             "workload": "256 requests x 69 layers x 8 heads, gamma+1=8 bf16 draft tokens, fp32 committed state, "
                         "ring length 16, accepted lengths geometric mean 2.7 clipped to [1,8]; 69 verify + 1 fold",
+            "fused_us_per_step": vf["fused_ms"] * 1e3, "fused_gbs": vf["fused_gbs"],
+            "fused_hbm_frac": vf["fused_gbs"] / HBM_PEAK_GBS,
+            "fused_workload": "the same step as 69 kda_fold_verify launches (each folds the previous window of "
+                              "its layer into the committed state, then verifies the next window from it)",
         }
     print(json.dumps(line), flush=True)
 

@@ -260,6 +260,40 @@ kda_status kda_replay_fold(int batch, int n_heads, int n_layers, int n_slots, fl
                            const int32_t* slot_idx, const kda_ring* ring,
                            const int32_t* ring_start, const int32_t* accepted_len, void* stream);
 
+/*
+ * Fused fold-then-verify of one layer [LMSYS-RSSM]. The fold of a speculative
+ * step and the verify of the next step read the same committed state; this
+ * entry point does both in one pass over it. For each request b and head h of
+ * `layer`:
+ *   1. fold: advance state_pool[slot_b, layer, h] in place by the first
+ *      fold_len[b] ring entries from position fold_start[b], exactly as
+ *      kda_replay_fold does (same step function, lane ownership and reduction
+ *      order: the state is bit-identical to kda_replay_fold's);
+ *   2. verify: from that state, exactly as kda_verify without a commit (o and
+ *      the ring entries at ring_start[b] + t are bit-identical to kda_verify's
+ *      on the folded pool).
+ * So a step sequence "verify; fold over all layers" becomes one
+ * kda_fold_verify per layer per step, folding the previous step's window.
+ *
+ *  batch .. slot_idx, o : as kda_verify; bf16 q/k/v only, 1 <= n_tok <= 8.
+ *  ring                 : required, ring->len a power of two in [2 n_tok, 16]
+ *                         (so at most 8 entries are folded).
+ *  fold_start           : int32 [batch] or NULL (= 0): ring position of the
+ *                         previous window's first entry.
+ *  fold_len             : int32 [batch], required; 0 folds nothing (the state
+ *                         is not written); clamped to [0, ring->len / 2].
+ *  ring_start           : int32 [batch] or NULL (= 0): where this step's
+ *                         entries go. Precondition (not checked): the folded
+ *                         entries and this step's entries do not overlap
+ *                         modulo ring->len (a ring of at least 2 n_tok holds
+ *                         the window being folded plus the next one).
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_DEVICE.
+ */
+kda_status kda_fold_verify(int batch, int n_tok, int n_heads, int n_layers, int layer, int n_slots,
+                           const kda_inputs* in, float* state_pool, const int32_t* slot_idx, float* o,
+                           const kda_ring* ring, const int32_t* fold_start, const int32_t* fold_len,
+                           const int32_t* ring_start, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -233,6 +233,74 @@ kda_status kda_chunk_prefill(const kda_plan* p, const kda_inputs* in, const floa
   return ok();
 }
 
+kda_status kda_fold_verify(int batch, int n_tok, int n_heads, int n_layers, int layer, int n_slots,
+                           const kda_inputs* in, float* state_pool, const int32_t* slot_idx, float* o,
+                           const kda_ring* ring, const int32_t* fold_start, const int32_t* fold_len,
+                           const int32_t* ring_start, float scale, void* stream) {
+  if (batch < 0 || n_tok < 1 || n_heads < 1 || n_layers < 1 || n_slots < 1 || layer < 0 || layer >= n_layers)
+    return fail(KDA_ERR_INVALID_ARG, "kda_fold_verify: bad batch/n_tok/n_heads/n_layers/layer/n_slots");
+  if (n_tok > 8) return fail(KDA_ERR_UNSUPPORTED, "kda_fold_verify: n_tok must be <= 8");
+  if ((int64_t)batch * n_heads > 0x7fffffffLL) return fail(KDA_ERR_INVALID_ARG, "kda_fold_verify: grid too large");
+  if (!ring || !ring->k || !ring->v || !ring->gk || !ring->beta)
+    return fail(KDA_ERR_INVALID_ARG, "kda_fold_verify: the ring is required");
+  if (!pow2(ring->len) || ring->len < 2 * n_tok)
+    return fail(KDA_ERR_INVALID_ARG, "kda_fold_verify: ring length must be a power of two >= 2 * n_tok");
+  if (ring->len > 16) return fail(KDA_ERR_UNSUPPORTED, "kda_fold_verify: ring length must be <= 16");
+  if (!fold_len) return fail(KDA_ERR_INVALID_ARG, "kda_fold_verify: fold_len is required");
+  if (batch == 0) return ok();
+  if (!in || !in->q || !in->k || !in->v || !in->gk || !in->beta)
+    return fail(KDA_ERR_INVALID_ARG, "kda_fold_verify: q, k, v, gk and beta are required");
+  if (!state_pool || !slot_idx || !o)
+    return fail(KDA_ERR_INVALID_ARG, "kda_fold_verify: state_pool, slot_idx and o are required");
+  const size_t rows = (size_t)batch * n_tok * n_heads;
+  const size_t pool_b = (size_t)n_slots * n_layers * n_heads * kState;
+  const size_t o_b = rows * KDA_HEAD_DIM * 4;
+  const size_t ring_units = (size_t)n_slots * n_layers * n_heads * ring->len;
+  const void* bufs[] = {in->q, in->k, in->v, in->gk, in->beta, state_pool};
+  const size_t bsz[] = {rows * KDA_HEAD_DIM * 2, rows * KDA_HEAD_DIM * 2, rows * KDA_HEAD_DIM * 2,
+                        rows * KDA_HEAD_DIM * 4, rows * 4, pool_b};
+  const void* rb[] = {ring->k, ring->v, ring->gk, ring->beta};
+  const size_t rs[] = {ring_units * KDA_HEAD_DIM * 2, ring_units * KDA_HEAD_DIM * 2, ring_units * KDA_HEAD_DIM * 4,
+                       ring_units * 4};
+  for (int i = 0; i < 6; ++i) {
+    if (overlap(o, o_b, bufs[i], bsz[i])) return fail(KDA_ERR_INVALID_ARG, "kda_fold_verify: o overlaps an input or the pool");
+    for (int j = 0; j < 4; ++j)
+      if (overlap(rb[j], rs[j], bufs[i], bsz[i]))
+        return fail(KDA_ERR_INVALID_ARG, "kda_fold_verify: the ring overlaps an input or the pool");
+  }
+  for (int j = 0; j < 4; ++j)
+    if (overlap(rb[j], rs[j], o, o_b)) return fail(KDA_ERR_INVALID_ARG, "kda_fold_verify: the ring overlaps o");
+
+  kda::VerifyArgs a{};
+  a.batch = batch;
+  a.n_tok = n_tok;
+  a.n_heads = n_heads;
+  a.n_layers = n_layers;
+  a.layer = layer;
+  a.n_slots = n_slots;
+  a.q = in->q;
+  a.k = in->k;
+  a.v = in->v;
+  a.gk = in->gk;
+  a.beta = in->beta;
+  a.state_pool = state_pool;
+  a.slot_idx = slot_idx;
+  a.o = o;
+  a.ring_k = ring->k;
+  a.ring_v = ring->v;
+  a.ring_gk = ring->gk;
+  a.ring_beta = ring->beta;
+  a.ring_len = ring->len;
+  a.ring_start = ring_start;
+  a.scale = scale;
+  a.fold_len = fold_len;
+  a.fold_start = fold_start;
+  a.fold_pool = state_pool;
+  const hipError_t e = kda::launch_fold_verify(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail("kda_fold_verify: launch", e);
+  return ok();
+}
+
 kda_status kda_verify(int batch, int n_tok, int n_heads, int n_layers, int layer, int n_slots, kda_dtype qkv_dtype,
                       const kda_inputs* in, const float* state_pool, const int32_t* slot_idx, float* o,
                       const kda_ring* ring, const int32_t* ring_start, const int32_t* commit_len, float* commit_pool,

@@ -25,6 +25,11 @@ struct VerifyArgs {
   const int32_t* commit_len;  // nullptr: no commit
   float* commit_pool;
   float scale;
+  // fused fold-then-verify (nullptr fold_len: plain verify): fold fold_len[b] entries of the
+  // previous window, at ring positions fold_start[b] + i, into fold_pool (== state_pool) first
+  const int32_t* fold_len;
+  const int32_t* fold_start;  // nullptr: 0
+  float* fold_pool;
 };
 
 struct FoldArgs {
@@ -72,6 +77,8 @@ hipError_t launch_verify(const VerifyArgs& a, bool f32_inputs, hipStream_t strea
 // chunked-form verify on the matrix cores: bf16 inputs, n_tok <= 16, no recurrent commit
 bool verify_chunk_eligible(const VerifyArgs& a, bool f32_inputs);
 hipError_t launch_verify_chunk(const VerifyArgs& a, hipStream_t stream);
+// fused fold-then-verify: bf16 inputs, n_tok <= 8, ring of at most 16 entries
+hipError_t launch_fold_verify(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_fold(const FoldArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int grid, hipStream_t stream);
 int prefill_max_grid(int device);

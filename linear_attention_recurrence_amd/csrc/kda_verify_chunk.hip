@@ -30,6 +30,7 @@
 // Two workgroups fit on a CU.
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_step.h"
 
 namespace kda {
 
@@ -52,13 +53,18 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 template <int NT>
 struct alignas(16) VerifyLds {
   uint16_t sh[4][D][32];   // per wave: fp16 S0[c][32w + j]
-  uint16_t kt[VT][TV];     // fp16 k e^G, rows t
-  uint16_t qt[VT][TV];     // fp16 q e^G
-  uint16_t rk[VT][TV];     // bf16 k e^G
-  uint16_t rqh[VT][TV];    // bf16 q e^G, hi
-  uint16_t rql[VT][TV];    //                lo
-  uint16_t ckh[VT][TV];    // bf16 k e^{-G}, hi
-  uint16_t ckl[VT][TV];    //                 lo
+  union {
+    struct {
+      uint16_t kt[VT][TV];     // fp16 k e^G, rows t
+      uint16_t qt[VT][TV];     // fp16 q e^G
+      uint16_t rk[VT][TV];     // bf16 k e^G
+      uint16_t rqh[VT][TV];    // bf16 q e^G, hi
+      uint16_t rql[VT][TV];    //                lo
+      uint16_t ckh[VT][TV];    // bf16 k e^{-G}, hi
+      uint16_t ckl[VT][TV];    //                 lo
+    };
+    FoldLds fold;  // fused fold: the previous window's entries, staged before the rows are formed
+  };
   uint16_t v[VT][D];       // bf16 v rows
   uint16_t xh[VT][PS];     // fp16 X = (I + A)^-1, rows t
   uint16_t ph[VT][PS];     // fp16 P, rows t
@@ -113,7 +119,7 @@ __device__ __forceinline__ void split_h4(const f32x4& a, f16x4& hi, f16x4& lo, f
 // global store of a unit is unconditional (the outputs of padded tokens are
 // dropped by the buffer range check), so the compiler's wait before the next
 // unit's first use of its prefetched registers leaves the stores in flight.
-template <bool RING, int NT>
+template <bool RING, int NT, bool FOLD>
 __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
   __shared__ VerifyLds<NT> L;
   const int tid = threadIdx.x;
@@ -153,14 +159,38 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
   // the last one)
   constexpr int NI = NT / 8;
   const int ti = tid >> 5, c4 = 4 * (tid & 31);
+  // the fold's ownership of the state (the recurrence step's): rows r0 .. r0 + 15, columns col0 .. col0 + 3
+  const int r0 = 16 * (lane & 7), col0 = 32 * wave + 4 * (lane >> 3);
   float4 sv[16];
   uint2 pk[NI], pq[NI], pv[NI];
   float4 pg[NI];
   float pb[NI];
+  uint2 fk, fv;  // fused fold: entry ti of the previous window (channels c4 .. c4 + 3)
+  float4 fg;
+  float fb;
+  // entries of the previous window to fold for request b (clamped like the fold's)
+  auto fold_n = [&](int b) {
+    const int n = sload_i32(A.fold_len + b), nmax = A.ring_len >> 1;
+    return n < 0 ? 0 : (n > nmax ? nmax : n);
+  };
   auto prefetch = [&](int b, int h, size_t unit) {
-    const float* sp = A.state_pool + unit * D * D + 32 * wave + 4 * (lane & 7);
+    if constexpr (FOLD) {
+      const float* sp = A.state_pool + unit * D * D + col0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sv[i] = *reinterpret_cast<const float4*>(sp + (size_t)(8 * i + (lane >> 3)) * D);
+      for (int i = 0; i < 16; ++i) sv[i] = *reinterpret_cast<const float4*>(sp + (size_t)(r0 + i) * D);
+      // entries past the window re-read its last one (or its first, for an empty window)
+      const int n = fold_n(b), fs = A.fold_start ? sload_i32(A.fold_start + b) : 0;
+      const int pos = (fs + min(ti, max(n - 1, 0))) & (A.ring_len - 1);
+      const size_t re = (unit * A.ring_len + pos) * D + c4;
+      fk = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.ring_k) + re);
+      fv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.ring_v) + re);
+      fg = *reinterpret_cast<const float4*>(A.ring_gk + re);
+      fb = A.ring_beta[unit * A.ring_len + pos];
+    } else {
+      const float* sp = A.state_pool + unit * D * D + 32 * wave + 4 * (lane & 7);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv[i] = *reinterpret_cast<const float4*>(sp + (size_t)(8 * i + (lane >> 3)) * D);
+    }
     const size_t row0 = (size_t)b * T * H + h;
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
@@ -200,11 +230,20 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     size_t unit;
     const bool ok = unit_of(u, b, h, unit);  // wave-uniform
     __syncthreads();                         // the previous unit's LDS readers are done
-    // state slice to fp16 in LDS
+    float S[16][4];                          // fused fold: the state, in the recurrence step's ownership
+    int fn = 0;                              // entries to fold
+    if constexpr (FOLD) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t lo = pack2(h16(sv[i].x), h16(sv[i].y)), hi = pack2(h16(sv[i].z), h16(sv[i].w));
-      *reinterpret_cast<uint2*>(&L.sh[wave][8 * i + (lane >> 3)][4 * (lane & 7)]) = make_uint2(lo, hi);
+      for (int i = 0; i < 16; ++i) { S[i][0] = sv[i].x; S[i][1] = sv[i].y; S[i][2] = sv[i].z; S[i][3] = sv[i].w; }
+      fn = fold_n(b);
+      if (ti < fn) stage_entry(L.fold, ti, c4, fk, fv, fg, fb);
+    } else {
+      // state slice to fp16 in LDS
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t lo = pack2(h16(sv[i].x), h16(sv[i].y)), hi = pack2(h16(sv[i].z), h16(sv[i].w));
+        *reinterpret_cast<uint2*>(&L.sh[wave][8 * i + (lane >> 3)][4 * (lane & 7)]) = make_uint2(lo, hi);
+      }
     }
     // raw inputs: staging rows, v and beta for the chain, and the ring (bit copies; tokens past
     // the window rewrite the last entry with the same bits)
@@ -234,17 +273,49 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pb[n]), rb_rs, 4 * pos, 0, kStream);
       }
     }
-    {
-      // the next unit streams in while this one computes (past the last unit: this one again,
-      // so that every iteration issues the same loads)
+    // the next unit streams in while this one computes (past the last unit: this one again,
+    // so that every iteration issues the same loads); the fused fold issues it after its fold,
+    // whose state shares the registers
+    auto prefetch_next = [&]() {
       int bn, hn;
       size_t unitn;
       const int un = u + (int)gridDim.x;
       unit_of(un < n_units ? un : u, bn, hn, unitn);
       prefetch(bn, hn, unitn);
-    }
+    };
+    if constexpr (!FOLD) prefetch_next();
     const size_t row0 = (size_t)b * T * H + h;  // input row of token t: row0 + t * H
     __syncthreads();
+    if constexpr (FOLD) {
+      // the previous window's accepted entries, replayed exactly as the fold does, then the
+      // committed state written back in place (dropped by an empty range when the slot is
+      // invalid or nothing is folded) and its fp16 copy staged for the verify below
+      for (int tt = 0; tt < fn; ++tt) step_update(S, L.fold, tt, r0, col0);
+      const __amdgpu_buffer_rsrc_t prs =
+          __builtin_amdgcn_make_buffer_rsrc(A.fold_pool + unit * D * D, 0, (ok && fn > 0) ? D * D * 4 : 0, kBufWord3);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(S[i][0]), __float_as_uint(S[i][1]),
+                                                     __float_as_uint(S[i][2]), __float_as_uint(S[i][3])},
+                                               prs, ((r0 + i) * D + col0) * 4, 0, 0);
+        const uint32_t lo = pack2(h16(S[i][0]), h16(S[i][1])), hi = pack2(h16(S[i][2]), h16(S[i][3]));
+        *reinterpret_cast<uint2*>(&L.sh[wave][r0 + i][4 * (lane >> 3)]) = make_uint2(lo, hi);
+      }
+      prefetch_next();
+      __syncthreads();
+      // the fold's staging shares memory with the operand rows kt, qt, rk and rqh (FoldLds spans
+      // 16.4 KB of them): their padding rows NT .. 15, which every MFMA tile reads, must be zero
+      // again (a non-finite value there times a zero entry of P would reach O)
+      static_assert(sizeof(FoldLds) <= 4 * sizeof(L.kt), "the fold staging must fit in kt, qt, rk and rqh");
+      static_assert(offsetof(VerifyLds<NT>, qt) == offsetof(VerifyLds<NT>, kt) + sizeof(L.kt) &&
+                        offsetof(VerifyLds<NT>, rqh) == offsetof(VerifyLds<NT>, kt) + 3 * sizeof(L.kt),
+                    "kt, qt, rk and rqh are consecutive");
+      for (int e = tid; e < 4 * (VT - NT) * (D / 8); e += 256) {
+        const int arr = e / ((VT - NT) * (D / 8)), rem = e % ((VT - NT) * (D / 8));
+        *reinterpret_cast<uint4*>(&L.kt[0][0] + arr * VT * TV + (NT + rem / (D / 8)) * TV + 8 * (rem % (D / 8))) =
+            make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
 
     // ---- decay factors of channel c over tokens t0 .. t0 + NH - 1, from the decay summed over
     // the tokens before them
@@ -369,7 +440,17 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
 }
 
 bool verify_chunk_eligible(const VerifyArgs& a, bool f32_inputs) {
-  return !f32_inputs && a.n_tok >= 1 && a.n_tok <= VT && a.commit_len == nullptr;
+  return !f32_inputs && a.n_tok >= 1 && a.n_tok <= VT && a.commit_len == nullptr && a.fold_len == nullptr;
+}
+
+hipError_t launch_fold_verify(const VerifyArgs& a, hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const long units = (long)a.batch * a.n_heads;
+  const long slots = 2L * prefill_max_grid(dev);  // two resident workgroups per CU
+  const dim3 grid((unsigned)(units < slots ? units : slots)), block(256);
+  hipLaunchKernelGGL((verify_chunk_kernel<true, 8, true>), grid, block, 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_verify_chunk(const VerifyArgs& a, hipStream_t stream) {
@@ -381,11 +462,11 @@ hipError_t launch_verify_chunk(const VerifyArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(units < slots ? units : slots)), block(256);
   const bool ring = a.ring_k != nullptr;
   if (a.n_tok <= 8) {
-    if (ring) hipLaunchKernelGGL((verify_chunk_kernel<true, 8>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((verify_chunk_kernel<false, 8>), grid, block, 0, stream, a);
+    if (ring) hipLaunchKernelGGL((verify_chunk_kernel<true, 8, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((verify_chunk_kernel<false, 8, false>), grid, block, 0, stream, a);
   } else {
-    if (ring) hipLaunchKernelGGL((verify_chunk_kernel<true, 16>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((verify_chunk_kernel<false, 16>), grid, block, 0, stream, a);
+    if (ring) hipLaunchKernelGGL((verify_chunk_kernel<true, 16, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((verify_chunk_kernel<false, 16, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -31,7 +31,7 @@ KDA_CHUNK = 32
 
 EXPORTS = ("kda_abi_version", "kda_last_error", "kda_plan_create", "kda_plan_create_ex", "kda_plan_v_blocks",
            "kda_plan_workspace_bytes", "kda_plan_num_items", "kda_plan_items", "kda_plan_upload", "kda_plan_destroy",
-           "kda_chunk_prefill", "kda_verify", "kda_replay_fold")
+           "kda_chunk_prefill", "kda_verify", "kda_replay_fold", "kda_fold_verify")
 
 
 class KdaError(RuntimeError):
@@ -79,8 +79,10 @@ def lib():
         L.kda_verify.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(_Inputs), vp, vp, vp,
                                  ctypes.POINTER(_Ring), vp, vp, vp, f32, vp]
         L.kda_replay_fold.argtypes = [i32, i32, i32, i32, vp, vp, ctypes.POINTER(_Ring), vp, vp, vp]
+        L.kda_fold_verify.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(_Inputs), vp, vp, vp,
+                                      ctypes.POINTER(_Ring), vp, vp, vp, f32, vp]
         for f in ("kda_plan_create", "kda_plan_create_ex", "kda_plan_items", "kda_plan_upload", "kda_chunk_prefill",
-                  "kda_verify", "kda_replay_fold"):
+                  "kda_verify", "kda_replay_fold", "kda_fold_verify"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -248,6 +250,29 @@ def kda_verify(q, k, v, gk, beta, state_pool, slot_idx, o, layer, n_tok, ring=No
     _check(lib().kda_verify(B, n_tok, H, L, layer, S, KDA_F32 if f32 else KDA_BF16, ctypes.byref(ins),
                             _ptr(state_pool), _ptr(slot_idx), _ptr(o), rc, _ptr(ring_start), _ptr(commit_len),
                             _ptr(commit_pool), float(scale), _stream(stream)))
+
+
+def kda_fold_verify(q, k, v, gk, beta, state_pool, slot_idx, o, layer, n_tok, ring, fold_len, fold_start=None,
+                    ring_start=None, scale=1.0, stream=None):
+    """Fold the previous window of `layer` into state_pool, then verify n_tok draft tokens from it
+    (see kda_fold_verify in include/kda.h)."""
+    S, L, H, Dh = state_pool.shape[0], state_pool.shape[1], state_pool.shape[2], KDA_HEAD_DIM
+    B = slot_idx.shape[0]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (B * n_tok, H, Dh), _BF)
+    _need(gk, "gk", (B * n_tok, H, Dh), _F32)
+    _need(beta, "beta", (B * n_tok, H), _F32)
+    _need(state_pool, "state_pool", (S, L, H, Dh, Dh), _F32)
+    _need(slot_idx, "slot_idx", (B,), _I32)
+    _need(o, "o", (B * n_tok, H, Dh), _F32)
+    _need(fold_len, "fold_len", (B,), _I32)
+    _need(fold_start, "fold_start", (B,), _I32, allow_none=True)
+    _need(ring_start, "ring_start", (B,), _I32, allow_none=True)
+    ring.check(S, L, H)
+    ins = _Inputs(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(), beta.data_ptr())
+    _check(lib().kda_fold_verify(B, n_tok, H, L, layer, S, ctypes.byref(ins), _ptr(state_pool), _ptr(slot_idx),
+                                 _ptr(o), ctypes.byref(ring.c()), _ptr(fold_start), _ptr(fold_len), _ptr(ring_start),
+                                 float(scale), _stream(stream)))
 
 
 def kda_replay_fold(state_pool, slot_idx, ring, accepted_len, ring_start=None, stream=None):

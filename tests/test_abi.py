@@ -169,6 +169,31 @@ def test_fold_rejects_bad_arguments():
     assert L.kda_replay_fold(0, 2, 3, 4, pool, slots, ctypes.byref(r16), None, acc, None) == 0
 
 
+def test_fold_verify_rejects_bad_arguments():
+    L = kda.lib()
+    ins = _inputs()
+    pool, slots, o = ctypes.c_void_p(0x20000000), ctypes.c_void_p(0x30000000), ctypes.c_void_p(0x40000000)
+    flen = ctypes.c_void_p(0x31000000)
+
+    def call(B=2, T=8, H=2, Lyr=3, layer=0, S=4, ring=_ring(16), fold_len=flen, o_=o, pool_=pool):
+        r = ctypes.byref(ring) if ring is not None else None
+        return L.kda_fold_verify(B, T, H, Lyr, layer, S, ctypes.byref(ins), pool_, slots, o_, r, None, fold_len, None,
+                                 1.0, None)
+
+    assert call(T=0) == 1
+    assert call(layer=3) == 1
+    assert call(ring=None) == 1                     # the ring is required
+    assert call(fold_len=None) == 1                 # so are the fold lengths
+    assert call(ring=_ring(12)) == 1                # not a power of two
+    assert call(T=4, ring=_ring(4)) == 1            # < 2 * n_tok
+    assert call(T=9, ring=_ring(32)) == 2           # more than 8 draft tokens
+    assert call(T=4, ring=_ring(32)) == 2           # a ring longer than 16 (folds of more than 8 entries)
+    assert "16" in kda.kda_last_error()
+    assert call(o_=ctypes.c_void_p(0x20000000)) == 1  # o overlaps the state pool
+    assert call(pool_=ctypes.c_void_p(0xC000000)) == 1  # the pool overlaps the ring
+    assert call(B=0) == 0                           # nothing to do
+
+
 def test_binding_checks_shapes_without_device():
     import torch
 

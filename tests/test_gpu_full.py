@@ -180,6 +180,28 @@ def test_spec_step_256x69x8(gpu):
     log(f"spec step worst {worst:.2e}")
     assert worst <= TOL
 
+    # The next step through the fused path: kda_fold_verify per layer folds this step's window
+    # (positions 0..T-1, accepted lengths acc) into a fresh copy of the committed pool and verifies
+    # the next window (positions T..2T-1) from it; it must equal the fold above followed by a
+    # verify of the next window from the folded pool, bit for bit.
+    log("spec step: next step, fused fold-then-verify against fold + verify")
+    ring_next = torch.full((B,), T, dtype=torch.int32, device=DEV)
+    ring_f = kda.Ring(ring.k.clone(), ring.v.clone(), ring.gk.clone(), ring.beta.clone())
+    pool_f = sg.states(seed, S * Lyr * H, DEV).view(S, Lyr, H, 128, 128)
+    for l in range(Lyr):
+        ins2 = sg.prefill_inputs(seed, B * T, H, DEV, sub=Lyr + l)
+        o_ref = torch.empty((B * T, H, 128), device=DEV)
+        kda.kda_verify(*ins2, pool, slot_idx, o_ref, layer=l, n_tok=T, ring=ring, ring_start=ring_next)
+        o_f = torch.empty((B * T, H, 128), device=DEV)
+        kda.kda_fold_verify(*ins2, pool_f, slot_idx, o_f, layer=l, n_tok=T, ring=ring_f, fold_len=acc,
+                            fold_start=ring_start, ring_start=ring_next)
+        assert torch.equal(o_f, o_ref), f"fused fold-then-verify output differs at layer {l}"
+    torch.cuda.synchronize()
+    assert torch.equal(pool_f, pool), "fused fold differs from the fold"
+    for a, b in ((ring_f.k, ring.k), (ring_f.v, ring.v), (ring_f.gk, ring.gk), (ring_f.beta, ring.beta)):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
 
 def test_long_context_1m_then_decode(gpu):
     H, T = 96, 1048576

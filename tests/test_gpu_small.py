@@ -129,6 +129,60 @@ def test_verify_and_fold_small(gpu):
             assert torch.equal(folded[s], pool0[s])
 
 
+@pytest.mark.parametrize("T,R", [(8, 16), (5, 16), (1, 2), (3, 8)])
+def test_fold_verify_bitwise(gpu, T, R):
+    """kda_fold_verify == kda_replay_fold of the previous window, then kda_verify of the new one, bit for
+    bit: the folded pool (every layer, every slot), o, and the ring (the previous window untouched, the new
+    entries written); fold lengths 0 .. R/2 (0 must not write), an invalid slot, windows that wrap."""
+    seed, B, H, L, S = 41, 6, 2, 3, 8
+    g = torch.Generator().manual_seed(seed + T)
+    slot_idx = torch.randperm(S, generator=g)[:B].to(torch.int32)
+    slot_idx[3] = -1
+    pool0 = sg.states(seed, S * L * H, DEV).view(S, L, H, 128, 128)
+    ring = kda.Ring.empty(S, L, H, R, DEV)
+    fold_start = torch.randint(0, 4 * R, (B,), generator=g, dtype=torch.int32)
+    prev_T = R // 2
+    # the previous window: a verify of prev_T tokens recorded at fold_start
+    prev = [sg.prefill_inputs(seed + 1, B * prev_T, H, DEV, sub=l) for l in range(L)]
+    scratch_o = torch.empty((B * prev_T, H, 128), device=DEV)
+    for l in range(L):
+        kda.kda_verify(*prev[l], pool0, slot_idx.to(DEV), scratch_o, layer=l, n_tok=prev_T, ring=ring,
+                       ring_start=fold_start.to(DEV))
+    fold_len = torch.tensor([prev_T, 0, 1, 2, prev_T - 1 if prev_T > 1 else 0, 3 % (prev_T + 1)], dtype=torch.int32)
+    ring_start = fold_start + prev_T  # the next window starts where the previous one ended
+    ins = [sg.prefill_inputs(seed + 2, B * T, H, DEV, sub=l) for l in range(L)]
+    # reference: fold, then verify from the folded pool
+    ref_pool = pool0.clone()
+    ref_ring = kda.Ring(ring.k.clone(), ring.v.clone(), ring.gk.clone(), ring.beta.clone())
+    kda.kda_replay_fold(ref_pool, slot_idx.to(DEV), ref_ring, fold_len.to(DEV), ring_start=fold_start.to(DEV))
+    ref_o = []
+    for l in range(L):
+        o = torch.full((B * T, H, 128), -9.0, device=DEV)
+        kda.kda_verify(*ins[l], ref_pool, slot_idx.to(DEV), o, layer=l, n_tok=T, ring=ref_ring,
+                       ring_start=ring_start.to(DEV), scale=0.7)
+        ref_o.append(o)
+    # fused, one layer at a time
+    pool = pool0.clone()
+    fus_o = []
+    for l in range(L):
+        o = torch.full((B * T, H, 128), -9.0, device=DEV)
+        kda.kda_fold_verify(*ins[l], pool, slot_idx.to(DEV), o, layer=l, n_tok=T, ring=ring, fold_len=fold_len.to(DEV),
+                            fold_start=fold_start.to(DEV), ring_start=ring_start.to(DEV), scale=0.7)
+        fus_o.append(o)
+    torch.cuda.synchronize()
+    log(f"fold_verify T={T} R={R}: fold lengths {fold_len.tolist()}, slots {slot_idx.tolist()}")
+    assert torch.equal(pool, ref_pool)
+    for l in range(L):
+        assert torch.equal(fus_o[l], ref_o[l])
+    for a, b in ((ring.k, ref_ring.k), (ring.v, ref_ring.v), (ring.gk, ref_ring.gk), (ring.beta, ref_ring.beta)):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+    # the invalid slot's request wrote nothing; fold length 0 left its state as it was
+    assert torch.all(fus_o[0].view(B, T, H, 128)[3] == -9.0)
+    s1 = int(slot_idx[1])
+    assert torch.equal(pool[s1], pool0[s1])
+
+
 @pytest.mark.parametrize("T,use_ring", [(1, True), (5, True), (8, True), (16, True), (8, False), (17, True)])
 def test_verify_without_commit(gpu, T, use_ring):
     """The call shape of a speculative step (no recurrent commit): up to 16 tokens take the chunked
