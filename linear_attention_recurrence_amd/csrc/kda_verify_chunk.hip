@@ -173,11 +173,21 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     const int n = sload_i32(A.fold_len + b), nmax = A.ring_len >> 1;
     return n < 0 ? 0 : (n > nmax ? nmax : n);
   };
-  auto prefetch = [&](int b, int h, size_t unit) {
+  // the state slice of a unit (in the fold's ownership on the fused path)
+  auto prefetch_state = [&](size_t unit) {
     if constexpr (FOLD) {
       const float* sp = A.state_pool + unit * D * D + col0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sv[i] = *reinterpret_cast<const float4*>(sp + (size_t)(r0 + i) * D);
+    } else {
+      const float* sp = A.state_pool + unit * D * D + 32 * wave + 4 * (lane & 7);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv[i] = *reinterpret_cast<const float4*>(sp + (size_t)(8 * i + (lane >> 3)) * D);
+    }
+  };
+  // the raw inputs of a unit (and the entries to fold on the fused path)
+  auto prefetch_inputs = [&](int b, int h, size_t unit) {
+    if constexpr (FOLD) {
       // entries past the window re-read its last one (or its first, for an empty window)
       const int n = fold_n(b), fs = A.fold_start ? sload_i32(A.fold_start + b) : 0;
       const int pos = (fs + min(ti, max(n - 1, 0))) & (A.ring_len - 1);
@@ -186,10 +196,6 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
       fv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.ring_v) + re);
       fg = *reinterpret_cast<const float4*>(A.ring_gk + re);
       fb = A.ring_beta[unit * A.ring_len + pos];
-    } else {
-      const float* sp = A.state_pool + unit * D * D + 32 * wave + 4 * (lane & 7);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sv[i] = *reinterpret_cast<const float4*>(sp + (size_t)(8 * i + (lane >> 3)) * D);
     }
     const size_t row0 = (size_t)b * T * H + h;
 #pragma unroll
@@ -206,7 +212,9 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     int b, h;
     size_t unit;
     unit_of(blockIdx.x, b, h, unit);
-    prefetch(b, h, unit);
+    if constexpr (!FOLD) prefetch_state(unit);
+    prefetch_inputs(b, h, unit);
+    if constexpr (FOLD) prefetch_state(unit);
     // The same stores as the end of an iteration, into empty ranges (dropped): the loop is
     // then entered with the same pattern of outstanding memory operations from both sides,
     // and the compiler's wait for the prefetched registers need not drain the stores.
@@ -276,14 +284,14 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     // the next unit streams in while this one computes (past the last unit: this one again,
     // so that every iteration issues the same loads); the fused fold issues it after its fold,
     // whose state shares the registers
-    auto prefetch_next = [&]() {
-      int bn, hn;
-      size_t unitn;
+    int bn, hn;
+    size_t unitn;
+    {
       const int un = u + (int)gridDim.x;
       unit_of(un < n_units ? un : u, bn, hn, unitn);
-      prefetch(bn, hn, unitn);
-    };
-    if constexpr (!FOLD) prefetch_next();
+    }
+    if constexpr (!FOLD) prefetch_state(unitn);
+    prefetch_inputs(bn, hn, unitn);
     const size_t row0 = (size_t)b * T * H + h;  // input row of token t: row0 + t * H
     __syncthreads();
     if constexpr (FOLD) {
@@ -301,7 +309,7 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
         const uint32_t lo = pack2(h16(S[i][0]), h16(S[i][1])), hi = pack2(h16(S[i][2]), h16(S[i][3]));
         *reinterpret_cast<uint2*>(&L.sh[wave][r0 + i][4 * (lane >> 3)]) = make_uint2(lo, hi);
       }
-      prefetch_next();
+      prefetch_state(unitn);
       __syncthreads();
       // the fold's staging shares memory with the operand rows kt, qt, rk and rqh (FoldLds spans
       // 16.4 KB of them): their padding rows NT .. 15, which every MFMA tile reads, must be zero
