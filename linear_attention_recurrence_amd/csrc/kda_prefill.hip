@@ -690,9 +690,13 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
   }
 
   // the last workgroup out resets the counters, so a later launch with the
-  // same resident work list starts from zero
+  // same resident work list starts from zero. No fence is needed: every
+  // workgroup's last draw from the counter has returned its value (the loop
+  // above ended on it) before its increment of `done` is issued, so when the
+  // last increment returns, no draw of this launch is still to be performed.
+  // (A release fence here would also write back this XCD's L2 once per
+  // workgroup, a few microseconds at the end of the launch.)
   if (tid == 0) {
-    __threadfence();
     const int d = atomicAdd(&A.ws->done, 1);
     if (d == (int)gridDim.x - 1) {
       atomicExch(&A.ws->counter, 0);

@@ -129,12 +129,13 @@ def test_verify_and_fold_small(gpu):
             assert torch.equal(folded[s], pool0[s])
 
 
-@pytest.mark.parametrize("T,R", [(8, 16), (5, 16), (1, 2), (3, 8)])
-def test_fold_verify_bitwise(gpu, T, R):
+@pytest.mark.parametrize("T,R,B,H", [(8, 16, 6, 2), (5, 16, 6, 2), (1, 2, 6, 2), (3, 8, 6, 2), (8, 16, 5, 3)])
+def test_fold_verify_bitwise(gpu, T, R, B, H):
     """kda_fold_verify == kda_replay_fold of the previous window, then kda_verify of the new one, bit for
     bit: the folded pool (every layer, every slot), o, and the ring (the previous window untouched, the new
-    entries written); fold lengths 0 .. R/2 (0 must not write), an invalid slot, windows that wrap."""
-    seed, B, H, L, S = 41, 6, 2, 3, 8
+    entries written); fold lengths 0 .. R/2 (0 must not write), an invalid slot, windows that wrap, and an
+    odd number of (request, head) units (a workgroup's second half then has no unit of its own)."""
+    seed, L, S = 41, 3, 8
     g = torch.Generator().manual_seed(seed + T)
     slot_idx = torch.randperm(S, generator=g)[:B].to(torch.int32)
     slot_idx[3] = -1
@@ -148,7 +149,7 @@ def test_fold_verify_bitwise(gpu, T, R):
     for l in range(L):
         kda.kda_verify(*prev[l], pool0, slot_idx.to(DEV), scratch_o, layer=l, n_tok=prev_T, ring=ring,
                        ring_start=fold_start.to(DEV))
-    fold_len = torch.tensor([prev_T, 0, 1, 2, prev_T - 1 if prev_T > 1 else 0, 3 % (prev_T + 1)], dtype=torch.int32)
+    fold_len = torch.tensor([prev_T, 0, 1, 2, prev_T - 1 if prev_T > 1 else 0, 3 % (prev_T + 1)][:B], dtype=torch.int32)
     ring_start = fold_start + prev_T  # the next window starts where the previous one ended
     ins = [sg.prefill_inputs(seed + 2, B * T, H, DEV, sub=l) for l in range(L)]
     # reference: fold, then verify from the folded pool
@@ -183,14 +184,16 @@ def test_fold_verify_bitwise(gpu, T, R):
     assert torch.equal(pool[s1], pool0[s1])
 
 
-@pytest.mark.parametrize("T,use_ring", [(1, True), (5, True), (8, True), (16, True), (8, False), (17, True)])
-def test_verify_without_commit(gpu, T, use_ring):
+@pytest.mark.parametrize("T,use_ring,H", [(1, True, 2), (5, True, 2), (8, True, 2), (16, True, 2), (8, False, 2),
+                                           (17, True, 2), (8, True, 3), (16, True, 3)])
+def test_verify_without_commit(gpu, T, use_ring, H):
     """The call shape of a speculative step (no recurrent commit): up to 16 tokens take the chunked
     matrix-core path, longer windows the token-by-token kernel; either way the outputs match the
-    oracle, the ring holds the raw inputs bit for bit and the committed state is untouched."""
-    seed, B, H, L, S = 41 + T, 3, 2, 2, 6
+    oracle, the ring holds the raw inputs bit for bit and the committed state is untouched. H = 3 makes
+    the number of (request, head) units odd."""
+    seed, B, L, S = 41 + T, 3, 2, 6
     R = 32 if T <= 16 else 64
-    log(f"verify without commit T={T} ring={use_ring}")
+    log(f"verify without commit T={T} ring={use_ring} H={H}")
     slot_idx, pool, ins, ring_start = make_verify_case(seed, B, T, H, L, S, R)
     slot_idx[1] = -1  # a request with no slot: skipped, its outputs stay as they were
     pool0 = pool.clone()
