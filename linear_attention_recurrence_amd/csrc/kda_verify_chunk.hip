@@ -173,18 +173,24 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     const int n = sload_i32(A.fold_len + b), nmax = A.ring_len >> 1;
     return n < 0 ? 0 : (n > nmax ? nmax : n);
   };
-  // the state slice of a unit (in the fold's ownership on the fused path)
-  auto prefetch_state = [&](size_t unit) {
+  // loads i0 .. i1 - 1 of the 16 that bring in the state slice of a unit (in the fold's ownership
+  // on the fused path). The next unit's slice is issued in three pieces, between the compute
+  // phases: all 16 at once fill the memory queue and stall the issuing wave until most of them
+  // have returned, with this unit's compute still to do.
+  auto prefetch_state = [&](size_t unit, int i0, int i1) {
     if constexpr (FOLD) {
       const float* sp = A.state_pool + unit * D * D + col0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sv[i] = *reinterpret_cast<const float4*>(sp + (size_t)(r0 + i) * D);
+      for (int i = 0; i < 16; ++i)
+        if (i >= i0 && i < i1) sv[i] = *reinterpret_cast<const float4*>(sp + (size_t)(r0 + i) * D);
     } else {
       const float* sp = A.state_pool + unit * D * D + 32 * wave + 4 * (lane & 7);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sv[i] = *reinterpret_cast<const float4*>(sp + (size_t)(8 * i + (lane >> 3)) * D);
+      for (int i = 0; i < 16; ++i)
+        if (i >= i0 && i < i1) sv[i] = *reinterpret_cast<const float4*>(sp + (size_t)(8 * i + (lane >> 3)) * D);
     }
   };
+  constexpr int kPiece1 = 4, kPiece2 = 10;  // loads issued after staging, after the decay factors, after A and P
   // the raw inputs of a unit (and the entries to fold on the fused path)
   auto prefetch_inputs = [&](int b, int h, size_t unit) {
     if constexpr (FOLD) {
@@ -212,9 +218,9 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     int b, h;
     size_t unit;
     unit_of(blockIdx.x, b, h, unit);
-    if constexpr (!FOLD) prefetch_state(unit);
+    if constexpr (!FOLD) prefetch_state(unit, 0, 16);
     prefetch_inputs(b, h, unit);
-    if constexpr (FOLD) prefetch_state(unit);
+    if constexpr (FOLD) prefetch_state(unit, 0, 16);
     // The same stores as the end of an iteration, into empty ranges (dropped): the loop is
     // then entered with the same pattern of outstanding memory operations from both sides,
     // and the compiler's wait for the prefetched registers need not drain the stores.
@@ -282,16 +288,16 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
       }
     }
     // the next unit streams in while this one computes (past the last unit: this one again,
-    // so that every iteration issues the same loads); the fused fold issues it after its fold,
-    // whose state shares the registers
+    // so that every iteration issues the same loads); the fused fold issues its state after the
+    // fold, whose state shares the registers
     int bn, hn;
     size_t unitn;
     {
       const int un = u + (int)gridDim.x;
       unit_of(un < n_units ? un : u, bn, hn, unitn);
     }
-    if constexpr (!FOLD) prefetch_state(unitn);
     prefetch_inputs(bn, hn, unitn);
+    if constexpr (!FOLD) prefetch_state(unitn, 0, kPiece1);
     const size_t row0 = (size_t)b * T * H + h;  // input row of token t: row0 + t * H
     __syncthreads();
     if constexpr (FOLD) {
@@ -309,7 +315,7 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
         const uint32_t lo = pack2(h16(S[i][0]), h16(S[i][1])), hi = pack2(h16(S[i][2]), h16(S[i][3]));
         *reinterpret_cast<uint2*>(&L.sh[wave][r0 + i][4 * (lane >> 3)]) = make_uint2(lo, hi);
       }
-      prefetch_state(unitn);
+      prefetch_state(unitn, 0, kPiece1);
       __syncthreads();
       // the fold's staging shares memory with the operand rows kt, qt, rk and rqh (FoldLds spans
       // 16.4 KB of them): their padding rows NT .. 15, which every MFMA tile reads, must be zero
@@ -351,6 +357,7 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
         L.ckh[t][c] = hi; L.ckl[t][c] = lo;
       }
     }
+    prefetch_state(unitn, kPiece1, kPiece2);
     __syncthreads();
 
     // ---- A, P and X = (I + A)^-1 (wave 0)
@@ -415,6 +422,7 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
         }
       }
     }
+    prefetch_state(unitn, kPiece2, 16);
     __syncthreads();  // X and P are complete
 
     // ---- R = diag(beta)(V - Kt S0), W = X R, O^T = scale (QT + W^T P^T)
