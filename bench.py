@@ -10,7 +10,9 @@ events on the launch stream. Beside it, in the same JSON line:
   layers x 8 heads, gamma + 1 = 8 bf16 draft tokens, ring length 16, accepted
   lengths geometric (mean 2.7, clipped to [1, 8])" = 69 kda_verify launches +
   one kda_replay_fold launch, in us/step (committed states restored from a
-  pristine copy outside the timed region before every step);
+  pristine copy outside the timed region before every step); beside it the
+  same step through kda_fold_verify, and the verify with trimmed windows
+  (1..8 tokens per request, packed) through kda_verify_ragged;
 * ``roofline``: HBM roofline of the prefill kernel (algorithmic bytes per
   launch / measured launch time, against 8 TB/s);
 * ``cpu_baseline``: the fp64 oracle (token-by-token) timed on this host's
@@ -184,17 +186,49 @@ def bench_verify_fold(args, torch, kda, sg, synth):
         torch.cuda.synchronize()
         fused_step(ftimes)
     fus = sum(ftimes) / len(ftimes)
+
+    # The verify with trimmed windows: request b keeps n_b of its 8 draft tokens (1..8), packed back to
+    # back; one kda_verify_ragged per layer. The committed pool is only read.
+    import numpy as np
+
+    win = synth.trimmed_windows(seed, B, T)
+    cu_r = np.concatenate([[0], np.cumsum(win)]).astype(np.int32)
+    tot_r = int(cu_r[-1])
+    del ins
+    ins_r = [sg.prefill_inputs(seed, tot_r, H, dev, sub=l) for l in range(Lyr)]
+    cu_d = torch.from_numpy(cu_r).to(dev)
+    o_r = torch.empty((tot_r, H, 128), device=dev)
+
+    def ragged_step(times):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for l in range(Lyr):
+            kda.kda_verify_ragged(*ins_r[l], cu_d, pool, slot_idx, o_r, layer=l, max_tok=T, ring=ring,
+                                  ring_start=ring_start)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        if times is not None:
+            times.append(ev[0].elapsed_time(ev[1]))
+
+    for _ in range(max(1, args.warmup // 2)):
+        ragged_step(None)
+    rtimes = []
+    for _ in range(args.vf_steps):
+        ragged_step(rtimes)
+    rag = sum(rtimes) / len(rtimes)
     units = S * Lyr * H
     acc_mean = float(acc.float().mean())
     v_bytes = units * (65536 + T * (768 + 512 + 4 + 512 + 1028))  # state + inputs + o + ring entries
     f_bytes = units * (2 * 65536) + int(round(float(acc.float().sum()) * Lyr * H * 1028))
     # fused: the state read once, written back, the folded entries read, the verify's inputs and outputs
     fv_bytes = units * (2 * 65536 + T * (768 + 512 + 4 + 512 + 1028)) + int(round(float(acc.float().sum()) * Lyr * H * 1028))
+    r_bytes = units * 65536 + tot_r * Lyr * H * (768 + 512 + 4 + 512 + 1028)
     res = dict(verify_ms=ver, fold_ms=fol, accept_mean=acc_mean,
                verify_gbs=v_bytes / (ver * 1e-3) / 1e9, fold_gbs=f_bytes / (fol * 1e-3) / 1e9,
                verify_bytes=v_bytes, fold_bytes=f_bytes, fused_ms=fus, fused_bytes=fv_bytes,
-               fused_gbs=fv_bytes / (fus * 1e-3) / 1e9)
-    del pool, pristine, ring, ins, o
+               fused_gbs=fv_bytes / (fus * 1e-3) / 1e9, ragged_ms=rag, ragged_bytes=r_bytes,
+               ragged_gbs=r_bytes / (rag * 1e-3) / 1e9, ragged_mean_window=float(win.mean()))
+    del pool, pristine, ring, ins_r, o, o_r
     return res
 
 
@@ -242,7 +276,8 @@ def main():
         vf = bench_verify_fold(args, torch, kda, sg, synth)
         print(json.dumps({"verify_us": vf["verify_ms"] * 1e3, "fold_us": vf["fold_ms"] * 1e3,
                           "verify_gbs": vf["verify_gbs"], "fold_gbs": vf["fold_gbs"],
-                          "fused_us": vf["fused_ms"] * 1e3, "fused_gbs": vf["fused_gbs"]}), flush=True)
+                          "fused_us": vf["fused_ms"] * 1e3, "fused_gbs": vf["fused_gbs"],
+                          "ragged_verify_us": vf["ragged_ms"] * 1e3, "ragged_gbs": vf["ragged_gbs"]}), flush=True)
         return
     log("prefill: generating inputs and timing")
     pf = bench_prefill(args, torch, kda, sg, synth)
@@ -300,6 +335,10 @@ def main():
             "fused_hbm_frac": vf["fused_gbs"] / HBM_PEAK_GBS,
             "fused_workload": "the same step as 69 kda_fold_verify launches (each folds the previous window of "
                               "its layer into the committed state, then verifies the next window from it)",
+            "ragged_verify_us_per_step": vf["ragged_ms"] * 1e3, "ragged_gbs": vf["ragged_gbs"],
+            "ragged_hbm_frac": vf["ragged_gbs"] / HBM_PEAK_GBS, "ragged_mean_window": vf["ragged_mean_window"],
+            "ragged_workload": "the verify of the same step with trimmed windows: request b keeps n_b of its 8 "
+                               "draft tokens (uniform on 1..8), packed back to back; 69 kda_verify_ragged launches",
         }
     print(json.dumps(line), flush=True)
 

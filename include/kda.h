@@ -33,7 +33,14 @@
  *      layer, with no device read-back.
  *  [B200-RING] same notes, section "DSPARK and KDA state" (decode-side
  *      choices): a small ring per slot holding (v, k, gate, beta); its length
- *      is a power of two and at least 2 * (gamma + 1).
+ *      is a power of two and at least 2 * (gamma + 1). The same list names
+ *      the two verify layouts: static (every request verifies all gamma + 1
+ *      tokens) and ragged (windows trimmed per request by confidence).
+ *  [LMSYS-SPEC] "SGLang and Miles Add Day-0 Support for Kimi K3", section
+ *      "Speculative decoding with DSpark": a per-step planner keeps each
+ *      request's verify tokens only while their expected value covers their
+ *      cost and trims the rest of the window before the target forward; the
+ *      tokens that remain are verified exactly as before.
  *
  * Conventions for every entry point:
  *  - Pointers to tensors are DEVICE pointers unless the name ends in _host.
@@ -63,7 +70,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 #define KDA_HEAD_DIM 128 /* K = V = 128, fixed at build time */
 #define KDA_CHUNK 32     /* prefill chunk length; snap_interval must be a multiple */
 
@@ -293,6 +300,40 @@ kda_status kda_fold_verify(int batch, int n_tok, int n_heads, int n_layers, int 
                            const kda_inputs* in, float* state_pool, const int32_t* slot_idx, float* o,
                            const kda_ring* ring, const int32_t* fold_start, const int32_t* fold_len,
                            const int32_t* ring_start, float scale, void* stream);
+
+/*
+ * Ragged verify of one layer [LMSYS-SPEC], [B200-RING]: request b verifies
+ * its own trimmed window of n_b draft tokens, packed back to back. Each
+ * window is verified exactly as kda_verify without a commit verifies a
+ * window of that length (o and the ring entries are bit-identical to a
+ * kda_verify call with n_tok = n_b for that request); the committed state is
+ * never written. A later kda_replay_fold may fold up to n_b of the recorded
+ * entries.
+ *
+ *  batch          : requests (>= 0).
+ *  max_tok        : 1..16, a bound on every n_b (windows longer are cut).
+ *  total_tok      : rows of the packed tensors (>= 0; 0 = nothing to do).
+ *  n_heads .. n_slots, state_pool, slot_idx : as kda_verify.
+ *  in             : bf16 q/k/v, fp32 gk/beta; row cu_tok[b] + t of
+ *                   [total_tok, H, 128] is token t of request b.
+ *  cu_tok         : int32 [batch + 1], required: the windows' prefix sums,
+ *                   cu_tok[0] = 0, nondecreasing, cu_tok[batch] = total_tok.
+ *                   Read on the device and clamped there: the window of b
+ *                   is rows [s, e) with s = cu_tok[b] and e = cu_tok[b + 1]
+ *                   clamped into [0, total_tok] and e >= s, cut to max_tok
+ *                   rows; so no value of cu_tok addresses a row outside the
+ *                   tensors. An empty window writes nothing.
+ *  o              : fp32 [total_tok, H, 128]; rows of a skipped request
+ *                   (invalid slot) are not written.
+ *  ring, ring_start : as kda_verify; ring->len >= 2 * max_tok. Entry t < n_b
+ *                   of request b goes to (ring_start[b] + t) & (len - 1);
+ *                   the other entries of the ring are not touched.
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_DEVICE.
+ */
+kda_status kda_verify_ragged(int batch, int max_tok, int total_tok, int n_heads, int n_layers, int layer,
+                             int n_slots, const kda_inputs* in, const int32_t* cu_tok,
+                             const float* state_pool, const int32_t* slot_idx, float* o,
+                             const kda_ring* ring, const int32_t* ring_start, float scale, void* stream);
 
 #ifdef __cplusplus
 }

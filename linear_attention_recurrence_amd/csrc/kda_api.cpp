@@ -376,6 +376,83 @@ kda_status kda_verify(int batch, int n_tok, int n_heads, int n_layers, int layer
   return ok();
 }
 
+kda_status kda_verify_ragged(int batch, int max_tok, int total_tok, int n_heads, int n_layers, int layer, int n_slots,
+                             const kda_inputs* in, const int32_t* cu_tok, const float* state_pool,
+                             const int32_t* slot_idx, float* o, const kda_ring* ring, const int32_t* ring_start,
+                             float scale, void* stream) {
+  if (batch < 0 || max_tok < 1 || max_tok > 16 || total_tok < 0 || n_heads < 1 || n_layers < 1 || n_slots < 1 ||
+      layer < 0 || layer >= n_layers)
+    return fail(KDA_ERR_INVALID_ARG, "kda_verify_ragged: bad batch/max_tok/total_tok/n_heads/n_layers/layer/n_slots");
+  if ((int64_t)batch * n_heads > 0x7fffffffLL || (int64_t)total_tok * n_heads * KDA_HEAD_DIM * 4 > 0x7fffffffLL)
+    return fail(KDA_ERR_INVALID_ARG, "kda_verify_ragged: too large");
+  if (!cu_tok) return fail(KDA_ERR_INVALID_ARG, "kda_verify_ragged: cu_tok is required");
+  if (batch == 0 || total_tok == 0) return ok();
+  if (!in || !in->q || !in->k || !in->v || !in->gk || !in->beta)
+    return fail(KDA_ERR_INVALID_ARG, "kda_verify_ragged: q, k, v, gk and beta are required");
+  if (!state_pool || !slot_idx || !o)
+    return fail(KDA_ERR_INVALID_ARG, "kda_verify_ragged: state_pool, slot_idx and o are required");
+  if (ring) {
+    if (!ring->k || !ring->v || !ring->gk || !ring->beta)
+      return fail(KDA_ERR_INVALID_ARG, "kda_verify_ragged: ring buffers are NULL");
+    if (!pow2(ring->len) || ring->len < 2 * max_tok)
+      return fail(KDA_ERR_INVALID_ARG, "kda_verify_ragged: ring length must be a power of two >= 2 * max_tok");
+  }
+  const size_t rows = (size_t)total_tok * n_heads;
+  const size_t pool_b = (size_t)n_slots * n_layers * n_heads * kState;
+  const size_t o_b = rows * KDA_HEAD_DIM * 4;
+  const size_t ring_units = (size_t)n_slots * n_layers * n_heads * (ring ? ring->len : 0);
+  const void* bufs[] = {in->q, in->k, in->v, in->gk, in->beta, state_pool, cu_tok};
+  const size_t bsz[] = {rows * KDA_HEAD_DIM * 2, rows * KDA_HEAD_DIM * 2, rows * KDA_HEAD_DIM * 2,
+                        rows * KDA_HEAD_DIM * 4, rows * 4, pool_b, ((size_t)batch + 1) * 4};
+  for (int i = 0; i < 7; ++i) {
+    if (overlap(o, o_b, bufs[i], bsz[i])) return fail(KDA_ERR_INVALID_ARG, "kda_verify_ragged: o overlaps an input");
+    if (ring) {
+      const void* rb[] = {ring->k, ring->v, ring->gk, ring->beta};
+      const size_t rs[] = {ring_units * KDA_HEAD_DIM * 2, ring_units * KDA_HEAD_DIM * 2, ring_units * KDA_HEAD_DIM * 4,
+                           ring_units * 4};
+      for (int j = 0; j < 4; ++j)
+        if (overlap(rb[j], rs[j], bufs[i], bsz[i]))
+          return fail(KDA_ERR_INVALID_ARG, "kda_verify_ragged: ring overlaps an input");
+    }
+  }
+  if (ring) {
+    const void* rb[] = {ring->k, ring->v, ring->gk, ring->beta};
+    const size_t rs[] = {ring_units * KDA_HEAD_DIM * 2, ring_units * KDA_HEAD_DIM * 2, ring_units * KDA_HEAD_DIM * 4,
+                         ring_units * 4};
+    for (int j = 0; j < 4; ++j)
+      if (overlap(rb[j], rs[j], o, o_b)) return fail(KDA_ERR_INVALID_ARG, "kda_verify_ragged: the ring overlaps o");
+  }
+  kda::VerifyArgs a{};
+  a.batch = batch;
+  a.n_tok = max_tok;
+  a.n_heads = n_heads;
+  a.n_layers = n_layers;
+  a.layer = layer;
+  a.n_slots = n_slots;
+  a.q = in->q;
+  a.k = in->k;
+  a.v = in->v;
+  a.gk = in->gk;
+  a.beta = in->beta;
+  a.state_pool = state_pool;
+  a.slot_idx = slot_idx;
+  a.o = o;
+  if (ring) {
+    a.ring_k = ring->k;
+    a.ring_v = ring->v;
+    a.ring_gk = ring->gk;
+    a.ring_beta = ring->beta;
+    a.ring_len = ring->len;
+  }
+  a.ring_start = ring_start;
+  a.scale = scale;
+  a.cu_tok = cu_tok;
+  a.total_tok = total_tok;
+  const hipError_t e = kda::launch_verify_chunk(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail("kda_verify_ragged: launch", e);
+  return ok();
+}
+
 kda_status kda_replay_fold(int batch, int n_heads, int n_layers, int n_slots, float* state_pool, const int32_t* slot_idx,
                            const kda_ring* ring, const int32_t* ring_start, const int32_t* accepted_len, void* stream) {
   if (batch < 0 || n_heads < 1 || n_layers < 1 || n_slots < 1)

@@ -30,6 +30,10 @@ struct VerifyArgs {
   const int32_t* fold_len;
   const int32_t* fold_start;  // nullptr: 0
   float* fold_pool;
+  // ragged windows (nullptr cu_tok: every request has n_tok tokens at rows b * n_tok + t): request
+  // b's window is rows [cu_tok[b], cu_tok[b + 1]) of total_tok, clamped, at most n_tok long
+  const int32_t* cu_tok;
+  int total_tok;
 };
 
 struct FoldArgs {

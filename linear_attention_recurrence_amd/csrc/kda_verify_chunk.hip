@@ -115,18 +115,20 @@ __device__ __forceinline__ void split_h4(const f32x4& a, f16x4& hi, f16x4& lo, f
 
 // Persistent: each workgroup walks units u = blockIdx.x, + gridDim.x, ...; the
 // next unit's committed state and raw inputs are loaded into registers while
-// the current one computes. NT is the padded window (8 or 16 tokens). Every
+// the current one computes. NT is the padded window (8 or 16 tokens); with
+// RAGGED each request has its own window (rows cu_tok[b] .. cu_tok[b + 1] - 1,
+// clamped), otherwise every request has n_tok tokens at rows b n_tok + t. Every
 // global store of a unit is unconditional (the outputs of padded tokens are
 // dropped by the buffer range check), so the compiler's wait before the next
 // unit's first use of its prefetched registers leaves the stores in flight.
-template <bool RING, int NT, bool FOLD>
+template <bool RING, int NT, bool FOLD, bool RAGGED>
 __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
   __shared__ VerifyLds<NT> L;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, lr = lane & 15;
   const int H = A.n_heads;
-  const int T = A.n_tok;  // 1 .. NT
+  const int T = A.n_tok;  // 1 .. NT (with RAGGED: the bound on every window)
   const int n_units = A.batch * H;
   constexpr int NH = NT / 2;              // tokens per input thread
   const int c = tid & (D - 1);            // input thread: channel c ...
@@ -191,6 +193,20 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     }
   };
   constexpr int kPiece1 = 4, kPiece2 = 10;  // loads issued after staging, after the decay factors, after A and P
+  // the window of request b: its first input row and its length tn <= T. Ragged bounds are
+  // clamped into [0, total_tok] (the host passes total_tok >= 1), so a row index never leaves
+  // the tensors whatever cu_tok holds
+  auto window = [&](int b, size_t& first, int& tn) {
+    if constexpr (RAGGED) {
+      const int s = min(max(sload_i32(A.cu_tok + b), 0), A.total_tok);
+      const int e = min(max(sload_i32(A.cu_tok + b + 1), s), A.total_tok);
+      first = (size_t)s;
+      tn = min(e - s, T);
+    } else {
+      first = (size_t)b * T;
+      tn = T;
+    }
+  };
   // the raw inputs of a unit (and the entries to fold on the fused path)
   auto prefetch_inputs = [&](int b, int h, size_t unit) {
     if constexpr (FOLD) {
@@ -203,10 +219,14 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
       fg = *reinterpret_cast<const float4*>(A.ring_gk + re);
       fb = A.ring_beta[unit * A.ring_len + pos];
     }
-    const size_t row0 = (size_t)b * T * H + h;
+    size_t first;
+    int tn;
+    window(b, first, tn);
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
-      const size_t r = row0 + (size_t)min(ti + 8 * n, T - 1) * H;
+      // tokens past the window re-read its last row (an empty window: a row that exists)
+      const size_t tr = first + (size_t)min(ti + 8 * n, max(tn - 1, 0));
+      const size_t r = (RAGGED ? min(tr, (size_t)A.total_tok - 1) : tr) * H + h;
       pk[n] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.k) + r * D + c4);
       pq[n] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.q) + r * D + c4);
       pv[n] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.v) + r * D + c4);
@@ -262,9 +282,12 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     // raw inputs: staging rows, v and beta for the chain, and the ring (bit copies; tokens past
     // the window rewrite the last entry with the same bits)
     const int rstart = (RING && A.ring_start) ? sload_i32(A.ring_start + b) : 0;
-    __amdgpu_buffer_rsrc_t rk_rs, rv_rs, rg_rs, rb_rs;  // this unit's ring rows (empty without a slot)
+    size_t first;  // this request's window: input rows first .. first + tn - 1
+    int tn;
+    window(b, first, tn);
+    __amdgpu_buffer_rsrc_t rk_rs, rv_rs, rg_rs, rb_rs;  // this unit's ring rows (empty without a slot or a window)
     if constexpr (RING) {
-      const int nrow = ok ? A.ring_len : 0;
+      const int nrow = (ok && tn > 0) ? A.ring_len : 0;
       rk_rs = __builtin_amdgcn_make_buffer_rsrc(static_cast<uint16_t*>(A.ring_k) + unit * A.ring_len * D, 0, nrow * D * 2, kBufWord3);
       rv_rs = __builtin_amdgcn_make_buffer_rsrc(static_cast<uint16_t*>(A.ring_v) + unit * A.ring_len * D, 0, nrow * D * 2, kBufWord3);
       rg_rs = __builtin_amdgcn_make_buffer_rsrc(A.ring_gk + unit * A.ring_len * D, 0, nrow * D * 4, kBufWord3);
@@ -273,14 +296,14 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
       const int t = ti + 8 * n;
-      const bool ok_t = t < T;
+      const bool ok_t = t < tn;
       *reinterpret_cast<uint2*>(&L.kin[t][c4]) = pk[n];
       *reinterpret_cast<uint2*>(&L.qin[t][c4]) = pq[n];
       *reinterpret_cast<float4*>(&L.gin[t][c4]) = pg[n];
       *reinterpret_cast<uint2*>(&L.v[t][c4]) = ok_t ? pv[n] : make_uint2(0u, 0u);
       if (c4 == 0) L.beta[t] = ok_t ? pb[n] : 0.f;
       if constexpr (RING) {
-        const int pos = (rstart + min(t, T - 1)) & (A.ring_len - 1);
+        const int pos = (rstart + min(t, tn - 1)) & (A.ring_len - 1);
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pk[n]), rk_rs, 2 * (pos * D + c4), 0, kStream);
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pv[n]), rv_rs, 2 * (pos * D + c4), 0, kStream);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pg[n]), rg_rs, 4 * (pos * D + c4), 0, kStream);
@@ -298,7 +321,7 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     }
     prefetch_inputs(bn, hn, unitn);
     if constexpr (!FOLD) prefetch_state(unitn, 0, kPiece1);
-    const size_t row0 = (size_t)b * T * H + h;  // input row of token t: row0 + t * H
+    const size_t row0 = first * H + h;  // input row of token t: row0 + t * H
     __syncthreads();
     if constexpr (FOLD) {
       // the previous window's accepted entries, replayed exactly as the fold does, then the
@@ -337,12 +360,12 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
       float gs = 0.f;
       if (t0) {
 #pragma unroll
-        for (int j = 0; j < NH; ++j) gs += (j < T) ? L.gin[j][c] : 0.f;
+        for (int j = 0; j < NH; ++j) gs += (j < tn) ? L.gin[j][c] : 0.f;
       }
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
         const int t = t0 + j;
-        const bool ok_t = t < T;
+        const bool ok_t = t < tn;
         const float kv = bf2f(L.kin[t][c]), qv = bf2f(L.qin[t][c]);
         gs += ok_t ? L.gin[t][c] : 0.f;
         const float e = __expf(gs), ie = __expf(-gs);
@@ -427,7 +450,7 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
 
     // ---- R = diag(beta)(V - Kt S0), W = X R, O^T = scale (QT + W^T P^T)
     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-        A.o + row0 * D, 0, ok ? (int)((((uint32_t)T - 1) * H + 1) * D * 4) : 0, kBufWord3);
+        A.o + row0 * D, 0, (ok && tn > 0) ? (int)((((uint32_t)tn - 1) * H + 1) * D * 4) : 0, kBufWord3);
     const f16x4 xa = __builtin_bit_cast(f16x4, lds8(&L.xh[lr][4 * g]));
     const f16x4 pa = __builtin_bit_cast(f16x4, lds8(&L.ph[lr][4 * g]));
     const float4 b4 = *reinterpret_cast<const float4*>(&L.beta[4 * g]);
@@ -465,7 +488,7 @@ hipError_t launch_fold_verify(const VerifyArgs& a, hipStream_t stream) {
   const long units = (long)a.batch * a.n_heads;
   const long slots = 2L * prefill_max_grid(dev);  // two resident workgroups per CU
   const dim3 grid((unsigned)(units < slots ? units : slots)), block(256);
-  hipLaunchKernelGGL((verify_chunk_kernel<true, 8, true>), grid, block, 0, stream, a);
+  hipLaunchKernelGGL((verify_chunk_kernel<true, 8, true, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -477,12 +500,20 @@ hipError_t launch_verify_chunk(const VerifyArgs& a, hipStream_t stream) {
   const long slots = per_cu * prefill_max_grid(dev);
   const dim3 grid((unsigned)(units < slots ? units : slots)), block(256);
   const bool ring = a.ring_k != nullptr;
-  if (a.n_tok <= 8) {
-    if (ring) hipLaunchKernelGGL((verify_chunk_kernel<true, 8, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((verify_chunk_kernel<false, 8, false>), grid, block, 0, stream, a);
+  if (a.cu_tok) {
+    if (a.n_tok <= 8) {
+      if (ring) hipLaunchKernelGGL((verify_chunk_kernel<true, 8, false, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((verify_chunk_kernel<false, 8, false, true>), grid, block, 0, stream, a);
+    } else {
+      if (ring) hipLaunchKernelGGL((verify_chunk_kernel<true, 16, false, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((verify_chunk_kernel<false, 16, false, true>), grid, block, 0, stream, a);
+    }
+  } else if (a.n_tok <= 8) {
+    if (ring) hipLaunchKernelGGL((verify_chunk_kernel<true, 8, false, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((verify_chunk_kernel<false, 8, false, false>), grid, block, 0, stream, a);
   } else {
-    if (ring) hipLaunchKernelGGL((verify_chunk_kernel<true, 16, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((verify_chunk_kernel<false, 16, false>), grid, block, 0, stream, a);
+    if (ring) hipLaunchKernelGGL((verify_chunk_kernel<true, 16, false, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((verify_chunk_kernel<false, 16, false, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -31,7 +31,7 @@ KDA_CHUNK = 32
 
 EXPORTS = ("kda_abi_version", "kda_last_error", "kda_plan_create", "kda_plan_create_ex", "kda_plan_v_blocks",
            "kda_plan_workspace_bytes", "kda_plan_num_items", "kda_plan_items", "kda_plan_upload", "kda_plan_destroy",
-           "kda_chunk_prefill", "kda_verify", "kda_replay_fold", "kda_fold_verify")
+           "kda_chunk_prefill", "kda_verify", "kda_replay_fold", "kda_fold_verify", "kda_verify_ragged")
 
 
 class KdaError(RuntimeError):
@@ -81,8 +81,10 @@ def lib():
         L.kda_replay_fold.argtypes = [i32, i32, i32, i32, vp, vp, ctypes.POINTER(_Ring), vp, vp, vp]
         L.kda_fold_verify.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(_Inputs), vp, vp, vp,
                                       ctypes.POINTER(_Ring), vp, vp, vp, f32, vp]
+        L.kda_verify_ragged.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(_Inputs), vp, vp, vp, vp,
+                                        ctypes.POINTER(_Ring), vp, f32, vp]
         for f in ("kda_plan_create", "kda_plan_create_ex", "kda_plan_items", "kda_plan_upload", "kda_chunk_prefill",
-                  "kda_verify", "kda_replay_fold", "kda_fold_verify"):
+                  "kda_verify", "kda_replay_fold", "kda_fold_verify", "kda_verify_ragged"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -273,6 +275,32 @@ def kda_fold_verify(q, k, v, gk, beta, state_pool, slot_idx, o, layer, n_tok, ri
     _check(lib().kda_fold_verify(B, n_tok, H, L, layer, S, ctypes.byref(ins), _ptr(state_pool), _ptr(slot_idx),
                                  _ptr(o), ctypes.byref(ring.c()), _ptr(fold_start), _ptr(fold_len), _ptr(ring_start),
                                  float(scale), _stream(stream)))
+
+
+def kda_verify_ragged(q, k, v, gk, beta, cu_tok, state_pool, slot_idx, o, layer, max_tok, ring=None, ring_start=None,
+                      scale=1.0, stream=None):
+    """Verify each request's own trimmed window of draft tokens for one layer; the windows are packed
+    back to back, request b's at rows cu_tok[b] .. cu_tok[b + 1] - 1 (see kda_verify_ragged in
+    include/kda.h). cu_tok is a device int32 tensor of batch + 1 prefix sums."""
+    S, L, H, Dh = state_pool.shape[0], state_pool.shape[1], state_pool.shape[2], KDA_HEAD_DIM
+    B = slot_idx.shape[0]
+    total = q.shape[0]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (total, H, Dh), _BF)
+    _need(gk, "gk", (total, H, Dh), _F32)
+    _need(beta, "beta", (total, H), _F32)
+    _need(cu_tok, "cu_tok", (B + 1,), _I32)
+    _need(state_pool, "state_pool", (S, L, H, Dh, Dh), _F32)
+    _need(slot_idx, "slot_idx", (B,), _I32)
+    _need(o, "o", (total, H, Dh), _F32)
+    _need(ring_start, "ring_start", (B,), _I32, allow_none=True)
+    rc = None
+    if ring is not None:
+        ring.check(S, L, H)
+        rc = ctypes.byref(ring.c())
+    ins = _Inputs(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(), beta.data_ptr())
+    _check(lib().kda_verify_ragged(B, max_tok, total, H, L, layer, S, ctypes.byref(ins), _ptr(cu_tok), _ptr(state_pool),
+                                   _ptr(slot_idx), _ptr(o), rc, _ptr(ring_start), float(scale), _stream(stream)))
 
 
 def kda_replay_fold(state_pool, slot_idx, ring, accepted_len, ring_start=None, stream=None):

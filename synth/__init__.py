@@ -36,6 +36,7 @@ _NP = {F64: np.float64, F32: np.float32, BF16: np.uint16}
 
 # tensor ids
 T_Q, T_K, T_V, T_GK, T_BETA, T_STATE, T_LENS, T_ACCEPT = 1, 2, 3, 4, 5, 6, 7, 8
+T_WINDOW = 9
 T_DEC_Q, T_DEC_K, T_DEC_V, T_DEC_GK, T_DEC_BETA = 11, 12, 13, 14, 15
 
 D = 128  # K = V = 128
@@ -126,6 +127,13 @@ def geometric_accept(seed, n, mean=2.7, cap=8):
     u = uniform(seed, T_ACCEPT, 0, n)
     g = 1 + np.floor(np.log(u) / math.log(1.0 - p))
     return np.minimum(cap, g).astype(np.int64)
+
+
+def trimmed_windows(seed, n, cap=8):
+    """Verify windows kept by a per-request trimming planner: uniform on {1, ..., cap}. The pages give
+    no distribution for the trimmed lengths; this spreads the windows over the whole range."""
+    u = uniform(seed, T_WINDOW, 0, n)
+    return np.minimum(cap, 1 + np.floor(u * cap)).astype(np.int64)
 
 
 PREFILL_CONFIGS = {

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), f"libkda.so does not export {n}"
     assert set(names) == set(K.EXPORTS)
-    assert kda.kda_abi_version() == 2
+    assert kda.kda_abi_version() == 3
 
 
 def test_plan_lpt_order_and_ties():
@@ -192,6 +192,32 @@ def test_fold_verify_rejects_bad_arguments():
     assert call(o_=ctypes.c_void_p(0x20000000)) == 1  # o overlaps the state pool
     assert call(pool_=ctypes.c_void_p(0xC000000)) == 1  # the pool overlaps the ring
     assert call(B=0) == 0                           # nothing to do
+
+
+def test_verify_ragged_rejects_bad_arguments():
+    L = kda.lib()
+    ins = _inputs()
+    pool, slots, o = ctypes.c_void_p(0x20000000), ctypes.c_void_p(0x30000000), ctypes.c_void_p(0x40000000)
+    cu = ctypes.c_void_p(0x31000000)
+
+    def call(B=2, max_tok=8, total=10, H=2, Lyr=3, layer=0, S=4, ring=_ring(16), cu_=cu, o_=o):
+        r = ctypes.byref(ring) if ring is not None else None
+        return L.kda_verify_ragged(B, max_tok, total, H, Lyr, layer, S, ctypes.byref(ins), cu_, pool, slots, o_, r,
+                                   None, 1.0, None)
+
+    assert call(max_tok=0) == 1
+    assert call(max_tok=17, ring=_ring(64)) == 1    # windows of at most 16 tokens
+    assert call(total=-1) == 1
+    assert call(B=-1) == 1
+    assert call(layer=3) == 1
+    assert call(cu_=None) == 1                      # the window bounds are required
+    assert call(ring=_ring(12)) == 1                # not a power of two
+    assert call(max_tok=16, ring=_ring(16)) == 1    # < 2 * max_tok
+    assert call(o_=ctypes.c_void_p(0x20000000)) == 1  # o overlaps the state pool
+    assert call(o_=ctypes.c_void_p(0x31000000)) == 1  # o overlaps cu_tok
+    assert call(o_=ctypes.c_void_p(0xC000000)) == 1   # o overlaps the ring
+    assert call(B=0) == 0                           # nothing to do
+    assert call(total=0) == 0                       # every window is empty
 
 
 def test_binding_checks_shapes_without_device():

@@ -121,6 +121,71 @@ def test_prefill_varlen_h96_snapshots(gpu):
     assert max(worst.values()) <= TOL
 
 
+def test_ragged_verify_256x69x8(gpu):
+    """The speculative-step shape with trimmed windows (1..8 tokens per request, packed back to back):
+    every layer through kda_verify_ragged; the ring holds each window's raw inputs bit for bit and its
+    positions past the window are untouched; the committed pool is not written; 48 sampled units
+    against the oracle."""
+    c = synth.VERIFY_CONFIG
+    seed, B, Lyr, H, T, R = c["seed"], c["B"], c["L"], c["H"], c["T"], c["R"]
+    S = B
+    win = synth.trimmed_windows(seed, B, T)
+    cu = np.concatenate([[0], np.cumsum(win)]).astype(np.int32)
+    total = int(cu[-1])
+    log(f"ragged spec step: {total} tokens over {B} requests (mean window {win.mean():.2f})")
+    pool = sg.states(seed, S * Lyr * H, DEV).view(S, Lyr, H, 128, 128)
+    slot_idx = torch.arange(B, dtype=torch.int32, device=DEV)
+    ring_start = torch.zeros(B, dtype=torch.int32, device=DEV)
+    ring = kda.Ring.empty(S, Lyr, H, R, DEV)
+
+    def ibits(t):
+        return t.view(torch.int16 if t.element_size() == 2 else torch.int32)
+
+    for t in (ring.k, ring.v, ring.gk, ring.beta):
+        ibits(t).fill_(-7)
+    cu_d = torch.from_numpy(cu).to(DEV)
+    # entry t < n_b of request b is packed row cu[b] + t (past the window: a valid row, masked below)
+    t_idx = torch.arange(T)
+    n_b = torch.from_numpy(win)
+    valid = (t_idx[None, :] < n_b[:, None]).to(DEV)
+    rows = (torch.from_numpy(cu[:-1]).long()[:, None] + torch.minimum(t_idx[None, :], n_b[:, None] - 1)).to(DEV)
+    rng = np.random.default_rng(5)
+    samples = sorted({(int(rng.integers(B)), int(rng.integers(Lyr)), int(rng.integers(H))) for _ in range(48)})
+    o_s = {}
+    for l in range(Lyr):
+        ins = sg.prefill_inputs(seed, total, H, DEV, sub=l)
+        o = torch.empty((total, H, 128), device=DEV)
+        kda.kda_verify_ragged(*ins, cu_d, pool, slot_idx, o, layer=l, max_tok=T, ring=ring, ring_start=ring_start)
+        for src, rt in ((ins[1], ring.k), (ins[2], ring.v), (ins[3], ring.gk)):
+            want = ibits(src)[rows].permute(0, 2, 1, 3)  # [B, H, T, 128]
+            got = ibits(rt[:, l, :, :T])
+            m = valid[:, None, :, None]
+            assert torch.equal(torch.where(m, got, 0), torch.where(m, want, 0)), f"ring entries differ at layer {l}"
+            assert bool(torch.all(torch.where(m, -7, got) == -7)), f"ring written past a window at layer {l}"
+        want = ibits(ins[4])[rows].permute(0, 2, 1)
+        got = ibits(ring.beta[:, l, :, :T])
+        assert torch.equal(torch.where(valid[:, None, :], got, 0), torch.where(valid[:, None, :], want, 0))
+        assert bool(torch.all(torch.where(valid[:, None, :], -7, got) == -7))
+        for (b, ll, h) in samples:
+            if ll == l:
+                o_s[(b, ll, h)] = np_(o[int(cu[b]):int(cu[b + 1]), h])
+    torch.cuda.synchronize()
+    fresh = sg.states(seed, S * Lyr * H, DEV).view(S, Lyr, H, 128, 128)
+    assert torch.equal(pool, fresh), "verify wrote the committed state"
+    del fresh
+
+    def run(u):
+        b, l, h = u
+        q, k, v, gk, beta = synth.prefill_rows(seed, H, int(cu[b]), int(win[b]), h=h, sub=l)
+        S0 = synth.state_rows(seed, (b * Lyr + l) * H + h, 1)[0]
+        o_ref, _, _ = oracle.verify(q, k, v, gk, beta, S0)
+        return block_err(o_s[u], o_ref)
+
+    worst = max(oracle.run_parallel(run, samples, threads=threads()))
+    log(f"ragged spec step worst {worst:.2e}")
+    assert worst <= TOL
+
+
 def test_spec_step_256x69x8(gpu):
     c = synth.VERIFY_CONFIG
     seed, B, Lyr, H, T, R = c["seed"], c["B"], c["L"], c["H"], c["T"], c["R"]

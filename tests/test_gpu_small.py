@@ -228,6 +228,148 @@ def test_verify_without_commit(gpu, T, use_ring, H):
     assert worst <= TOL
 
 
+def ragged_windows(cu, total, max_tok):
+    """The windows kda_verify_ragged reads from cu_tok (clamped as include/kda.h states): (first row, length)."""
+    out = []
+    for b in range(len(cu) - 1):
+        s0 = min(max(int(cu[b]), 0), total)
+        e = min(max(int(cu[b + 1]), s0), total)
+        out.append((s0, min(e - s0, max_tok)))
+    return out
+
+
+def check_ragged(seed, l, cu, total, max_tok, H, slot_idx, pool0, o, ring, ring0, ring_start, R, scale):
+    """o against the oracle on every window, the ring entries bit for bit, and everything outside the
+    windows untouched (o rows not in any window, ring positions not written)."""
+    worst = 0.0
+    on = np_(o)
+    covered = np.zeros(total, dtype=bool)
+    written = {}
+    for b, (first, n) in enumerate(ragged_windows(cu, total, max_tok)):
+        s = int(slot_idx[b])
+        if n == 0 or s < 0:
+            continue
+        covered[first:first + n] = True
+        for h in range(H):
+            q_, k_, v_, gk_, beta_ = synth.prefill_rows(seed, H, first, n, h=h, sub=l)
+            o_ref, _, _ = oracle.verify(q_, k_, v_, gk_, beta_, np_(pool0[s, l, h]), scale=scale)
+            worst = max(worst, block_err(on[first:first + n, h], o_ref))
+            pos = [(int(ring_start[b]) + t) & (R - 1) for t in range(n)]
+            written.setdefault((s, h), set()).update(pos)
+            assert np.array_equal(bits(ring.k[s, l, h, pos]).view(np.uint16), k_)
+            assert np.array_equal(bits(ring.v[s, l, h, pos]).view(np.uint16), v_)
+            assert np.array_equal(np_(ring.gk[s, l, h, pos]), gk_)
+            assert np.array_equal(np_(ring.beta[s, l, h, pos]), beta_)
+    assert np.all(on[~covered] == -9.0), "rows outside every window were written"
+    for t_new, t_old in ((ring.k, ring0.k), (ring.v, ring0.v), (ring.gk, ring0.gk), (ring.beta, ring0.beta)):
+        a, b_ = bits(t_new[:, l]), bits(t_old[:, l])
+        for (s, h), pos in written.items():
+            pos = sorted(pos)
+            a[s, h, pos] = b_[s, h, pos]
+        assert np.array_equal(a, b_), "ring entries outside the windows changed"
+    return worst
+
+
+@pytest.mark.parametrize("max_tok,lens", [(8, [3, 0, 8, 1, 5, 7, 2]), (16, [16, 9, 0, 2, 13, 8, 1]),
+                                          (8, [8, 8, 8, 8, 8, 8, 8])])
+def test_verify_ragged(gpu, max_tok, lens):
+    """Per-request trimmed windows packed back to back: o against the oracle on each window, the ring
+    entries bit for bit and nothing else written (empty windows, an invalid slot); o and ring bitwise
+    equal to one kda_verify call per request with n_tok = n_b where both take the same padded window;
+    all windows full equals a plain kda_verify call bit for bit; the committed state untouched."""
+    seed, H, L, S, R = 77 + max_tok + sum(lens), 3, 2, 10, 32
+    B = len(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total = int(cu[-1])
+    g = torch.Generator().manual_seed(seed)
+    slot_idx = torch.randperm(S, generator=g)[:B].to(torch.int32)
+    slot_idx[3] = -1
+    pool = sg.states(seed, S * L * H, DEV).view(S, L, H, 128, 128)
+    pool0 = pool.clone()
+    ring_start = torch.randint(0, 4 * R, (B,), generator=g, dtype=torch.int32)
+    ring = kda.Ring.empty(S, L, H, R, DEV)
+    for t in (ring.k, ring.v, ring.gk, ring.beta):
+        t.view(torch.int16 if t.element_size() == 2 else torch.int32).fill_(-7)
+    ring0 = kda.Ring(ring.k.clone(), ring.v.clone(), ring.gk.clone(), ring.beta.clone())
+    ref_ring = kda.Ring(ring.k.clone(), ring.v.clone(), ring.gk.clone(), ring.beta.clone())
+    cu_d, slot_d, rs_d = torch.from_numpy(cu).to(DEV), slot_idx.to(DEV), ring_start.to(DEV)
+    worst = 0.0
+    log(f"ragged verify max_tok={max_tok} lens={lens}")
+    for l in range(L):
+        ins = sg.prefill_inputs(seed, total, H, DEV, sub=l)
+        o = torch.full((total, H, 128), -9.0, device=DEV)
+        kda.kda_verify_ragged(*ins, cu_d, pool, slot_d, o, layer=l, max_tok=max_tok, ring=ring, ring_start=rs_d,
+                              scale=0.6)
+        # the same windows one request at a time through kda_verify
+        ref_o = torch.full((total, H, 128), -9.0, device=DEV)
+        for b, n in enumerate(lens):
+            if n == 0:
+                continue
+            r0, r1 = int(cu[b]), int(cu[b + 1])
+            kda.kda_verify(*(x[r0:r1] for x in ins), pool, slot_d[b:b + 1], ref_o[r0:r1], layer=l, n_tok=n,
+                           ring=ref_ring, ring_start=rs_d[b:b + 1], scale=0.6)
+        if all(n == max_tok for n in lens):
+            full_o = torch.full((total, H, 128), -9.0, device=DEV)
+            kda.kda_verify(*ins, pool, slot_d, full_o, layer=l, n_tok=max_tok, scale=0.6)
+        torch.cuda.synchronize()
+        worst = max(worst, check_ragged(seed, l, cu, total, max_tok, H, slot_idx, pool0, o, ring, ring0, ring_start,
+                                        R, 0.6))
+        for b, n in enumerate(lens):
+            if n and (n > 8) == (max_tok > 8):  # the same padded window (8 or 16 tokens) on both paths
+                r0, r1 = int(cu[b]), int(cu[b + 1])
+                assert torch.equal(o[r0:r1], ref_o[r0:r1])
+        if all(n == max_tok for n in lens):
+            assert torch.equal(o, full_o)
+    for a, b_ in ((ring.k, ref_ring.k), (ring.v, ref_ring.v), (ring.gk, ref_ring.gk), (ring.beta, ref_ring.beta)):
+        assert np.array_equal(bits(a), bits(b_))  # bit patterns: the sentinel fill is a NaN in fp32
+    assert torch.equal(pool, pool0), "verify wrote the committed state"
+    log(f"ragged verify worst err {worst:.2e}")
+    assert worst <= TOL
+
+
+def test_verify_ragged_clamps_bounds(gpu):
+    """Window bounds outside [0, total_tok], a decreasing step and a window longer than max_tok read as
+    include/kda.h states (clamped, empty, cut): the outputs follow those windows and rows outside them
+    are not written."""
+    seed, H, L, S, R, max_tok = 91, 2, 1, 6, 16, 8
+    cu = np.array([-4, 5, 3, 19, 40], dtype=np.int32)  # windows [0,5), empty, [3,11) cut from 16 rows, [19,20)
+    total = 20
+    B = len(cu) - 1
+    slot_idx = torch.tensor([4, 0, 2, 5], dtype=torch.int32)
+    pool = sg.states(seed, S * L * H, DEV).view(S, L, H, 128, 128)
+    pool0 = pool.clone()
+    ring_start = torch.tensor([0, 3, 9, 15], dtype=torch.int32)
+    ring = kda.Ring.empty(S, L, H, R, DEV)
+    for t in (ring.k, ring.v, ring.gk, ring.beta):
+        t.view(torch.int16 if t.element_size() == 2 else torch.int32).fill_(-7)
+    ring0 = kda.Ring(ring.k.clone(), ring.v.clone(), ring.gk.clone(), ring.beta.clone())
+    ins = sg.prefill_inputs(seed, total, H, DEV)
+    o = torch.full((total, H, 128), -9.0, device=DEV)
+    assert [w for w in ragged_windows(cu, total, max_tok)] == [(0, 5), (5, 0), (3, 8), (19, 1)]
+    kda.kda_verify_ragged(*ins, torch.from_numpy(cu).to(DEV), pool, slot_idx.to(DEV), o, layer=0, max_tok=max_tok,
+                          ring=ring, ring_start=ring_start.to(DEV))
+    torch.cuda.synchronize()
+    # windows 0 and 2 share rows 3 and 4, so o is checked per window from separate calls below
+    worst = 0.0
+    for keep in ([0, 1, 3], [2]):
+        cu_k = cu.copy()
+        o_k = torch.full((total, H, 128), -9.0, device=DEV)
+        sl = slot_idx.clone()
+        for b in range(B):
+            if b not in keep:
+                sl[b] = -1
+        ring_k = kda.Ring(ring0.k.clone(), ring0.v.clone(), ring0.gk.clone(), ring0.beta.clone())
+        kda.kda_verify_ragged(*ins, torch.from_numpy(cu_k).to(DEV), pool, sl.to(DEV), o_k, layer=0, max_tok=max_tok,
+                              ring=ring_k, ring_start=ring_start.to(DEV))
+        torch.cuda.synchronize()
+        worst = max(worst, check_ragged(0 + seed, 0, cu, total, max_tok, H, sl, pool0, o_k, ring_k, ring0, ring_start,
+                                        R, 1.0))
+    assert torch.equal(pool, pool0)
+    assert np.all(np_(o)[11:19] == -9.0) and np.all(np_(o)[19] != -9.0)
+    log(f"ragged verify with clamped bounds: worst err {worst:.2e}")
+    assert worst <= TOL
+
+
 @pytest.mark.parametrize("T,accs", [(8, [1, 2, 3, 4, 5, 6, 7, 8]), (1, [1, 0, 1, 1, 0, 1, 1, 0])])
 def test_fold_bitexact_every_length(gpu, T, accs):
     seed, H, L, R = 40 + T, 3, 3, 16
