@@ -42,14 +42,15 @@
 //     the B operand of the next products by permuting the reduction index
 //     identically in both operands. Phase 1: Kt S0, Qt S0, R, W = X R and
 //     O = Qt S0 + P W (stored straight from the accumulators); phase 2: the
-//     state update and the snapshot.
+//     state update, the snapshot, and the sums below.
 //   producer waves 4-7 prepare chunk c+1. Phase 1: raw q, k, gk, beta
 //     (prefetched into registers two periods ahead) become decay factors,
 //     per-wave partial A and P tiles and the fp16 operand rows of the chain;
 //     raw v goes from global memory straight into LDS (global_load_lds) for
-//     the chain. Phase 2: the operand rows go to LDS, one wave sums the P
-//     partials, one sums the off-diagonal A block; at the end of the period
-//     consumer wave 0 inverts the diagonal blocks of I + A.
+//     the chain. Phase 2: the operand rows go to LDS and the loads of the
+//     chunk after next are issued; meanwhile, after their state update, three
+//     consumer waves turn the partials into the next chunk's X (wave 0 inverts
+//     the diagonal blocks of I + A), P (wave 1) and -A10 (wave 2).
 // Everything the two stages exchange is double-buffered by chunk parity, so
 // a period needs just its two barriers. Operands that a product needs
 // transposed are read with the transposing LDS load (ds_read_b64_tr_b16)
@@ -85,7 +86,7 @@ struct alignas(16) PrefillLds {
   uint16_t pm[2][C][SQ];               // fp16  P, rows t, columns i
   float beta[2][C];
   float dlast[2][D];                   // e^{G_31} per key channel
-  // producer-only scratch
+  // partial tiles (producers write, the chain sums) and the solve's scratch
   float part[4][6][16][20];            // per-wave partial A and P tiles over 32 channels, [col][row] (padded)
   float ar[C][ATS];                    // diagonal blocks of A, fp32, rows i
   int item;
@@ -499,11 +500,7 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
           issue(use, c1 + 2);
           asm volatile("" ::: "memory");
           issue_vc(c1 + 1);  // into the buffer the chain read in this period's phase 1
-          if (c1 < nch) {
-            stage1b(L, keep, b1, pw, g, lr);
-            if (pw == 1) stage2_p(L, b1, lane);
-            else if (pw == 2) stage2_a10(L, b1, lane);
-          }
+          if (c1 < nch) stage1b(L, keep, b1, pw, g, lr);
           // everything older than this period's 12 loads has landed: the next chunk's
           // register set and the v rows the chain reads in the next period
           __builtin_amdgcn_s_waitcnt(0x0f7c);  // vmcnt(12)
@@ -669,8 +666,11 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
                   for (int r = 0; r < 4; ++r) dst[(16 * mc + r) * D + 16 * nv] = S[mc][nv][r];
             }
           }
-          // X for the next chunk (its A partials were written by the producers in phase 1)
+          // the next chunk's X, P and -A10 from the partials the producers wrote in phase 1, on three
+          // of the chain waves (the producers' phase 2 is taken up by issuing the next loads)
           if (cw == 0 && p + 1 < nch) stage2_solve(L, (p + 1) & 1, lane);
+          else if (cw == 1 && p + 1 < nch) stage2_p(L, (p + 1) & 1, lane);
+          else if (cw == 2 && p + 1 < nch) stage2_a10(L, (p + 1) & 1, lane);
           __syncthreads();
         }
 
