@@ -266,7 +266,9 @@ __device__ __forceinline__ void stage1(PrefillLds& L, const Raw& cur, int nc, in
   float k0[8], k1[8], q0[8], q1[8];
   unpack_bf16x8(cur.k0, k0); unpack_bf16x8(cur.k1, k1);
   unpack_bf16x8(cur.q0, q0); unpack_bf16x8(cur.q1, q1);
-  float xr0[8], xr1[8], yc0[8], yc1[8], e0[8], e1[8], f0[8], f1[8];
+  float xr0[8], xr1[8], yc0[8], yc1[8], e0[8], e1[8], f0[8], f1[8], dl[8];
+  // no branch inside this loop: its 16 prefix-sum chains and 32 exponentials are independent
+  // across channels and interleave only within one basic block
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     // prefix sums inside each 16-token block, then the four exponentials
@@ -282,7 +284,11 @@ __device__ __forceinline__ void stage1(PrefillLds& L, const Raw& cur, int nc, in
     e1[i] = T0 * p1;
     f0[i] = yc0[i] * T1;                      // e^{G_31 - G_t}
     f1[i] = T1 * r1;
-    if (tl == 0) L.dlast[b][c8 + i] = T0 * T1;
+    dl[i] = T0 * T1;                          // e^{G_31}
+  }
+  if (tl == 0) {
+    *reinterpret_cast<float4*>(&L.dlast[b][c8]) = make_float4(dl[0], dl[1], dl[2], dl[3]);
+    *reinterpret_cast<float4*>(&L.dlast[b][c8 + 4]) = make_float4(dl[4], dl[5], dl[6], dl[7]);
   }
   // fp16 operand rows of the chain, written to LDS in phase 2
   kp_.qt[0] = pk8_mul(q0, e0); kp_.qt[1] = pk8_mul(q1, e1);
