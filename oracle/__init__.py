@@ -41,7 +41,9 @@ def lib():
                                         vp, vp, vp]
         L.kda_oracle_fold.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
         L.kda_oracle_chunked.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, vp, dbl, vp, vp]
-        for f in (L.kda_oracle_recurrent, L.kda_oracle_verify, L.kda_oracle_fold, L.kda_oracle_chunked):
+        L.kda_oracle_gated_rmsnorm.argtypes = [i64, i32, vp, vp, vp, dbl, vp]
+        for f in (L.kda_oracle_recurrent, L.kda_oracle_verify, L.kda_oracle_fold, L.kda_oracle_chunked,
+                  L.kda_oracle_gated_rmsnorm):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -130,6 +132,19 @@ def chunked(q, k, v, gk, beta, S0=None, scale=1.0, chunk=64):
     if rc != 0:
         raise ValueError("kda_oracle_chunked rejected its arguments")
     return o, S
+
+
+def gated_rmsnorm(o, g, w, eps):
+    """Output gated RMSNorm over the last axis (rows of V): o / sqrt(mean(o^2) + eps) * w * sigmoid(g)."""
+    o, g, w = f64(o), f64(g), f64(w)
+    V = o.shape[-1]
+    if g.shape != o.shape or w.shape != (V,):
+        raise ValueError("gated_rmsnorm: g must match o, w must have the row length")
+    y = np.empty_like(o)
+    rc = lib().kda_oracle_gated_rmsnorm(o.size // V, V, _p(o), _p(g), _p(w), float(eps), _p(y))
+    if rc != 0:
+        raise ValueError("kda_oracle_gated_rmsnorm rejected its arguments")
+    return y
 
 
 def run_parallel(fn, items, threads=None):

@@ -253,3 +253,30 @@ int kda_oracle_chunked(int64_t L, int K, int V, int C, const double* q, const do
   free(Snew);
   return 0;
 }
+
+/*
+ * Output gated RMSNorm, one row of V values per (token, head):
+ *   y[j] = o[j] / sqrt(mean_j' o[j']^2 + eps) * w[j] * sigmoid(g[j]),
+ *   sigmoid(x) = 1 / (1 + exp(-x)).
+ * Source: Kimi K3 B200 deployment notes (zdszero.github.io), the prefill /
+ * decode kernel-fusion items: the KDA output goes through a gated RMSNorm
+ * that reads the attention output at its native stride, the one fusion
+ * allowed fast math (tolerance 8e-3). The notes name the operation but not its
+ * formula; the reading here is the plain one for "RMSNorm with an output
+ * gate": each row is divided by its root mean square (eps inside the root),
+ * scaled per channel by a weight shared by all heads, and multiplied
+ * elementwise by the logistic sigmoid of the gate.
+ */
+int kda_oracle_gated_rmsnorm(int64_t rows, int V, const double* o, const double* g, const double* w, double eps,
+                             double* y) {
+  if (rows < 0 || V < 1 || !(eps >= 0.0)) return 1;
+  for (int64_t r = 0; r < rows; ++r) {
+    const double* orow = o + r * V;
+    const double* grow = g + r * V;
+    double ss = 0.0;
+    for (int j = 0; j < V; ++j) ss += orow[j] * orow[j];
+    const double inv = 1.0 / sqrt(ss / V + eps);
+    for (int j = 0; j < V; ++j) y[r * V + j] = orow[j] * inv * w[j] * (1.0 / (1.0 + exp(-grow[j])));
+  }
+  return 0;
+}

@@ -237,3 +237,62 @@ def test_sizes_match_pages():
         m = 2 * (ex["gamma"] + 1)
         assert m == ex["min_len"]
         assert 1 << math.ceil(math.log2(m)) == ex["len"]
+
+
+# ---------------------------------------------------------------- output gated RMSNorm
+# The pages name the operation (a gated RMSNorm on the KDA output) but not its formula; these pin the
+# oracle's reading of it: divide each row by its root mean square (eps inside the root), scale by a
+# per-channel weight, multiply by the logistic sigmoid of the gate.
+
+def test_gated_rmsnorm_unit_rms_with_open_gate():
+    """w = 1, eps = 0 and a gate far in saturation: every row comes out with mean square exactly 1 (a
+    sum instead of a mean, a missing root or a missing square would all miss this)."""
+    rng = np.random.default_rng(11)
+    o = rng.standard_normal((7, 128)) * rng.uniform(0.01, 100.0, (7, 1))
+    y = oracle.gated_rmsnorm(o, np.full(o.shape, 60.0), np.ones(128), 0.0)
+    assert np.allclose(np.mean(y * y, axis=1), 1.0, rtol=0, atol=1e-14)
+    assert np.all(np.sign(y) == np.sign(o))
+
+
+def test_gated_rmsnorm_gate_values():
+    """The gate is a logistic sigmoid of g itself: g = 0 halves the output exactly, a strongly negative
+    g closes it, a strongly positive one leaves the normalised row (a sign slip swaps the last two)."""
+    rng = np.random.default_rng(12)
+    o, w = rng.standard_normal((5, 128)), rng.standard_normal(128)
+    open_ = oracle.gated_rmsnorm(o, np.full(o.shape, 60.0), w, 1e-6)
+    half = oracle.gated_rmsnorm(o, np.zeros(o.shape), w, 1e-6)
+    shut = oracle.gated_rmsnorm(o, np.full(o.shape, -60.0), w, 1e-6)
+    assert np.array_equal(half, 0.5 * open_)
+    assert np.max(np.abs(shut)) < 1e-20 * np.max(np.abs(open_))
+    g1 = np.log(3.0)  # sigmoid(ln 3) = 3/4
+    q = oracle.gated_rmsnorm(o, np.full(o.shape, g1), w, 1e-6)
+    assert np.allclose(q, 0.75 * open_, rtol=1e-15, atol=0)
+
+
+def test_gated_rmsnorm_invariances():
+    """Scale invariance at eps = 0 (RMSNorm ignores the row's magnitude), oddness in o, equivariance
+    under a channel permutation of (o, g, w), and the weight acting per channel."""
+    rng = np.random.default_rng(13)
+    o, g, w = rng.standard_normal((6, 128)), rng.standard_normal((6, 128)), rng.standard_normal(128)
+    y = oracle.gated_rmsnorm(o, g, w, 0.0)
+    assert np.allclose(oracle.gated_rmsnorm(37.5 * o, g, w, 0.0), y, rtol=1e-13, atol=0)
+    assert np.array_equal(oracle.gated_rmsnorm(-o, g, w, 0.0), -y)
+    perm = rng.permutation(128)
+    assert np.allclose(oracle.gated_rmsnorm(o[:, perm], g[:, perm], w[perm], 0.0), y[:, perm], rtol=1e-14, atol=0)
+    w2 = w.copy()
+    w2[5] *= 2.0
+    y2 = oracle.gated_rmsnorm(o, g, w2, 0.0)
+    assert np.array_equal(y2[:, 5], 2.0 * y[:, 5]) and np.array_equal(np.delete(y2, 5, 1), np.delete(y, 5, 1))
+
+
+def test_gated_rmsnorm_eps():
+    """eps sits inside the root and is added to the mean square: with eps = ms the row shrinks by
+    exactly 1/sqrt(2); with eps far above ms the map becomes linear, o / sqrt(eps)."""
+    rng = np.random.default_rng(14)
+    o = rng.standard_normal((1, 128))
+    ms = float(np.mean(o * o))
+    g, w = np.full(o.shape, 60.0), np.ones(128)
+    y0 = oracle.gated_rmsnorm(o, g, w, 0.0)
+    assert np.allclose(oracle.gated_rmsnorm(o, g, w, ms), y0 / math.sqrt(2.0), rtol=1e-14, atol=0)
+    big = 1e12
+    assert np.allclose(oracle.gated_rmsnorm(o, g, w, big), o / math.sqrt(big), rtol=1e-9, atol=0)
