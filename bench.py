@@ -13,6 +13,9 @@ events on the launch stream. Beside it, in the same JSON line:
   pristine copy outside the timed region before every step); beside it the
   same step through kda_fold_verify, and the verify with trimmed windows
   (1..8 tokens per request, packed) through kda_verify_ragged;
+* ``prefill_gated_norm``: the same prefill with the output gated RMSNorm,
+  fused into its epilogue (kda_chunk_prefill_gated) and unfused (the prefill,
+  then kda_gated_rmsnorm over its fp32 output);
 * ``roofline``: HBM roofline of the prefill kernel (algorithmic bytes per
   launch / measured launch time, against 8 TB/s);
 * ``cpu_baseline``: the fp64 oracle (token-by-token) timed on this host's
@@ -115,6 +118,58 @@ def bench_prefill(args, torch, kda, sg, synth):
     res = dict(ms=ms, value=tokens_heads / (ms * 1e-3), bytes=byts, achieved=achieved, N=N, L=L, H=H)
     del q, k, v, gk, beta, o, st, S0
     return res
+
+
+def bench_prefill_gated(args, torch, kda, sg, synth):
+    """The headline prefill with the output gated RMSNorm: fused (kda_chunk_prefill_gated, bf16 y) against
+    the same two steps unfused (kda_chunk_prefill, then kda_gated_rmsnorm over its fp32 o)."""
+    dev = "cuda:0"
+    N, L, H = 4, 2048, 64
+    seed = synth.PREFILL_CONFIGS[1]["seed"]
+    cu = synth.cu_seqlens([L] * N)
+    T = int(cu[-1])
+    q, k, v, gk, beta = sg.prefill_inputs(seed, T, H, dev)
+    gate = sg.gate(seed, T, H, dev)
+    w = torch.from_numpy(synth.norm_weight(seed)).to(dev)
+    S0 = sg.states(seed, N * H, dev).view(N, H, 128, 128)
+    o = torch.empty((T, H, 128), device=dev)
+    y = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    st = torch.empty((N, H, 128, 128), device=dev)
+    plan = kda.kda_plan_create(cu, n_heads=H)
+    ws = torch.empty(kda.kda_plan_workspace_bytes(plan), dtype=torch.uint8, device=dev)
+    kda.kda_plan_upload(plan, ws)
+    flags = kda.KDA_PREFILL_PLAN_RESIDENT
+    eps = 1e-6
+
+    def fused():
+        kda.kda_chunk_prefill_gated(plan, q, k, v, gk, beta, gate, w, eps, st, y, ws, state_in=S0, flags=flags)
+
+    def unfused():
+        kda.kda_chunk_prefill(plan, q, k, v, gk, beta, st, o, ws, state_in=S0, flags=flags)
+        kda.kda_gated_rmsnorm(o, gate, w, eps, y)
+
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, step in (("fused", fused), ("unfused", unfused)):
+        settle(step, torch)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / args.steps
+    th = N * L * H
+    st_b = N * H * 65536 * 2
+    # fused: q, k, v, gate bf16 + gk fp32 + beta + y bf16 = 1,796 B per token*head; unfused adds the norm's
+    # own pass (o fp32 read, gate read, y written) on top of the plain prefill's 1,796 B
+    fused_b, unfused_b = th * 1796 + st_b, th * (1796 + 1024) + st_b
+    del q, k, v, gk, beta, gate, o, y, st, S0
+    return dict(fused_ms=res["fused"], unfused_ms=res["unfused"], fused_bytes=fused_b, unfused_bytes=unfused_b,
+                tokens_heads=th)
 
 
 def bench_verify_fold(args, torch, kda, sg, synth):
@@ -282,6 +337,10 @@ def main():
     log("prefill: generating inputs and timing")
     pf = bench_prefill(args, torch, kda, sg, synth)
     log(f"prefill: {pf['ms'] * 1e3:.1f} us/launch, {pf['achieved']:.0f} GB/s")
+    pg = None
+    if not args.prefill_only:
+        log("prefill with the output gated RMSNorm: fused and unfused")
+        pg = bench_prefill_gated(args, torch, kda, sg, synth)
     vf = None
     if not (args.no_verify_fold or args.prefill_only):
         log("verify+fold: generating inputs and timing")
@@ -320,9 +379,19 @@ def main():
                    "n_seq": pf["N"], "seq_len": pf["L"], "heads": pf["H"], "head_dim": 128},
         "roofline": {"bound": "hbm", "achieved": pf["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": pf["achieved"] / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "kda::prefill_kernel", "algorithmic_bytes_per_launch": pf["bytes"]},
+                     "kernel": "kda::prefill_kernel<false>", "algorithmic_bytes_per_launch": pf["bytes"]},
         "cpu_baseline": cpu,
     }
+    if pg is not None:
+        line["prefill_gated_norm"] = {
+            "fused_us": pg["fused_ms"] * 1e3, "unfused_us": pg["unfused_ms"] * 1e3,
+            "fused_tokens_heads_per_s": pg["tokens_heads"] / (pg["fused_ms"] * 1e-3),
+            "fused_gbs": pg["fused_bytes"] / (pg["fused_ms"] * 1e-3) / 1e9,
+            "fused_hbm_frac": pg["fused_bytes"] / (pg["fused_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "workload": "the headline prefill followed by the output gated RMSNorm (gate N(0,1) bf16, weights "
+                        "1 + 0.1 N(0,1), eps 1e-6, bf16 y): kda_chunk_prefill_gated vs kda_chunk_prefill + "
+                        "kda_gated_rmsnorm",
+        }
     if vf is not None:
         line["verify_fold"] = {
             "us_per_step": (vf["verify_ms"] + vf["fold_ms"]) * 1e3,

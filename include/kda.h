@@ -36,6 +36,12 @@
  *      is a power of two and at least 2 * (gamma + 1). The same list names
  *      the two verify layouts: static (every request verifies all gamma + 1
  *      tokens) and ragged (windows trimmed per request by confidence).
+ *  [B200-NORM] same notes, prefill / decode kernel-fusion items: the KDA
+ *      output passes through a gated RMSNorm that reads the attention output
+ *      at its native stride; that norm is the one fusion allowed fast math
+ *      (tolerance 8e-3). The formula is not printed; the reading used here is
+ *      RMSNorm over the head's 128 channels (eps inside the root), a weight
+ *      per channel, and a sigmoid output gate.
  *  [LMSYS-SPEC] "SGLang and Miles Add Day-0 Support for Kimi K3", section
  *      "Speculative decoding with DSpark": a per-step planner keeps each
  *      request's verify tokens only while their expected value covers their
@@ -205,6 +211,51 @@ kda_status kda_chunk_prefill(const kda_plan* plan, const kda_inputs* in, const f
                              float* state_out, float* o, float* snap, int snap_slots,
                              int32_t* snap_count, void* workspace, float scale, int flags,
                              void* stream);
+
+/*
+ * Chunked prefill with the output gated RMSNorm fused into its epilogue
+ * [B200-NORM]: exactly kda_chunk_prefill, except that instead of o the kernel
+ * writes
+ *   y[t][h][j] = bf16( o[t][h][j] / sqrt(mean_j' o[t][h][j']^2 + eps)
+ *                      * norm_w[j] * sigmoid(gate[t][h][j]) )
+ * where o is kda_chunk_prefill's fp32 output (the same bits, never stored),
+ * sigmoid(x) = 1 / (1 + e^-x), and bf16 rounding is to nearest even. The
+ * arithmetic and its summation order are those of kda_gated_rmsnorm, so y is
+ * bit-identical to kda_gated_rmsnorm applied to kda_chunk_prefill's o.
+ *
+ *  gate   : bf16 [T, H, 128].
+ *  norm_w : fp32 [128], one weight per channel, shared by all heads.
+ *  eps    : finite, >= 0.
+ *  y      : bf16 [T, H, 128]; it may not overlap any input or state buffer.
+ *  Every other argument as kda_chunk_prefill. The plan must have one value
+ *  block per (sequence, head) (whole rows of o): KDA_ERR_UNSUPPORTED otherwise.
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_DEVICE.
+ */
+kda_status kda_chunk_prefill_gated(const kda_plan* plan, const kda_inputs* in, const void* gate,
+                                   const float* norm_w, float eps, const float* state_in,
+                                   float* state_out, void* y, float* snap, int snap_slots,
+                                   int32_t* snap_count, void* workspace, float scale, int flags,
+                                   void* stream);
+
+/*
+ * The output gated RMSNorm on its own [B200-NORM], for an o written by
+ * kda_chunk_prefill or kda_verify: rows of 128 values,
+ *   y[r][j] = bf16( o[r][j] / sqrt(mean_j' o[r][j']^2 + eps) * norm_w[j] * sigmoid(gate[r][j]) ).
+ * Fast-math arithmetic (hardware exp2, reciprocal and reciprocal square root)
+ * in a fixed summation order: a row is cut into 16 slices of 8 values,
+ * slice 4w + q = columns 32w + 4q + {0..3} then 32w + 16 + 4q + {0..3}; each
+ * slice's squares are summed in that order, then the slice sums in slice order.
+ *
+ *  rows   : number of rows (>= 0), e.g. T * H.
+ *  o      : fp32 [rows, 128].
+ *  gate   : bf16 [rows, 128].
+ *  norm_w : fp32 [128].
+ *  eps    : finite, >= 0.
+ *  y      : bf16 [rows, 128]; may not overlap an input.
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_DEVICE.
+ */
+kda_status kda_gated_rmsnorm(int64_t rows, const float* o, const void* gate, const float* norm_w, float eps,
+                             void* y, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Per-slot raw-input ring [LMSYS-RSSM], [B200-RING]: for each (slot, layer,

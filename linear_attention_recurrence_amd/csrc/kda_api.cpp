@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -161,42 +162,50 @@ void kda_plan_destroy(kda_plan* p) {
   delete p;
 }
 
-kda_status kda_chunk_prefill(const kda_plan* p, const kda_inputs* in, const float* state_in, float* state_out,
-                             float* o, float* snap, int snap_slots, int32_t* snap_count, void* workspace,
-                             float scale, int flags, void* stream) {
-  if (!p) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: plan is NULL");
-  if (!in) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: inputs are NULL");
-  if (!state_out) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: state_out is NULL");
-  if (!workspace) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: workspace is NULL");
-  if (flags & ~KDA_PREFILL_PLAN_RESIDENT) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: unknown flags");
+// kda_chunk_prefill and kda_chunk_prefill_gated: the same checks and launch; the gated form writes
+// bf16 y (the output gated RMSNorm of o) instead of fp32 o
+static kda_status prefill_call(const char* fn, const kda_plan* p, const kda_inputs* in, const float* state_in,
+                               float* state_out, float* o, const void* gate, const float* norm_w, float eps, void* y,
+                               float* snap, int snap_slots, int32_t* snap_count, void* workspace, float scale,
+                               int flags, void* stream) {
+  const bool gated = y != nullptr;
+  auto bad = [&](kda_status st, const char* what) { return fail(st, std::string(fn) + ": " + what); };
+  if (!p) return bad(KDA_ERR_INVALID_ARG, "plan is NULL");
+  if (!in) return bad(KDA_ERR_INVALID_ARG, "inputs are NULL");
+  if (!state_out) return bad(KDA_ERR_INVALID_ARG, "state_out is NULL");
+  if (!workspace) return bad(KDA_ERR_INVALID_ARG, "workspace is NULL");
+  if (flags & ~KDA_PREFILL_PLAN_RESIDENT) return bad(KDA_ERR_INVALID_ARG, "unknown flags");
+  if (gated && !(eps >= 0.f && eps < INFINITY)) return bad(KDA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (gated && p->v_blocks != 1)
+    return bad(KDA_ERR_UNSUPPORTED, "the fused norm needs whole rows: a plan with one value block per (sequence, head)");
   const int64_t T = p->total_tokens;
   const int H = p->n_heads;
-  if (T > 0 && (!in->q || !in->k || !in->v || !in->gk || !in->beta || !o))
-    return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: q, k, v, gk, beta and o are required");
+  void* out = gated ? y : static_cast<void*>(o);
+  if (T > 0 && (!in->q || !in->k || !in->v || !in->gk || !in->beta || !out))
+    return bad(KDA_ERR_INVALID_ARG, gated ? "q, k, v, gk, beta and y are required" : "q, k, v, gk, beta and o are required");
+  if (gated && T > 0 && (!gate || !norm_w)) return bad(KDA_ERR_INVALID_ARG, "gate and norm_w are required");
   const bool snaps = p->snap_interval > 0 && snap != nullptr;
-  if (snaps && snap_slots < 1) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: snap_slots must be >= 1");
+  if (snaps && snap_slots < 1) return bad(KDA_ERR_INVALID_ARG, "snap_slots must be >= 1");
   const size_t tok = (size_t)T * H;
   const size_t qkv_b = tok * KDA_HEAD_DIM * 2, gk_b = tok * KDA_HEAD_DIM * 4, beta_b = tok * 4;
-  const size_t o_b = tok * KDA_HEAD_DIM * 4;
+  const size_t o_b = tok * KDA_HEAD_DIM * (gated ? 2 : 4);
   const size_t st_b = (size_t)p->n_seq * H * kState;
   const size_t snap_b = snaps ? (size_t)p->n_seq * snap_slots * H * kState : 0;
-  const void* ins[5] = {in->q, in->k, in->v, in->gk, in->beta};
-  const size_t insz[5] = {qkv_b, qkv_b, qkv_b, gk_b, beta_b};
-  for (int i = 0; i < 5; ++i) {
-    if (overlap(o, o_b, ins[i], insz[i])) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: o overlaps an input");
-    if (overlap(state_out, st_b, ins[i], insz[i]))
-      return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: state_out overlaps an input");
-    if (snaps && overlap(snap, snap_b, ins[i], insz[i]))
-      return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: snap overlaps an input");
+  const void* ins[7] = {in->q, in->k, in->v, in->gk, in->beta, gated ? gate : nullptr, gated ? norm_w : nullptr};
+  const size_t insz[7] = {qkv_b, qkv_b, qkv_b, gk_b, beta_b, qkv_b, (size_t)KDA_HEAD_DIM * 4};
+  for (int i = 0; i < 7; ++i) {
+    if (overlap(out, o_b, ins[i], insz[i])) return bad(KDA_ERR_INVALID_ARG, gated ? "y overlaps an input" : "o overlaps an input");
+    if (overlap(state_out, st_b, ins[i], insz[i])) return bad(KDA_ERR_INVALID_ARG, "state_out overlaps an input");
+    if (snaps && overlap(snap, snap_b, ins[i], insz[i])) return bad(KDA_ERR_INVALID_ARG, "snap overlaps an input");
   }
-  if (overlap(o, o_b, state_out, st_b) || overlap(o, o_b, state_in, st_b) || (snaps && overlap(o, o_b, snap, snap_b)))
-    return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: o overlaps a state buffer");
+  if (overlap(out, o_b, state_out, st_b) || overlap(out, o_b, state_in, st_b) || (snaps && overlap(out, o_b, snap, snap_b)))
+    return bad(KDA_ERR_INVALID_ARG, gated ? "y overlaps a state buffer" : "o overlaps a state buffer");
   if (state_in != state_out && overlap(state_in, st_b, state_out, st_b))
-    return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: state_in and state_out overlap without being equal");
+    return bad(KDA_ERR_INVALID_ARG, "state_in and state_out overlap without being equal");
   if (snaps && (overlap(snap, snap_b, state_out, st_b) || overlap(snap, snap_b, state_in, st_b)))
-    return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: snap overlaps a state buffer");
-  if (overlap(workspace, p->bytes, o, o_b) || overlap(workspace, p->bytes, state_out, st_b))
-    return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: workspace overlaps an output");
+    return bad(KDA_ERR_INVALID_ARG, "snap overlaps a state buffer");
+  if (overlap(workspace, p->bytes, out, o_b) || overlap(workspace, p->bytes, state_out, st_b))
+    return bad(KDA_ERR_INVALID_ARG, "workspace overlaps an output");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!(flags & KDA_PREFILL_PLAN_RESIDENT)) {
@@ -205,7 +214,7 @@ kda_status kda_chunk_prefill(const kda_plan* p, const kda_inputs* in, const floa
   }
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return device_fail("kda_chunk_prefill: hipGetDevice", e);
+  if (e != hipSuccess) return device_fail(fn, e);
   kda::PrefillArgs a{};
   a.n_seq = p->n_seq;
   a.n_heads = H;
@@ -218,7 +227,7 @@ kda_status kda_chunk_prefill(const kda_plan* p, const kda_inputs* in, const floa
   a.beta = in->beta;
   a.state_in = state_in;
   a.state_out = state_out;
-  a.o = o;
+  a.o = gated ? nullptr : o;
   a.snap = snaps ? snap : nullptr;
   a.snap_slots = snaps ? snap_slots : 0;
   a.snap_interval = snaps ? p->snap_interval : 0;
@@ -227,9 +236,48 @@ kda_status kda_chunk_prefill(const kda_plan* p, const kda_inputs* in, const floa
   a.items = reinterpret_cast<const int4*>(static_cast<char*>(workspace) + sizeof(kda::PrefillWsHeader));
   a.n_vblk = p->v_blocks;
   a.scale = scale;
+  if (gated) {
+    a.gate = static_cast<const uint16_t*>(gate);
+    a.norm_w = norm_w;
+    a.eps = eps;
+    a.y = static_cast<uint16_t*>(y);
+  }
   const int grid = std::min(p->n_items, kda::prefill_max_grid(dev));
   e = kda::launch_prefill(a, grid, s);
-  if (e != hipSuccess) return device_fail("kda_chunk_prefill: launch", e);
+  if (e != hipSuccess) return device_fail(fn, e);
+  return ok();
+}
+
+kda_status kda_chunk_prefill(const kda_plan* p, const kda_inputs* in, const float* state_in, float* state_out,
+                             float* o, float* snap, int snap_slots, int32_t* snap_count, void* workspace,
+                             float scale, int flags, void* stream) {
+  return prefill_call("kda_chunk_prefill", p, in, state_in, state_out, o, nullptr, nullptr, 0.f, nullptr, snap,
+                      snap_slots, snap_count, workspace, scale, flags, stream);
+}
+
+kda_status kda_chunk_prefill_gated(const kda_plan* p, const kda_inputs* in, const void* gate, const float* norm_w,
+                                   float eps, const float* state_in, float* state_out, void* y, float* snap,
+                                   int snap_slots, int32_t* snap_count, void* workspace, float scale, int flags,
+                                   void* stream) {
+  if (!y) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill_gated: y is NULL");
+  return prefill_call("kda_chunk_prefill_gated", p, in, state_in, state_out, nullptr, gate, norm_w, eps, y, snap,
+                      snap_slots, snap_count, workspace, scale, flags, stream);
+}
+
+kda_status kda_gated_rmsnorm(int64_t rows, const float* o, const void* gate, const float* norm_w, float eps, void* y,
+                             void* stream) {
+  if (rows < 0) return fail(KDA_ERR_INVALID_ARG, "kda_gated_rmsnorm: rows < 0");
+  if (!(eps >= 0.f && eps < INFINITY)) return fail(KDA_ERR_INVALID_ARG, "kda_gated_rmsnorm: eps must be finite and >= 0");
+  if (rows == 0) return ok();
+  if (rows > ((int64_t)1 << 34)) return fail(KDA_ERR_INVALID_ARG, "kda_gated_rmsnorm: too many rows");
+  if (!o || !gate || !norm_w || !y) return fail(KDA_ERR_INVALID_ARG, "kda_gated_rmsnorm: o, gate, norm_w and y are required");
+  const size_t yb = (size_t)rows * KDA_HEAD_DIM * 2;
+  if (overlap(y, yb, o, (size_t)rows * KDA_HEAD_DIM * 4) || overlap(y, yb, gate, yb) ||
+      overlap(y, yb, norm_w, (size_t)KDA_HEAD_DIM * 4))
+    return fail(KDA_ERR_INVALID_ARG, "kda_gated_rmsnorm: y overlaps an input");
+  const hipError_t e = kda::launch_gated_rmsnorm(rows, o, static_cast<const uint16_t*>(gate), norm_w, eps,
+                                                 static_cast<uint16_t*>(y), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail("kda_gated_rmsnorm: launch", e);
   return ok();
 }
 

@@ -75,9 +75,17 @@ struct PrefillArgs {
   const int4* items;  // (sequence, head | value block << 16, first token, length)
   int n_vblk;         // value blocks per (sequence, head): 1 (all 128 columns) or 2 (halves)
   float scale;
+  // the fused output gated RMSNorm (y != nullptr, whole-chain items only): y replaces o
+  const uint16_t* gate;  // bf16 [T, H, 128]
+  const float* norm_w;   // fp32 [128]
+  float eps;
+  uint16_t* y;           // bf16 [T, H, 128]
 };
 
 hipError_t launch_verify(const VerifyArgs& a, bool f32_inputs, hipStream_t stream);
+// the output gated RMSNorm on its own: rows of 128 fp32 values -> bf16
+hipError_t launch_gated_rmsnorm(int64_t rows, const float* o, const uint16_t* gate, const float* w, float eps,
+                                uint16_t* y, hipStream_t stream);
 // chunked-form verify on the matrix cores: bf16 inputs, n_tok <= 16, no recurrent commit
 bool verify_chunk_eligible(const VerifyArgs& a, bool f32_inputs);
 hipError_t launch_verify_chunk(const VerifyArgs& a, hipStream_t stream);

@@ -59,8 +59,11 @@
 
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_norm.h"
 
 namespace kda {
+
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2v;
 
 constexpr int C = 32;      // chunk length
 constexpr int TM = 152;    // token-major row stride (16-bit elements; 128 + 24 pad: rows 12 banks apart)
@@ -90,6 +93,12 @@ struct alignas(16) PrefillLds {
   float part[4][6][16][20];            // per-wave partial A and P tiles over 32 channels, [col][row] (padded)
   float ar[C][ATS];                    // diagonal blocks of A, fp32, rows i
   int item;
+  // the fused output norm (kda_chunk_prefill_gated): raw gate rows (stored like vr), per-token slice
+  // sums of squares of o, and the norm weights
+  uint16_t gr[2][C][D];
+  float ssq[C][16];   // slice sums of squares of the chunk's o, [token][slice]
+  float rs[C];        // 1 / rms of each token row
+  float nw[D];
 };
 
 __device__ __forceinline__ uint2 lds8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
@@ -217,8 +226,8 @@ __device__ __forceinline__ void load_raw(Raw& r, const PrefillArgs& A, size_t ro
 
 // raw v rows of a chunk straight into LDS: 4 rows of 256 bytes per instruction, rows
 // 16r + 4w .. 16r + 4w + 3 (r < 2) from wave w of a role; 16-byte chunks land at chunk ^ (2 row & 15)
-__device__ __forceinline__ void issue_v(const PrefillArgs& A, uint16_t (&dst)[C][D], size_t row0, int nc, int wu, int lane) {
-  const uint16_t* vsrc = A.v + row0 * D;
+__device__ __forceinline__ void issue_v(const uint16_t* src, const PrefillArgs& A, uint16_t (&dst)[C][D], size_t row0, int nc, int wu, int lane) {
+  const uint16_t* vsrc = src + row0 * D;
   const uint32_t HD = (uint32_t)A.n_heads * D;
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
@@ -431,6 +440,10 @@ __device__ __forceinline__ void stage2_p(PrefillLds& L, int b, int lane) {
   }
 }
 
+// GATED: the output gated RMSNorm replaces the store of o (whole-chain items only): phase 1 keeps o in
+// registers and writes each token's slice sums of squares; the next period's phase 1 (or the item's
+// end, for its last chunk) adds them in slice order and writes y in bf16.
+template <bool GATED>
 __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
   __shared__ PrefillLds L;
   const int tid = threadIdx.x;
@@ -445,6 +458,9 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
   for (int e = tid; e < 2 * 16 * 16; e += NT) {
     const int b = e >> 8, i = (e >> 4) & 15, j = 16 + (e & 15);
     L.pm[b][i][j] = 0;
+  }
+  if constexpr (GATED) {
+    for (int i = tid; i < D; i += NT) L.nw[i] = A.norm_w[i];
   }
 
   for (;;) {
@@ -476,9 +492,10 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
       // Raw inputs are prefetched two periods ahead: q, k, gk, beta into registers, alternating
       // between two sets (chunk c lives in set c & 1 from the period that issues it, c - 3,
       // until its stage 1 in period c - 1), and v straight into vr[c & 1] (issued in period
-      // c - 2, read by the chain in period c). Every period issues the same 12 loads (past the
-      // last chunk they re-read it), so the compiler's waits before each register use count
-      // exactly, and the wait that closes a period can leave just that period's loads in flight.
+      // c - 2, read by the chain in period c; with GATED the gate rows go into gr[c & 1] the same
+      // way). Every period issues the same 12 loads (14 with GATED; past the last chunk they re-read
+      // it), so the compiler's waits before each register use count exactly, and the wait that
+      // closes a period can leave just that period's loads in flight.
       if (nch == 0) {
         __syncthreads();
         __syncthreads();
@@ -490,7 +507,8 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
         };
         auto issue_vc = [&](int c) {
           c = min(c, nch - 1);
-          issue_v(A, L.vr[c & 1], (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), pw, lane);
+          issue_v(A.v, A, L.vr[c & 1], (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), pw, lane);
+          if constexpr (GATED) issue_v(A.gate, A, L.gr[c & 1], (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), pw, lane);
         };
         issue(ra, 0);
         asm volatile("" ::: "memory");  // keep the issue order: set a, v of chunk 0, set b
@@ -507,9 +525,10 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
           asm volatile("" ::: "memory");
           issue_vc(c1 + 1);  // into the buffer the chain read in this period's phase 1
           if (c1 < nch) stage1b(L, keep, b1, pw, g, lr);
-          // everything older than this period's 12 loads has landed: the next chunk's
-          // register set and the v rows the chain reads in the next period
-          __builtin_amdgcn_s_waitcnt(0x0f7c);  // vmcnt(12)
+          // everything older than this period's 12 (14) loads has landed: the next chunk's
+          // register set and the v (and gate) rows the chain reads in the next period
+          if constexpr (GATED) __builtin_amdgcn_s_waitcnt(0x0f7e);  // vmcnt(14): the gate rows are 2 more loads
+          else __builtin_amdgcn_s_waitcnt(0x0f7c);                  // vmcnt(12)
           __syncthreads();
         };
         // periods -1 .. nch-1 in pairs, so that both sets' loads are issued on every path
@@ -553,6 +572,34 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
             for (int nv = 0; nv < NV; ++nv) S[mc][nv] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         f16x8 Wh[NV], Wl[NV];
+
+        // GATED: o of tokens lr and 16 + lr of the last chunk and their gate bits (columns c0 .. c0 + 3),
+        // kept in registers from the phase 1 that forms them to the next period's phase 1, where the
+        // output gated RMSNorm of that chunk runs just before the new o replaces them. Its stores then
+        // go out late in phase 1, as the plain path's stores of o do: in phase 2, or early in phase 1,
+        // they would wait behind the producers' burst of loads in a full memory queue
+        f32x4 Og[2][NV];
+        uint2 Gq[2][NV];
+        auto norm_epilogue = [&](int pc) {
+          if constexpr (GATED && NV == 2) {
+            // rows past the chunk end fall outside the buffer range and are dropped by the hardware
+            const int ncc = min(C, len - C * pc);
+            const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+                A.y + ((size_t)(tok0 + C * pc) * H + h) * D, 0, (int)((((uint32_t)ncc - 1) * H * D + D) * 2), 0x00020000);
+  #pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+              const uint32_t t = 16 * mt + lr;
+              const float rstd = L.rs[t];
+  #pragma unroll
+              for (int nv = 0; nv < 2; ++nv) {
+                const float4 w4 = *reinterpret_cast<const float4*>(&L.nw[cb + 16 * nv + 4 * g]);
+                const uint2 yv = norm_apply4(Og[mt][nv], Gq[mt][nv], w4, rstd);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2v, yv), yrs,
+                                                      (int)((t * H * D + cb + 16 * nv + 4 * g) * 2), 0, 0);
+              }
+            }
+          }
+        };
 
         for (int p = -1; p < nch; ++p) {
           const int b = p & 1;
@@ -622,6 +669,7 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
             }
   #pragma unroll
             for (int nv = 0; nv < NV; ++nv) split_h8(W[0][nv], W[1][nv], Wh[nv], Wl[nv], mone);
+            if (p >= 1) norm_epilogue(p - 1);  // (GATED only) the previous chunk's output, before its o is replaced
 
             // ---------------- O^T = scale (S0^T Qt^T + W^T P^T), stored from the accumulators ----------------
             // lane (g, lr) holds O[16mt + lr][cb + 16nv + 4g + r], r < 4: one 16-byte store per tile
@@ -635,9 +683,16 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
                 f32x4 acc = QT[nv][mt];
                 acc = mfma_h(Wh[nv], pa, acc);
                 acc = mfma_h(Wl[nv], pa, acc);
-                if (t < nc)
+                if constexpr (GATED) {
+                  Og[mt][nv] = f32x4{A.scale * acc[0], A.scale * acc[1], A.scale * acc[2], A.scale * acc[3]};
+                  const int c0 = cb + 16 * nv + 4 * g;
+                  Gq[mt][nv] = *reinterpret_cast<const uint2*>(&L.gr[b][t][8 * ((c0 >> 3) ^ ((2 * t) & 15)) + (c0 & 7)]);
+                } else if (t < nc) {
                   *reinterpret_cast<float4*>(orow + 16 * nv) = make_float4(A.scale * acc[0], A.scale * acc[1], A.scale * acc[2], A.scale * acc[3]);
+                }
               }
+              // this lane's slice (4 cw + g) of token t: columns 32 cw + 4 g + {0..3}, then + 16
+              if constexpr (GATED && NV == 2) L.ssq[t][4 * cw + g] = norm_slice_ssq(Og[mt][0], Og[mt][1]);
             }
           }
           __syncthreads();
@@ -672,6 +727,22 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
                   for (int r = 0; r < 4; ++r) dst[(16 * mc + r) * D + 16 * nv] = S[mc][nv][r];
             }
           }
+          // (GATED) 1 / rms of each of this chunk's token rows from the slice sums of phase 1, on the
+          // chain wave with the most slack in phase 2; the next period's phase 1 uses them
+          if constexpr (GATED && NV == 2) {
+            if (cw == 3 && p >= 0 && lane < C) {
+              float ss = 0.f;  // the 16 slice sums, in slice order
+  #pragma unroll
+              for (int k4 = 0; k4 < 4; ++k4) {
+                const float4 s4 = *reinterpret_cast<const float4*>(&L.ssq[lane][4 * k4]);
+                ss = ss + s4.x;
+                ss = ss + s4.y;
+                ss = ss + s4.z;
+                ss = ss + s4.w;
+              }
+              L.rs[lane] = norm_rstd(ss, A.eps);
+            }
+          }
           // the next chunk's X, P and -A10 from the partials the producers wrote in phase 1, on three
           // of the chain waves (the producers' phase 2 is taken up by issuing the next loads)
           if (cw == 0 && p + 1 < nch) stage2_solve(L, (p + 1) & 1, lane);
@@ -679,6 +750,8 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
           else if (cw == 2 && p + 1 < nch) stage2_a10(L, (p + 1) & 1, lane);
           __syncthreads();
         }
+
+        if (nch >= 1) norm_epilogue(nch - 1);  // (GATED only) the last chunk's output
 
         float* dst = A.state_out + unit * D * D + soff;
   #pragma unroll
@@ -689,7 +762,7 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
             for (int r = 0; r < 4; ++r) dst[(16 * mc + r) * D + 16 * nv] = S[mc][nv][r];
 
       };
-      if (A.n_vblk == 1) chain(std::integral_constant<int, 2>{});
+      if (GATED || A.n_vblk == 1) chain(std::integral_constant<int, 2>{});
       else chain(std::integral_constant<int, 1>{});
       if (A.snap_count && h == 0 && vb == 0 && tid == 0) A.snap_count[n] = A.snap_interval > 0 ? len / A.snap_interval : 0;
     }
@@ -724,7 +797,8 @@ int prefill_max_grid(int device) {
 
 hipError_t launch_prefill(const PrefillArgs& a, int grid, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_kernel, dim3(grid), dim3(NT), 0, stream, a);
+  if (a.y) hipLaunchKernelGGL(prefill_kernel<true>, dim3(grid), dim3(NT), 0, stream, a);
+  else hipLaunchKernelGGL(prefill_kernel<false>, dim3(grid), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 

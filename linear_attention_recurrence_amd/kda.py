@@ -31,7 +31,8 @@ KDA_CHUNK = 32
 
 EXPORTS = ("kda_abi_version", "kda_last_error", "kda_plan_create", "kda_plan_create_ex", "kda_plan_v_blocks",
            "kda_plan_workspace_bytes", "kda_plan_num_items", "kda_plan_items", "kda_plan_upload", "kda_plan_destroy",
-           "kda_chunk_prefill", "kda_verify", "kda_replay_fold", "kda_fold_verify", "kda_verify_ragged")
+           "kda_chunk_prefill", "kda_chunk_prefill_gated", "kda_gated_rmsnorm", "kda_verify", "kda_replay_fold",
+           "kda_fold_verify", "kda_verify_ragged")
 
 
 class KdaError(RuntimeError):
@@ -76,6 +77,9 @@ def lib():
         L.kda_plan_destroy.argtypes = [vp]
         L.kda_plan_destroy.restype = None
         L.kda_chunk_prefill.argtypes = [vp, ctypes.POINTER(_Inputs), vp, vp, vp, vp, i32, vp, vp, f32, i32, vp]
+        L.kda_chunk_prefill_gated.argtypes = [vp, ctypes.POINTER(_Inputs), vp, vp, f32, vp, vp, vp, vp, i32, vp, vp,
+                                              f32, i32, vp]
+        L.kda_gated_rmsnorm.argtypes = [ctypes.c_int64, vp, vp, vp, f32, vp, vp]
         L.kda_verify.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(_Inputs), vp, vp, vp,
                                  ctypes.POINTER(_Ring), vp, vp, vp, f32, vp]
         L.kda_replay_fold.argtypes = [i32, i32, i32, i32, vp, vp, ctypes.POINTER(_Ring), vp, vp, vp]
@@ -84,7 +88,8 @@ def lib():
         L.kda_verify_ragged.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(_Inputs), vp, vp, vp, vp,
                                         ctypes.POINTER(_Ring), vp, f32, vp]
         for f in ("kda_plan_create", "kda_plan_create_ex", "kda_plan_items", "kda_plan_upload", "kda_chunk_prefill",
-                  "kda_verify", "kda_replay_fold", "kda_fold_verify", "kda_verify_ragged"):
+                  "kda_chunk_prefill_gated", "kda_gated_rmsnorm", "kda_verify", "kda_replay_fold", "kda_fold_verify",
+                  "kda_verify_ragged"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -199,6 +204,42 @@ def kda_chunk_prefill(plan, q, k, v, gk, beta, state_out, o, workspace, state_in
     _check(lib().kda_chunk_prefill(plan.handle, ctypes.byref(ins), _ptr(state_in), _ptr(state_out), _ptr(o),
                                    _ptr(snap), int(snap_slots), _ptr(snap_count), _ptr(workspace), float(scale),
                                    int(flags), _stream(stream)))
+
+
+def kda_chunk_prefill_gated(plan, q, k, v, gk, beta, gate, norm_w, eps, state_out, y, workspace, state_in=None,
+                            snap=None, snap_slots=0, snap_count=None, scale=1.0, flags=0, stream=None):
+    """Chunked prefill with the output gated RMSNorm fused in: writes bf16 y instead of fp32 o (see
+    kda_chunk_prefill_gated in include/kda.h)."""
+    T, H, N, Dh = plan.total_tokens, plan.n_heads, plan.n_seq, KDA_HEAD_DIM
+    for name, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("y", y)):
+        _need(t, name, (T, H, Dh), _BF)
+    _need(gk, "gk", (T, H, Dh), _F32)
+    _need(beta, "beta", (T, H), _F32)
+    _need(norm_w, "norm_w", (Dh,), _F32)
+    _need(state_out, "state_out", (N, H, Dh, Dh), _F32)
+    _need(state_in, "state_in", (N, H, Dh, Dh), _F32, allow_none=True)
+    if snap is not None:
+        _need(snap, "snap", (N, snap_slots, H, Dh, Dh), _F32)
+    _need(snap_count, "snap_count", (N,), _I32, allow_none=True)
+    _need(workspace, "workspace", (kda_plan_workspace_bytes(plan),), (torch.uint8,))
+    ins = _Inputs(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(), beta.data_ptr())
+    _check(lib().kda_chunk_prefill_gated(plan.handle, ctypes.byref(ins), _ptr(gate), _ptr(norm_w), float(eps),
+                                         _ptr(state_in), _ptr(state_out), _ptr(y), _ptr(snap), int(snap_slots),
+                                         _ptr(snap_count), _ptr(workspace), float(scale), int(flags), _stream(stream)))
+
+
+def kda_gated_rmsnorm(o, gate, norm_w, eps, y, stream=None):
+    """The output gated RMSNorm over rows of 128 (see kda_gated_rmsnorm in include/kda.h); o fp32, gate and
+    y bf16, all [..., 128] of the same shape, norm_w fp32 [128]."""
+    Dh = KDA_HEAD_DIM
+    if o.shape[-1] != Dh:
+        raise ValueError(f"o has rows of {o.shape[-1]}, expected {Dh}")
+    _need(o, "o", tuple(o.shape), _F32)
+    _need(gate, "gate", tuple(o.shape), _BF)
+    _need(y, "y", tuple(o.shape), _BF)
+    _need(norm_w, "norm_w", (Dh,), _F32)
+    _check(lib().kda_gated_rmsnorm(o.numel() // Dh, _ptr(o), _ptr(gate), _ptr(norm_w), float(eps), _ptr(y),
+                                   _stream(stream)))
 
 
 class Ring:

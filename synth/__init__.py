@@ -37,6 +37,7 @@ _NP = {F64: np.float64, F32: np.float32, BF16: np.uint16}
 # tensor ids
 T_Q, T_K, T_V, T_GK, T_BETA, T_STATE, T_LENS, T_ACCEPT = 1, 2, 3, 4, 5, 6, 7, 8
 T_WINDOW = 9
+T_GATE, T_NORMW = 10, 16  # inputs of the output gated RMSNorm
 T_DEC_Q, T_DEC_K, T_DEC_V, T_DEC_GK, T_DEC_BETA = 11, 12, 13, 14, 15
 
 D = 128  # K = V = 128
@@ -181,6 +182,22 @@ def prefill_rows(seed, H, t0, nt, h=None, qkv_dtype=BF16, tids=(T_Q, T_K, T_V, T
     gk = rows(seed, tg, sub, NEG_SOFTPLUS, F32, r0, step, n).reshape(shp)
     beta = rows(seed, tb, sub, SIGMOID, F32, r0, step, n, row_len=1).reshape(bshp)
     return q, k, v, gk, beta
+
+
+def gate_rows(seed, H, t0, nt, h=None, sub=0):
+    """Output-gate values N(0,1) in bf16 for tokens [t0, t0+nt) of a packed [T, H, 128] batch (indexed like
+    prefill_rows; with h given, that head only). The pages give no distribution for the gate."""
+    if h is None:
+        r0, step, n, shp = t0 * H, 1, nt * H, (nt, H, D)
+    else:
+        r0, step, n, shp = t0 * H + h, H, nt, (nt, D)
+    return rows(seed, T_GATE, sub, NORMAL, BF16, r0, step, n).reshape(shp)
+
+
+def norm_weight(seed):
+    """Per-channel weights of the output norm, fp32(1 + 0.1 N(0,1)) (the pages give none)."""
+    x = rows(seed, T_NORMW, 0, NORMAL, F64, 0, 1, 1)
+    return (1.0 + 0.1 * x.reshape(D)).astype(np.float32)
 
 
 def state_rows(seed, unit0, n_units, unit_step=1, tid=T_STATE, sub=0, sigma=0.1, dtype=F32):

@@ -58,6 +58,12 @@ def prefill_inputs(seed, T, H, device, qkv_dtype=torch.bfloat16, tids=(T_Q, T_K,
     return q, k, v, gk, beta
 
 
+def gate(seed, T, H, device, sub=0):
+    """Output-gate values [T, H, 128] bf16 on device (the rows synth.gate_rows gives on the host)."""
+    from . import T_GATE
+    return fill(torch.empty((T, H, D), dtype=torch.bfloat16, device=device), seed, T_GATE, sub, NORMAL)
+
+
 def states(seed, n_units, device, tid=T_STATE, sub=0, sigma=0.1, out=None):
     """n_units states N(0, sigma^2) as [n_units, 128, 128] fp32 (unit u = rows u*128 ..)."""
     if out is None:

@@ -220,6 +220,34 @@ def test_verify_ragged_rejects_bad_arguments():
     assert call(total=0) == 0                       # every window is empty
 
 
+def test_gated_rejects_bad_arguments():
+    L = kda.lib()
+    o, g, w, y = (ctypes.c_void_p(x) for x in (0x20000000, 0x30000000, 0x31000000, 0x40000000))
+    norm = lambda rows=16, eps=1e-6, o_=o, y_=y: L.kda_gated_rmsnorm(rows, o_, g, w, eps, y_, None)
+    assert norm(rows=-1) == 1
+    assert norm(eps=-1.0) == 1
+    assert norm(eps=float("inf")) == 1
+    assert norm(o_=None) == 1
+    assert norm(y_=ctypes.c_void_p(0x20000000 + 64)) == 1  # y overlaps o
+    assert norm(rows=0) == 0                                # nothing to do
+    ins = _inputs()
+    ws, st = ctypes.c_void_p(0x50000000), ctypes.c_void_p(0x60000000)
+    p1 = kda.kda_plan_create([0, 64, 100], n_heads=2)
+    p2 = kda.kda_plan_create([0, 64, 100], n_heads=2, v_blocks=2)
+
+    def pre(plan=p1, gate=g, eps=1e-6, y_=y):
+        return L.kda_chunk_prefill_gated(plan.handle, ctypes.byref(ins), gate, w, eps, None, st, y_, None, 0, None,
+                                         ws, 1.0, 0, None)
+
+    assert pre(y_=None) == 1
+    assert pre(gate=None) == 1
+    assert pre(eps=-0.5) == 1
+    assert pre(plan=p2) == 2                                # half-row items cannot normalise a row
+    assert "value block" in kda.kda_last_error()
+    assert pre(y_=ctypes.c_void_p(0x30000000)) == 1         # y overlaps the gate
+    assert pre(y_=ctypes.c_void_p(0x60000000)) == 1         # y overlaps state_out
+
+
 def test_binding_checks_shapes_without_device():
     import torch
 

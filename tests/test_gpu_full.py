@@ -99,6 +99,44 @@ def test_prefill_4x2048_h64_all_units(gpu):
     assert max(worst.values()) <= TOL
 
 
+def test_prefill_gated_4x2048_h64(gpu):
+    """The headline prefill with the output gated RMSNorm fused in: y bit-identical to the plain prefill
+    followed by kda_gated_rmsnorm on all 524,288 (token, head) rows, the final states bit-identical, and
+    two heads of y against the oracle (fp64 prefill, then the norm) at the pages' 8e-3."""
+    c = synth.PREFILL_CONFIGS[1]
+    seed, lens, H, eps = c["seed"], c["lengths"], c["H"], 1e-6
+    cu = synth.cu_seqlens(lens)
+    T, N = int(cu[-1]), len(lens)
+    plan = kda.kda_plan_create(cu, n_heads=H)
+    ins = sg.prefill_inputs(seed, T, H, DEV)
+    gate = sg.gate(seed, T, H, DEV)
+    w = synth.norm_weight(seed)
+    wd = torch.from_numpy(w).to(DEV)
+    S0 = sg.states(seed, N * H, DEV).view(N, H, 128, 128)
+    ws = torch.empty(kda.kda_plan_workspace_bytes(plan), dtype=torch.uint8, device=DEV)
+    o = torch.empty((T, H, 128), device=DEV)
+    st = torch.empty((N, H, 128, 128), device=DEV)
+    kda.kda_chunk_prefill(plan, *ins, st, o, ws, state_in=S0)
+    y_ref = torch.empty((T, H, 128), dtype=torch.bfloat16, device=DEV)
+    kda.kda_gated_rmsnorm(o, gate, wd, eps, y_ref)
+    y = torch.empty((T, H, 128), dtype=torch.bfloat16, device=DEV)
+    st2 = torch.empty_like(st)
+    kda.kda_chunk_prefill_gated(plan, *ins, gate, wd, eps, st2, y, ws, state_in=S0)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), "fused norm differs from the unfused pair"
+    assert torch.equal(st2, st)
+    yb = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    worst = 0.0
+    for n, h in ((0, 0), (3, 63)):
+        t0 = int(cu[n])
+        o_ref, _, _, _ = oracle_prefill_unit(seed, H, t0, lens[n], h, S0=np_(S0[n, h]))
+        ref = oracle.gated_rmsnorm(o_ref, synth.gate_rows(seed, H, t0, lens[n], h=h), w, eps)
+        yv = (yb[t0:t0 + lens[n], h].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        worst = max(worst, float(np.max(np.max(np.abs(yv - ref), axis=1) / np.max(np.abs(ref), axis=1))))
+    log(f"gated prefill 4x2048 H64: worst row err {worst:.2e}")
+    assert worst <= 8e-3
+
+
 def test_prefill_varlen_h96_snapshots(gpu):
     H = 96
     lens = synth.prefill_lengths(2)

@@ -552,3 +552,94 @@ def test_prefill_exactness_properties(gpu):
     torch.cuda.synchronize()
     assert torch.equal(st7[0], st1[1]), "restored snapshot did not continue bit for bit"
     assert torch.equal(o7, o1[t0:t0 + 32])
+
+
+# ---------------------------------------------------------------- output gated RMSNorm
+TOL_NORM = 8e-3  # the pages' tolerance for the fast-math output norm (bf16 y, hardware exp/rcp/rsqrt)
+
+
+def bf16_dev(bits_u16):
+    return torch.from_numpy(np.ascontiguousarray(bits_u16).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def row_errs(y_bits, ref):
+    """Per row of 128: max |y - ref| / max |ref| (rows of ref that are exactly zero must come out zero)."""
+    y = (y_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(-1, 128)
+    ref = np.asarray(ref, dtype=np.float64).reshape(-1, 128)
+    den = np.max(np.abs(ref), axis=1)
+    err = np.max(np.abs(y - ref), axis=1)
+    assert np.all(err[den == 0] == 0)
+    return err[den > 0] / den[den > 0]
+
+
+def test_gated_rmsnorm_standalone(gpu):
+    """kda_gated_rmsnorm against the oracle: 37 rows (a partial block), magnitudes from 1e-3 to 1e3, a zero
+    row (eps > 0 sends it to zero), saturated gates, eps = 0 on the nonzero rows."""
+    rng = np.random.default_rng(21)
+    rows = 37
+    o = (rng.standard_normal((rows, 128)) * rng.uniform(1e-3, 1e3, (rows, 1))).astype(np.float32)
+    o[5] = 0.0
+    gx = rng.standard_normal((rows, 128)) * 2.0
+    gx[7], gx[8] = 30.0, -30.0
+    gx[9, :64] = 40.0
+    g_bits = synth.round_bf16(gx)
+    w = synth.norm_weight(3)
+    od, gd, wd = torch.from_numpy(o).to(DEV), bf16_dev(g_bits), torch.from_numpy(w).to(DEV)
+    log("gated rmsnorm: standalone")
+    for eps, sel in ((1e-6, np.arange(rows)), (0.0, np.delete(np.arange(rows), 5))):
+        y = torch.empty((rows, 128), dtype=torch.bfloat16, device=DEV)
+        kda.kda_gated_rmsnorm(od[sel].contiguous(), gd[sel].contiguous(), wd, eps, y[: len(sel)])
+        torch.cuda.synchronize()
+        ref = oracle.gated_rmsnorm(o[sel], g_bits[sel], w, eps)
+        errs = row_errs(bits(y[: len(sel)]).view(np.uint16), ref)
+        log(f"gated rmsnorm eps={eps}: worst row err {errs.max():.2e}")
+        assert errs.max() <= TOL_NORM
+
+
+def test_prefill_gated(gpu):
+    """kda_chunk_prefill_gated on a ragged batch (empty, 1-token and partial-chunk sequences, state_in,
+    snapshots): y bit-identical to kda_gated_rmsnorm applied to kda_chunk_prefill's o, the states and
+    snapshots bit-identical to kda_chunk_prefill's, and y against the oracle (fp64 prefill, then the norm)
+    on every (sequence, head); a two-value-block plan is refused."""
+    seed, H, eps = 29, 3, 1e-6
+    lens = [0, 1, 31, 33, 64, 100, 257]
+    cu = synth.cu_seqlens(lens)
+    T, N = int(cu[-1]), len(lens)
+    plan = kda.kda_plan_create(cu, n_heads=H, snap_interval=64)
+    ins = sg.prefill_inputs(seed, T, H, DEV)
+    gate = sg.gate(seed, T, H, DEV)
+    w = synth.norm_weight(seed)
+    wd = torch.from_numpy(w).to(DEV)
+    S0 = sg.states(seed, N * H, DEV).view(N, H, 128, 128)
+    log("gated prefill: plain prefill + standalone norm")
+    o, st, snap, cnt = run_prefill(plan, ins, state_in=S0, snap_slots=2, scale=0.8)
+    y_ref = torch.empty((T, H, 128), dtype=torch.bfloat16, device=DEV)
+    kda.kda_gated_rmsnorm(o, gate, wd, eps, y_ref)
+    log("gated prefill: fused")
+    y = torch.full((T, H, 128), 7.0, dtype=torch.bfloat16, device=DEV)
+    st2 = torch.empty_like(st)
+    snap2 = torch.full_like(snap, -5.0)
+    cnt2 = torch.full_like(cnt, -1)
+    ws = torch.empty(kda.kda_plan_workspace_bytes(plan), dtype=torch.uint8, device=DEV)
+    kda.kda_chunk_prefill_gated(plan, *ins, gate, wd, eps, st2, y, ws, state_in=S0, snap=snap2, snap_slots=2,
+                                snap_count=cnt2, scale=0.8)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(y), bits(y_ref)), "fused norm differs from prefill + kda_gated_rmsnorm"
+    assert torch.equal(st2, st) and torch.equal(snap2, snap) and torch.equal(cnt2, cnt)
+    yb = bits(y).view(np.uint16)
+    worst = 0.0
+    for n in range(N):
+        t0, L = int(cu[n]), lens[n]
+        if L == 0:
+            continue
+        for h in range(H):
+            o_ref, _, _, _ = oracle_prefill_unit(seed, H, t0, L, h, S0=np_(S0[n, h]), scale=0.8)
+            ref = oracle.gated_rmsnorm(o_ref, synth.gate_rows(seed, H, t0, L, h=h), w, eps)
+            worst = max(worst, float(row_errs(yb[t0:t0 + L, h], ref).max()))
+    log(f"gated prefill: worst row err {worst:.2e}")
+    assert worst <= TOL_NORM
+    split = kda.kda_plan_create(cu, n_heads=H, v_blocks=2)
+    with pytest.raises(kda.KdaError) as e:
+        kda.kda_chunk_prefill_gated(split, *ins, gate, wd, eps, st2, y, torch.empty(
+            kda.kda_plan_workspace_bytes(split), dtype=torch.uint8, device=DEV))
+    assert e.value.status == kda.KDA_ERR_UNSUPPORTED
