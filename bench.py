@@ -40,7 +40,7 @@ METRIC = "KDA prefill tokens*heads/s and verify+fold us/step at 1 GPU; % of roof
 # HBM bytes per prefill launch measured by rocprofv3 PMC (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, the
 # factors that make a plain 1 GiB copy read 1 GiB and write 1 GiB); set to None whenever the kernel
 # changes until it is measured again
-PREFILL_TRAFFIC_BYTES = 980_480_103
+PREFILL_TRAFFIC_BYTES = 980_824_721
 
 
 def parse():
