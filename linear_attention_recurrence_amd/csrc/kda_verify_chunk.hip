@@ -307,7 +307,9 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pk[n]), rk_rs, 2 * (pos * D + c4), 0, kStream);
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pv[n]), rv_rs, 2 * (pos * D + c4), 0, kStream);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pg[n]), rg_rs, 4 * (pos * D + c4), 0, kStream);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pb[n]), rb_rs, 4 * pos, 0, kStream);
+        // beta is one value per token: only the lane of channel 0 stores it (the others aim past the
+        // range and are dropped), instead of 32 lanes storing the same four bytes
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pb[n]), rb_rs, c4 == 0 ? 4 * pos : 0x7ffffff0, 0, kStream);
       }
     }
     // the next unit streams in while this one computes (past the last unit: this one again,
