@@ -42,8 +42,9 @@ def lib():
         L.kda_oracle_fold.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
         L.kda_oracle_chunked.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, vp, dbl, vp, vp]
         L.kda_oracle_gated_rmsnorm.argtypes = [i64, i32, vp, vp, vp, dbl, vp]
+        L.kda_oracle_prologue.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, dbl, vp, vp, vp, vp, vp, vp]
         for f in (L.kda_oracle_recurrent, L.kda_oracle_verify, L.kda_oracle_fold, L.kda_oracle_chunked,
-                  L.kda_oracle_gated_rmsnorm):
+                  L.kda_oracle_gated_rmsnorm, L.kda_oracle_prologue):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -145,6 +146,25 @@ def gated_rmsnorm(o, g, w, eps):
     if rc != 0:
         raise ValueError("kda_oracle_gated_rmsnorm rejected its arguments")
     return y
+
+
+def prologue(xq, xk, xv, conv_w, state_in, b_raw, g_raw, eps):
+    """The KDA prologue of one sequence: xq, xk, xv [L, H, 128]; conv_w [3, H*128, W]; state_in
+    [3, W-1, H*128]; b_raw [L, H]; g_raw [L, H, 128]. Returns q, k, v [L, H, 128], beta [L, H],
+    gk [L, H, 128] and state_out [3, W-1, H*128], all fp64."""
+    xq, xk, xv, conv_w, state_in, b_raw, g_raw = (f64(a) for a in (xq, xk, xv, conv_w, state_in, b_raw, g_raw))
+    L, H = xq.shape[0], xq.shape[1]
+    W = conv_w.shape[2]
+    if conv_w.shape != (3, H * 128, W) or state_in.shape != (3, W - 1, H * 128):
+        raise ValueError("prologue: conv_w must be [3, H*128, W] and state_in [3, W-1, H*128]")
+    q, k, v = (np.empty((L, H, 128)) for _ in range(3))
+    beta, gk = np.empty((L, H)), np.empty((L, H, 128))
+    state_out = np.empty((3, W - 1, H * 128))
+    rc = lib().kda_oracle_prologue(L, H, W, _p(xq), _p(xk), _p(xv), _p(conv_w), _p(state_in), _p(b_raw), _p(g_raw),
+                                   float(eps), _p(q), _p(k), _p(v), _p(beta), _p(gk), _p(state_out))
+    if rc != 0:
+        raise ValueError("kda_oracle_prologue rejected its arguments")
+    return q, k, v, beta, gk, state_out
 
 
 def run_parallel(fn, items, threads=None):

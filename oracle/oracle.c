@@ -280,3 +280,70 @@ int kda_oracle_gated_rmsnorm(int64_t rows, int V, const double* o, const double*
   }
   return 0;
 }
+
+/*
+ * The KDA prologue for one sequence of L tokens, H heads of 128 channels (HC = 128 H channels per
+ * row), conv width W (1..8):
+ *   for each of the three projections x = xq, xk, xv (rows [L][HC]), with the W - 1 rows before the
+ *   sequence taken from state_in ([3][W-1][HC], row W - 2 the latest):
+ *     c_t[ch] = sum_{j < W} w[ch][j] * x_{t - W + 1 + j}[ch]       causal depthwise convolution
+ *     u_t[ch] = c_t[ch] * sigmoid(c_t[ch])                          SiLU
+ *   q_t, k_t = u_t / sqrt(sum over the head's 128 channels of u_t^2 + eps)   (per head)
+ *   v_t      = u_t
+ *   beta_t[h]  = sigmoid(b_raw_t[h]),   gk_t[ch] = -log(1 + exp(g_raw_t[ch]))
+ *   state_out  = the last W - 1 rows of [state_in; x]   (per projection)
+ * Sources: Kimi K3 B200 deployment notes (zdszero.github.io), the prefill / decode kernel-fusion
+ * items: the three short conv1d calls on q, k and v with their SiLU and the conv-state carry become
+ * one kernel, and the beta copy + sigmoid another, both bit-exact to the unfused path. The notes give
+ * neither the conv width nor the decay-gate formula; the readings here: W is an argument (4 in the
+ * tests and the bench), q and k are L2-normalised per head after the SiLU (eps inside the root), and
+ * gk = -softplus(g_raw), the form under which exp(gk) = sigmoid(-g_raw) is a decay in (0, 1).
+ */
+int kda_oracle_prologue(int64_t L, int H, int W, const double* xq, const double* xk, const double* xv,
+                        const double* conv_w, const double* state_in, const double* b_raw, const double* g_raw,
+                        double eps, double* q, double* k, double* v, double* beta, double* gk, double* state_out) {
+  if (L < 0 || H < 1 || W < 1 || W > 8 || !(eps >= 0.0)) return 1;
+  const int64_t HC = (int64_t)H * 128;
+  const double* xs[3] = {xq, xk, xv};
+  double* outs[3] = {q, k, v};
+  double* u = (double*)malloc(sizeof(double) * (size_t)HC);
+  if (!u) return 2;
+  for (int which = 0; which < 3; ++which) {
+    const double* x = xs[which];
+    const double* w = conv_w + (int64_t)which * HC * W;
+    const double* st = state_in + (int64_t)which * (W - 1) * HC;
+    for (int64_t t = 0; t < L; ++t) {
+      for (int64_t ch = 0; ch < HC; ++ch) {
+        double c = 0.0;
+        for (int j = 0; j < W; ++j) {
+          const int64_t p = t - (W - 1) + j;  // position of tap j, < 0 inside the carried state
+          const double xv_ = p >= 0 ? x[p * HC + ch] : st[(p + (W - 1)) * HC + ch];
+          c += w[ch * W + j] * xv_;
+        }
+        u[ch] = c / (1.0 + exp(-c));
+      }
+      for (int h = 0; h < H; ++h) {
+        const double* uh = u + (int64_t)h * 128;
+        double* o = outs[which] + t * HC + (int64_t)h * 128;
+        if (which < 2) {
+          double ss = 0.0;
+          for (int j = 0; j < 128; ++j) ss += uh[j] * uh[j];
+          const double inv = 1.0 / sqrt(ss + eps);
+          for (int j = 0; j < 128; ++j) o[j] = uh[j] * inv;
+        } else {
+          for (int j = 0; j < 128; ++j) o[j] = uh[j];
+        }
+      }
+    }
+    double* so = state_out + (int64_t)which * (W - 1) * HC;
+    for (int r = 0; r < W - 1; ++r) {
+      const int64_t p = L - (W - 1) + r;
+      for (int64_t ch = 0; ch < HC; ++ch) so[r * HC + ch] = p >= 0 ? x[p * HC + ch] : st[(p + (W - 1)) * HC + ch];
+    }
+  }
+  for (int64_t t = 0; t < L; ++t)
+    for (int h = 0; h < H; ++h) beta[t * H + h] = 1.0 / (1.0 + exp(-b_raw[t * H + h]));
+  for (int64_t i = 0; i < L * HC; ++i) gk[i] = -log1p(exp(g_raw[i]));
+  free(u);
+  return 0;
+}

@@ -296,3 +296,93 @@ def test_gated_rmsnorm_eps():
     assert np.allclose(oracle.gated_rmsnorm(o, g, w, ms), y0 / math.sqrt(2.0), rtol=1e-14, atol=0)
     big = 1e12
     assert np.allclose(oracle.gated_rmsnorm(o, g, w, big), o / math.sqrt(big), rtol=1e-9, atol=0)
+
+
+# ---------------------------------------------------------------- the KDA prologue
+# The pages name the fused operations (short conv on q/k/v with SiLU and the conv-state carry, beta's
+# sigmoid) but give neither the conv width nor the decay-gate formula; these pin the oracle's reading:
+# a causal depthwise conv whose tap j reads token t - W + 1 + j, SiLU, per-head L2 norm of q and k,
+# beta = sigmoid, gk = -softplus, and a state that carries the last W - 1 raw rows.
+
+def _prologue_case(rng, L, H, W, w=None):
+    x = [rng.standard_normal((L, H, 128)) for _ in range(3)]
+    cw = rng.standard_normal((3, H * 128, W)) if w is None else np.broadcast_to(w, (3, H * 128, W)).copy()
+    st = rng.standard_normal((3, W - 1, H * 128))
+    b, g = rng.standard_normal((L, H)), rng.standard_normal((L, H, 128))
+    return x, cw, st, b, g
+
+
+def test_prologue_taps_and_state():
+    """Tap W-1 is the current token, tap 0 the token W-1 back (taken from the carried state for the
+    first tokens); a reversed or shifted convolution fails one of the two."""
+    rng = np.random.default_rng(31)
+    L, H, W = 6, 1, 4
+    silu = lambda c: c / (1.0 + np.exp(-c))
+    x, _, st, b, g = _prologue_case(rng, L, H, W)
+    now = np.zeros(W); now[W - 1] = 1.0
+    _, _, v, _, _, _ = oracle.prologue(*x, np.broadcast_to(now, (3, 128, W)).copy(), st, b, g, 0.0)
+    assert np.allclose(v, silu(x[2]), rtol=1e-14, atol=0)  # (numpy's exp and libm's may differ in the last bit)
+    old = np.zeros(W); old[0] = 1.0
+    _, _, v, _, _, _ = oracle.prologue(*x, np.broadcast_to(old, (3, 128, W)).copy(), st, b, g, 0.0)
+    xv = x[2].reshape(L, 128)
+    for t in range(L):
+        src = xv[t - (W - 1)] if t >= W - 1 else st[2, t]  # state row t holds token t - (W - 1)
+        assert np.allclose(v[t].reshape(128), silu(src), rtol=1e-14, atol=0)
+
+
+def test_prologue_conv_sums_taps():
+    """Weights (1, -1) on the two newest taps of a sequence that is constant in time (state included)
+    give a zero pre-activation, so SiLU(0) = 0 exactly; changing one state row breaks it only where that
+    row is read."""
+    rng = np.random.default_rng(32)
+    L, H, W = 5, 1, 3
+    x, _, st, b, g = _prologue_case(rng, L, H, W)
+    row = rng.standard_normal(128)
+    xs = [np.broadcast_to(row, (L, 1, 128)).copy() for _ in range(3)]
+    sts = np.broadcast_to(row, (3, W - 1, 128)).copy()
+    w = np.array([0.0, -1.0, 1.0])
+    _, _, v, _, _, _ = oracle.prologue(*xs, np.broadcast_to(w, (3, 128, W)).copy(), sts, b, g, 0.0)
+    assert np.all(v == 0.0)
+    sts[2, W - 2] += 1.0  # the newest carried row: read only by token 0's middle tap
+    _, _, v, _, _, _ = oracle.prologue(*xs, np.broadcast_to(w, (3, 128, W)).copy(), sts, b, g, 0.0)
+    assert np.all(v[0] != 0.0) and np.all(v[1:] == 0.0)
+
+
+def test_prologue_norms_and_gates():
+    """q and k come out with unit norm per (token, head) at eps = 0, v is not normalised; beta is the
+    logistic sigmoid of its logit (1/2 at 0, 3/4 at ln 3) and exp(gk) = sigmoid(-g_raw), so gk <= 0."""
+    rng = np.random.default_rng(33)
+    L, H, W = 7, 3, 4
+    x, cw, st, b, g = _prologue_case(rng, L, H, W)
+    b[0, 0], b[0, 1] = 0.0, math.log(3.0)
+    g[0, 0, :2] = (0.0, math.log(3.0))
+    q, k, v, beta, gk, _ = oracle.prologue(*x, cw, st, b, g, 0.0)
+    assert np.allclose(np.linalg.norm(q, axis=2), 1.0, rtol=0, atol=1e-14)
+    assert np.allclose(np.linalg.norm(k, axis=2), 1.0, rtol=0, atol=1e-14)
+    assert not np.allclose(np.linalg.norm(v, axis=2), 1.0)
+    assert beta[0, 0] == 0.5 and abs(beta[0, 1] - 0.75) < 1e-15
+    assert abs(gk[0, 0, 0] + math.log(2.0)) < 1e-15 and abs(gk[0, 0, 1] + math.log(4.0)) < 1e-15
+    assert np.all(gk <= 0) and np.allclose(np.exp(gk), 1.0 / (1.0 + np.exp(g)), rtol=1e-14, atol=0)
+    # eps sits inside the root, added to the sum of squares: eps = |u|^2 of a row shrinks it by 1/sqrt(2)
+    uk = k[2, 1]  # the unit row at eps = 0
+    _, _, vk, _, _, _ = oracle.prologue(x[1], x[1], x[1], cw[[1, 1, 1]], st[[1, 1, 1]], b, g, 0.0)
+    ek = float(np.sum(vk[2, 1] ** 2))  # |u|^2 of k's row
+    _, k3, _, _, _, _ = oracle.prologue(*x, cw, st, b, g, ek)
+    assert np.allclose(k3[2, 1], uk / math.sqrt(2.0), rtol=1e-13, atol=0)
+
+
+def test_prologue_state_carry():
+    """Running a sequence in two calls, the first call's state_out feeding the second, gives the same
+    outputs and final state as one call (all W in 1..5, split points inside the first W - 1 tokens)."""
+    rng = np.random.default_rng(34)
+    for W in (1, 2, 3, 4, 5):
+        L, H = 9, 2
+        x, cw, st, b, g = _prologue_case(rng, L, H, W)
+        full = oracle.prologue(*x, cw, st, b, g, 1e-6)
+        for m in (0, 1, W - 1, 5, L):
+            m = max(0, min(L, m))
+            a = oracle.prologue(*(t[:m] for t in x), cw, st, b[:m], g[:m], 1e-6)
+            c = oracle.prologue(*(t[m:] for t in x), cw, a[5], b[m:], g[m:], 1e-6)
+            for i in range(5):
+                assert np.array_equal(np.concatenate([a[i], c[i]]), full[i])
+            assert np.array_equal(c[5], full[5])
