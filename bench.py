@@ -16,6 +16,8 @@ events on the launch stream. Beside it, in the same JSON line:
 * ``prefill_gated_norm``: the same prefill with the output gated RMSNorm,
   fused into its epilogue (kda_chunk_prefill_gated) and unfused (the prefill,
   then kda_gated_rmsnorm over its fp32 output);
+* ``prologue``: the step before the recurrence (kda_prologue) over the same
+  tokens, in us and GB/s;
 * ``roofline``: HBM roofline of the prefill kernel (algorithmic bytes per
   launch / measured launch time, against 8 TB/s);
 * ``cpu_baseline``: the fp64 oracle (token-by-token) timed on this host's
@@ -170,6 +172,48 @@ def bench_prefill_gated(args, torch, kda, sg, synth):
     del q, k, v, gk, beta, gate, o, y, st, S0
     return dict(fused_ms=res["fused"], unfused_ms=res["unfused"], fused_bytes=fused_b, unfused_bytes=unfused_b,
                 tokens_heads=th)
+
+
+def bench_prologue(args, torch, kda, sg, synth):
+    """The KDA prologue (short conv width 4 + SiLU with the state carry, q/k L2 norm, beta sigmoid,
+    gk = -softplus) over the headline prefill's tokens: one kda_prologue launch."""
+    import numpy as np
+
+    dev = "cuda:0"
+    N, L, H, W = 4, 2048, 64, 4
+    seed = synth.PREFILL_CONFIGS[1]["seed"]
+    cu = torch.from_numpy(synth.cu_seqlens([L] * N).astype(np.int32)).to(dev)
+    T = N * L
+    g = torch.Generator(device=dev).manual_seed(seed)
+    xs = [torch.randn((T, H, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(3)]
+    conv_w = 0.5 * torch.randn((3, H * 128, W), generator=g, device=dev)
+    st_in = torch.randn((N, 3, W - 1, H * 128), generator=g, device=dev).to(torch.bfloat16)
+    st_out = torch.empty_like(st_in)
+    b_raw = torch.randn((T, H), generator=g, device=dev)
+    g_raw = torch.randn((T, H, 128), generator=g, device=dev)
+    outs = [torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    beta, gk = torch.empty((T, H), device=dev), torch.empty((T, H, 128), device=dev)
+
+    def step():
+        kda.kda_prologue(cu, *xs, conv_w, b_raw, g_raw, *outs, beta, gk, conv_state_in=st_in, conv_state_out=st_out)
+
+    settle(step, torch)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # per token*head: x_q, x_k, x_v bf16 in (768) + g_raw (512) + b_raw (4); q, k, v bf16 out (768) + gk (512)
+    # + beta (4) = 2,568 B; plus the carried state in and out
+    byts = T * H * 2568 + 2 * N * 3 * (W - 1) * H * 128 * 2
+    del xs, conv_w, st_in, st_out, b_raw, g_raw, outs, beta, gk
+    return dict(ms=ms, bytes=byts, gbs=byts / (ms * 1e-3) / 1e9)
 
 
 def bench_verify_fold(args, torch, kda, sg, synth):
@@ -341,6 +385,10 @@ def main():
     if not args.prefill_only:
         log("prefill with the output gated RMSNorm: fused and unfused")
         pg = bench_prefill_gated(args, torch, kda, sg, synth)
+    pro = None
+    if not args.prefill_only:
+        log("prologue")
+        pro = bench_prologue(args, torch, kda, sg, synth)
     vf = None
     if not (args.no_verify_fold or args.prefill_only):
         log("verify+fold: generating inputs and timing")
@@ -391,6 +439,13 @@ def main():
             "workload": "the headline prefill followed by the output gated RMSNorm (gate N(0,1) bf16, weights "
                         "1 + 0.1 N(0,1), eps 1e-6, bf16 y): kda_chunk_prefill_gated vs kda_chunk_prefill + "
                         "kda_gated_rmsnorm",
+        }
+    if pro is not None:
+        line["prologue"] = {
+            "us": pro["ms"] * 1e3, "gbs": pro["gbs"], "hbm_frac": pro["gbs"] / HBM_PEAK_GBS,
+            "workload": "kda_prologue over the headline prefill's 8,192 tokens x 64 heads: conv width 4 with the "
+                        "state carried in and out, SiLU, q/k L2 norm, beta sigmoid, gk = -softplus (2,568 B per "
+                        "token*head)",
         }
     if vf is not None:
         line["verify_fold"] = {

@@ -257,6 +257,46 @@ kda_status kda_chunk_prefill_gated(const kda_plan* plan, const kda_inputs* in, c
 kda_status kda_gated_rmsnorm(int64_t rows, const float* o, const void* gate, const float* norm_w, float eps,
                              void* y, void* stream);
 
+/*
+ * The KDA prologue, the step before the recurrence, in one launch [B200-NORM]
+ * (same kernel-fusion items: the three short conv1d calls with their SiLU and
+ * the conv-state carry fused, beta's sigmoid fused). For a THD-packed batch of
+ * n_seq sequences (token ranges from cu_seqlens), H heads of 128 channels
+ * (HC = 128 H per row) and conv width W, for each projection x in (xq, xk, xv):
+ *   c_t[ch] = sum_{j < W} conv_w[x][ch][j] * x_{t - W + 1 + j}[ch]
+ *             (the W - 1 tokens before a sequence come from conv_state_in)
+ *   u_t     = c_t * sigmoid(c_t)                                    (SiLU)
+ *   q_t, k_t = u_t / sqrt(sum over the head's 128 channels of u_t^2 + eps)
+ *   v_t      = u_t
+ * and beta = sigmoid(b_raw), gk = -log(1 + exp(g_raw)). The width and the
+ * gate's form are readings (the notes give neither): exp(gk) = sigmoid(-g_raw)
+ * is a decay in (0, 1), the input kda_chunk_prefill and kda_verify take.
+ *
+ *  n_seq, total_tokens, n_heads : N, T, H.   conv_width : W in 1..8.
+ *  cu_seqlens     : device int32 [N + 1], cu[0] = 0, nondecreasing, cu[N] = T;
+ *                   read clamped, so no value of it addresses memory outside
+ *                   the buffers here.
+ *  xq, xk, xv     : bf16 [T, H, 128].        conv_w : fp32 [3, HC, W].
+ *  conv_state_in  : bf16 [N, 3, W - 1, HC] (row W - 2 the latest token) or
+ *                   NULL (zeros: fresh sequences).
+ *  conv_state_out : same layout, or NULL (not written): the last W - 1 rows of
+ *                   each sequence (older state rows for a sequence shorter
+ *                   than W - 1). It may not overlap conv_state_in.
+ *  b_raw : fp32 [T, H].  g_raw : fp32 [T, H, 128].  eps : finite, >= 0.
+ *  q, k, v : bf16 [T, H, 128] (nearest even).  beta : fp32 [T, H].
+ *  gk : fp32 [T, H, 128].  No output may overlap an input or another output.
+ *  xq, xk, xv, conv_w, conv_state_in/out, g_raw, q, k, v and gk must be 16-byte
+ *  aligned.
+ * SiLU, sigmoid and the norm's 1/sqrt use the hardware exp2, reciprocal and
+ * reciprocal square root (bf16 outputs); gk is accurate to a few fp32 ulps.
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_DEVICE.
+ */
+kda_status kda_prologue(int n_seq, int64_t total_tokens, int n_heads, int conv_width,
+                        const int32_t* cu_seqlens, const void* xq, const void* xk, const void* xv,
+                        const float* conv_w, const void* conv_state_in, void* conv_state_out,
+                        const float* b_raw, const float* g_raw, float eps, void* q, void* k, void* v,
+                        float* beta, float* gk, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Per-slot raw-input ring [LMSYS-RSSM], [B200-RING]: for each (slot, layer,
  * head), len entries of (v, k, gk, beta), 1,028 bytes per entry.

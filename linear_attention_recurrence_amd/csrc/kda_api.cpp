@@ -501,6 +501,63 @@ kda_status kda_verify_ragged(int batch, int max_tok, int total_tok, int n_heads,
   return ok();
 }
 
+kda_status kda_prologue(int n_seq, int64_t total_tokens, int n_heads, int conv_width, const int32_t* cu_seqlens,
+                        const void* xq, const void* xk, const void* xv, const float* conv_w, const void* conv_state_in,
+                        void* conv_state_out, const float* b_raw, const float* g_raw, float eps, void* q, void* k,
+                        void* v, float* beta, float* gk, void* stream) {
+  if (n_seq < 0 || total_tokens < 0 || n_heads < 1 || conv_width < 1 || conv_width > 8)
+    return fail(KDA_ERR_INVALID_ARG, "kda_prologue: bad n_seq/total_tokens/n_heads/conv_width");
+  if (!(eps >= 0.f && eps < INFINITY)) return fail(KDA_ERR_INVALID_ARG, "kda_prologue: eps must be finite and >= 0");
+  if (total_tokens > 0 && n_seq < 1) return fail(KDA_ERR_INVALID_ARG, "kda_prologue: tokens without sequences");
+  if (total_tokens * n_heads > ((int64_t)1 << 33)) return fail(KDA_ERR_INVALID_ARG, "kda_prologue: too large");
+  if (n_seq == 0) return ok();
+  if (!cu_seqlens || !conv_w) return fail(KDA_ERR_INVALID_ARG, "kda_prologue: cu_seqlens and conv_w are required");
+  if (total_tokens > 0 && (!xq || !xk || !xv || !b_raw || !g_raw || !q || !k || !v || !beta || !gk))
+    return fail(KDA_ERR_INVALID_ARG, "kda_prologue: the projections, logits and outputs are required");
+  {
+    const void* al[11] = {xq, xk, xv, conv_w, conv_state_in, conv_state_out, g_raw, q, k, v, gk};
+    for (const void* p : al)
+      if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return fail(KDA_ERR_INVALID_ARG, "kda_prologue: a row buffer is not 16-byte aligned");
+  }
+  const size_t rows = (size_t)total_tokens * n_heads;
+  const size_t xb = rows * KDA_HEAD_DIM * 2, gb = rows * KDA_HEAD_DIM * 4, bb = rows * 4;
+  const size_t stb = (size_t)n_seq * 3 * (conv_width - 1) * n_heads * KDA_HEAD_DIM * 2;
+  const size_t wb = (size_t)3 * n_heads * KDA_HEAD_DIM * conv_width * 4;
+  const void* ins[8] = {xq, xk, xv, conv_w, conv_state_in, b_raw, g_raw, cu_seqlens};
+  const size_t insz[8] = {xb, xb, xb, wb, stb, bb, gb, ((size_t)n_seq + 1) * 4};
+  const void* outs[6] = {q, k, v, beta, gk, conv_state_out};
+  const size_t outsz[6] = {xb, xb, xb, bb, gb, stb};
+  for (int o = 0; o < 6; ++o) {
+    for (int i = 0; i < 8; ++i)
+      if (overlap(outs[o], outsz[o], ins[i], insz[i])) return fail(KDA_ERR_INVALID_ARG, "kda_prologue: an output overlaps an input");
+    for (int o2 = o + 1; o2 < 6; ++o2)
+      if (overlap(outs[o], outsz[o], outs[o2], outsz[o2])) return fail(KDA_ERR_INVALID_ARG, "kda_prologue: two outputs overlap");
+  }
+  kda::PrologueArgs a{};
+  a.n_seq = n_seq;
+  a.n_heads = n_heads;
+  a.conv_width = conv_width;
+  a.total_tokens = total_tokens;
+  a.cu_seqlens = cu_seqlens;
+  a.xq = static_cast<const uint16_t*>(xq);
+  a.xk = static_cast<const uint16_t*>(xk);
+  a.xv = static_cast<const uint16_t*>(xv);
+  a.conv_w = conv_w;
+  a.state_in = conv_width > 1 ? static_cast<const uint16_t*>(conv_state_in) : nullptr;
+  a.state_out = conv_width > 1 ? static_cast<uint16_t*>(conv_state_out) : nullptr;
+  a.b_raw = b_raw;
+  a.g_raw = g_raw;
+  a.eps = eps;
+  a.q = static_cast<uint16_t*>(q);
+  a.k = static_cast<uint16_t*>(k);
+  a.v = static_cast<uint16_t*>(v);
+  a.beta = beta;
+  a.gk = gk;
+  const hipError_t e = kda::launch_prologue(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail("kda_prologue: launch", e);
+  return ok();
+}
+
 kda_status kda_replay_fold(int batch, int n_heads, int n_layers, int n_slots, float* state_pool, const int32_t* slot_idx,
                            const kda_ring* ring, const int32_t* ring_start, const int32_t* accepted_len, void* stream) {
   if (batch < 0 || n_heads < 1 || n_layers < 1 || n_slots < 1)

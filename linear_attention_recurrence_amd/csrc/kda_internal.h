@@ -82,6 +82,28 @@ struct PrefillArgs {
   uint16_t* y;           // bf16 [T, H, 128]
 };
 
+// the KDA prologue: short conv + SiLU (+ L2 norm for q, k), beta sigmoid, gk = -softplus
+struct PrologueArgs {
+  int n_seq, n_heads, conv_width;
+  int64_t total_tokens;
+  const int32_t* cu_seqlens;  // [n_seq + 1], read clamped
+  const uint16_t* xq;         // bf16 [T, H, 128] projections
+  const uint16_t* xk;
+  const uint16_t* xv;
+  const float* conv_w;        // fp32 [3, H * 128, W]
+  const uint16_t* state_in;   // bf16 [n_seq, 3, W - 1, H * 128] or nullptr (zeros)
+  uint16_t* state_out;        // same layout or nullptr (not written)
+  const float* b_raw;         // fp32 [T, H]
+  const float* g_raw;         // fp32 [T, H, 128]
+  float eps;
+  uint16_t* q;                // bf16 [T, H, 128]
+  uint16_t* k;
+  uint16_t* v;
+  float* beta;                // fp32 [T, H]
+  float* gk;                  // fp32 [T, H, 128]
+};
+hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream);
+
 hipError_t launch_verify(const VerifyArgs& a, bool f32_inputs, hipStream_t stream);
 // the output gated RMSNorm on its own: rows of 128 fp32 values -> bf16
 hipError_t launch_gated_rmsnorm(int64_t rows, const float* o, const uint16_t* gate, const float* w, float eps,

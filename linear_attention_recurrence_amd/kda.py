@@ -31,8 +31,8 @@ KDA_CHUNK = 32
 
 EXPORTS = ("kda_abi_version", "kda_last_error", "kda_plan_create", "kda_plan_create_ex", "kda_plan_v_blocks",
            "kda_plan_workspace_bytes", "kda_plan_num_items", "kda_plan_items", "kda_plan_upload", "kda_plan_destroy",
-           "kda_chunk_prefill", "kda_chunk_prefill_gated", "kda_gated_rmsnorm", "kda_verify", "kda_replay_fold",
-           "kda_fold_verify", "kda_verify_ragged")
+           "kda_chunk_prefill", "kda_chunk_prefill_gated", "kda_gated_rmsnorm", "kda_prologue", "kda_verify",
+           "kda_replay_fold", "kda_fold_verify", "kda_verify_ragged")
 
 
 class KdaError(RuntimeError):
@@ -80,6 +80,8 @@ def lib():
         L.kda_chunk_prefill_gated.argtypes = [vp, ctypes.POINTER(_Inputs), vp, vp, f32, vp, vp, vp, vp, i32, vp, vp,
                                               f32, i32, vp]
         L.kda_gated_rmsnorm.argtypes = [ctypes.c_int64, vp, vp, vp, f32, vp, vp]
+        L.kda_prologue.argtypes = [i32, ctypes.c_int64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp,
+                                   vp, vp, vp]
         L.kda_verify.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(_Inputs), vp, vp, vp,
                                  ctypes.POINTER(_Ring), vp, vp, vp, f32, vp]
         L.kda_replay_fold.argtypes = [i32, i32, i32, i32, vp, vp, ctypes.POINTER(_Ring), vp, vp, vp]
@@ -88,8 +90,8 @@ def lib():
         L.kda_verify_ragged.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(_Inputs), vp, vp, vp, vp,
                                         ctypes.POINTER(_Ring), vp, f32, vp]
         for f in ("kda_plan_create", "kda_plan_create_ex", "kda_plan_items", "kda_plan_upload", "kda_chunk_prefill",
-                  "kda_chunk_prefill_gated", "kda_gated_rmsnorm", "kda_verify", "kda_replay_fold", "kda_fold_verify",
-                  "kda_verify_ragged"):
+                  "kda_chunk_prefill_gated", "kda_gated_rmsnorm", "kda_prologue", "kda_verify", "kda_replay_fold",
+                  "kda_fold_verify", "kda_verify_ragged"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -240,6 +242,29 @@ def kda_gated_rmsnorm(o, gate, norm_w, eps, y, stream=None):
     _need(norm_w, "norm_w", (Dh,), _F32)
     _check(lib().kda_gated_rmsnorm(o.numel() // Dh, _ptr(o), _ptr(gate), _ptr(norm_w), float(eps), _ptr(y),
                                    _stream(stream)))
+
+
+def kda_prologue(cu_seqlens, xq, xk, xv, conv_w, b_raw, g_raw, q, k, v, beta, gk, conv_state_in=None,
+                 conv_state_out=None, eps=1e-6, stream=None):
+    """The KDA prologue in one launch (see kda_prologue in include/kda.h): short conv + SiLU of the q/k/v
+    projections with the conv-state carry, per-head L2 norm of q and k, beta = sigmoid, gk = -softplus.
+    cu_seqlens is a device int32 tensor of n_seq + 1 prefix sums."""
+    T, H, Dh = xq.shape[0], xq.shape[1], KDA_HEAD_DIM
+    N = cu_seqlens.shape[0] - 1
+    W = conv_w.shape[-1]
+    for name, t in (("xq", xq), ("xk", xk), ("xv", xv), ("q", q), ("k", k), ("v", v)):
+        _need(t, name, (T, H, Dh), _BF)
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), _I32)
+    _need(conv_w, "conv_w", (3, H * Dh, W), _F32)
+    _need(b_raw, "b_raw", (T, H), _F32)
+    _need(beta, "beta", (T, H), _F32)
+    _need(g_raw, "g_raw", (T, H, Dh), _F32)
+    _need(gk, "gk", (T, H, Dh), _F32)
+    _need(conv_state_in, "conv_state_in", (N, 3, W - 1, H * Dh), _BF, allow_none=True)
+    _need(conv_state_out, "conv_state_out", (N, 3, W - 1, H * Dh), _BF, allow_none=True)
+    _check(lib().kda_prologue(N, T, H, W, _ptr(cu_seqlens), _ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_w),
+                              _ptr(conv_state_in), _ptr(conv_state_out), _ptr(b_raw), _ptr(g_raw), float(eps), _ptr(q),
+                              _ptr(k), _ptr(v), _ptr(beta), _ptr(gk), _stream(stream)))
 
 
 class Ring:

@@ -248,6 +248,27 @@ def test_gated_rejects_bad_arguments():
     assert pre(y_=ctypes.c_void_p(0x60000000)) == 1         # y overlaps state_out
 
 
+def test_prologue_rejects_bad_arguments():
+    L = kda.lib()
+    P = [ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(13)]
+    cu, xq, xk, xv, w, sin, sout, b, g, q, k, v, beta = P
+    gk = ctypes.c_void_p(0xE0000000)
+
+    def call(N=2, T=10, H=2, W=4, eps=1e-6, sin_=sin, sout_=sout, q_=q, cu_=cu):
+        return L.kda_prologue(N, T, H, W, cu_, xq, xk, xv, w, sin_, sout_, b, g, eps, q_, k, v, beta, gk, None)
+
+    assert call(W=0) == 1 and call(W=9) == 1      # conv width 1..8
+    assert call(H=0) == 1 and call(T=-1) == 1
+    assert call(N=0) == 1                          # tokens without sequences
+    assert call(eps=-1.0) == 1
+    assert call(cu_=None) == 1
+    assert call(q_=None) == 1
+    assert call(sout_=ctypes.c_void_p(0x60000000 + 16)) == 1  # the carried state is not updated in place
+    assert call(q_=ctypes.c_void_p(0xA0000000 + 8)) == 1      # row buffers are 16-byte aligned
+    assert call(q_=ctypes.c_void_p(0x20000000)) == 1          # q overlaps xq
+    assert call(N=0, T=0) == 0                                # nothing to do
+
+
 def test_binding_checks_shapes_without_device():
     import torch
 

@@ -643,3 +643,82 @@ def test_prefill_gated(gpu):
         kda.kda_chunk_prefill_gated(split, *ins, gate, wd, eps, st2, y, torch.empty(
             kda.kda_plan_workspace_bytes(split), dtype=torch.uint8, device=DEV))
     assert e.value.status == kda.KDA_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- the KDA prologue
+def _prologue_inputs(rng, T, N, H, W):
+    xs = [synth.round_bf16(rng.standard_normal((T, H, 128))) for _ in range(3)]
+    conv_w = (0.5 * rng.standard_normal((3, H * 128, W))).astype(np.float32)
+    st = synth.round_bf16(rng.standard_normal((N, 3, max(W - 1, 0), H * 128)))
+    b = rng.standard_normal((T, H)).astype(np.float32)
+    g = (2.0 * rng.standard_normal((T, H, 128))).astype(np.float32)
+    return xs, conv_w, st, b, g
+
+
+def _run_prologue(cu, xs, conv_w, st, b, g, eps, with_state=True):
+    T, H = xs[0].shape[0], xs[0].shape[1]
+    N, W = len(cu) - 1, conv_w.shape[2]
+    dev = [bf16_dev(x) for x in xs]
+    outs = [torch.full((T, H, 128), 3.0, dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    beta = torch.full((T, H), -1.0, device=DEV)
+    gk = torch.full((T, H, 128), 1.0, device=DEV)
+    sin = bf16_dev(st) if with_state else None
+    sout = torch.full((N, 3, W - 1, H * 128), 5.0, dtype=torch.bfloat16, device=DEV)
+    kda.kda_prologue(torch.from_numpy(np.asarray(cu, dtype=np.int32)).to(DEV), *dev,
+                     torch.from_numpy(conv_w).to(DEV), torch.from_numpy(b).to(DEV), torch.from_numpy(g).to(DEV),
+                     *outs, beta, gk, conv_state_in=sin, conv_state_out=sout, eps=eps)
+    torch.cuda.synchronize()
+    return [bits(o).view(np.uint16) for o in outs], np_(beta), np_(gk), bits(sout).view(np.uint16)
+
+
+@pytest.mark.parametrize("W", [4, 1, 2, 8])
+def test_prologue(gpu, W):
+    """kda_prologue on a ragged batch (lengths 0, 1, 2, 5, 40, 100 around the conv width) against the
+    oracle per sequence: q, k, v per row at bf16 accuracy, beta and gk elementwise, the carried state bit
+    for bit; without an incoming state it equals a zero state; a batch split in two calls, the first
+    call's state feeding the second, gives the same bits as one call."""
+    rng = np.random.default_rng(40 + W)
+    H, eps = 3, 1e-6
+    lens = [0, 1, 2, 5, 40, 100]
+    cu = synth.cu_seqlens(lens)
+    T, N = int(cu[-1]), len(lens)
+    xs, conv_w, st, b, g = _prologue_inputs(rng, T, N, H, W)
+    log(f"prologue W={W}")
+    (q, k, v), beta, gk, sout = _run_prologue(cu, xs, conv_w, st, b, g, eps)
+    worst = {"qkv": 0.0, "beta": 0.0, "gk": 0.0}
+    for n in range(N):
+        s0, L = int(cu[n]), lens[n]
+        st_n = (st[n].astype(np.uint32) << 16).view(np.float32)  # the bf16 state rows, widened exactly
+        ref = oracle.prologue(*(x[s0:s0 + L] for x in xs), conv_w, st_n, b[s0:s0 + L], g[s0:s0 + L], eps)
+        for got, r in zip((q, k, v), ref[:3]):
+            if L:
+                worst["qkv"] = max(worst["qkv"], float(row_errs(got[s0:s0 + L], r).max()))
+        if L:
+            worst["beta"] = max(worst["beta"], float(np.max(np.abs(beta[s0:s0 + L] - ref[3]) / np.abs(ref[3]))))
+            worst["gk"] = max(worst["gk"], float(np.max(np.abs(gk[s0:s0 + L] - ref[4]) / np.abs(ref[4]))))
+        if W > 1:
+            assert np.array_equal((sout[n].astype(np.uint32) << 16).view(np.float32), ref[5].astype(np.float32))
+    log(f"prologue W={W}: worst {worst}")
+    assert worst["qkv"] <= 5e-3 and worst["beta"] <= 1e-5 and worst["gk"] <= 1e-5
+    # no incoming state = a zero state
+    zero = np.zeros_like(st)
+    a = _run_prologue(cu, xs, conv_w, st, b, g, eps, with_state=False)
+    z = _run_prologue(cu, xs, conv_w, zero, b, g, eps)
+    for x_, y_ in zip(a[0] + [a[3]], z[0] + [z[3]]):
+        assert np.array_equal(x_, y_)
+    # the batch in two calls with the state carried: sequence n's tokens split at m_n
+    if W > 1:
+        cut = [min(L, 3) for L in lens]
+        first = [[x[int(cu[n]):int(cu[n]) + cut[n]] for n in range(N)] for x in xs]
+        second = [[x[int(cu[n]) + cut[n]:int(cu[n + 1])] for n in range(N)] for x in xs]
+        pick = lambda arr, parts: np.concatenate([arr[int(cu[n]) + lo:int(cu[n]) + hi] for n, (lo, hi) in enumerate(parts)])
+        p1 = [(0, cut[n]) for n in range(N)]
+        p2 = [(cut[n], lens[n]) for n in range(N)]
+        c1, c2 = synth.cu_seqlens([c for c in cut]), synth.cu_seqlens([L - c for L, c in zip(lens, cut)])
+        r1 = _run_prologue(c1, [np.concatenate(f) for f in first], conv_w, st, pick(b, p1), pick(g, p1), eps)
+        r2 = _run_prologue(c2, [np.concatenate(f) for f in second], conv_w, r1[3], pick(b, p2), pick(g, p2), eps)
+        for i in range(3):
+            joined = np.concatenate([np.concatenate([r1[0][i][int(c1[n]):int(c1[n + 1])], r2[0][i][int(c2[n]):int(c2[n + 1])]])
+                                     for n in range(N)])
+            assert np.array_equal(joined, (q, k, v)[i])
+        assert np.array_equal(r2[3], sout)
