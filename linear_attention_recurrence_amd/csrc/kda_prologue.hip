@@ -18,24 +18,33 @@ namespace kda {
 
 namespace {
 
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// two floats to a bf16 pair, nearest even (one v_cvt_pk_bf16_f32 on gfx950), the first in the low half
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, bf16x2v));
+}
+
 // SiLU and the sigmoid through the hardware exp2 and reciprocal (the outputs are bf16, so their ~1 ulp
 // errors vanish in the rounding); gk through an accurate form, since it feeds the recurrence's decay
 __device__ __forceinline__ float sigmoid_fast(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
 }
-// -softplus(g) = -(max(g, 0) + log(1 + x)) with x = e^-|g| in (0, 1]: log(1 + x) by the first six terms
-// of its series while x < 1/64 (error below x^7 / 7), else as log(u) x / (u - 1) with u = fl(1 + x), which
-// cancels the rounding of 1 + x (u - 1 is exact)
+// -softplus(g) = -(max(g, 0) + log(1 + x)) with x = e^-|g| in (0, 1]. log(1 + x) = 2 atanh(s) with
+// s = x / (2 + x) in (0, 1/3], by the odd series 2 (s + s^3/3 + ... + s^11/11): the first omitted
+// term is below 2 (1/3)^13 / 13 < 1e-7 of log 2, and every term is positive, so there is no
+// cancellation for any x, the tiny ones included.
 __device__ __forceinline__ float neg_softplus(float g) {
   const float x = __builtin_amdgcn_exp2f(fabsf(g) * -1.4426950408889634f);
-  float l;
-  if (x < 0.015625f) {
-    l = x * (1.0f - x * (0.5f - x * (0.33333334f - x * (0.25f - x * (0.2f - x * 0.16666667f)))));
-  } else {
-    const float u = 1.0f + x;
-    l = __builtin_amdgcn_logf(u) * 0.6931471805599453f * (x / (u - 1.0f));
-  }
-  return -(fmaxf(g, 0.0f) + l);
+  const float sv = x * __builtin_amdgcn_rcpf(2.0f + x);
+  const float z = sv * sv;
+  float poly = __builtin_fmaf(z, 2.0f / 11.0f, 2.0f / 9.0f);
+  poly = __builtin_fmaf(z, poly, 2.0f / 7.0f);
+  poly = __builtin_fmaf(z, poly, 2.0f / 5.0f);
+  poly = __builtin_fmaf(z, poly, 2.0f / 3.0f);
+  poly = __builtin_fmaf(z, poly, 2.0f);
+  return -__builtin_fmaf(sv, poly, fmaxf(g, 0.0f));
 }
 
 // sum over the 16 lanes of a DPP row, as every lane's value (inclusive scan by row shifts, then lane 15
@@ -62,22 +71,32 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int n_seq, int64_t T, i
 
 constexpr int kStrip = 32;  // tokens per wave
 
-__device__ __forceinline__ uint32_t word(const uint4& u, int i) { return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w; }
+// a row of 8 bf16 channels widened to fp32 (exact)
+__device__ __forceinline__ void widen8(const uint4& r, float* f) {
+  const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(wd[i] << 16);
+    f[2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
+  }
+}
 
 // A wave takes four adjacent heads over a strip of kStrip consecutive tokens; lane 16 r + cg holds
 // channels 8 cg .. 8 cg + 7 of head 4 hq + r (16-byte row loads, 1 KB per wave instruction). Per
-// projection it loads its 8 W conv weights once, then slides a register window of the last W - 1 rows
-// along the strip, so each x row is read once (plus W - 1 halo rows per strip). The strip's sequence
-// structure is the same for all lanes: at a sequence start the window is refilled from that sequence's
-// carried state. The head's sums of squares for the q and k norms are DPP row sums over 16 lanes.
+// projection it loads its 8 W conv weights once and keeps the last W rows, widened to fp32, in a ring
+// of W register sets, and the raw rows of the next U tokens in a second ring (U >= 4, a multiple of W,
+// so a wave keeps U row loads in flight); the token loop is unrolled by U, so the slot of every tap is a
+// compile-time index and nothing moves. Each x row is read once (plus W - 1 halo rows per strip). The strip's
+// sequence structure is the same for all lanes: at a sequence start the ring is refilled from that
+// sequence's carried state. The q and k norms are DPP row sums over a row's 16 lanes.
 template <int W>
 __global__ void __launch_bounds__(256) prologue_kernel(PrologueArgs A) {
-  constexpr int NW = W > 1 ? W - 1 : 1;
+  constexpr int U = W <= 2 ? 4 : W == 3 ? 6 : W;  // row prefetch distance and unroll, a multiple of W
   const int lane = threadIdx.x & 63;
   const int H = A.n_heads;
   const int n_hq = (H + 3) >> 2;
   const int64_t T = A.total_tokens;
-  const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t wv = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   const int64_t strip = wv / n_hq;
   const int hq = (int)(wv - strip * n_hq);
   const int64_t t0 = strip * kStrip;
@@ -87,12 +106,11 @@ __global__ void __launch_bounds__(256) prologue_kernel(PrologueArgs A) {
   const bool act = h_raw < H;  // a row group past the last head repeats it and stores nothing
   const int h = min(h_raw, H - 1);
   const int64_t HC = (int64_t)H * D;
-  const int64_t ch = (int64_t)h * D + 8 * (lane & 15);
-  const int n0 = __builtin_amdgcn_readfirstlane(seq_of(A.cu_seqlens, A.n_seq, T, t0));
-  const uint16_t* xs[3] = {A.xq, A.xk, A.xv};
-  uint16_t* outs[3] = {A.q, A.k, A.v};
+  const int ch = h * D + 8 * (lane & 15);  // the lane's first channel; row p of a projection at + p HC
+  const int n0 = seq_of(A.cu_seqlens, A.n_seq, T, t0);
   for (int which = 0; which < 3; ++which) {
-    const uint16_t* x = xs[which];
+    const uint16_t* x = which == 0 ? A.xq : which == 1 ? A.xk : A.xv;
+    uint16_t* out = which == 0 ? A.q : which == 1 ? A.k : A.v;
     float w[8][W];
     {
       const float4* wp = reinterpret_cast<const float4*>(A.conv_w + ((int64_t)which * HC + ch) * W);
@@ -104,76 +122,79 @@ __global__ void __launch_bounds__(256) prologue_kernel(PrologueArgs A) {
         for (int q = 0; q < 4; ++q) w[(4 * f + q) / W][(4 * f + q) % W] = e[q];
       }
     }
-    // the row that tap-position q of token p reads: x[q] inside the sequence (start s), else row
-    // q - s + W - 1 of the sequence's carried state (in [0, W - 1) because q >= p - W + 1 >= s - W + 1)
+    // the row that token q stands for when sequence n (start s) reads it: x[q] inside the sequence,
+    // else row q - s + W - 1 of the carried state (in [0, W - 1) because q >= s - W + 1 where it is read)
     auto tap_row = [&](int n, int64_t s, int64_t q) -> uint4 {
       if (q >= s) return *reinterpret_cast<const uint4*>(x + q * HC + ch);
       if (A.state_in)
         return *reinterpret_cast<const uint4*>(A.state_in + (((int64_t)n * 3 + which) * (W - 1) + (q - s + W - 1)) * HC + ch);
       return make_uint4(0u, 0u, 0u, 0u);
     };
+    float R[W][8];  // R[(p - t0 - a) mod W] = row of token p - a, for the token p being computed and a < W
     int n = n0;
     int64_t s = min(max((int64_t)A.cu_seqlens[n], (int64_t)0), t0);
     int64_t e = n + 1 < A.n_seq ? min(max((int64_t)A.cu_seqlens[n + 1], t0 + 1), T) : T;  // next start, > t0
-    uint4 win[NW];
+    // the rows before t0 (ages 1 .. W - 1 at the first token, which sits in slot 0)
 #pragma unroll
-    for (int i = 0; i < W - 1; ++i) win[i] = tap_row(n, s, t0 - (W - 1) + i);
-    uint4 nxt = *reinterpret_cast<const uint4*>(x + t0 * HC + ch);
-    for (int64_t p = t0; p < t1; ++p) {
-      const uint4 cur = nxt;
-      nxt = *reinterpret_cast<const uint4*>(x + min(p + 1, t1 - 1) * HC + ch);
-      if (p >= e) {  // p starts a later sequence: find it, refill the window from its state
-        n = __builtin_amdgcn_readfirstlane(seq_of(A.cu_seqlens, A.n_seq, T, p));
-        s = min(max((int64_t)A.cu_seqlens[n], (int64_t)0), p);
-        e = n + 1 < A.n_seq ? min(max((int64_t)A.cu_seqlens[n + 1], p + 1), T) : T;
+    for (int a = 1; a < W; ++a) widen8(tap_row(n, s, t0 - a), R[W - a]);
+    uint4 pre[U];  // raw rows of the next U tokens, token p in slot (p - t0) mod U
 #pragma unroll
-        for (int i = 0; i < W - 1; ++i) win[i] = tap_row(n, s, p - (W - 1) + i);
-      }
-      float c[8];
+    for (int d = 0; d < U; ++d)
+      if (t0 + d < t1) pre[d] = *reinterpret_cast<const uint4*>(x + (t0 + d) * HC + ch);
+    for (int64_t pb = t0; pb < t1; pb += U) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c[2 * i] = w[2 * i][W - 1] * bf2f(word(cur, i) & 0xffffu);
-        c[2 * i + 1] = w[2 * i + 1][W - 1] * bf2f(word(cur, i) >> 16);
-      }
+      for (int kk = 0; kk < U; ++kk) {
+        const int64_t p = pb + kk;
+        const int k = kk % W;  // ring slot of token p
+        if (p < t1) {  // wave-uniform
+          widen8(pre[kk], R[k]);
+          if (p + U < t1) pre[kk] = *reinterpret_cast<const uint4*>(x + (p + U) * HC + ch);
+          if (p >= e) {  // p starts a later sequence: find it, refill the older slots from its state
+            n = seq_of(A.cu_seqlens, A.n_seq, T, p);
+            s = min(max((int64_t)A.cu_seqlens[n], (int64_t)0), p);
+            e = n + 1 < A.n_seq ? min(max((int64_t)A.cu_seqlens[n + 1], p + 1), T) : T;
 #pragma unroll
-      for (int j = 0; j < W - 1; ++j) {
+            for (int a = 1; a < W; ++a) widen8(tap_row(n, s, p - a), R[(k - a + W) % W]);
+          }
+          float c[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          c[2 * i] = c[2 * i] + w[2 * i][j] * bf2f(word(win[j], i) & 0xffffu);
-          c[2 * i + 1] = c[2 * i + 1] + w[2 * i + 1][j] * bf2f(word(win[j], i) >> 16);
+          for (int i = 0; i < 8; ++i) c[i] = w[i][W - 1] * R[k][i];
+#pragma unroll
+          for (int j = 0; j < W - 1; ++j) {  // tap j reads token p - (W - 1) + j
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[i] = __builtin_fmaf(w[i][j], R[(k + 1 + j) % W][i], c[i]);
+          }
+          float u[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) u[i] = c[i] * sigmoid_fast(c[i]);
+          if (which < 2) {
+            float ss = u[0] * u[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) ss = __builtin_fmaf(u[i], u[i], ss);
+            const float r = __builtin_amdgcn_rsqf(row_sum16(ss) + A.eps);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) u[i] = u[i] * r;
+          }
+          if (act)
+            *reinterpret_cast<uint4*>(out + p * HC + ch) = make_uint4(cvt_pk_bf16(u[0], u[1]), cvt_pk_bf16(u[2], u[3]),
+                                                                  cvt_pk_bf16(u[4], u[5]), cvt_pk_bf16(u[6], u[7]));
         }
       }
-#pragma unroll
-      for (int j = 0; j + 1 < W - 1; ++j) win[j] = win[j + 1];
-      if (W > 1) win[NW - 1] = cur;
-      float u[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) u[i] = c[i] * sigmoid_fast(c[i]);
-      if (which < 2) {
-        float ss = u[0] * u[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) ss = ss + u[i] * u[i];
-        const float r = __builtin_amdgcn_rsqf(row_sum16(ss) + A.eps);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) u[i] = u[i] * r;
-      }
-      if (act)
-        *reinterpret_cast<uint4*>(outs[which] + p * HC + ch) =
-            make_uint4(pack2(f2bf(u[0]), f2bf(u[1])), pack2(f2bf(u[2]), f2bf(u[3])), pack2(f2bf(u[4]), f2bf(u[5])),
-                       pack2(f2bf(u[6]), f2bf(u[7])));
     }
   }
   // the gates, elementwise over the strip
 #pragma unroll 4
   for (int64_t p = t0; p < t1; ++p) {
-    const float4 ga = *reinterpret_cast<const float4*>(A.g_raw + p * HC + ch);
-    const float4 gb = *reinterpret_cast<const float4*>(A.g_raw + p * HC + ch + 4);
+    const float* gp = A.g_raw + p * HC + ch;
+    float* gkp = A.gk + p * HC + ch;
+    const float4 ga = *reinterpret_cast<const float4*>(gp);
+    const float4 gb = *reinterpret_cast<const float4*>(gp + 4);
     if (act) {
-      *reinterpret_cast<float4*>(A.gk + p * HC + ch) = make_float4(neg_softplus(ga.x), neg_softplus(ga.y), neg_softplus(ga.z), neg_softplus(ga.w));
-      *reinterpret_cast<float4*>(A.gk + p * HC + ch + 4) = make_float4(neg_softplus(gb.x), neg_softplus(gb.y), neg_softplus(gb.z), neg_softplus(gb.w));
+      *reinterpret_cast<float4*>(gkp) = make_float4(neg_softplus(ga.x), neg_softplus(ga.y), neg_softplus(ga.z), neg_softplus(ga.w));
+      *reinterpret_cast<float4*>(gkp + 4) = make_float4(neg_softplus(gb.x), neg_softplus(gb.y), neg_softplus(gb.z), neg_softplus(gb.w));
     }
   }
-  // beta: lane 16 r + j of the wave takes token t0 + 4 j' ... of head 4 hq + r, 16 tokens per pass
+  // beta: the 16 lanes of head 4 hq + r take 16 tokens of the strip per pass
   for (int64_t p = t0 + (lane & 15); p < t1; p += 16)
     if (act) A.beta[p * H + h] = sigmoid_fast(A.b_raw[p * H + h]);
 }

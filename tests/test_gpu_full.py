@@ -12,6 +12,7 @@ Workloads (synthetic, seeded, shapes from the pages; K = V = 128):
              accepted lengths geometric (mean 2.7, clipped to [1, 8])
   long:      1 x 1,048,576 tokens, H = 96, snapshots every 4096 into 2
              slots, then 128 single-token decode steps
+  prologue:  the 4 x 2048, H = 64 batch through kda_prologue, conv width 4
 """
 import numpy as np
 import pytest
@@ -135,6 +136,58 @@ def test_prefill_gated_4x2048_h64(gpu):
         worst = max(worst, float(np.max(np.max(np.abs(yv - ref), axis=1) / np.max(np.abs(ref), axis=1))))
     log(f"gated prefill 4x2048 H64: worst row err {worst:.2e}")
     assert worst <= 8e-3
+
+
+def _row_errs(y_bits, ref):
+    """Per row of 128: max |y - ref| / max |ref| (rows of ref that are exactly zero must come out zero)."""
+    y = (y_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(-1, 128)
+    ref = np.asarray(ref, dtype=np.float64).reshape(-1, 128)
+    den = np.max(np.abs(ref), axis=1)
+    err = np.max(np.abs(y - ref), axis=1)
+    assert np.all(err[den == 0] == 0)
+    return err[den > 0] / den[den > 0]
+
+
+def test_prologue_4x2048_h64(gpu):
+    """The KDA prologue at the headline prefill's size in the bench's configuration (4 x 2048 tokens,
+    H = 64, conv width 4, state carried in and out): every (token, head) row of q, k, v against the
+    oracle at bf16 accuracy, every beta and gk at 1e-5 relative, the carried state bit for bit."""
+    rng = np.random.default_rng(2048)
+    N, L, H, W, eps = 4, 2048, 64, 4, 1e-6
+    lens = [L] * N
+    cu = synth.cu_seqlens(lens)
+    T = N * L
+    xs = [synth.round_bf16(rng.standard_normal((T, H, 128))) for _ in range(3)]
+    conv_w = (0.5 * rng.standard_normal((3, H * 128, W))).astype(np.float32)
+    st = synth.round_bf16(rng.standard_normal((N, 3, W - 1, H * 128)))
+    b = rng.standard_normal((T, H)).astype(np.float32)
+    g = (2.0 * rng.standard_normal((T, H, 128))).astype(np.float32)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    outs = [torch.empty((T, H, 128), dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    beta, gk = torch.empty((T, H), device=DEV), torch.empty((T, H, 128), device=DEV)
+    sout = torch.empty((N, 3, W - 1, H * 128), dtype=torch.bfloat16, device=DEV)
+    bf = lambda a: to_dev(a.view(np.int16)).view(torch.bfloat16)
+    kda.kda_prologue(to_dev(cu.astype(np.int32)), *(bf(x) for x in xs), to_dev(conv_w), to_dev(b), to_dev(g),
+                     *outs, beta, gk, conv_state_in=bf(st), conv_state_out=sout, eps=eps)
+    torch.cuda.synchronize()
+    got = [o.view(torch.int16).cpu().numpy().view(np.uint16) for o in outs]
+    beta_h, gk_h = np_(beta), np_(gk)
+    sout_h = sout.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def one(n):
+        s0 = int(cu[n])
+        ref = oracle.prologue(*(x[s0:s0 + L] for x in xs), conv_w, st[n], b[s0:s0 + L], g[s0:s0 + L], eps)
+        qkv = max(float(_row_errs(gt[s0:s0 + L], r).max()) for gt, r in zip(got, ref[:3]))
+        eb = float(np.max(np.abs(beta_h[s0:s0 + L] - ref[3]) / np.abs(ref[3])))
+        eg = float(np.max(np.abs(gk_h[s0:s0 + L] - ref[4]) / np.abs(ref[4])))
+        same = np.array_equal(synth.bf16_to_f64(sout_h[n]), ref[5])
+        return qkv, eb, eg, same
+
+    res = oracle.run_parallel(one, range(N), threads=min(N, threads()))
+    qkv, eb, eg = (max(r[i] for r in res) for i in range(3))
+    log(f"prologue 4x2048 H64 W4: worst row err q/k/v {qkv:.2e}, beta {eb:.2e}, gk {eg:.2e}")
+    assert all(r[3] for r in res), "carried state differs from the oracle's"
+    assert qkv <= 5e-3 and eb <= 1e-5 and eg <= 1e-5
 
 
 def test_prefill_varlen_h96_snapshots(gpu):
