@@ -216,6 +216,39 @@ def bench_prologue(args, torch, kda, sg, synth):
     return dict(ms=ms, bytes=byts, gbs=byts / (ms * 1e-3) / 1e9)
 
 
+def bench_state_moves(args, torch, kda, sg, synth):
+    """The prefix-cache snapshot of the speculative step's batch: 256 requests, each a slot of 69 layers x
+    8 heads of 128 x 128 fp32 state (36.2 MB), copied working -> fresh slot in one kda_state_move launch;
+    the moves come from the host slot protocol (SlotPool.open, then snapshot per request)."""
+    dev = "cuda:0"
+    c = synth.VERIFY_CONFIG
+    B, Lyr, H = c["B"], c["L"], c["H"]
+    slots = kda.SlotPool(2 * B)
+    pool = torch.zeros((2 * B, Lyr, H, 128, 128), device=dev)
+    reqs = [slots.open()[0] for _ in range(B)]
+    moves = torch.tensor([slots.snapshot(r) for r in reqs], dtype=torch.int32, device=dev)
+    flat = pool.view(2 * B, -1)
+
+    def step():
+        kda.kda_state_move(flat, moves)
+
+    settle(step, torch)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    byts = 2 * B * Lyr * H * 65536
+    del pool, flat
+    return dict(ms=ms, bytes=byts, gbs=byts / (ms * 1e-3) / 1e9)
+
+
 def bench_verify_fold(args, torch, kda, sg, synth):
     dev = "cuda:0"
     c = synth.VERIFY_CONFIG
@@ -389,6 +422,10 @@ def main():
     if not args.prefill_only:
         log("prologue")
         pro = bench_prologue(args, torch, kda, sg, synth)
+    mvs = None
+    if not args.prefill_only:
+        log("state moves")
+        mvs = bench_state_moves(args, torch, kda, sg, synth)
     vf = None
     if not (args.no_verify_fold or args.prefill_only):
         log("verify+fold: generating inputs and timing")
@@ -446,6 +483,12 @@ def main():
             "workload": "kda_prologue over the headline prefill's 8,192 tokens x 64 heads: conv width 4 with the "
                         "state carried in and out, SiLU, q/k L2 norm, beta sigmoid, gk = -softplus (2,568 B per "
                         "token*head)",
+        }
+    if mvs is not None:
+        line["state_moves"] = {
+            "us": mvs["ms"] * 1e3, "gbs": mvs["gbs"], "hbm_frac": mvs["gbs"] / HBM_PEAK_GBS,
+            "workload": "prefix-cache snapshot of 256 requests' working slots (69 layers x 8 heads of 128 x 128 "
+                        "fp32 each, 36.2 MB) into fresh slots: one kda_state_move launch, 18.5 GB moved",
         }
     if vf is not None:
         line["verify_fold"] = {

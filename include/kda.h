@@ -42,6 +42,17 @@
  *      (tolerance 8e-3). The formula is not printed; the reading used here is
  *      RMSNorm over the head's 128 channels (eps inside the root), a weight
  *      per channel, and a sigmoid output gate.
+ *  [LMSYS-MOVES] same post and section, the three state moves: the
+ *      copy-on-write that restores a cached checkpoint into the working slot
+ *      and the snapshot at a track boundary are copies on the serial forward
+ *      stream; snapshots go to a ping-pong pair whose second slot exists only
+ *      around the snapshot; caching donates the latest snapshot's slot index
+ *      to the radix tree (no bytes move) and a fresh slot backfills, so a
+ *      snapshot never writes a slot a donate handed out.
+ *  [B200-CKPT] Kimi K3 B200 deployment notes, the CuTe FlashKDA prefill
+ *      item: the prefix cache checkpoints the state every 256 tokens, so
+ *      every chunk but a request's last is cut to a multiple of 256 and the
+ *      state at a chunk's end is an exact checkpoint.
  *  [LMSYS-SPEC] "SGLang and Miles Add Day-0 Support for Kimi K3", section
  *      "Speculative decoding with DSpark": a per-step planner keeps each
  *      request's verify tokens only while their expected value covers their
@@ -76,7 +87,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 #define KDA_HEAD_DIM 128 /* K = V = 128, fixed at build time */
 #define KDA_CHUNK 32     /* prefill chunk length; snap_interval must be a multiple */
 
@@ -85,7 +96,8 @@ typedef enum {
   KDA_ERR_INVALID_ARG = 1, /* NULL required pointer, bad count, forbidden alias, bad ring length */
   KDA_ERR_UNSUPPORTED = 2, /* a combination this build does not implement (fp32 inputs with a ring) */
   KDA_ERR_DEVICE = 3,      /* the HIP runtime reported an error while enqueuing work */
-  KDA_ERR_HOST_ALLOC = 4   /* pinned host allocation for a plan failed */
+  KDA_ERR_HOST_ALLOC = 4,  /* pinned host allocation for a plan failed */
+  KDA_ERR_NO_SLOT = 5      /* the state pool has no free slot (nothing was changed) */
 } kda_status;
 
 typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
@@ -425,6 +437,104 @@ kda_status kda_verify_ragged(int batch, int max_tok, int total_tok, int n_heads,
                              int n_slots, const kda_inputs* in, const int32_t* cu_tok,
                              const float* state_pool, const int32_t* slot_idx, float* o,
                              const kda_ring* ring, const int32_t* ring_start, float scale, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Prefix-cache state moves [LMSYS-MOVES] [B200-CKPT]. The state pool is the
+ * one kda_verify and kda_replay_fold take: fp32 [n_slots, n_layers, H, 128,
+ * 128], a slot holding every layer and head of one request. A request's live
+ * state is its working slot. Restores and snapshots are whole-slot copies
+ * (kda_state_move) enqueued on the forward stream between the forwards that
+ * produce and consume the state; donating moves ownership only.
+ * ------------------------------------------------------------------------- */
+
+/* One whole-slot copy: pool[dst] = pool[src]. */
+typedef struct {
+  int32_t src;
+  int32_t dst;
+} kda_move;
+
+/*
+ * Copies pool[moves[i].src] to pool[moves[i].dst] for i < n_moves, bit for
+ * bit, in one launch [LMSYS-MOVES].
+ *  n_moves     : >= 0.   moves : DEVICE kda_move[n_moves].
+ *  n_slots     : slots in the pool (>= 1).
+ *  slot_floats : floats per slot (n_layers * H * 128 * 128), a positive
+ *                multiple of 4.
+ *  pool        : DEVICE fp32 [n_slots, slot_floats], 16-byte aligned.
+ * A move with src or dst outside [0, n_slots), or src == dst, is skipped.
+ * No move may write a slot another move of the same call reads or writes
+ * (the slot protocol below never emits such a pair); moves of separate calls
+ * are ordered by the stream.
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_DEVICE.
+ */
+kda_status kda_state_move(int n_moves, const kda_move* moves, int n_slots, int64_t slot_floats, float* pool,
+                          void* stream);
+
+/*
+ * Checkpoint-aligned chunking [B200-CKPT], host only. Splits an extend of
+ * len tokens that starts after pos0 tokens already in the state into chunks
+ * of at most budget tokens. Every chunk but the last ends at the last
+ * multiple of align within its budget (an exact checkpoint position); where
+ * no multiple of align lies within the budget the chunk takes the whole
+ * budget. The last chunk takes the rest (<= budget).
+ *  pos0 >= 0, len >= 0, budget >= 1, align >= 1 (256 for the cache).
+ *  lens_host : host int64[max_chunks] receiving the chunk lengths.
+ *  *n_chunks : the number of chunks (also when it exceeds max_chunks, which
+ *              returns KDA_ERR_INVALID_ARG; lens_host then holds the first
+ *              max_chunks).
+ * Errors: KDA_ERR_INVALID_ARG.
+ */
+kda_status kda_chunk_split(int64_t pos0, int64_t len, int64_t budget, int64_t align, int64_t* lens_host,
+                           int max_chunks, int* n_chunks);
+
+/*
+ * Slot ownership under the three moves [LMSYS-MOVES], host only. Every slot
+ * of the pool has one owner: the free list, one open request, or the tree
+ * (the prefix cache). The calls change owners and fill in the copies to
+ * enqueue with kda_state_move; they never touch device memory and are not
+ * thread-safe (one scheduler thread owns a kda_slots).
+ *   open     : takes a free slot as the working slot; with cached_slot (a
+ *              slot the tree owns) also returns the copy-on-write move
+ *              cached_slot -> working (the tree's checkpoint is not changed).
+ *   snapshot : takes a free slot as the target (the ping-pong pair's second
+ *              slot), returns the move working -> target, makes the target
+ *              the latest snapshot and frees the one it supersedes (later
+ *              writes to that slot are ordered after this copy by the
+ *              stream).
+ *   donate   : hands the latest snapshot to the tree (no copy); the next
+ *              snapshot takes a fresh slot, so a snapshot never writes a slot
+ *              the tree owns.
+ *   close    : frees the working slot and a snapshot not donated.
+ *   release  : the tree evicts a slot it owns back to the free list.
+ * A request holds at most two slots between calls (working and latest).
+ * KDA_ERR_NO_SLOT leaves every owner unchanged. KDA_ERR_INVALID_ARG covers a
+ * restore from a slot the tree does not own, a request this pool did not
+ * open (or already closed), a donate without a snapshot, and a release of a
+ * slot the tree does not own.
+ */
+typedef struct kda_slots kda_slots;
+
+typedef struct {
+  int32_t id;      /* request id, >= 0 while open; -1 after close */
+  int32_t working; /* the slot every forward reads and overwrites */
+  int32_t snap;    /* the latest snapshot's slot, -1 = none */
+} kda_request_slots;
+
+#define KDA_SLOT_FREE (-1) /* kda_slots_owner: on the free list */
+#define KDA_SLOT_TREE (-2) /* kda_slots_owner: owned by the tree */
+
+kda_status kda_slots_create(int n_slots, kda_slots** out);
+void kda_slots_destroy(kda_slots* slots);
+int kda_slots_free_count(const kda_slots* slots);
+/* The owner of a slot: a request id, KDA_SLOT_FREE or KDA_SLOT_TREE; -3 for a bad slot. */
+int kda_slots_owner(const kda_slots* slots, int32_t slot);
+/* restore_host: host kda_move[1], required when cached_slot != -1; *n_moves = 0 or 1. */
+kda_status kda_request_open(kda_slots* slots, int32_t cached_slot, kda_request_slots* r, kda_move* restore_host,
+                            int* n_moves);
+kda_status kda_request_snapshot(kda_slots* slots, kda_request_slots* r, kda_move* move_host);
+kda_status kda_request_donate(kda_slots* slots, kda_request_slots* r, int32_t* slot);
+kda_status kda_request_close(kda_slots* slots, kda_request_slots* r);
+kda_status kda_slot_release(kda_slots* slots, int32_t slot);
 
 #ifdef __cplusplus
 }

@@ -26,6 +26,12 @@ kda_status fail(kda_status s, const std::string& msg) {
 
 kda_status ok() { return KDA_OK; }
 
+}  // namespace
+
+kda_status kda::fail(kda_status s, const char* msg) { return ::fail(s, msg); }
+
+namespace {
+
 kda_status device_fail(const char* what, hipError_t e) {
   return fail(KDA_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
 }
@@ -555,6 +561,21 @@ kda_status kda_prologue(int n_seq, int64_t total_tokens, int n_heads, int conv_w
   a.gk = gk;
   const hipError_t e = kda::launch_prologue(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail("kda_prologue: launch", e);
+  return ok();
+}
+
+kda_status kda_state_move(int n_moves, const kda_move* moves, int n_slots, int64_t slot_floats, float* pool,
+                          void* stream) {
+  if (n_moves < 0 || n_slots < 1 || slot_floats < 4 || slot_floats % 4 != 0)
+    return fail(KDA_ERR_INVALID_ARG, "kda_state_move: bad n_moves/n_slots/slot_floats (a positive multiple of 4)");
+  if (n_moves == 0) return ok();
+  if (!moves || !pool) return fail(KDA_ERR_INVALID_ARG, "kda_state_move: moves and pool are required");
+  if (reinterpret_cast<uintptr_t>(pool) % 16 != 0) return fail(KDA_ERR_INVALID_ARG, "kda_state_move: pool is not 16-byte aligned");
+  if ((uint64_t)slot_floats > (uint64_t)INT64_MAX / 4 / (uint64_t)n_slots) return fail(KDA_ERR_INVALID_ARG, "kda_state_move: pool too large");
+  if (overlap(moves, (size_t)n_moves * sizeof(kda_move), pool, (size_t)n_slots * (size_t)slot_floats * 4))
+    return fail(KDA_ERR_INVALID_ARG, "kda_state_move: moves overlaps the pool");
+  const hipError_t e = kda::launch_state_move(n_moves, moves, n_slots, slot_floats, pool, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail("kda_state_move: launch", e);
   return ok();
 }
 

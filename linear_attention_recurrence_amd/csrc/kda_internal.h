@@ -4,7 +4,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/kda.h"
+
 namespace kda {
+
+// sets the thread-local text behind kda_last_error and returns s (defined in kda_api.cpp)
+kda_status fail(kda_status s, const char* msg);
+inline kda_status ok() { return KDA_OK; }
 
 struct VerifyArgs {
   int batch, n_tok, n_heads, n_layers, layer, n_slots;
@@ -103,6 +109,8 @@ struct PrologueArgs {
   float* gk;                  // fp32 [T, H, 128]
 };
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream);
+hipError_t launch_state_move(int n_moves, const kda_move* moves, int n_slots, int64_t slot_floats, float* pool,
+                             hipStream_t stream);
 
 hipError_t launch_verify(const VerifyArgs& a, bool f32_inputs, hipStream_t stream);
 // the output gated RMSNorm on its own: rows of 128 fp32 values -> bf16

@@ -22,7 +22,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
 
-KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_DEVICE, KDA_ERR_HOST_ALLOC = 0, 1, 2, 3, 4
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_DEVICE, KDA_ERR_HOST_ALLOC, KDA_ERR_NO_SLOT = 0, 1, 2, 3, 4, 5
+KDA_SLOT_FREE, KDA_SLOT_TREE = -1, -2
 KDA_BF16, KDA_F32 = 0, 1
 KDA_PLAN_LPT, KDA_PLAN_FIFO = 0, 1
 KDA_PREFILL_PLAN_RESIDENT = 1
@@ -32,7 +33,9 @@ KDA_CHUNK = 32
 EXPORTS = ("kda_abi_version", "kda_last_error", "kda_plan_create", "kda_plan_create_ex", "kda_plan_v_blocks",
            "kda_plan_workspace_bytes", "kda_plan_num_items", "kda_plan_items", "kda_plan_upload", "kda_plan_destroy",
            "kda_chunk_prefill", "kda_chunk_prefill_gated", "kda_gated_rmsnorm", "kda_prologue", "kda_verify",
-           "kda_replay_fold", "kda_fold_verify", "kda_verify_ragged")
+           "kda_replay_fold", "kda_fold_verify", "kda_verify_ragged", "kda_state_move", "kda_chunk_split",
+           "kda_slots_create", "kda_slots_destroy", "kda_slots_free_count", "kda_slots_owner", "kda_request_open",
+           "kda_request_snapshot", "kda_request_donate", "kda_request_close", "kda_slot_release")
 
 
 class KdaError(RuntimeError):
@@ -49,6 +52,15 @@ class _Inputs(ctypes.Structure):
 class _Ring(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("gk", ctypes.c_void_p),
                 ("beta", ctypes.c_void_p), ("len", ctypes.c_int)]
+
+
+class _Move(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_int32), ("dst", ctypes.c_int32)]
+
+
+class RequestSlots(ctypes.Structure):
+    """A request's slots (kda_request_slots): id, working slot, latest snapshot (-1 = none)."""
+    _fields_ = [("id", ctypes.c_int32), ("working", ctypes.c_int32), ("snap", ctypes.c_int32)]
 
 
 _lib = None
@@ -89,6 +101,24 @@ def lib():
                                       ctypes.POINTER(_Ring), vp, vp, vp, f32, vp]
         L.kda_verify_ragged.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(_Inputs), vp, vp, vp, vp,
                                         ctypes.POINTER(_Ring), vp, f32, vp]
+        i64 = ctypes.c_int64
+        L.kda_state_move.argtypes = [i32, vp, i32, i64, vp, vp]
+        L.kda_chunk_split.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64), i32, ctypes.POINTER(i32)]
+        L.kda_slots_create.argtypes = [i32, ctypes.POINTER(vp)]
+        L.kda_slots_destroy.argtypes = [vp]
+        L.kda_slots_destroy.restype = None
+        L.kda_slots_free_count.argtypes = [vp]
+        L.kda_slots_free_count.restype = i32
+        L.kda_slots_owner.argtypes = [vp, i32]
+        L.kda_slots_owner.restype = i32
+        L.kda_request_open.argtypes = [vp, i32, ctypes.POINTER(RequestSlots), ctypes.POINTER(_Move), ctypes.POINTER(i32)]
+        L.kda_request_snapshot.argtypes = [vp, ctypes.POINTER(RequestSlots), ctypes.POINTER(_Move)]
+        L.kda_request_donate.argtypes = [vp, ctypes.POINTER(RequestSlots), ctypes.POINTER(i32)]
+        L.kda_request_close.argtypes = [vp, ctypes.POINTER(RequestSlots)]
+        L.kda_slot_release.argtypes = [vp, i32]
+        for f in ("kda_state_move", "kda_chunk_split", "kda_slots_create", "kda_request_open", "kda_request_snapshot",
+                  "kda_request_donate", "kda_request_close", "kda_slot_release"):
+            getattr(L, f).restype = i32
         for f in ("kda_plan_create", "kda_plan_create_ex", "kda_plan_items", "kda_plan_upload", "kda_chunk_prefill",
                   "kda_chunk_prefill_gated", "kda_gated_rmsnorm", "kda_prologue", "kda_verify", "kda_replay_fold",
                   "kda_fold_verify", "kda_verify_ragged"):
@@ -380,3 +410,72 @@ def kda_replay_fold(state_pool, slot_idx, ring, accepted_len, ring_start=None, s
     ring.check(S, L, H)
     _check(lib().kda_replay_fold(B, H, L, S, _ptr(state_pool), _ptr(slot_idx), ctypes.byref(ring.c()),
                                  _ptr(ring_start), _ptr(accepted_len), _stream(stream)))
+
+
+# ---------------------------------------------------------------- prefix-cache state moves
+def kda_state_move(pool, moves, stream=None):
+    """Whole-slot copies pool[src] -> pool[dst] for each row (src, dst) of moves, in one launch (see
+    include/kda.h). pool: fp32 [n_slots, ...] contiguous; moves: int32 [n, 2] on the device."""
+    if moves.dim() != 2 or moves.shape[1] != 2:
+        raise ValueError("moves must be int32 [n, 2]")
+    _need(moves, "moves", tuple(moves.shape), _I32)
+    if pool.dim() < 2:
+        raise ValueError("pool must be [n_slots, ...]")
+    _need(pool, "pool", tuple(pool.shape), _F32)
+    _check(lib().kda_state_move(moves.shape[0], _ptr(moves), pool.shape[0], pool[0].numel(), _ptr(pool),
+                                _stream(stream)))
+
+
+def kda_chunk_split(pos0, length, budget, align=256):
+    """Checkpoint-aligned chunk lengths for an extend of `length` tokens after `pos0` (see include/kda.h)."""
+    n = ctypes.c_int32(0)
+    st = lib().kda_chunk_split(pos0, length, budget, align, None, 0, ctypes.byref(n))  # counts the chunks
+    if st != KDA_OK and n.value == 0:
+        _check(st)
+    buf = (ctypes.c_int64 * max(n.value, 1))()
+    _check(lib().kda_chunk_split(pos0, length, budget, align, buf, n.value, ctypes.byref(n)))
+    return [int(buf[i]) for i in range(n.value)]
+
+
+class SlotPool:
+    """Ownership of a state pool's slots under the three state moves (kda_slots in include/kda.h). Host
+    only: the moves it returns are enqueued with kda_state_move on the forward stream."""
+
+    def __init__(self, n_slots):
+        h = ctypes.c_void_p()
+        _check(lib().kda_slots_create(n_slots, ctypes.byref(h)))
+        self._h = h
+        self.n_slots = n_slots
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.kda_slots_destroy(self._h)
+            self._h = None
+
+    def free_count(self):
+        return lib().kda_slots_free_count(self._h)
+
+    def owner(self, slot):
+        return lib().kda_slots_owner(self._h, slot)
+
+    def open(self, cached_slot=-1):
+        """-> (RequestSlots, [(src, dst)]): the working slot, and the copy-on-write move if restoring."""
+        r, mv, n = RequestSlots(), _Move(), ctypes.c_int32(0)
+        _check(lib().kda_request_open(self._h, cached_slot, ctypes.byref(r), ctypes.byref(mv), ctypes.byref(n)))
+        return r, ([(mv.src, mv.dst)] if n.value else [])
+
+    def snapshot(self, r):
+        mv = _Move()
+        _check(lib().kda_request_snapshot(self._h, ctypes.byref(r), ctypes.byref(mv)))
+        return (mv.src, mv.dst)
+
+    def donate(self, r):
+        slot = ctypes.c_int32(-1)
+        _check(lib().kda_request_donate(self._h, ctypes.byref(r), ctypes.byref(slot)))
+        return slot.value
+
+    def close(self, r):
+        _check(lib().kda_request_close(self._h, ctypes.byref(r)))
+
+    def release(self, slot):
+        _check(lib().kda_slot_release(self._h, slot))

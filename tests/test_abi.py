@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), f"libkda.so does not export {n}"
     assert set(names) == set(K.EXPORTS)
-    assert kda.kda_abi_version() == 3
+    assert kda.kda_abi_version() == 4
 
 
 def test_plan_lpt_order_and_ties():
@@ -267,6 +267,23 @@ def test_prologue_rejects_bad_arguments():
     assert call(q_=ctypes.c_void_p(0xA0000000 + 8)) == 1      # row buffers are 16-byte aligned
     assert call(q_=ctypes.c_void_p(0x20000000)) == 1          # q overlaps xq
     assert call(N=0, T=0) == 0                                # nothing to do
+
+
+def test_state_move_rejects_bad_arguments():
+    L = kda.lib()
+    pool = ctypes.c_void_p(0x40000000)
+    moves = ctypes.c_void_p(0x80000000)
+
+    def call(n=3, mv=moves, S=4, sf=16384, pl=pool):
+        return L.kda_state_move(n, mv, S, sf, pl, None)
+
+    assert call(n=-1) == 1 and call(S=0) == 1
+    assert call(sf=0) == 1 and call(sf=6) == 1                  # a positive multiple of 4 floats
+    assert call(mv=None) == 1 and call(pl=None) == 1
+    assert call(pl=ctypes.c_void_p(0x40000000 + 4)) == 1         # 16-byte aligned pool
+    assert call(mv=ctypes.c_void_p(0x40000000 + 64)) == 1        # the move list inside the pool
+    assert call(S=2, sf=1 << 62) == 1                            # size overflow
+    assert call(n=0, mv=None, pl=None) == 0                      # nothing to do
 
 
 def test_binding_checks_shapes_without_device():

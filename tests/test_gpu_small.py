@@ -722,3 +722,91 @@ def test_prologue(gpu, W):
                                      for n in range(N)])
             assert np.array_equal(joined, (q, k, v)[i])
         assert np.array_equal(r2[3], sout)
+
+
+# ---------------------------------------------------------------- prefix-cache state moves
+def test_state_move_bit_copy(gpu):
+    """kda_state_move copies whole slots bit for bit (NaN and denormal patterns included); moves with a
+    slot out of range or src == dst are skipped; every slot no move writes keeps its bits. Three slot
+    sizes cover the unrolled body and the tail of the copy loop."""
+    rng = np.random.default_rng(77)
+    for S, per_slot in ((12, 2 * 3 * 128 * 128), (9, 4), (7, 4 * 1000 + 12)):
+        bits0 = rng.integers(-2**31, 2**31, size=(S, per_slot), dtype=np.int64).astype(np.int32)
+        pool = torch.from_numpy(bits0.copy()).to(DEV).view(torch.float32)
+        dsts = rng.permutation(S)[:S // 2]
+        srcs = [s for s in rng.permutation(S) if s not in set(dsts)][:len(dsts)]
+        moves = [(int(a), int(b)) for a, b in zip(srcs, dsts)] + [(-1, 0), (0, S), (S + 3, 1), (2, 2), (1, -7)]
+        log(f"state move: {S} slots x {per_slot} floats, {len(moves)} moves")
+        kda.kda_state_move(pool, torch.tensor(moves, dtype=torch.int32, device=DEV))
+        torch.cuda.synchronize()
+        want = bits0.copy()
+        for a, b in zip(srcs, dsts):
+            want[b] = bits0[a]
+        assert np.array_equal(pool.view(torch.int32).cpu().numpy(), want)
+
+
+def test_prefix_cache_flow(gpu):
+    """The three state moves around real prefills, one layer, H = 4. Request A prefills 700 tokens in
+    checkpoint-aligned chunks (256, 256, 188), its working slot updated in place; after each chunk a
+    snapshot, and the 256- and 512-token checkpoints donated to the tree. Request B shares A's first 512
+    tokens: it restores the 512 checkpoint by copy-on-write and prefills its own 300 further tokens.
+    Checks: each donated checkpoint equals a one-call prefill of that prefix bit for bit and is unchanged
+    after B ran; B's outputs and final state equal a one-call prefill of its whole 812-token sequence bit
+    for bit; and against the oracle on two heads (2e-3)."""
+    H, seed_a, seed_b = 4, 31, 32
+    pool_slots = kda.SlotPool(6)
+    pool = torch.full((6, 1, H, 128, 128), float("nan"), device=DEV)
+
+    def prefill(ins, L, state_in, state_out):
+        plan = kda.kda_plan_create([0, L], n_heads=H)
+        ws = torch.empty(kda.kda_plan_workspace_bytes(plan), dtype=torch.uint8, device=DEV)
+        o = torch.empty((L, H, 128), device=DEV)
+        kda.kda_chunk_prefill(plan, *ins, state_out, o, ws, state_in=state_in)
+        return o
+
+    def move(mv):
+        kda.kda_state_move(pool.view(6, -1), torch.tensor([mv], dtype=torch.int32, device=DEV))
+
+    A = sg.prefill_inputs(seed_a, 700, H, DEV)
+    B_tail = sg.prefill_inputs(seed_b, 300, H, DEV)
+    tree = {}
+    ra, _ = pool_slots.open()
+    w = ra.working
+    pos = 0
+    for L in kda.kda_chunk_split(0, 700, 300):
+        log(f"prefix flow: A chunk [{pos}, {pos + L})")
+        ins = [t[pos:pos + L] for t in A]
+        prefill(ins, L, pool[w] if pos else None, pool[w])
+        move(pool_slots.snapshot(ra))
+        pos += L
+        if pos % 256 == 0:
+            tree[pos] = pool_slots.donate(ra)
+    assert sorted(tree) == [256, 512]
+    pool_slots.close(ra)
+    torch.cuda.synchronize()
+    ckpt = {p: pool[s].clone() for p, s in tree.items()}
+    for p in (256, 512):
+        ref = torch.empty((1, H, 128, 128), device=DEV)
+        prefill([t[:p] for t in A], p, None, ref)
+        torch.cuda.synchronize()
+        assert torch.equal(ckpt[p].view(torch.int32), ref.view(torch.int32)), f"checkpoint {p} differs"
+
+    rb, mv = pool_slots.open(tree[512])
+    assert mv == [(tree[512], rb.working)]
+    move(mv[0])
+    log("prefix flow: B restores 512 and prefills 300")
+    assert kda.kda_chunk_split(512, 300, 300) == [300]
+    o_b = prefill(B_tail, 300, pool[rb.working], pool[rb.working])
+    full = [torch.cat([a[:512], b]) for a, b in zip(A, B_tail)]
+    st_full = torch.empty((1, H, 128, 128), device=DEV)
+    o_full = prefill(full, 812, None, st_full)
+    torch.cuda.synchronize()
+    assert torch.equal(pool[tree[512]].view(torch.int32), ckpt[512].view(torch.int32)), "the tree's checkpoint changed"
+    assert torch.equal(o_b.view(torch.int32), o_full[512:].view(torch.int32))
+    assert torch.equal(pool[rb.working].view(torch.int32), st_full.view(torch.int32))
+    for h in (0, 3):
+        _, S512, _, _ = oracle_prefill_unit(seed_a, H, 0, 512, h)
+        o_ref, S_end, _, _ = oracle_prefill_unit(seed_b, H, 0, 300, h, S0=S512)
+        assert block_err(np_(o_b[:, h]), o_ref) <= TOL
+        assert block_err(np_(pool[rb.working, 0, h]), S_end) <= TOL
+    pool_slots.close(rb)
