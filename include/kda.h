@@ -284,7 +284,8 @@ kda_status kda_gated_rmsnorm(int64_t rows, const float* o, const void* gate, con
  * gate's form are readings (the notes give neither): exp(gk) = sigmoid(-g_raw)
  * is a decay in (0, 1), the input kda_chunk_prefill and kda_verify take.
  *
- *  n_seq, total_tokens, n_heads : N, T, H.   conv_width : W in 1..8.
+ *  n_seq, total_tokens, n_heads : N, T, H (H <= 65535, T * H <= 2^33,
+ *                   N * 3 * (W - 1) * H * 128 <= 2^38).   conv_width : W in 1..8.
  *  cu_seqlens     : device int32 [N + 1], cu[0] = 0, nondecreasing, cu[N] = T;
  *                   read clamped, so no value of it addresses memory outside
  *                   the buffers here.

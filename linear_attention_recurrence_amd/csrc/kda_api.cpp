@@ -515,7 +515,9 @@ kda_status kda_prologue(int n_seq, int64_t total_tokens, int n_heads, int conv_w
     return fail(KDA_ERR_INVALID_ARG, "kda_prologue: bad n_seq/total_tokens/n_heads/conv_width");
   if (!(eps >= 0.f && eps < INFINITY)) return fail(KDA_ERR_INVALID_ARG, "kda_prologue: eps must be finite and >= 0");
   if (total_tokens > 0 && n_seq < 1) return fail(KDA_ERR_INVALID_ARG, "kda_prologue: tokens without sequences");
-  if (total_tokens * n_heads > ((int64_t)1 << 33)) return fail(KDA_ERR_INVALID_ARG, "kda_prologue: too large");
+  if (n_heads > 0xffff) return fail(KDA_ERR_INVALID_ARG, "kda_prologue: n_heads must be <= 65535");
+  if (total_tokens * n_heads > ((int64_t)1 << 33) || (int64_t)n_seq * 3 * (conv_width - 1) * n_heads * KDA_HEAD_DIM > ((int64_t)1 << 38))
+    return fail(KDA_ERR_INVALID_ARG, "kda_prologue: too large");
   if (n_seq == 0) return ok();
   if (!cu_seqlens || !conv_w) return fail(KDA_ERR_INVALID_ARG, "kda_prologue: cu_seqlens and conv_w are required");
   if (total_tokens > 0 && (!xq || !xk || !xv || !b_raw || !g_raw || !q || !k || !v || !beta || !gk))

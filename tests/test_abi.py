@@ -258,7 +258,8 @@ def test_prologue_rejects_bad_arguments():
         return L.kda_prologue(N, T, H, W, cu_, xq, xk, xv, w, sin_, sout_, b, g, eps, q_, k, v, beta, gk, None)
 
     assert call(W=0) == 1 and call(W=9) == 1      # conv width 1..8
-    assert call(H=0) == 1 and call(T=-1) == 1
+    assert call(H=0) == 1 and call(T=-1) == 1 and call(H=70000) == 1
+    assert call(N=1 << 30, H=60000, W=8) == 1                # the carried state's grid would overflow
     assert call(N=0) == 1                          # tokens without sequences
     assert call(eps=-1.0) == 1
     assert call(cu_=None) == 1

@@ -810,3 +810,21 @@ def test_prefix_cache_flow(gpu):
         assert block_err(np_(o_b[:, h]), o_ref) <= TOL
         assert block_err(np_(pool[rb.working, 0, h]), S_end) <= TOL
     pool_slots.close(rb)
+
+
+def test_prologue_empty_batch(gpu):
+    """A batch whose sequences are all empty: no token outputs, and the carried state comes out equal to
+    the state that went in, bit for bit (W = 4 and W = 8)."""
+    rng = np.random.default_rng(9)
+    for W in (4, 8):
+        N, H = 3, 2
+        st = synth.round_bf16(rng.standard_normal((N, 3, W - 1, H * 128)))
+        conv_w = torch.zeros((3, H * 128, W), device=DEV)
+        sout = torch.full((N, 3, W - 1, H * 128), 7.0, dtype=torch.bfloat16, device=DEV)
+        e = torch.empty((0, H, 128), dtype=torch.bfloat16, device=DEV)
+        kda.kda_prologue(torch.zeros(N + 1, dtype=torch.int32, device=DEV), e, e, e, conv_w,
+                         torch.empty((0, H), device=DEV), torch.empty((0, H, 128), device=DEV),
+                         torch.empty_like(e), torch.empty_like(e), torch.empty_like(e), torch.empty((0, H), device=DEV),
+                         torch.empty((0, H, 128), device=DEV), conv_state_in=bf16_dev(st), conv_state_out=sout)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(sout).view(np.uint16), st)
