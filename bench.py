@@ -249,6 +249,80 @@ def bench_state_moves(args, torch, kda, sg, synth):
     return dict(ms=ms, bytes=byts, gbs=byts / (ms * 1e-3) / 1e9)
 
 
+def bench_long_context(args, torch, kda, sg, synth):
+    """The long-context workload: one 1,048,576-token sequence x 96 heads through kda_chunk_prefill (the
+    automatic plan: 192 half-chains; snapshots every 4096 tokens into 2 slots), then 128 single-token
+    decode steps from its final state (kda_verify, n_tok = 1, commit in place), launched one by one and
+    as one replayed HIP graph."""
+    dev = "cuda:0"
+    c = synth.PREFILL_CONFIGS[4]
+    seed, H, T = c["seed"], c["H"], sum(c["lengths"])
+    torch.cuda.empty_cache()  # about 180 GB of inputs and outputs follow
+    cu = synth.cu_seqlens([T])
+    plan = kda.kda_plan_create(cu, n_heads=H, snap_interval=c["snap_interval"], v_blocks=0)
+    ins = sg.prefill_inputs(seed, T, H, dev)
+    o = torch.empty((T, H, 128), device=dev)
+    st = torch.empty((1, H, 128, 128), device=dev)
+    slots = c["snap_slots"]
+    snap = torch.empty((1, slots, H, 128, 128), device=dev)
+    cnt = torch.empty((1,), dtype=torch.int32, device=dev)
+    ws = torch.empty(kda.kda_plan_workspace_bytes(plan), dtype=torch.uint8, device=dev)
+    kda.kda_plan_upload(plan, ws)
+
+    def step():
+        kda.kda_chunk_prefill(plan, *ins, st, o, ws, snap=snap, snap_slots=slots, snap_count=cnt,
+                              flags=kda.KDA_PREFILL_PLAN_RESIDENT)
+
+    n = max(1, min(args.steps, 3))
+    step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    byts = prefill_bytes(1, T, H, with_state_in=False) + (T // c["snap_interval"]) * H * 65536
+    del ins, o
+    torch.cuda.empty_cache()
+    # decode
+    steps = synth.DECODE_STEPS
+    tids = (synth.T_DEC_Q, synth.T_DEC_K, synth.T_DEC_V, synth.T_DEC_GK, synth.T_DEC_BETA)
+    dq, dk, dv, dg, db = sg.prefill_inputs(seed, steps, H, dev, tids=tids)
+    pool = st.view(1, 1, H, 128, 128).clone()
+    slot = torch.zeros(1, dtype=torch.int32, device=dev)
+    one = torch.ones(1, dtype=torch.int32, device=dev)
+    dec_o = torch.empty((steps, H, 128), device=dev)
+
+    def decode():
+        for t in range(steps):
+            kda.kda_verify(dq[t:t + 1], dk[t:t + 1], dv[t:t + 1], dg[t:t + 1], db[t:t + 1], pool, slot,
+                           dec_o[t:t + 1], layer=0, n_tok=1, commit_len=one, commit_pool=pool)
+
+    def timed(fn, reps):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * steps)
+
+    decode()
+    eager_us = timed(decode, 5)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        decode()
+    g.replay()
+    graph_us = timed(g.replay, 5)
+    dec_bytes = H * (2 * 65536 + 1796)
+    return dict(ms=ms, bytes=byts, gbs=byts / (ms * 1e-3) / 1e9, T=T, H=H, items=kda.kda_plan_num_items(plan),
+                eager_us=eager_us, graph_us=graph_us, dec_gbs=dec_bytes / (graph_us * 1e-6) / 1e9)
+
+
 def bench_verify_fold(args, torch, kda, sg, synth):
     dev = "cuda:0"
     c = synth.VERIFY_CONFIG
@@ -426,6 +500,14 @@ def main():
     if not args.prefill_only:
         log("state moves")
         mvs = bench_state_moves(args, torch, kda, sg, synth)
+    lc = None
+    if not args.prefill_only:
+        log("long context: 1M x 96 prefill, then 128 decode steps")
+        try:
+            lc = bench_long_context(args, torch, kda, sg, synth)
+        except torch.cuda.OutOfMemoryError as e:  # the headline line must still be printed
+            log(f"long context skipped: {e}")
+            torch.cuda.empty_cache()
     vf = None
     if not (args.no_verify_fold or args.prefill_only):
         log("verify+fold: generating inputs and timing")
@@ -483,6 +565,16 @@ def main():
             "workload": "kda_prologue over the headline prefill's 8,192 tokens x 64 heads: conv width 4 with the "
                         "state carried in and out, SiLU, q/k L2 norm, beta sigmoid, gk = -softplus (2,568 B per "
                         "token*head)",
+        }
+    if lc is not None:
+        line["long_context"] = {
+            "prefill_ms": lc["ms"], "prefill_tokens_heads_per_s": lc["T"] * lc["H"] / (lc["ms"] * 1e-3),
+            "prefill_gbs": lc["gbs"], "prefill_hbm_frac": lc["gbs"] / HBM_PEAK_GBS, "prefill_items": lc["items"],
+            "decode_us_per_step_eager": lc["eager_us"], "decode_us_per_step_graph": lc["graph_us"],
+            "decode_gbs_graph": lc["dec_gbs"], "decode_hbm_frac_graph": lc["dec_gbs"] / HBM_PEAK_GBS,
+            "workload": "1 x 1,048,576 tokens, H=96, snapshots every 4096 into 2 slots (automatic plan: two value "
+                        "blocks per head), then 128 single-token decode steps (kda_verify n_tok=1, in-place commit), "
+                        "one launch per step and as one replayed HIP graph",
         }
     if mvs is not None:
         line["state_moves"] = {

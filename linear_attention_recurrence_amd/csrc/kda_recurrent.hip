@@ -23,6 +23,12 @@
 // 32*w + 4*(l>>3) .. +3 (64 floats). Sums over the key channel are a
 // sequential FMA chain over the thread's 16 rows, then a butterfly over the
 // eight lanes l&7 that share the columns (DPP quad_perm x2, row_half_mirror).
+// A column of S evolves independently of the others given the key-side values,
+// and each 32-column block is one wave's: so when there are few (request, head)
+// pairs (single-request decode: 96 heads for 256 compute units) verify runs one
+// 64-thread workgroup per (request, head, 32-column block), each wave computing
+// its columns exactly as it would inside the 256-thread workgroup (same lanes,
+// same reduction order), so outputs and commits are bit for bit the same.
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_step.h"
@@ -40,15 +46,18 @@ __device__ __forceinline__ float4 load4(const void* base, size_t idx) {
   }
 }
 
-template <bool F32, bool RING>
+template <bool F32, bool RING, bool SPLIT>
 __global__ void __launch_bounds__(256) verify_kernel(VerifyArgs A) {
   __shared__ StepLds L;
+  constexpr int NT = SPLIT ? 64 : 256;  // threads per workgroup
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int lane = tid & 63;
+  const int wave = SPLIT ? (int)(blockIdx.x & 3) : tid >> 6;       // the 32-column block
+  const int ub = SPLIT ? (int)(blockIdx.x >> 2) : (int)blockIdx.x;  // (request, head)
   const int r0 = 16 * (lane & 7);
   const int col0 = 32 * wave + 4 * (lane >> 3);
-  const int b = blockIdx.x / A.n_heads;
-  const int h = blockIdx.x - b * A.n_heads;
+  const int b = ub / A.n_heads;
+  const int h = ub - b * A.n_heads;
   const int slot = A.slot_idx[b];
   if (slot < 0 || slot >= A.n_slots) return;  // whole workgroup skips together
   const size_t unit = ((size_t)slot * A.n_layers + A.layer) * A.n_heads + h;
@@ -65,8 +74,8 @@ __global__ void __launch_bounds__(256) verify_kernel(VerifyArgs A) {
   for (int t0 = 0; t0 < A.n_tok; t0 += TB) {
     const int nb = (A.n_tok - t0) < TB ? (A.n_tok - t0) : TB;
     __syncthreads();  // the previous batch is no longer read
-    {
-      const int tt = tid >> 5, c4 = (tid & 31) * 4;
+    for (int x = tid; x < 32 * TB; x += NT) {  // one pass with 256 threads
+      const int tt = x >> 5, c4 = (x & 31) * 4;
       if (tt < nb) {
         const size_t row = ((size_t)b * A.n_tok + t0 + tt) * A.n_heads + h;
         const size_t e = row * D + c4;
@@ -82,7 +91,7 @@ __global__ void __launch_bounds__(256) verify_kernel(VerifyArgs A) {
         *reinterpret_cast<float4*>(&L.v[tt][c4]) = v4;
         const float beta = A.beta[row];
         if (c4 == 0) L.beta[tt] = beta;
-        if constexpr (RING) {
+        if (RING && (!SPLIT || wave == 0)) {
           // raw inputs, bit for bit, into ring position (start + t) & (len - 1)
           const int pos = (rstart + t0 + tt) & (A.ring_len - 1);
           const size_t rrow = unit * A.ring_len + pos;
@@ -165,11 +174,21 @@ __global__ void __launch_bounds__(256) fold_kernel(FoldArgs A) {
 
 hipError_t launch_verify(const VerifyArgs& a, bool f32, hipStream_t stream) {
   if (verify_chunk_eligible(a, f32)) return launch_verify_chunk(a, stream);
-  const dim3 grid((unsigned)a.batch * (unsigned)a.n_heads), block(256);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const long units = (long)a.batch * a.n_heads;
   const bool ring = a.ring_k != nullptr;
-  if (f32) hipLaunchKernelGGL((verify_kernel<true, false>), grid, block, 0, stream, a);
-  else if (ring) hipLaunchKernelGGL((verify_kernel<false, true>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((verify_kernel<false, false>), grid, block, 0, stream, a);
+  if (units < 2L * prefill_max_grid(dev)) {  // fewer than two (request, head) pairs per CU: split columns
+    const dim3 grid((unsigned)(4 * units)), block(64);
+    if (f32) hipLaunchKernelGGL((verify_kernel<true, false, true>), grid, block, 0, stream, a);
+    else if (ring) hipLaunchKernelGGL((verify_kernel<false, true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((verify_kernel<false, false, true>), grid, block, 0, stream, a);
+  } else {
+    const dim3 grid((unsigned)units), block(256);
+    if (f32) hipLaunchKernelGGL((verify_kernel<true, false, false>), grid, block, 0, stream, a);
+    else if (ring) hipLaunchKernelGGL((verify_kernel<false, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((verify_kernel<false, false, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -828,3 +828,44 @@ def test_prologue_empty_batch(gpu):
                          torch.empty((0, H, 128), device=DEV), conv_state_in=bf16_dev(st), conv_state_out=sout)
         torch.cuda.synchronize()
         assert np.array_equal(bits(sout).view(np.uint16), st)
+
+
+def test_decode_graph_replay(gpu):
+    """Single-token decode (kda_verify with n_tok = 1 and the commit written in place) captured as one HIP
+    graph of 16 steps: three replays, each from the same starting state restored by eager work, with
+    another eager decode run and synchronizations between them; every replay's outputs and final state
+    equal the eager run's bit for bit."""
+    H, steps, seed = 8, 16, 5
+    tids = (synth.T_DEC_Q, synth.T_DEC_K, synth.T_DEC_V, synth.T_DEC_GK, synth.T_DEC_BETA)
+    dq, dk, dv, dg, db = sg.prefill_inputs(seed, steps, H, DEV, tids=tids)
+    start = sg.states(seed, H, DEV).view(1, 1, H, 128, 128)
+    pool = start.clone()
+    slot = torch.zeros(1, dtype=torch.int32, device=DEV)
+    one = torch.ones(1, dtype=torch.int32, device=DEV)
+    out = torch.empty((steps, H, 128), device=DEV)
+
+    def decode(p, o):
+        for t in range(steps):
+            kda.kda_verify(dq[t:t + 1], dk[t:t + 1], dv[t:t + 1], dg[t:t + 1], db[t:t + 1], p, slot, o[t:t + 1],
+                           layer=0, n_tok=1, commit_len=one, commit_pool=p)
+
+    decode(pool, out)
+    torch.cuda.synchronize()
+    ref_o, ref_s = out.clone(), pool.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        decode(pool, out)
+    other_pool, other_out = start.clone(), torch.empty_like(out)
+    for r in range(3):
+        log(f"decode graph: replay {r}")
+        pool.copy_(start)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref_o.view(torch.int32)), f"replay {r}: outputs differ"
+        assert torch.equal(pool.view(torch.int32), ref_s.view(torch.int32)), f"replay {r}: state differs"
+        other_pool.copy_(start)
+        decode(other_pool, other_out)   # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(other_out.view(torch.int32), ref_o.view(torch.int32))
