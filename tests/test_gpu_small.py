@@ -869,3 +869,71 @@ def test_decode_graph_replay(gpu):
         decode(other_pool, other_out)   # eager work between the replays
         torch.cuda.synchronize()
         assert torch.equal(other_out.view(torch.int32), ref_o.view(torch.int32))
+
+
+def test_graph_replay_prefill_and_verify(gpu):
+    """A ragged prefill (resident plan, state_in, snapshots) and two layers of speculative verify (the
+    chunked path, ring written) each captured once as a HIP graph and replayed three times, with every
+    output cleared by eager work and the same call run eagerly between replays: each replay equals the
+    eager result bit for bit (outputs, states, snapshots, counts, ring)."""
+    seed, H = 12, 3
+    lens = [1, 31, 33, 100, 0, 257, 64]
+    cu = synth.cu_seqlens(lens)
+    T, N = int(cu[-1]), len(lens)
+    plan = kda.kda_plan_create(cu, n_heads=H, snap_interval=64)
+    ins = sg.prefill_inputs(seed, T, H, DEV)
+    S0 = sg.states(seed, N * H, DEV).view(N, H, 128, 128)
+    ws = torch.empty(kda.kda_plan_workspace_bytes(plan), dtype=torch.uint8, device=DEV)
+    kda.kda_plan_upload(plan, ws)
+    o = torch.empty((T, H, 128), device=DEV)
+    st = torch.empty((N, H, 128, 128), device=DEV)
+    snap = torch.empty((N, 2, H, 128, 128), device=DEV)
+    cnt = torch.empty((N,), dtype=torch.int32, device=DEV)
+    pf_bufs = (o, st, snap, cnt)
+
+    def prefill():
+        kda.kda_chunk_prefill(plan, *ins, st, o, ws, state_in=S0, snap=snap, snap_slots=2, snap_count=cnt,
+                              flags=kda.KDA_PREFILL_PLAN_RESIDENT)
+
+    B, Tv, Hv, L, S, R = 5, 8, 4, 2, 8, 16
+    slot_idx, pool, vins, ring_start = make_verify_case(seed, B, Tv, Hv, L, S, R)
+    slot_idx, ring_start = slot_idx.to(DEV), ring_start.to(DEV)
+    ring = kda.Ring.empty(S, L, Hv, R, DEV)
+    vo = torch.empty((L, B * Tv, Hv, 128), device=DEV)
+    vf_bufs = (vo, ring.k, ring.v, ring.gk, ring.beta)
+
+    def verify():
+        for l in range(L):
+            kda.kda_verify(*vins[l], pool, slot_idx, vo[l], layer=l, n_tok=Tv, ring=ring, ring_start=ring_start)
+
+    def clear(bufs):
+        for t in bufs:
+            t.fill_(-3) if t.dtype in (torch.int32, torch.int16) else t.fill_(float("nan"))
+
+    def snapshot(bufs):
+        return [t.view(torch.int16 if t.element_size() == 2 else torch.int32).clone() for t in bufs]
+
+    for name, fn, bufs in (("prefill", prefill, pf_bufs), ("verify", verify, vf_bufs)):
+        log(f"graph replay: {name}")
+        if name == "verify":
+            ring.k.zero_(); ring.v.zero_(); ring.gk.zero_(); ring.beta.zero_()
+        outs = bufs if name == "prefill" else bufs[:1]  # cleared before each call (ring slots not written stay 0)
+        clear(outs)
+        fn()
+        torch.cuda.synchronize()
+        ref = snapshot(bufs)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        for r in range(3):
+            clear(outs)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for a, b in zip(snapshot(bufs), ref):
+                assert torch.equal(a, b), f"{name}: replay {r} differs from the eager call"
+            clear(outs)
+            fn()  # the same call eagerly between replays
+            torch.cuda.synchronize()
+            for a, b in zip(snapshot(bufs), ref):
+                assert torch.equal(a, b), f"{name}: eager call after replay {r} differs"
