@@ -11,7 +11,11 @@ uint16, fp32, fp64).
 
 Parity pins: every function here is checked in ``tests/test_oracle.py``
 against closed forms, invariants, a brute-force matrix form on tiny shapes
-and an independently derived chunked algebra.
+and an independently derived chunked algebra. The pages print no worked
+example and no output value, so absolute outputs are parity unpinned by the
+pages themselves; for the output gated RMSNorm and the prologue even the
+formulas are readings (the pages name the operations only), pinned by those
+invariants alone.
 """
 from __future__ import annotations
 
