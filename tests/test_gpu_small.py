@@ -937,3 +937,19 @@ def test_graph_replay_prefill_and_verify(gpu):
             torch.cuda.synchronize()
             for a, b in zip(snapshot(bufs), ref):
                 assert torch.equal(a, b), f"{name}: eager call after replay {r} differs"
+
+
+def test_state_move_many_moves(gpu):
+    """More moves than one grid dimension holds (70,000 > 65,535): the kernel strides over the moves.
+    Slots of 4 floats; every even slot is copied to the next odd one, bit for bit."""
+    n = 70000
+    S = 2 * n
+    rng = np.random.default_rng(3)
+    bits0 = rng.integers(-2**31, 2**31, size=(S, 4), dtype=np.int64).astype(np.int32)
+    pool = torch.from_numpy(bits0.copy()).to(DEV).view(torch.float32)
+    moves = np.stack([np.arange(0, S, 2), np.arange(1, S, 2)], axis=1).astype(np.int32)
+    kda.kda_state_move(pool, torch.from_numpy(moves).to(DEV))
+    torch.cuda.synchronize()
+    want = bits0.copy()
+    want[1::2] = bits0[0::2]
+    assert np.array_equal(pool.view(torch.int32).cpu().numpy(), want)
