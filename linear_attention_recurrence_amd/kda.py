@@ -415,7 +415,10 @@ def kda_replay_fold(state_pool, slot_idx, ring, accepted_len, ring_start=None, s
 # ---------------------------------------------------------------- prefix-cache state moves
 def kda_state_move(pool, moves, stream=None):
     """Whole-slot copies pool[src] -> pool[dst] for each row (src, dst) of moves, in one launch (see
-    include/kda.h). pool: fp32 [n_slots, ...] contiguous; moves: int32 [n, 2] on the device."""
+    include/kda.h). pool: fp32 [n_slots, ...] contiguous; moves: int32 [n, 2] on the device (an empty
+    tensor: nothing to do)."""
+    if moves.numel() == 0:
+        return
     if moves.dim() != 2 or moves.shape[1] != 2:
         raise ValueError("moves must be int32 [n, 2]")
     _need(moves, "moves", tuple(moves.shape), _I32)

@@ -287,6 +287,15 @@ def test_state_move_rejects_bad_arguments():
     assert call(n=0, mv=None, pl=None) == 0                      # nothing to do
 
 
+def test_state_move_binding_empty_and_shapes():
+    import torch
+
+    pool = torch.zeros((2, 4))
+    kda.kda_state_move(pool, torch.tensor([], dtype=torch.int32))  # an empty move list is a no-op
+    with pytest.raises(ValueError):
+        kda.kda_state_move(pool, torch.zeros((3,), dtype=torch.int32))  # not [n, 2]
+
+
 def test_binding_checks_shapes_without_device():
     import torch
 
