@@ -953,3 +953,27 @@ def test_state_move_many_moves(gpu):
     want = bits0.copy()
     want[1::2] = bits0[0::2]
     assert np.array_equal(pool.view(torch.int32).cpu().numpy(), want)
+
+
+def test_prologue_clamps_bounds(gpu):
+    """cu_seqlens out of range, decreasing or negative (a caller's bug): the kernels read every bound
+    clamped into [0, T], so the call completes, every output is finite, and the first sequence, whose
+    bounds are valid, matches a call with well-formed bounds bit for bit."""
+    rng = np.random.default_rng(21)
+    H, W, T = 2, 4, 64
+    xs, conv_w, _, b, g = _prologue_inputs(rng, T, 4, H, W)
+    st = synth.round_bf16(rng.standard_normal((4, 3, W - 1, H * 128)))
+    bad = [0, 20, 10, 100000, T]           # sequence 1 decreasing, 2 past the end
+    good = [0, 20, 40, 50, T]
+    outs = {}
+    for name, cu in (("bad", bad), ("good", good)):
+        log(f"prologue clamps: {name} bounds {cu}")
+        outs[name] = _run_prologue(cu, xs, conv_w, st, b, g, 1e-6)
+    (q, k, v), beta, gk, sout = outs["bad"]
+    for arr in (q, k, v):
+        assert np.all(np.isfinite((arr.astype(np.uint32) << 16).view(np.float32)))
+    assert np.all(np.isfinite(beta)) and np.all(np.isfinite(gk))
+    assert np.all(np.isfinite((sout.astype(np.uint32) << 16).view(np.float32)))
+    (qg, kg, vg), _, _, _ = outs["good"]
+    for x_, y_ in ((q, qg), (k, kg), (v, vg)):
+        assert np.array_equal(x_[:20], y_[:20])
