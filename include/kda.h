@@ -53,6 +53,9 @@
  *      item: the prefix cache checkpoints the state every 256 tokens, so
  *      every chunk but a request's last is cut to a multiple of 256 and the
  *      state at a chunk's end is an exact checkpoint.
+ *  [B200-DECODE] Kimi K3 B200 deployment notes, the decode items of the
+ *      optimisation timeline: a fused KDA decode kernel (conv + KDA + output
+ *      norm) for the batch-1 shape, where a decode step is launch-bound.
  *  [LMSYS-SPEC] "SGLang and Miles Add Day-0 Support for Kimi K3", section
  *      "Speculative decoding with DSpark": a per-step planner keeps each
  *      request's verify tokens only while their expected value covers their
@@ -438,6 +441,39 @@ kda_status kda_verify_ragged(int batch, int max_tok, int total_tok, int n_heads,
                              int n_slots, const kda_inputs* in, const int32_t* cu_tok,
                              const float* state_pool, const int32_t* slot_idx, float* o,
                              const kda_ring* ring, const int32_t* ring_start, float scale, void* stream);
+
+/*
+ * One decode step of a KDA layer in one launch [B200-DECODE]: for each request
+ * b (one new token) and head h, the prologue of kda_prologue for that token
+ * (short conv with the conv state, SiLU, q/k L2 norm with qk_eps, beta and
+ * gk), the recurrent step of kda_verify with n_tok = 1 and the commit written
+ * in place into state_pool, and the output gated RMSNorm of kda_gated_rmsnorm
+ * with norm_eps. y, the committed state and the conv state are bit for bit
+ * those of kda_prologue, kda_verify (commit_len = 1, commit_pool = state_pool)
+ * and kda_gated_rmsnorm run one after another.
+ *  batch, n_heads (<= 65535), n_layers, layer, n_slots : as kda_verify.
+ *  conv_width : W in 1..8.
+ *  xq, xk, xv : bf16 [batch, H, 128], the token's projections.
+ *  conv_w     : fp32 [3, H * 128, W].
+ *  conv_state : bf16 [batch, 3, W - 1, H * 128] (row W - 2 the newest),
+ *               updated in place (the token becomes the newest row); NULL
+ *               only when W = 1.
+ *  b_raw : fp32 [batch, H].  g_raw : fp32 [batch, H, 128].
+ *  state_pool : fp32 [n_slots, L, H, 128, 128], updated in place.
+ *  slot_idx   : device int32 [batch]; a slot outside [0, n_slots) skips the
+ *               request whole (its outputs and conv state are not written).
+ *  gate : bf16 [batch, H, 128].  norm_w : fp32 [128].
+ *  y : bf16 [batch, H, 128].  o : fp32 [batch, H, 128] (the step's output
+ *      before the norm) or NULL.
+ *  Row buffers 16-byte aligned; no output may overlap an input or another
+ *  output; distinct slots.
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_DEVICE.
+ */
+kda_status kda_decode(int batch, int n_heads, int n_layers, int layer, int n_slots, int conv_width,
+                      const void* xq, const void* xk, const void* xv, const float* conv_w, void* conv_state,
+                      const float* b_raw, const float* g_raw, float* state_pool, const int32_t* slot_idx,
+                      const void* gate, const float* norm_w, float qk_eps, float norm_eps, float scale, void* y,
+                      float* o, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Prefix-cache state moves [LMSYS-MOVES] [B200-CKPT]. The state pool is the

@@ -581,6 +581,69 @@ kda_status kda_state_move(int n_moves, const kda_move* moves, int n_slots, int64
   return ok();
 }
 
+kda_status kda_decode(int batch, int n_heads, int n_layers, int layer, int n_slots, int conv_width,
+                      const void* xq, const void* xk, const void* xv, const float* conv_w, void* conv_state,
+                      const float* b_raw, const float* g_raw, float* state_pool, const int32_t* slot_idx,
+                      const void* gate, const float* norm_w, float qk_eps, float norm_eps, float scale, void* y,
+                      float* o, void* stream) {
+  if (batch < 0 || n_heads < 1 || n_heads > 0xffff || n_layers < 1 || layer < 0 || layer >= n_layers || n_slots < 1 ||
+      conv_width < 1 || conv_width > 8)
+    return fail(KDA_ERR_INVALID_ARG, "kda_decode: bad batch/n_heads/n_layers/layer/n_slots/conv_width");
+  if (!(qk_eps >= 0.f && qk_eps < INFINITY) || !(norm_eps >= 0.f && norm_eps < INFINITY) || !std::isfinite(scale))
+    return fail(KDA_ERR_INVALID_ARG, "kda_decode: eps values must be finite and >= 0, scale finite");
+  if ((int64_t)batch * n_heads > 0x7fffffffLL) return fail(KDA_ERR_INVALID_ARG, "kda_decode: grid too large");
+  if (batch == 0) return ok();
+  if (!xq || !xk || !xv || !conv_w || !b_raw || !g_raw || !state_pool || !slot_idx || !gate || !norm_w || !y ||
+      (conv_width > 1 && !conv_state))
+    return fail(KDA_ERR_INVALID_ARG, "kda_decode: a required pointer is NULL");
+  {
+    const void* al[11] = {xq, xk, xv, conv_w, conv_state, g_raw, state_pool, gate, norm_w, y, o};
+    for (const void* p : al)
+      if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return fail(KDA_ERR_INVALID_ARG, "kda_decode: a buffer is not 16-byte aligned");
+  }
+  const size_t rows = (size_t)batch * n_heads, HC = (size_t)n_heads * KDA_HEAD_DIM;
+  const size_t xb = rows * KDA_HEAD_DIM * 2;
+  const size_t csb = (size_t)batch * 3 * (conv_width - 1) * HC * 2;
+  const size_t poolb = (size_t)n_slots * n_layers * n_heads * kState;
+  const void* outs[4] = {conv_state, state_pool, y, o};
+  const size_t outsz[4] = {csb, poolb, xb, rows * KDA_HEAD_DIM * 4};
+  const void* ins[9] = {xq, xk, xv, conv_w, b_raw, g_raw, slot_idx, gate, norm_w};
+  const size_t insz[9] = {xb, xb, xb, 3 * HC * conv_width * 4, rows * 4, rows * KDA_HEAD_DIM * 4, (size_t)batch * 4, xb,
+                          (size_t)KDA_HEAD_DIM * 4};
+  for (int a = 0; a < 4; ++a) {
+    for (int i2 = 0; i2 < 9; ++i2)
+      if (overlap(outs[a], outsz[a], ins[i2], insz[i2])) return fail(KDA_ERR_INVALID_ARG, "kda_decode: an output overlaps an input");
+    for (int a2 = a + 1; a2 < 4; ++a2)
+      if (overlap(outs[a], outsz[a], outs[a2], outsz[a2])) return fail(KDA_ERR_INVALID_ARG, "kda_decode: two outputs overlap");
+  }
+  kda::DecodeArgs d{};
+  d.batch = batch;
+  d.n_heads = n_heads;
+  d.n_layers = n_layers;
+  d.layer = layer;
+  d.n_slots = n_slots;
+  d.conv_width = conv_width;
+  d.xq = static_cast<const uint16_t*>(xq);
+  d.xk = static_cast<const uint16_t*>(xk);
+  d.xv = static_cast<const uint16_t*>(xv);
+  d.conv_w = conv_w;
+  d.conv_state = static_cast<uint16_t*>(conv_state);
+  d.b_raw = b_raw;
+  d.g_raw = g_raw;
+  d.state_pool = state_pool;
+  d.slot_idx = slot_idx;
+  d.gate = static_cast<const uint16_t*>(gate);
+  d.norm_w = norm_w;
+  d.qk_eps = qk_eps;
+  d.norm_eps = norm_eps;
+  d.scale = scale;
+  d.y = static_cast<uint16_t*>(y);
+  d.o = o;
+  const hipError_t e = kda::launch_decode(d, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail("kda_decode: launch", e);
+  return ok();
+}
+
 kda_status kda_replay_fold(int batch, int n_heads, int n_layers, int n_slots, float* state_pool, const int32_t* slot_idx,
                            const kda_ring* ring, const int32_t* ring_start, const int32_t* accepted_len, void* stream) {
   if (batch < 0 || n_heads < 1 || n_layers < 1 || n_slots < 1)

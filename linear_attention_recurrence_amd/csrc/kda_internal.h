@@ -109,6 +109,26 @@ struct PrologueArgs {
   float* gk;                  // fp32 [T, H, 128]
 };
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t stream);
+
+// one fused decode step (prologue + recurrent step with in-place commit + output gated RMSNorm)
+struct DecodeArgs {
+  int batch, n_heads, n_layers, layer, n_slots, conv_width;
+  const uint16_t* xq;  // bf16 [B, H, 128] each
+  const uint16_t* xk;
+  const uint16_t* xv;
+  const float* conv_w;   // fp32 [3, H * 128, W]
+  uint16_t* conv_state;  // bf16 [B, 3, W - 1, H * 128], in place
+  const float* b_raw;    // fp32 [B, H]
+  const float* g_raw;    // fp32 [B, H, 128]
+  float* state_pool;     // fp32 [n_slots, L, H, 128, 128], the commit in place
+  const int32_t* slot_idx;
+  const uint16_t* gate;  // bf16 [B, H, 128]
+  const float* norm_w;   // fp32 [128]
+  float qk_eps, norm_eps, scale;
+  uint16_t* y;  // bf16 [B, H, 128]
+  float* o;     // fp32 [B, H, 128] or nullptr
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_state_move(int n_moves, const kda_move* moves, int n_slots, int64_t slot_floats, float* pool,
                              hipStream_t stream);
 

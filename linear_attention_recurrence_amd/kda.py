@@ -35,7 +35,7 @@ EXPORTS = ("kda_abi_version", "kda_last_error", "kda_plan_create", "kda_plan_cre
            "kda_chunk_prefill", "kda_chunk_prefill_gated", "kda_gated_rmsnorm", "kda_prologue", "kda_verify",
            "kda_replay_fold", "kda_fold_verify", "kda_verify_ragged", "kda_state_move", "kda_chunk_split",
            "kda_slots_create", "kda_slots_destroy", "kda_slots_free_count", "kda_slots_owner", "kda_request_open",
-           "kda_request_snapshot", "kda_request_donate", "kda_request_close", "kda_slot_release")
+           "kda_request_snapshot", "kda_request_donate", "kda_request_close", "kda_slot_release", "kda_decode")
 
 
 class KdaError(RuntimeError):
@@ -116,7 +116,8 @@ def lib():
         L.kda_request_donate.argtypes = [vp, ctypes.POINTER(RequestSlots), ctypes.POINTER(i32)]
         L.kda_request_close.argtypes = [vp, ctypes.POINTER(RequestSlots)]
         L.kda_slot_release.argtypes = [vp, i32]
-        for f in ("kda_state_move", "kda_chunk_split", "kda_slots_create", "kda_request_open", "kda_request_snapshot",
+        L.kda_decode.argtypes = [i32] * 6 + [vp] * 11 + [f32] * 3 + [vp] * 3
+        for f in ("kda_decode", "kda_state_move", "kda_chunk_split", "kda_slots_create", "kda_request_open", "kda_request_snapshot",
                   "kda_request_donate", "kda_request_close", "kda_slot_release"):
             getattr(L, f).restype = i32
         for f in ("kda_plan_create", "kda_plan_create_ex", "kda_plan_items", "kda_plan_upload", "kda_chunk_prefill",
@@ -295,6 +296,28 @@ def kda_prologue(cu_seqlens, xq, xk, xv, conv_w, b_raw, g_raw, q, k, v, beta, gk
     _check(lib().kda_prologue(N, T, H, W, _ptr(cu_seqlens), _ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_w),
                               _ptr(conv_state_in), _ptr(conv_state_out), _ptr(b_raw), _ptr(g_raw), float(eps), _ptr(q),
                               _ptr(k), _ptr(v), _ptr(beta), _ptr(gk), _stream(stream)))
+
+
+def kda_decode(xq, xk, xv, conv_w, conv_state, b_raw, g_raw, state_pool, slot_idx, gate, norm_w, y, layer=0,
+               o=None, qk_eps=1e-6, norm_eps=1e-6, scale=1.0, stream=None):
+    """One decode step of a KDA layer in one launch (see kda_decode in include/kda.h): the prologue of each
+    request's new token, the recurrent step with the commit in place, the output gated RMSNorm."""
+    B, H, Dh = xq.shape[0], xq.shape[1], KDA_HEAD_DIM
+    S, L = state_pool.shape[0], state_pool.shape[1]
+    W = conv_w.shape[-1]
+    for name, t in (("xq", xq), ("xk", xk), ("xv", xv), ("gate", gate), ("y", y)):
+        _need(t, name, (B, H, Dh), _BF)
+    _need(conv_w, "conv_w", (3, H * Dh, W), _F32)
+    _need(conv_state, "conv_state", (B, 3, W - 1, H * Dh), _BF, allow_none=W == 1)
+    _need(b_raw, "b_raw", (B, H), _F32)
+    _need(g_raw, "g_raw", (B, H, Dh), _F32)
+    _need(state_pool, "state_pool", (S, L, H, Dh, Dh), _F32)
+    _need(slot_idx, "slot_idx", (B,), _I32)
+    _need(norm_w, "norm_w", (Dh,), _F32)
+    _need(o, "o", (B, H, Dh), _F32, allow_none=True)
+    _check(lib().kda_decode(B, H, L, layer, S, W, _ptr(xq), _ptr(xk), _ptr(xv), _ptr(conv_w), _ptr(conv_state),
+                            _ptr(b_raw), _ptr(g_raw), _ptr(state_pool), _ptr(slot_idx), _ptr(gate), _ptr(norm_w),
+                            float(qk_eps), float(norm_eps), float(scale), _ptr(y), _ptr(o), _stream(stream)))
 
 
 class Ring:

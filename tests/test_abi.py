@@ -287,6 +287,23 @@ def test_state_move_rejects_bad_arguments():
     assert call(n=0, mv=None, pl=None) == 0                      # nothing to do
 
 
+def test_decode_rejects_bad_arguments():
+    L = kda.lib()
+    P = [ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(14)]
+    xq, xk, xv, w, cs, b, g, pool, slots, gate, nw, y, o, _ = P
+
+    def call(B=2, H=4, Lyr=3, layer=1, S=5, W=4, cs_=cs, y_=y, eps=1e-6, scale=1.0):
+        return L.kda_decode(B, H, Lyr, layer, S, W, xq, xk, xv, w, cs_, b, g, pool, slots, gate, nw, eps, eps, scale,
+                            y_, o, None)
+
+    assert call(W=0) == 1 and call(W=9) == 1 and call(layer=3) == 1 and call(H=70000) == 1
+    assert call(eps=-1.0) == 1 and call(scale=float("inf")) == 1
+    assert call(cs_=None) == 1                                  # the conv state is required for W > 1
+    assert call(y_=ctypes.c_void_p(0x10000000 + 16)) == 1       # y overlaps xq
+    assert call(y_=ctypes.c_void_p(0xC0000000 + 8)) == 1        # not 16-byte aligned
+    assert call(B=0) == 0                                       # nothing to do
+
+
 def test_state_move_binding_empty_and_shapes():
     import torch
 

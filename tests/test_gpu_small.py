@@ -977,3 +977,69 @@ def test_prologue_clamps_bounds(gpu):
     (qg, kg, vg), _, _, _ = outs["good"]
     for x_, y_ in ((q, qg), (k, kg), (v, vg)):
         assert np.array_equal(x_[:20], y_[:20])
+
+
+@pytest.mark.parametrize("W", [4, 1])
+def test_decode_fused(gpu, W):
+    """kda_decode (prologue + step with in-place commit + gated RMSNorm in one launch) against the three
+    launches it replaces: y, o, the committed pool and the conv state bit for bit; a request with no
+    slot is skipped whole. End to end against the oracle (prologue, q/k/v rounded to bf16 as the
+    recurrence takes them, the recurrence, the norm): state 2e-3, y 8e-3 per row."""
+    rng = np.random.default_rng(60 + W)
+    B, H, Lyr, S, layer, eps = 3, 4, 2, 6, 1, 1e-6
+    xs = [synth.round_bf16(rng.standard_normal((B, H, 128))) for _ in range(3)]
+    conv_w = (0.5 * rng.standard_normal((3, H * 128, W))).astype(np.float32)
+    cs0 = synth.round_bf16(rng.standard_normal((B, 3, W - 1, H * 128)))
+    b = rng.standard_normal((B, H)).astype(np.float32)
+    g = (2.0 * rng.standard_normal((B, H, 128))).astype(np.float32)
+    gate = synth.round_bf16(rng.standard_normal((B, H, 128)))
+    nw = (1.0 + 0.1 * rng.standard_normal(128)).astype(np.float32)
+    slots = torch.tensor([4, -1, 1], dtype=torch.int32, device=DEV)
+    pool0 = sg.states(60 + W, S * Lyr * H, DEV).view(S, Lyr, H, 128, 128)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    xd = [bf16_dev(x) for x in xs]
+    wd, bd, gd, gated, nwd = dev(conv_w), dev(b), dev(g), bf16_dev(gate), dev(nw)
+    log(f"decode fused W={W}")
+    # fused
+    pool_f, cs_f = pool0.clone(), bf16_dev(cs0)
+    y_f = torch.full((B, H, 128), 9.0, dtype=torch.bfloat16, device=DEV)
+    o_f = torch.full((B, H, 128), 9.0, device=DEV)
+    kda.kda_decode(*xd, wd, cs_f if W > 1 else None, bd, gd, pool_f, slots, gated, nwd, y_f, layer=layer, o=o_f,
+                   qk_eps=eps, norm_eps=eps)
+    # the chain it replaces
+    pool_c = pool0.clone()
+    q, k, v = (torch.empty((B, H, 128), dtype=torch.bfloat16, device=DEV) for _ in range(3))
+    beta, gk = torch.empty((B, H), device=DEV), torch.empty((B, H, 128), device=DEV)
+    cs_out = torch.empty((B, 3, W - 1, H * 128), dtype=torch.bfloat16, device=DEV)
+    kda.kda_prologue(torch.arange(B + 1, dtype=torch.int32, device=DEV), *xd, wd, bd, gd, q, k, v, beta, gk,
+                     conv_state_in=bf16_dev(cs0) if W > 1 else None, conv_state_out=cs_out if W > 1 else None, eps=eps)
+    o_c = torch.full((B, H, 128), 9.0, device=DEV)
+    one = torch.ones(B, dtype=torch.int32, device=DEV)
+    kda.kda_verify(q, k, v, gk, beta, pool_c, slots, o_c, layer=layer, n_tok=1, commit_len=one, commit_pool=pool_c)
+    y_c = torch.empty((B, H, 128), dtype=torch.bfloat16, device=DEV)
+    kda.kda_gated_rmsnorm(o_c, gated, nwd, eps, y_c)
+    torch.cuda.synchronize()
+    ok = [0, 2]
+    assert torch.equal(y_f[ok].view(torch.int16), y_c[ok].view(torch.int16))
+    assert torch.equal(o_f[ok].view(torch.int32), o_c[ok].view(torch.int32))
+    assert torch.equal(pool_f.view(torch.int32), pool_c.view(torch.int32))
+    assert torch.all(y_f[1].float() == 9.0) and torch.all(o_f[1] == 9.0)
+    if W > 1:
+        csf = bits(cs_f).view(np.uint16)
+        assert np.array_equal(csf[ok], bits(cs_out).view(np.uint16)[ok])
+        assert np.array_equal(csf[1], cs0[1])
+    # end to end against the oracle
+    worst_s, worst_y = 0.0, 0.0
+    yb = bits(y_f).view(np.uint16)
+    for r, s in ((0, 4), (2, 1)):
+        st = (cs0[r].astype(np.uint32) << 16).view(np.float32) if W > 1 else np.zeros((3, 0, H * 128))
+        qo, ko, vo, bo, go, _ = oracle.prologue(*(x[r:r + 1] for x in xs), conv_w, st, b[r:r + 1], g[r:r + 1], eps)
+        for h in range(H):
+            qh, kh, vh = (synth.bf16_to_f64(synth.round_bf16(t[:, h])) for t in (qo, ko, vo))
+            o_ref, S_ref, _, _ = oracle.recurrent(qh, kh, vh, go[:, h], bo[:, h], np_(pool0[s, layer, h]))
+            y_ref = oracle.gated_rmsnorm(o_ref, synth.bf16_to_f64(gate[r:r + 1, h]), nw, eps)
+            worst_s = max(worst_s, block_err(np_(pool_f[s, layer, h]), S_ref))
+            yv = synth.bf16_to_f64(yb[r, h])
+            worst_y = max(worst_y, float(np.max(np.abs(yv - y_ref[0])) / np.max(np.abs(y_ref[0]))))
+    log(f"decode fused W={W}: worst state {worst_s:.2e}, y {worst_y:.2e}")
+    assert worst_s <= TOL and worst_y <= 8e-3
