@@ -319,8 +319,45 @@ def bench_long_context(args, torch, kda, sg, synth):
     g.replay()
     graph_us = timed(g.replay, 5)
     dec_bytes = H * (2 * 65536 + 1796)
+    # a whole decode layer from the projections: prologue + step + gated RMSNorm, as three launches per
+    # step (kda_prologue, kda_verify, kda_gated_rmsnorm) and as one (kda_decode), both replayed as graphs
+    W = 4
+    gen = torch.Generator(device=dev).manual_seed(seed)
+    xs = [torch.randn((steps, H, 128), generator=gen, device=dev).to(torch.bfloat16) for _ in range(3)]
+    conv_w = 0.5 * torch.randn((3, H * 128, W), generator=gen, device=dev)
+    cst = [torch.randn((1, 3, W - 1, H * 128), generator=gen, device=dev).to(torch.bfloat16) for _ in range(2)]
+    b_raw = torch.randn((steps, H), generator=gen, device=dev)
+    g_raw = torch.randn((steps, H, 128), generator=gen, device=dev)
+    gate = torch.randn((steps, H, 128), generator=gen, device=dev).to(torch.bfloat16)
+    norm_w = 1.0 + 0.1 * torch.randn((128,), generator=gen, device=dev)
+    y = torch.empty((steps, H, 128), dtype=torch.bfloat16, device=dev)
+    q, k, v = (torch.empty((1, H, 128), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    beta, gk, o1 = torch.empty((1, H), device=dev), torch.empty((1, H, 128), device=dev), torch.empty((1, H, 128), device=dev)
+    cu1 = torch.tensor([0, 1], dtype=torch.int32, device=dev)
+
+    def chain():
+        for t in range(steps):
+            kda.kda_prologue(cu1, xs[0][t:t + 1], xs[1][t:t + 1], xs[2][t:t + 1], conv_w, b_raw[t:t + 1],
+                             g_raw[t:t + 1], q, k, v, beta, gk, conv_state_in=cst[t & 1], conv_state_out=cst[1 - (t & 1)])
+            kda.kda_verify(q, k, v, gk, beta, pool, slot, o1, layer=0, n_tok=1, commit_len=one, commit_pool=pool)
+            kda.kda_gated_rmsnorm(o1, gate[t:t + 1], norm_w, 1e-6, y[t:t + 1])
+
+    def fused():
+        for t in range(steps):
+            kda.kda_decode(xs[0][t:t + 1], xs[1][t:t + 1], xs[2][t:t + 1], conv_w, cst[0], b_raw[t:t + 1],
+                           g_raw[t:t + 1], pool, slot, gate[t:t + 1], norm_w, y[t:t + 1])
+
+    graphs = {}
+    for name, fn in (("chain", chain), ("fused", fused)):
+        fn()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn()
+        gr.replay()
+        graphs[name] = timed(gr.replay, 5)
     return dict(ms=ms, bytes=byts, gbs=byts / (ms * 1e-3) / 1e9, T=T, H=H, items=kda.kda_plan_num_items(plan),
-                eager_us=eager_us, graph_us=graph_us, dec_gbs=dec_bytes / (graph_us * 1e-6) / 1e9)
+                eager_us=eager_us, graph_us=graph_us, dec_gbs=dec_bytes / (graph_us * 1e-6) / 1e9,
+                layer_chain_us=graphs["chain"], layer_fused_us=graphs["fused"])
 
 
 def bench_verify_fold(args, torch, kda, sg, synth):
@@ -572,9 +609,13 @@ def main():
             "prefill_gbs": lc["gbs"], "prefill_hbm_frac": lc["gbs"] / HBM_PEAK_GBS, "prefill_items": lc["items"],
             "decode_us_per_step_eager": lc["eager_us"], "decode_us_per_step_graph": lc["graph_us"],
             "decode_gbs_graph": lc["dec_gbs"], "decode_hbm_frac_graph": lc["dec_gbs"] / HBM_PEAK_GBS,
+            "decode_layer_us_per_step_three_launches": lc["layer_chain_us"],
+            "decode_layer_us_per_step_fused": lc["layer_fused_us"],
             "workload": "1 x 1,048,576 tokens, H=96, snapshots every 4096 into 2 slots (automatic plan: two value "
                         "blocks per head), then 128 single-token decode steps (kda_verify n_tok=1, in-place commit), "
-                        "one launch per step and as one replayed HIP graph",
+                        "one launch per step and as one replayed HIP graph; and a whole decode layer from the "
+                        "projections (conv width 4, gated output norm) as kda_prologue + kda_verify + "
+                        "kda_gated_rmsnorm per step vs one kda_decode per step, both replayed as graphs",
         }
     if mvs is not None:
         line["state_moves"] = {
