@@ -72,7 +72,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs A) {
       }
     }
     // taps 0 .. W - 2 are the carried rows (row W - 2 the newest), tap W - 1 the token itself
-    uint16_t* cs = A.conv_state + ((int64_t)b * 3 + which) * (W - 1) * HC + ch;
+    uint16_t* cs = W > 1 ? A.conv_state + ((int64_t)b * 3 + which) * (W - 1) * HC + ch : nullptr;  // none at W = 1
     const uint4 xr = *reinterpret_cast<const uint4*>(x + row * D + 8 * cg);
     uint4 tr[W > 1 ? W - 1 : 1];
 #pragma unroll
