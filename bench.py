@@ -86,7 +86,7 @@ def settle(step, torch, seconds=0.25):
 def bench_prefill(args, torch, kda, sg, synth):
     dev = "cuda:0"
     N, L, H = 4, 2048, 64
-    cfg = synth.PREFILL_CONFIGS[1]
+    cfg = synth.PREFILL_CONFIGS["prefill_4x2048_h64"]
     seed = cfg["seed"]
     cu = synth.cu_seqlens([L] * N)
     T = int(cu[-1])
@@ -127,7 +127,7 @@ def bench_prefill_gated(args, torch, kda, sg, synth):
     the same two steps unfused (kda_chunk_prefill, then kda_gated_rmsnorm over its fp32 o)."""
     dev = "cuda:0"
     N, L, H = 4, 2048, 64
-    seed = synth.PREFILL_CONFIGS[1]["seed"]
+    seed = synth.PREFILL_CONFIGS["prefill_4x2048_h64"]["seed"]
     cu = synth.cu_seqlens([L] * N)
     T = int(cu[-1])
     q, k, v, gk, beta = sg.prefill_inputs(seed, T, H, dev)
@@ -181,7 +181,7 @@ def bench_prologue(args, torch, kda, sg, synth):
 
     dev = "cuda:0"
     N, L, H, W = 4, 2048, 64, 4
-    seed = synth.PREFILL_CONFIGS[1]["seed"]
+    seed = synth.PREFILL_CONFIGS["prefill_4x2048_h64"]["seed"]
     cu = torch.from_numpy(synth.cu_seqlens([L] * N).astype(np.int32)).to(dev)
     T = N * L
     g = torch.Generator(device=dev).manual_seed(seed)
@@ -255,7 +255,7 @@ def bench_long_context(args, torch, kda, sg, synth):
     decode steps from its final state (kda_verify, n_tok = 1, commit in place), launched one by one and
     as one replayed HIP graph."""
     dev = "cuda:0"
-    c = synth.PREFILL_CONFIGS[4]
+    c = synth.PREFILL_CONFIGS["long_1m_h96"]
     seed, H, T = c["seed"], c["H"], sum(c["lengths"])
     torch.cuda.empty_cache()  # about 180 GB of inputs and outputs follow
     cu = synth.cu_seqlens([T])
@@ -479,7 +479,7 @@ def cpu_baseline(synth, oracle):
     """The fp64 oracle, as it is, on this host's cores: every (sequence, head) unit of the
     prefill workload (4 x 2048 tokens x 64 heads). Input generation is not timed."""
     N, L, H = 4, 2048, 64
-    seed = synth.PREFILL_CONFIGS[1]["seed"]
+    seed = synth.PREFILL_CONFIGS["prefill_4x2048_h64"]["seed"]
     threads = min(16, os.cpu_count() or 1)
     units = [(n, h) for n in range(N) for h in range(H)]
     data = {}

@@ -139,10 +139,10 @@ def trimmed_windows(seed, n, cap=8):
 
 PREFILL_CONFIGS = {
     # name: (seed, lengths spec, heads, qkv dtype, initial state, snap interval, snap slots)
-    0: dict(seed=0, N=1, lengths=[64], H=1, state_in="zero", snap_interval=0, snap_slots=0),
-    1: dict(seed=1, N=4, lengths=[2048] * 4, H=64, state_in="normal", snap_interval=0, snap_slots=0),
-    2: dict(seed=2, N=32, lengths="loguniform", H=96, state_in=None, snap_interval=2048, snap_slots=2),
-    4: dict(seed=4, N=1, lengths=[1048576], H=96, state_in=None, snap_interval=4096, snap_slots=2),
+    "single_64": dict(seed=0, N=1, lengths=[64], H=1, state_in="zero", snap_interval=0, snap_slots=0),
+    "prefill_4x2048_h64": dict(seed=1, N=4, lengths=[2048] * 4, H=64, state_in="normal", snap_interval=0, snap_slots=0),
+    "varlen_h96": dict(seed=2, N=32, lengths="loguniform", H=96, state_in=None, snap_interval=2048, snap_slots=2),
+    "long_1m_h96": dict(seed=4, N=1, lengths=[1048576], H=96, state_in=None, snap_interval=4096, snap_slots=2),
 }
 
 VERIFY_CONFIG = dict(seed=3, B=256, L=69, H=8, T=8, R=16, accept_mean=2.7)
@@ -150,7 +150,7 @@ DECODE_STEPS = 128  # single-token decode steps after the long prefill
 
 
 def prefill_lengths(cfg):
-    c = PREFILL_CONFIGS[cfg] if isinstance(cfg, int) else cfg
+    c = PREFILL_CONFIGS[cfg] if isinstance(cfg, str) else cfg
     if isinstance(c["lengths"], str):
         return loguniform_lengths(c["seed"], c["N"])
     return np.asarray(c["lengths"], dtype=np.int64)

@@ -57,7 +57,7 @@ def prefill_run(cfg, lens, H, state_in=None, snap_slots=0, order=kda.KDA_PLAN_LP
     snap = torch.full((N, snap_slots, H, 128, 128), -5.0, device=DEV) if snap_slots else None
     cnt = torch.full((N,), -1, dtype=torch.int32, device=DEV)
     ms = prefill_launch(plan, ins, o, st, snap, cnt, snap_slots, state_in=state_in)
-    log(f"prefill config {cfg}: {kda.kda_plan_num_items(plan)} items ({kda.kda_plan_v_blocks(plan)} value "
+    log(f"prefill {cfg}: {kda.kda_plan_num_items(plan)} items ({kda.kda_plan_v_blocks(plan)} value "
         f"block(s) each), {ms:.2f} ms")
     return plan, cu, ins, o, st, snap, cnt
 
@@ -93,9 +93,9 @@ def test_prefill_4x2048_h64_all_units(gpu):
     H = 64
     log("prefill 4x2048 H64: GPU run")
     S0 = sg.states(1, 4 * H, DEV).view(4, H, 128, 128)
-    plan, cu, ins, o, st, _, _ = prefill_run(1, lens, H, state_in=S0)
+    plan, cu, ins, o, st, _, _ = prefill_run("prefill_4x2048_h64", lens, H, state_in=S0)
     log("prefill 4x2048 H64: oracle on all 256 units")
-    worst, _ = check_units(1, cu, H, [(n, h) for n in range(4) for h in range(H)], o, st, S0=np_(S0))
+    worst, _ = check_units("prefill_4x2048_h64", cu, H, [(n, h) for n in range(4) for h in range(H)], o, st, S0=np_(S0))
     log(f"prefill 4x2048 H64 worst {worst}")
     assert max(worst.values()) <= TOL
 
@@ -104,7 +104,7 @@ def test_prefill_gated_4x2048_h64(gpu):
     """The headline prefill with the output gated RMSNorm fused in: y bit-identical to the plain prefill
     followed by kda_gated_rmsnorm on all 524,288 (token, head) rows, the final states bit-identical, and
     two heads of y against the oracle (fp64 prefill, then the norm) at the pages' 8e-3."""
-    c = synth.PREFILL_CONFIGS[1]
+    c = synth.PREFILL_CONFIGS["prefill_4x2048_h64"]
     seed, lens, H, eps = c["seed"], c["lengths"], c["H"], 1e-6
     cu = synth.cu_seqlens(lens)
     T, N = int(cu[-1]), len(lens)
@@ -192,13 +192,13 @@ def test_prologue_4x2048_h64(gpu):
 
 def test_prefill_varlen_h96_snapshots(gpu):
     H = 96
-    lens = synth.prefill_lengths(2)
+    lens = synth.prefill_lengths("varlen_h96")
     log(f"prefill varlen: {len(lens)} sequences, total {int(lens.sum())} tokens, max {int(lens.max())}")
-    plan, cu, ins, o, st, snap, cnt = prefill_run(2, lens, H, snap_slots=2)
+    plan, cu, ins, o, st, snap, cnt = prefill_run("varlen_h96", lens, H, snap_slots=2)
     # counts are exact integers for every sequence
     assert np.array_equal(np_(cnt), lens // 2048)
     # longest-first and input order give the same bits
-    _, _, _, o2, st2, snap2, _ = prefill_run(2, lens, H, snap_slots=2, order=kda.KDA_PLAN_FIFO)
+    _, _, _, o2, st2, snap2, _ = prefill_run("varlen_h96", lens, H, snap_slots=2, order=kda.KDA_PLAN_FIFO)
     assert torch.equal(o, o2) and torch.equal(st, st2) and torch.equal(snap, snap2)
     del o2, st2, snap2
     longest, shortest = int(np.argmax(lens)), int(np.argmin(lens))
@@ -207,7 +207,7 @@ def test_prefill_varlen_h96_snapshots(gpu):
     units += [(int(rng.integers(len(lens))), int(rng.integers(H))) for _ in range(24)]
     units = sorted(set(units))
     log(f"prefill varlen: oracle on {len(units)} units")
-    worst, _ = check_units(2, cu, H, units, o, st, snap=snap, snap_slots=2, interval=2048)
+    worst, _ = check_units("varlen_h96", cu, H, units, o, st, snap=snap, snap_slots=2, interval=2048)
     log(f"prefill varlen worst {worst}")
     assert max(worst.values()) <= TOL
 
@@ -361,12 +361,12 @@ def test_spec_step_256x69x8(gpu):
 
 def test_long_context_1m_then_decode(gpu):
     H, T = 96, 1048576
-    cfg = synth.PREFILL_CONFIGS[4]
+    cfg = synth.PREFILL_CONFIGS["long_1m_h96"]
     seed = cfg["seed"]
     log("long context: generating 1M x 96 inputs on the device")
     # 96 (sequence, head) chains for 256 compute units: the automatic plan splits each into two
     # value blocks; the whole-chain plan must give the same bits
-    plan, cu, ins, o, st, snap, cnt = prefill_run(4, [T], H, snap_slots=2, v_blocks=0)
+    plan, cu, ins, o, st, snap, cnt = prefill_run("long_1m_h96", [T], H, snap_slots=2, v_blocks=0)
     assert int(cnt[0]) == T // 4096
     heads = [7, 60]
     o_np = {h: np_(o[:, h]) for h in heads}

@@ -400,9 +400,9 @@ def test_fold_bitexact_every_length(gpu, T, accs):
     assert worst <= TOL
 
 
-def test_verify_fp32_inputs_config0(gpu):
+def test_verify_fp32_single_head_64(gpu):
     """Single sequence, 1 head, T = 64, fp32 everything, zero initial state (token-by-token path)."""
-    log("config 0 verify fp32")
+    log("single head x 64 tokens: verify on fp32 inputs")
     T, H = 64, 1
     q, k, v, gk, beta = sg.prefill_inputs(0, T, H, DEV, qkv_dtype=torch.float32)
     pool = torch.zeros((1, 1, H, 128, 128), device=DEV)
@@ -414,7 +414,7 @@ def test_verify_fp32_inputs_config0(gpu):
     hq, hk, hv, hg, hb = synth.prefill_rows(0, H, 0, T, h=0, qkv_dtype=synth.F32)
     o_ref, S_ref, _, _ = oracle.recurrent(hq, hk, hv, hg, hb)
     e_o, e_s = block_err(np_(o[:, 0]), o_ref), block_err(np_(commit[0, 0, 0]), S_ref)
-    log(f"config 0 fp32 verify: o {e_o:.2e} state {e_s:.2e}")
+    log(f"single head fp32 verify: o {e_o:.2e} state {e_s:.2e}")
     assert e_o <= TOL and e_s <= TOL
 
 
@@ -499,15 +499,15 @@ def test_prefill_value_blocks_bitwise(gpu, v_blocks):
         assert kda.kda_plan_v_blocks(split) == 2
 
 
-def test_prefill_config0_bf16(gpu):
-    """Config 0 through the chunked path on bf16-rounded q/k/v (the same draws)."""
+def test_prefill_single_head_64_bf16(gpu):
+    """The single-head 64-token fp32 case through the chunked path on bf16-rounded q/k/v (the same draws)."""
     lens = np.array([64])
     plan = kda.kda_plan_create(synth.cu_seqlens(lens), n_heads=1)
     ins = sg.prefill_inputs(0, 64, 1, DEV)
     o, st, _, cnt = run_prefill(plan, ins)
     torch.cuda.synchronize()
     w = check_prefill(0, plan, lens, 1, o, st, None, cnt)
-    log(f"config 0 chunked: {w}")
+    log(f"single head x 64 tokens, chunked: {w}")
     assert max(w.values()) <= TOL
 
 

@@ -103,7 +103,7 @@ def test_distributions():
 
 
 def test_workload_recipes():
-    L2 = synth.prefill_lengths(2)
+    L2 = synth.prefill_lengths("varlen_h96")
     assert len(L2) == 32 and L2.min() >= 64 and L2.max() <= 24576
     big = synth.loguniform_lengths(123, 200000)
     assert abs(big.mean() - (24576 - 64) / math.log(24576 / 64)) < 60  # log-uniform mean
