@@ -16,7 +16,8 @@
 // place) and kda_gated_rmsnorm run one after another, bit for bit.
 //
 // One 256-thread workgroup per (request, head). Wave 0: lanes 16 j + c (j = 0, 1, 2 for q, k, v) hold
-// channels 8c .. 8c + 7 of projection j; lanes 48..63 and the other waves take the gate. A request whose
+// channels 8c .. 8c + 7 of projection j, while wave 1 computes exp(gk) and wave 3 fetches the output
+// gate and norm weights, so that their loads overlap; wave 3 applies the norm at the end. A request whose
 // slot is outside [0, n_slots) is skipped whole (its conv state is not touched).
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -56,6 +57,26 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs A) {
 
   const int64_t HC = (int64_t)H * D;
   const size_t row = (size_t)b * H + h;  // the token's (request, head) row
+  // wave 3, lanes 0..15: the norm's gate and weights, fetched now so the loads overlap the prologue
+  const int s16 = lane & 15, wq = s16 >> 2, qq = s16 & 3;
+  const int ca = 32 * wq + 4 * qq, cb = ca + 16;
+  uint2 ga = make_uint2(0u, 0u), gb = make_uint2(0u, 0u);
+  float4 wa = make_float4(0.f, 0.f, 0.f, 0.f), wb = wa;
+  if (wave == 3 && lane < 16) {
+    const uint16_t* grow = A.gate + row * D;
+    ga = *reinterpret_cast<const uint2*>(grow + ca);
+    gb = *reinterpret_cast<const uint2*>(grow + cb);
+    wa = *reinterpret_cast<const float4*>(A.norm_w + ca);
+    wb = *reinterpret_cast<const float4*>(A.norm_w + cb);
+  }
+  // wave 1, lanes 0..31: exp(gk) of the token while wave 0 runs the prologue (the verify kernel's
+  // staging: a = exp(gk) with gk = -softplus(g); a * k follows once k is in LDS)
+  if (wave == 1 && lane < 32) {
+    const int c4 = 4 * lane;
+    const float4 g4 = *reinterpret_cast<const float4*>(A.g_raw + row * D + c4);
+    const float gk0 = neg_softplus(g4.x), gk1 = neg_softplus(g4.y), gk2 = neg_softplus(g4.z), gk3 = neg_softplus(g4.w);
+    *reinterpret_cast<float4*>(&L.a[0][c4]) = make_float4(expf(gk0), expf(gk1), expf(gk2), expf(gk3));
+  }
   if (wave == 0 && lane < 48) {
     const int which = lane >> 4, cg = lane & 15;
     const int ch = h * D + 8 * cg;
@@ -118,14 +139,11 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs A) {
   }
   if (wave == 0 && lane == 48) L.beta[0] = sigmoid_fast(A.b_raw[row]);
   __syncthreads();
-  if (tid < 32) {  // the verify kernel's staging of step 0: a = exp(gk), ak = a * k
-    const int c4 = 4 * tid;
-    const float4 g4 = *reinterpret_cast<const float4*>(A.g_raw + row * D + c4);
-    const float gk0 = neg_softplus(g4.x), gk1 = neg_softplus(g4.y), gk2 = neg_softplus(g4.z), gk3 = neg_softplus(g4.w);
-    const float a0 = expf(gk0), a1 = expf(gk1), a2 = expf(gk2), a3 = expf(gk3);
+  if (wave == 1 && lane < 32) {  // ak = a * k, as the verify kernel stages it
+    const int c4 = 4 * lane;
+    const float4 a4 = *reinterpret_cast<const float4*>(&L.a[0][c4]);
     const float4 k4 = *reinterpret_cast<const float4*>(&L.k[0][c4]);
-    *reinterpret_cast<float4*>(&L.a[0][c4]) = make_float4(a0, a1, a2, a3);
-    *reinterpret_cast<float4*>(&L.ak[0][c4]) = make_float4(a0 * k4.x, a1 * k4.y, a2 * k4.z, a3 * k4.w);
+    *reinterpret_cast<float4*>(&L.ak[0][c4]) = make_float4(a4.x * k4.x, a4.y * k4.y, a4.z * k4.z, a4.w * k4.w);
   }
   __syncthreads();
   step_update(S, L, 0, r0, col0);
@@ -148,16 +166,9 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs A) {
   }
   store_state(S, A.state_pool + unit * D * D, r0, col0);  // the commit, in place
   __syncthreads();
-  if (tid < 16) {  // the norm kernel's row: lane s holds slice s, sums gathered in slice order
-    const int s = tid, wq = s >> 2, q = s & 3;
-    const int ca = 32 * wq + 4 * q, cb = ca + 16;
+  if (wave == 3 && lane < 16) {  // the norm kernel's row: lane s holds slice s, sums gathered in slice order
     const f32x4 oa = *reinterpret_cast<const f32x4*>(&L.o[ca]);
     const f32x4 ob = *reinterpret_cast<const f32x4*>(&L.o[cb]);
-    const uint16_t* grow = A.gate + row * D;
-    const uint2 ga = *reinterpret_cast<const uint2*>(grow + ca);
-    const uint2 gb = *reinterpret_cast<const uint2*>(grow + cb);
-    const float4 wa = *reinterpret_cast<const float4*>(A.norm_w + ca);
-    const float4 wb = *reinterpret_cast<const float4*>(A.norm_w + cb);
     const float part = norm_slice_ssq(oa, ob);
     float ss = 0.f;
 #pragma unroll
