@@ -65,7 +65,7 @@
  * Conventions for every entry point:
  *  - Pointers to tensors are DEVICE pointers unless the name ends in _host.
  *    The caller owns every buffer; the library never allocates device
- *    memory. A plan owns pinned host memory only.
+ *    memory. A plan owns pinned host memory only (see kda_plan_destroy).
  *  - Layouts are row-major (C order); the last dimension is the head
  *    dimension 128. bf16 tensors hold IEEE bfloat16 bit patterns.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
@@ -134,7 +134,8 @@ typedef struct kda_plan kda_plan;
  * snap_interval: 0 = no snapshots; else a positive multiple of KDA_CHUNK.
  * order: KDA_PLAN_LPT or KDA_PLAN_FIFO.
  * *out receives an immutable plan, shareable across streams and threads.
- * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_HOST_ALLOC.
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_HOST_ALLOC; KDA_ERR_DEVICE if giving back the
+ * pinned buffers of destroyed plans failed (kda_host_release; no plan is made).
  */
 kda_status kda_plan_create(const int32_t* cu_seqlens_host, int n_seq, int n_heads,
                            int snap_interval, int order, kda_plan** out);
@@ -168,12 +169,28 @@ kda_status kda_plan_items(const kda_plan* plan, int32_t* items_host);
 
 /* Enqueue the upload of the work list into `workspace` (device, at least
  * kda_plan_workspace_bytes) and zero its counters. The copy reads the plan's
- * pinned host buffer asynchronously: destroy the plan only after the stream
- * has passed this point. */
+ * pinned host buffer asynchronously; destroying the plan right after the call
+ * is safe (its buffer is only queued for release, see kda_plan_destroy). */
 kda_status kda_plan_upload(const kda_plan* plan, void* workspace, void* stream);
 
-/* Free a plan (NULL is a no-op). */
-void kda_plan_destroy(kda_plan* plan);
+/*
+ * Free a plan (NULL is a no-op). Makes no HIP runtime call, so it is safe
+ * anywhere, including in a garbage collector's finalizer that runs while a
+ * graph is being captured: the plan's pinned buffer is queued and given back
+ * by the next kda_host_release (which every kda_plan_create calls first).
+ * Errors: KDA_ERR_HOST_ALLOC if the queue cannot grow (the buffer is then
+ * leaked until the process ends; the plan itself is freed).
+ */
+kda_status kda_plan_destroy(kda_plan* plan);
+
+/*
+ * Free the pinned buffers of destroyed plans (hipHostFree, which waits for
+ * the device). Call it outside graph capture; kda_plan_create and
+ * kda_plan_create_ex call it before they allocate, and report its failure as
+ * theirs. Errors: KDA_ERR_DEVICE with the runtime's text if any free fails
+ * (every queued buffer is attempted once and dropped from the queue).
+ */
+kda_status kda_host_release(void);
 
 /* Inputs of one layer. q, k, v: [rows, H, 128] in the call's q/k/v dtype;
  * gk: fp32 [rows, H, 128], per-token per-key-channel log-decay, gk <= 0;

@@ -49,6 +49,18 @@ constexpr size_t kState = (size_t)KDA_HEAD_DIM * KDA_HEAD_DIM * sizeof(float);
 
 }  // namespace
 
+namespace {
+
+// Pinned work-list buffers of destroyed plans. kda_plan_destroy makes no HIP
+// runtime call (it may run from a garbage collector's finalizer, at any
+// moment, including while another thread or the same one captures a graph,
+// where a synchronising call such as hipHostFree would invalidate the
+// capture); it queues the buffer here and kda_host_release frees it later.
+std::mutex g_released_mu;
+std::vector<void*> g_released;
+
+}  // namespace
+
 struct kda_plan {
   int n_seq = 0, n_heads = 0, snap_interval = 0, order = 0, v_blocks = 1, n_items = 0;
   int64_t total_tokens = 0;
@@ -69,10 +81,36 @@ kda_status kda_plan_create(const int32_t* cu_seqlens_host, int n_seq, int n_head
   return kda_plan_create_ex(cu_seqlens_host, n_seq, n_heads, snap_interval, order, 1, out);
 }
 
+kda_status kda_host_release(void) {
+  std::vector<void*> bufs;
+  {
+    std::lock_guard<std::mutex> lock(g_released_mu);
+    bufs.swap(g_released);
+  }
+  std::string err;
+  size_t failed = 0;
+  for (void* b : bufs) {
+    const hipError_t e = hipHostFree(b);
+    if (e != hipSuccess) {
+      if (failed++ == 0) err = hipGetErrorString(e);
+    }
+  }
+  if (failed)
+    return fail(KDA_ERR_DEVICE, "kda_host_release: hipHostFree failed for " + std::to_string(failed) + " of " +
+                                    std::to_string(bufs.size()) + " buffers: " + err);
+  return ok();
+}
+
 kda_status kda_plan_create_ex(const int32_t* cu_seqlens_host, int n_seq, int n_heads, int snap_interval,
                               int order, int v_blocks, kda_plan** out) {
   if (!out) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: out is NULL");
   *out = nullptr;
+  {
+    // creating a plan allocates pinned memory (not allowed under capture either), so it is
+    // also where the buffers of destroyed plans are given back
+    const kda_status rs = kda_host_release();
+    if (rs != KDA_OK) return fail(rs, std::string("kda_plan_create: ") + kda_last_error());
+  }
   if (!cu_seqlens_host) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: cu_seqlens_host is NULL");
   if (n_seq < 1 || n_heads < 1) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: n_seq and n_heads must be >= 1");
   if (n_heads > 0xffff) return fail(KDA_ERR_INVALID_ARG, "kda_plan_create: n_heads must be <= 65535");
@@ -161,11 +199,22 @@ kda_status kda_plan_upload(const kda_plan* p, void* workspace, void* stream) {
   return ok();
 }
 
-void kda_plan_destroy(kda_plan* p) {
-  if (!p) return;
-  if (p->pinned) (void)hipHostFree(p->upload);
-  else std::free(p->upload);
+kda_status kda_plan_destroy(kda_plan* p) {
+  if (!p) return ok();
+  if (p->pinned) {
+    std::lock_guard<std::mutex> lock(g_released_mu);
+    try {
+      g_released.push_back(p->upload);  // freed by the next kda_host_release (no HIP call here)
+    } catch (...) {
+      // the queue could not grow: the buffer stays allocated until the process ends
+      delete p;
+      return fail(KDA_ERR_HOST_ALLOC, "kda_plan_destroy: no host memory to queue the pinned buffer (leaked)");
+    }
+  } else {
+    std::free(p->upload);
+  }
   delete p;
+  return ok();
 }
 
 // kda_chunk_prefill and kda_chunk_prefill_gated: the same checks and launch; the gated form writes

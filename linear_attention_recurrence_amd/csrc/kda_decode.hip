@@ -29,14 +29,15 @@ namespace kda {
 
 namespace {
 
-struct DecodeLds {
+// 16-byte aligned, and beta after o: o is read and written as 16-byte vectors
+struct alignas(16) DecodeLds {
   float a[1][D];
   float ak[1][D];
   float k[1][D];
   float q[1][D];
   float v[1][D];
-  float beta[1];
   float o[D];
+  float beta[4];
 };
 
 template <int W>

@@ -32,6 +32,7 @@ KDA_CHUNK = 32
 
 EXPORTS = ("kda_abi_version", "kda_last_error", "kda_plan_create", "kda_plan_create_ex", "kda_plan_v_blocks",
            "kda_plan_workspace_bytes", "kda_plan_num_items", "kda_plan_items", "kda_plan_upload", "kda_plan_destroy",
+           "kda_host_release",
            "kda_chunk_prefill", "kda_chunk_prefill_gated", "kda_gated_rmsnorm", "kda_prologue", "kda_verify",
            "kda_replay_fold", "kda_fold_verify", "kda_verify_ragged", "kda_state_move", "kda_chunk_split",
            "kda_slots_create", "kda_slots_destroy", "kda_slots_free_count", "kda_slots_owner", "kda_request_open",
@@ -87,7 +88,9 @@ def lib():
         L.kda_plan_items.argtypes = [vp, vp]
         L.kda_plan_upload.argtypes = [vp, vp, vp]
         L.kda_plan_destroy.argtypes = [vp]
-        L.kda_plan_destroy.restype = None
+        L.kda_plan_destroy.restype = i32
+        L.kda_host_release.argtypes = []
+        L.kda_host_release.restype = i32
         L.kda_chunk_prefill.argtypes = [vp, ctypes.POINTER(_Inputs), vp, vp, vp, vp, i32, vp, vp, f32, i32, vp]
         L.kda_chunk_prefill_gated.argtypes = [vp, ctypes.POINTER(_Inputs), vp, vp, f32, vp, vp, vp, vp, i32, vp, vp,
                                               f32, i32, vp]
@@ -170,7 +173,10 @@ def kda_last_error():
 
 
 class Plan:
-    """Owner of a kda_plan* (host data only); destroyed with the object."""
+    """Owner of a kda_plan* (host data only). close() (or leaving a `with` block) destroys it; so does
+    garbage collection. kda_plan_destroy makes no HIP call, so a finalizer that runs while a graph is
+    being captured cannot disturb the capture (the pinned buffer is given back by a later
+    kda_plan_create or kda_host_release)."""
 
     def __init__(self, handle, cu_seqlens, n_heads, snap_interval):
         self.handle = handle
@@ -180,10 +186,26 @@ class Plan:
         self.snap_interval = snap_interval
         self.total_tokens = int(cu_seqlens[-1])
 
+    def close(self):
+        h, self.handle = getattr(self, "handle", None), None
+        if h:
+            _check(lib().kda_plan_destroy(h))
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
     def __del__(self):
-        if getattr(self, "handle", None) and _lib is not None:
-            _lib.kda_plan_destroy(self.handle)
-            self.handle = None
+        h, self.handle = getattr(self, "handle", None), None
+        if h and _lib is not None:
+            _lib.kda_plan_destroy(h)  # status not raised from a finalizer
+
+
+def kda_host_release():
+    """Free the pinned buffers of destroyed plans (not during graph capture)."""
+    _check(lib().kda_host_release())
 
 
 def kda_plan_create(cu_seqlens_host, n_heads, snap_interval=0, order=KDA_PLAN_LPT, v_blocks=1):

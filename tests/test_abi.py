@@ -35,6 +35,21 @@ def test_exports_every_declared_symbol():
     assert kda.kda_abi_version() == 4
 
 
+def test_plan_destroy_and_release():
+    """kda_plan_destroy returns a status (NULL is a no-op) and never needs the device; kda_host_release
+    with nothing queued (or the buffers of plans destroyed here, pageable without a device) is OK."""
+    L = kda.lib()
+    assert L.kda_plan_destroy(None) == K.KDA_OK
+    plans = [kda.kda_plan_create([0, 40, 75], n_heads=2) for _ in range(3)]
+    plans[0].close()
+    plans[0].close()  # a second close is a no-op
+    with plans[1] as p:
+        assert kda.kda_plan_num_items(p) == 4
+    assert plans[1].handle is None
+    del plans
+    kda.kda_host_release()
+
+
 def test_plan_lpt_order_and_ties():
     cu = [0, 5, 100, 100, 140, 235]  # lengths 5, 95, 0, 40, 95
     p = kda.kda_plan_create(cu, n_heads=3)

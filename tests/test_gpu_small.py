@@ -939,6 +939,50 @@ def test_graph_replay_prefill_and_verify(gpu):
                 assert torch.equal(a, b), f"{name}: eager call after replay {r} differs"
 
 
+def test_plan_destroy_inside_capture(gpu):
+    """Destroying plans while a graph is being captured (explicitly, and by the garbage collector
+    finalizing a plan held in a reference cycle) leaves the capture valid: kda_plan_destroy makes no HIP
+    call. The captured prefill, replayed, equals the eager call bit for bit; a later kda_host_release
+    gives the queued pinned buffers back."""
+    import gc
+    lens = [33, 70]
+    cu = synth.cu_seqlens(lens)
+    T, N, H = int(cu[-1]), len(lens), 2
+    plan = kda.kda_plan_create(cu, n_heads=H)
+    ins = sg.prefill_inputs(13, T, H, DEV)
+    ws = torch.empty(kda.kda_plan_workspace_bytes(plan), dtype=torch.uint8, device=DEV)
+    kda.kda_plan_upload(plan, ws)
+    o = torch.empty((T, H, 128), device=DEV)
+    st = torch.empty((N, H, 128, 128), device=DEV)
+
+    def prefill():
+        kda.kda_chunk_prefill(plan, *ins, st, o, ws, flags=kda.KDA_PREFILL_PLAN_RESIDENT)
+
+    prefill()
+    torch.cuda.synchronize()
+    ref = (o.clone(), st.clone())
+    doomed = [kda.kda_plan_create(cu, n_heads=H) for _ in range(3)]
+    cyc = {"plan": doomed[2]}
+    cyc["self"] = cyc  # only the cyclic collector frees this one
+    del doomed[2]
+    log("plan destroy inside capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        prefill()
+        doomed[0].close()
+        del doomed[1]
+        del cyc
+        gc.collect()
+    for r in range(2):
+        o.fill_(float("nan"))
+        st.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int32), ref[0].view(torch.int32)), f"replay {r}: o"
+        assert torch.equal(st.view(torch.int32), ref[1].view(torch.int32)), f"replay {r}: state"
+    kda.kda_host_release()
+
+
 def test_state_move_many_moves(gpu):
     """More moves than one grid dimension holds (70,000 > 65,535): the kernel strides over the moves.
     Slots of 4 floats; every even slot is copied to the next odd one, bit for bit."""
@@ -979,7 +1023,7 @@ def test_prologue_clamps_bounds(gpu):
         assert np.array_equal(x_[:20], y_[:20])
 
 
-@pytest.mark.parametrize("W", [4, 1])
+@pytest.mark.parametrize("W", [4, 1, 2, 8])
 def test_decode_fused(gpu, W):
     """kda_decode (prologue + step with in-place commit + gated RMSNorm in one launch) against the three
     launches it replaces: y, o, the committed pool and the conv state bit for bit; a request with no
