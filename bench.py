@@ -1,27 +1,32 @@
 """Benchmark of the KDA hot path on one MI355X.
 
 Headline (``value``): chunked-prefill throughput in tokens*heads/s on the
-workload "4 sequences x 2048 tokens, H = 64, K = V = 128, bf16 q/k/v, fp32
-gk/beta/state, state_in ~ N(0, 0.1^2)". One step = one kda_chunk_prefill call
-with the work list resident (one persistent-kernel launch), timed with HIP
-events on the launch stream. Beside it, in the same JSON line:
+largest prefill workload, "1 sequence of 1,048,576 tokens, H = 96, K = V =
+128, bf16 q/k/v, fp32 gk/beta/state, snapshots every 4096 tokens into 2
+ping-pong slots". One step = one kda_chunk_prefill call with the work list
+resident (one persistent-kernel launch); each step is timed with HIP events on
+the launch stream, after a 1 GiB scratch write (outside the timed region) that
+evicts the caches. Beside it, in the same JSON line:
 
-* ``verify_fold``: one speculative step of the workload "256 requests x 69
-  layers x 8 heads, gamma + 1 = 8 bf16 draft tokens, ring length 16, accepted
-  lengths geometric (mean 2.7, clipped to [1, 8])" = 69 kda_verify launches +
-  one kda_replay_fold launch, in us/step (committed states restored from a
+* ``roofline``: HBM roofline of that prefill kernel (algorithmic bytes per
+  launch / measured launch time, against 8 TB/s), with the HBM traffic of the
+  rocprofv3 counter profile kept under profiles/;
+* ``prefill_4x2048_h64``: the dense workload "4 sequences x 2048 tokens,
+  H = 64, state_in ~ N(0, 0.1^2)", the same way, plus its output gated RMSNorm
+  fused and unfused (``prefill_gated_norm``);
+* ``varlen_h96``: "32 sequences, lengths log-uniform in [64, 24576], H = 96,
+  snapshots every 2048 into 2 slots", longest-first against input order;
+* ``single_head_fp32``: the 64-token fp32 single head (launch-bound);
+* ``long_context`` decode: 128 single-token decode steps after the long prefill;
+* ``verify_fold``: one speculative step of "256 requests x 69 layers x 8
+  heads, gamma + 1 = 8 bf16 draft tokens, ring length 16, accepted lengths
+  geometric (mean 2.7, clipped to [1, 8])" = 69 kda_verify launches + one
+  kda_replay_fold launch, in us/step (committed states restored from a
   pristine copy outside the timed region before every step); beside it the
-  same step through kda_fold_verify, and the verify with trimmed windows
-  (1..8 tokens per request, packed) through kda_verify_ragged;
-* ``prefill_gated_norm``: the same prefill with the output gated RMSNorm,
-  fused into its epilogue (kda_chunk_prefill_gated) and unfused (the prefill,
-  then kda_gated_rmsnorm over its fp32 output);
-* ``prologue``: the step before the recurrence (kda_prologue) over the same
-  tokens, in us and GB/s;
-* ``roofline``: HBM roofline of the prefill kernel (algorithmic bytes per
-  launch / measured launch time, against 8 TB/s);
-* ``cpu_baseline``: the fp64 oracle (token-by-token) timed on this host's
-  cores over the same prefill workload.
+  same step through kda_fold_verify, and the verify with trimmed windows;
+* ``prologue``, ``state_moves``: the adjacent steps;
+* ``cpu_baseline``: the fp64 oracle (token-by-token) on the host cores this
+  process may use, on stated samples of every workload.
 
 Inputs are synthetic, generated on the device by the seeded generator.
 """
@@ -37,12 +42,18 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK = 2.5e15  # MI355X dense bf16/fp16 matrix peak, FLOP/s
+# algorithmic flops per token*head of the chunked form at the kernel's chunk C = 32, K = V = 128:
+# 2 [(3CK + 2CV) / 2 + 3KV] (the five chunk-by-chunk products at their triangular half, the three
+# state-shaped products in full)
+FLOP_PER_TOKEN_HEAD = 2 * ((3 * 32 * 128 + 2 * 32 * 128) // 2 + 3 * 128 * 128)
 METRIC = "KDA prefill tokens*heads/s and verify+fold us/step at 1 GPU; % of roofline"
 
 # HBM bytes per prefill launch measured by rocprofv3 PMC (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, the
-# factors that make a plain 1 GiB copy read 1 GiB and write 1 GiB); set to None whenever the kernel
-# changes until it is measured again
-PREFILL_TRAFFIC_BYTES = 980_824_721
+# factors that make a plain 1 GiB copy read 1 GiB and write 1 GiB), per workload; None for a workload
+# not measured with the current kernel (set to None whenever the kernel changes until it is measured again)
+PREFILL_TRAFFIC_BYTES = {"long_1m_h96": 263_047_197_952, "prefill_4x2048_h64": 980_824_721}
+FLUSH_BYTES = 1 << 30  # scratch written before every timed prefill rep: evicts the 256 MB Infinity Cache and L2s
 
 
 def parse():
@@ -53,7 +64,9 @@ def parse():
     ap.add_argument("--vf-steps", type=int, default=5, help="timed verify+fold steps")
     ap.add_argument("--no-verify-fold", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--prefill-only", action="store_true", help="time only the prefill (for profilers)")
+    ap.add_argument("--prefill-only", action="store_true", help="time only the headline prefill (for profilers)")
+    ap.add_argument("--only", choices=["long_1m_h96", "prefill_4x2048_h64", "varlen_h96", "verify_fold"],
+                    help="time only this workload (for profilers); no JSON headline unless it is long_1m_h96")
     ap.add_argument("--verify-fold-only", action="store_true", help="time only the speculative step (for profilers)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy, the reference kernel for scaling HBM byte counters")
@@ -72,6 +85,13 @@ def prefill_bytes(n_seq, L, H, with_state_in=True):
     return th * 1796 + st
 
 
+def workload_bytes(lens, H, with_state_in, snap_interval):
+    """prefill_bytes for a batch of lengths, plus 64 KiB per snapshot written."""
+    tot = int(sum(int(x) for x in lens))
+    snaps = sum(int(x) // snap_interval for x in lens) if snap_interval else 0
+    return tot * H * 1796 + len(lens) * H * 65536 * (2 if with_state_in else 1) + snaps * H * 65536
+
+
 def settle(step, torch, seconds=0.25):
     """Run the step untimed until `seconds` of wall time have passed: the GPU's clocks ramp up
     over the first ~100 launches of a short kernel, and the timed region should see the steady
@@ -83,43 +103,104 @@ def settle(step, torch, seconds=0.25):
         torch.cuda.synchronize()
 
 
-def bench_prefill(args, torch, kda, sg, synth):
+def time_reps(torch, step, reps, flush):
+    """Time `reps` calls of step(), each on its own with HIP events on the launch stream (the current
+    stream, which the binding launches on). Before each, outside the events, the 1 GiB scratch `flush`
+    is written on the same stream; the start event is recorded while that write still runs, so the
+    stream never idles between the event and the launch. Returns the per-call times in ms."""
+    stream = torch.cuda.current_stream()
+    out = []
+    for r in range(reps):
+        torch.cuda.synchronize()
+        flush.fill_(float(r & 7))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    return out
+
+
+def summary(times):
+    ts = sorted(times)
+    return dict(mean_ms=sum(ts) / len(ts), median_ms=ts[len(ts) // 2], min_ms=ts[0], reps=len(ts))
+
+
+def bench_prefill_workload(name, orders, reps, warmup, torch, kda, sg, synth, flush, v_blocks=1, short=False):
+    """One prefill workload of synth.PREFILL_CONFIGS on the device: every order in `orders` (a plan per
+    order, the work list resident), `warmup` untimed calls then `reps` timed ones each, a cache flush
+    before every timed call. Returns per order the time summary, plus the workload's sizes."""
     dev = "cuda:0"
-    N, L, H = 4, 2048, 64
-    cfg = synth.PREFILL_CONFIGS["prefill_4x2048_h64"]
-    seed = cfg["seed"]
-    cu = synth.cu_seqlens([L] * N)
-    T = int(cu[-1])
-    q, k, v, gk, beta = sg.prefill_inputs(seed, T, H, dev)
-    S0 = sg.states(seed, N * H, dev).view(N, H, 128, 128)
+    c = synth.PREFILL_CONFIGS[name]
+    seed, H = c["seed"], c["H"]
+    lens = synth.prefill_lengths(name)
+    cu = synth.cu_seqlens(lens)
+    T, N = int(cu[-1]), len(lens)
+    ins = sg.prefill_inputs(seed, T, H, dev)
+    S0 = sg.states(seed, N * H, dev).view(N, H, 128, 128) if c["state_in"] == "normal" else None
     o = torch.empty((T, H, 128), device=dev)
     st = torch.empty((N, H, 128, 128), device=dev)
-    plan = kda.kda_plan_create(cu, n_heads=H)
+    slots = c["snap_slots"]
+    snap = torch.empty((N, slots, H, 128, 128), device=dev) if slots else None
+    cnt = torch.empty((N,), dtype=torch.int32, device=dev)
+    res = {}
+    for order in orders:
+        plan = kda.kda_plan_create(cu, n_heads=H, snap_interval=c["snap_interval"], order=order, v_blocks=v_blocks)
+        ws = torch.empty(kda.kda_plan_workspace_bytes(plan), dtype=torch.uint8, device=dev)
+        kda.kda_plan_upload(plan, ws)
+
+        def step():
+            kda.kda_chunk_prefill(plan, *ins, st, o, ws, state_in=S0, snap=snap, snap_slots=slots, snap_count=cnt,
+                                  flags=kda.KDA_PREFILL_PLAN_RESIDENT)
+
+        if short:
+            settle(step, torch)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        r = summary(time_reps(torch, step, reps, flush))
+        r["items"] = kda.kda_plan_num_items(plan)
+        r["v_blocks"] = kda.kda_plan_v_blocks(plan)
+        res[order] = r
+        plan.close()
+    byts = workload_bytes(lens, H, S0 is not None, c["snap_interval"] if slots else 0)
+    out = dict(res=res, bytes=byts, tokens_heads=T * H, T=T, N=N, H=H, lens=lens, st=st)
+    del ins, o, snap, S0
+    return out
+
+
+def bench_single_head(torch, kda, sg, synth, flush):
+    """The 64-token fp32 single head (state zero): kda_verify on the fp32 inputs (n_tok = 64, no ring,
+    commit after 64) and kda_chunk_prefill on bf16-rounded copies of q, k, v. Launch-bound: us per call."""
+    dev = "cuda:0"
+    c = synth.PREFILL_CONFIGS["single_64"]
+    seed, T = c["seed"], c["lengths"][0]
+    q, k, v, gk, beta = sg.prefill_inputs(seed, T, 1, dev, qkv_dtype=torch.float32)
+    pool = torch.zeros((1, 1, 1, 128, 128), device=dev)
+    commit = torch.empty_like(pool)
+    slot = torch.zeros(1, dtype=torch.int32, device=dev)
+    clen = torch.full((1,), T, dtype=torch.int32, device=dev)
+    o = torch.empty((T, 1, 128), device=dev)
+
+    def verify():
+        kda.kda_verify(q, k, v, gk, beta, pool, slot, o, layer=0, n_tok=T, commit_len=clen, commit_pool=commit)
+
+    qb, kb, vb = (x.to(torch.bfloat16) for x in (q, k, v))
+    plan = kda.kda_plan_create(synth.cu_seqlens([T]), n_heads=1)
     ws = torch.empty(kda.kda_plan_workspace_bytes(plan), dtype=torch.uint8, device=dev)
     kda.kda_plan_upload(plan, ws)
-    flags = kda.KDA_PREFILL_PLAN_RESIDENT
+    st = torch.empty((1, 1, 128, 128), device=dev)
 
-    def step():
-        kda.kda_chunk_prefill(plan, q, k, v, gk, beta, st, o, ws, state_in=S0, flags=flags)
+    def prefill():
+        kda.kda_chunk_prefill(plan, qb, kb, vb, gk, beta, st, o, ws, flags=kda.KDA_PREFILL_PLAN_RESIDENT)
 
-    settle(step, torch)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    tokens_heads = N * L * H
-    byts = prefill_bytes(N, L, H)
-    achieved = byts / (ms * 1e-3) / 1e9
-    res = dict(ms=ms, value=tokens_heads / (ms * 1e-3), bytes=byts, achieved=achieved, N=N, L=L, H=H)
-    del q, k, v, gk, beta, o, st, S0
-    return res
+    out = {}
+    for name, fn in (("verify_fp32", verify), ("prefill_bf16", prefill)):
+        settle(fn, torch, 0.1)
+        out[name] = summary(time_reps(torch, fn, 20, flush))
+    plan.close()
+    return out
 
 
 def bench_prefill_gated(args, torch, kda, sg, synth):
@@ -249,44 +330,15 @@ def bench_state_moves(args, torch, kda, sg, synth):
     return dict(ms=ms, bytes=byts, gbs=byts / (ms * 1e-3) / 1e9)
 
 
-def bench_long_context(args, torch, kda, sg, synth):
-    """The long-context workload: one 1,048,576-token sequence x 96 heads through kda_chunk_prefill (the
-    automatic plan: 192 half-chains; snapshots every 4096 tokens into 2 slots), then 128 single-token
-    decode steps from its final state (kda_verify, n_tok = 1, commit in place), launched one by one and
-    as one replayed HIP graph."""
+def bench_decode(st, torch, kda, sg, synth):
+    """128 single-token decode steps of the long-context workload from its prefill's final state `st`
+    ([1, 96, 128, 128]): kda_verify (n_tok = 1, commit in place), launched one by one and as one replayed
+    HIP graph; then a whole decode layer from the projections as three launches per step and as one
+    kda_decode per step, both replayed as graphs."""
     dev = "cuda:0"
     c = synth.PREFILL_CONFIGS["long_1m_h96"]
-    seed, H, T = c["seed"], c["H"], sum(c["lengths"])
-    torch.cuda.empty_cache()  # about 180 GB of inputs and outputs follow
-    cu = synth.cu_seqlens([T])
-    plan = kda.kda_plan_create(cu, n_heads=H, snap_interval=c["snap_interval"], v_blocks=0)
-    ins = sg.prefill_inputs(seed, T, H, dev)
-    o = torch.empty((T, H, 128), device=dev)
-    st = torch.empty((1, H, 128, 128), device=dev)
-    slots = c["snap_slots"]
-    snap = torch.empty((1, slots, H, 128, 128), device=dev)
-    cnt = torch.empty((1,), dtype=torch.int32, device=dev)
-    ws = torch.empty(kda.kda_plan_workspace_bytes(plan), dtype=torch.uint8, device=dev)
-    kda.kda_plan_upload(plan, ws)
-
-    def step():
-        kda.kda_chunk_prefill(plan, *ins, st, o, ws, snap=snap, snap_slots=slots, snap_count=cnt,
-                              flags=kda.KDA_PREFILL_PLAN_RESIDENT)
-
-    n = max(1, min(args.steps, 3))
-    step()
-    torch.cuda.synchronize()
+    seed, H = c["seed"], c["H"]
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(n):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / n
-    byts = prefill_bytes(1, T, H, with_state_in=False) + (T // c["snap_interval"]) * H * 65536
-    del ins, o
-    torch.cuda.empty_cache()
     # decode
     steps = synth.DECODE_STEPS
     tids = (synth.T_DEC_Q, synth.T_DEC_K, synth.T_DEC_V, synth.T_DEC_GK, synth.T_DEC_BETA)
@@ -355,8 +407,7 @@ def bench_long_context(args, torch, kda, sg, synth):
             fn()
         gr.replay()
         graphs[name] = timed(gr.replay, 5)
-    return dict(ms=ms, bytes=byts, gbs=byts / (ms * 1e-3) / 1e9, T=T, H=H, items=kda.kda_plan_num_items(plan),
-                eager_us=eager_us, graph_us=graph_us, dec_gbs=dec_bytes / (graph_us * 1e-6) / 1e9,
+    return dict(eager_us=eager_us, graph_us=graph_us, dec_gbs=dec_bytes / (graph_us * 1e-6) / 1e9,
                 layer_chain_us=graphs["chain"], layer_fused_us=graphs["fused"])
 
 
@@ -475,28 +526,133 @@ def bench_verify_fold(args, torch, kda, sg, synth):
     return res
 
 
-def cpu_baseline(synth, oracle):
-    """The fp64 oracle, as it is, on this host's cores: every (sequence, head) unit of the
-    prefill workload (4 x 2048 tokens x 64 heads). Input generation is not timed."""
-    N, L, H = 4, 2048, 64
-    seed = synth.PREFILL_CONFIGS["prefill_4x2048_h64"]["seed"]
-    threads = min(16, os.cpu_count() or 1)
-    units = [(n, h) for n in range(N) for h in range(H)]
-    data = {}
-    for n, h in units:
-        q, k, v, gk, beta = synth.prefill_rows(seed, H, n * L, L, h=h)
-        S0 = synth.state_rows(seed, n * H + h, 1)[0]
-        data[(n, h)] = (oracle.f64(q), oracle.f64(k), oracle.f64(v), oracle.f64(gk), oracle.f64(beta), S0)
+def host_cores():
+    """(threads to use, nproc, CPUs this process may run on, CPU model). The oracle runs one unit per task
+    on the CPUs this process may use, capped by OMP_NUM_THREADS when the environment sets it (the share of
+    host cores a one-GPU job is given)."""
+    nproc = os.cpu_count() or 1
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = nproc
+    threads = aff
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        threads = min(threads, int(env))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return threads, nproc, aff, model
 
-    def run(u):
-        q, k, v, gk, beta, S0 = data[u]
+
+def cpu_baseline(synth, oracle):
+    """The fp64 oracle, as it is (token-by-token, one (sequence, head) or (request, layer, head) unit per
+    task), on stated samples of every workload. Input generation is not timed. A sample keeps the
+    workload's shapes and distributions, so its rate is the workload's rate."""
+    import numpy as np
+
+    threads, nproc, aff, model = host_cores()
+
+    def timed_units(units, prep, run):
+        data = dict(zip(units, oracle.run_parallel(prep, units, threads=threads)))
+        t0 = time.perf_counter()
+        oracle.run_parallel(lambda u: run(data[u]), units, threads=threads)
+        return time.perf_counter() - t0
+
+    def prefill_prep(name, t0_fn, L_fn, with_s0):
+        c = synth.PREFILL_CONFIGS[name]
+
+        def prep(u):
+            n, h = u
+            q, k, v, gk, beta = synth.prefill_rows(c["seed"], c["H"], t0_fn(n), L_fn(n), h=h)
+            S0 = synth.state_rows(c["seed"], n * c["H"] + h, 1)[0] if with_s0 else None
+            return tuple(oracle.f64(x) for x in (q, k, v, gk, beta)) + (S0,)
+        return prep
+
+    def prefill_run(d):
+        q, k, v, gk, beta, S0 = d
         oracle.recurrent(q, k, v, gk, beta, S0)
 
+    out = {}
+    # single head, 64 tokens, fp32: the whole workload
+    c0 = synth.PREFILL_CONFIGS["single_64"]
+    q, k, v, gk, beta = synth.prefill_rows(c0["seed"], 1, 0, 64, h=0, qkv_dtype=synth.F32)
+    args0 = tuple(oracle.f64(x) for x in (q, k, v, gk, beta))
     t0 = time.perf_counter()
-    oracle.run_parallel(run, units, threads=threads)
-    dt = time.perf_counter() - t0
-    return dict(value=N * L * H / dt, unit="tokens*heads/s", cores=threads, kind="oracle",
-                sample=f"full workload: {N} x {L} tokens x {H} heads (fp64 token-by-token), {dt:.2f} s wall")
+    for _ in range(200):
+        oracle.recurrent(*args0)
+    dt = (time.perf_counter() - t0) / 200
+    out["single_head_fp32"] = dict(value=64 / dt, unit="tokens*heads/s", sample="the whole workload (1 head x 64 "
+                                   f"tokens), mean of 200 runs: {dt * 1e6:.0f} us each")
+    # 4 x 2048, H64: every unit
+    L1 = 2048
+    units = [(n, h) for n in range(4) for h in range(64)]
+    dt = timed_units(units, prefill_prep("prefill_4x2048_h64", lambda n: n * L1, lambda n: L1, True), prefill_run)
+    out["prefill_4x2048_h64"] = dict(value=len(units) * L1 / dt, unit="tokens*heads/s",
+                                     sample=f"the whole workload: 256 (sequence, head) units x 2048 tokens, {dt:.2f} s")
+    # varlen H96: every sequence, 8 heads (0, 12, .., 84)
+    lens = synth.prefill_lengths("varlen_h96")
+    cu = synth.cu_seqlens(lens)
+    heads = list(range(0, 96, 12))
+    units = [(n, h) for n in range(len(lens)) for h in heads]
+    dt = timed_units(units, prefill_prep("varlen_h96", lambda n: int(cu[n]), lambda n: int(lens[n]), False),
+                     prefill_run)
+    th = int(sum(lens)) * len(heads)
+    out["varlen_h96"] = dict(value=th / dt, unit="tokens*heads/s",
+                             sample=f"all 32 sequences ({int(sum(lens))} tokens) x heads {heads} (fp64, no "
+                                    f"snapshot copies), {dt:.2f} s")
+    # long context: 16 heads (0, 6, .., 90) over the first 131,072 of the 1,048,576 tokens
+    L4 = 131072
+    heads4 = list(range(0, 96, 6))
+    units = [(0, h) for h in heads4]
+    dt = timed_units(units, prefill_prep("long_1m_h96", lambda n: 0, lambda n: L4, False), prefill_run)
+    out["long_1m_h96"] = dict(value=L4 * len(heads4) / dt, unit="tokens*heads/s",
+                              sample=f"heads {heads4} over tokens 0..{L4 - 1} of the 1,048,576 (the per-token cost "
+                                     f"does not depend on the position), {dt:.2f} s")
+    # speculative step: layer 0 of the 256 x 69 x 8 step (2,048 units): verify 8 tokens (ring recorded),
+    # then fold the accepted prefix; scaled by 69 layers to ms/step
+    vc = synth.VERIFY_CONFIG
+    acc = synth.geometric_accept(vc["seed"], vc["B"])
+    units = [(b, h) for b in range(vc["B"]) for h in range(vc["H"])]
+
+    def vprep(u):
+        b, h = u
+        q, k, v, gk, beta = synth.prefill_rows(vc["seed"], vc["H"], b * vc["T"], vc["T"], h=h, sub=0)
+        S0 = synth.state_rows(vc["seed"], (b * vc["L"] + 0) * vc["H"] + h, 1)[0]
+        return tuple(oracle.f64(x) for x in (q, k, v, gk, beta)) + (S0, int(acc[b]))
+
+    def vrun(d):
+        q, k, v, gk, beta, S0, n = d
+        _, _, ring = oracle.verify(q, k, v, gk, beta, S0)
+        S = np.array(S0, dtype=np.float64)
+        oracle.fold(n, ring["k"], ring["v"], ring["gk"], ring["beta"], S)
+
+    dt = timed_units(units, vprep, vrun)
+    out["verify_fold_256x69x8"] = dict(value=dt * vc["L"] * 1e3, unit="ms/step",
+                                       sample=f"layer 0 of the step (256 requests x 8 heads: verify 8 tokens, then "
+                                              f"fold the accepted prefix), {dt:.2f} s, x 69 layers")
+    head = out["long_1m_h96"]
+    return dict(value=head["value"], unit="tokens*heads/s", cores=threads, kind="oracle",
+                sample="long-context prefill: " + head["sample"], nproc=nproc, cpus_allowed=aff, cpu_model=model,
+                workloads=out)
+
+
+def prefill_leg(r, order, synth_name, traffic=None):
+    """JSON fields of one timed prefill workload in one order: time, throughput, HBM and MFMA fractions."""
+    t = r["res"][order]
+    ms = t["mean_ms"]
+    gbs = r["bytes"] / (ms * 1e-3) / 1e9
+    flops = r["tokens_heads"] * FLOP_PER_TOKEN_HEAD
+    return {"ms": ms, "median_ms": t["median_ms"], "min_ms": t["min_ms"], "reps": t["reps"],
+            "tokens_heads_per_s": r["tokens_heads"] / (ms * 1e-3), "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "mfma_frac": flops / (ms * 1e-3) / MFMA_BF16_PEAK, "algorithmic_bytes": r["bytes"],
+            "items": t["items"], "v_blocks": t["v_blocks"], "traffic": traffic}
 
 
 def main():
@@ -515,38 +671,78 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.init()
+    only = args.only
     if args.verify_fold_only:
-        vf = bench_verify_fold(args, torch, kda, sg, synth)
-        print(json.dumps({"verify_us": vf["verify_ms"] * 1e3, "fold_us": vf["fold_ms"] * 1e3,
-                          "verify_gbs": vf["verify_gbs"], "fold_gbs": vf["fold_gbs"],
-                          "fused_us": vf["fused_ms"] * 1e3, "fused_gbs": vf["fused_gbs"],
-                          "ragged_verify_us": vf["ragged_ms"] * 1e3, "ragged_gbs": vf["ragged_gbs"]}), flush=True)
-        return
-    log("prefill: generating inputs and timing")
-    pf = bench_prefill(args, torch, kda, sg, synth)
-    log(f"prefill: {pf['ms'] * 1e3:.1f} us/launch, {pf['achieved']:.0f} GB/s")
-    pg = None
-    if not args.prefill_only:
+        only = "verify_fold"
+    if args.prefill_only:
+        only = "long_1m_h96"
+    want = (lambda name: only is None or only == name)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    LPT, FIFO = kda.KDA_PLAN_LPT, kda.KDA_PLAN_FIFO
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+
+    head = None
+    if want("long_1m_h96"):
+        log("long context: 1M x 96 prefill (the headline)")
+        try:
+            lc = bench_prefill_workload("long_1m_h96", [LPT], args.steps, args.warmup, torch, kda, sg, synth, flush,
+                                        v_blocks=0)
+            head = prefill_leg(lc, LPT, "long_1m_h96", PREFILL_TRAFFIC_BYTES["long_1m_h96"])
+            log(f"long context: {head['ms']:.2f} ms/launch, {head['gbs']:.0f} GB/s")
+            st = lc["st"]
+            del lc
+            torch.cuda.empty_cache()
+            if only is None:
+                log("long context: 128 decode steps")
+                dec = bench_decode(st, torch, kda, sg, synth)
+                head["decode"] = {
+                    "us_per_step_eager": dec["eager_us"], "us_per_step_graph": dec["graph_us"],
+                    "gbs_graph": dec["dec_gbs"], "hbm_frac_graph": dec["dec_gbs"] / HBM_PEAK_GBS,
+                    "layer_us_per_step_three_launches": dec["layer_chain_us"],
+                    "layer_us_per_step_fused": dec["layer_fused_us"],
+                    "workload": "128 single-token decode steps from the long prefill's final state (kda_verify "
+                                "n_tok=1, in-place commit, 96 heads), one launch per step and as one replayed HIP "
+                                "graph; and a whole decode layer from the projections (conv width 4, gated output "
+                                "norm) as kda_prologue + kda_verify + kda_gated_rmsnorm per step vs one kda_decode "
+                                "per step, both replayed as graphs"}
+            del st
+        except torch.cuda.OutOfMemoryError as e:  # the line must still be printed
+            log(f"long context skipped: {e}")
+        torch.cuda.empty_cache()
+
+    dense = None
+    if want("prefill_4x2048_h64"):
+        log("prefill 4 x 2048, H64")
+        r = bench_prefill_workload("prefill_4x2048_h64", [LPT], args.steps, args.warmup, torch, kda, sg, synth, flush,
+                                   short=True)
+        dense = prefill_leg(r, LPT, "prefill_4x2048_h64", PREFILL_TRAFFIC_BYTES["prefill_4x2048_h64"])
+        log(f"prefill 4 x 2048: {dense['ms'] * 1e3:.1f} us/launch, {dense['gbs']:.0f} GB/s")
+        del r
+        torch.cuda.empty_cache()
+    varlen = None
+    if want("varlen_h96"):
+        log("varlen H96 prefill: longest-first and input order")
+        r = bench_prefill_workload("varlen_h96", [LPT, FIFO], 5, 1, torch, kda, sg, synth, flush)
+        varlen = {"lpt": prefill_leg(r, LPT, "varlen_h96"), "fifo": prefill_leg(r, FIFO, "varlen_h96"),
+                  "total_tokens": int(sum(r["lens"])), "n_seq": r["N"], "heads": r["H"]}
+        varlen["lpt_speedup"] = varlen["fifo"]["ms"] / varlen["lpt"]["ms"]
+        log(f"varlen: LPT {varlen['lpt']['ms']:.3f} ms, FIFO {varlen['fifo']['ms']:.3f} ms")
+        del r
+        torch.cuda.empty_cache()
+    single = bench_single_head(torch, kda, sg, synth, flush) if only is None else None
+    pg = pro = mvs = None
+    if only is None:
         log("prefill with the output gated RMSNorm: fused and unfused")
         pg = bench_prefill_gated(args, torch, kda, sg, synth)
-    pro = None
-    if not args.prefill_only:
         log("prologue")
         pro = bench_prologue(args, torch, kda, sg, synth)
-    mvs = None
-    if not args.prefill_only:
         log("state moves")
         mvs = bench_state_moves(args, torch, kda, sg, synth)
-    lc = None
-    if not args.prefill_only:
-        log("long context: 1M x 96 prefill, then 128 decode steps")
-        try:
-            lc = bench_long_context(args, torch, kda, sg, synth)
-        except torch.cuda.OutOfMemoryError as e:  # the headline line must still be printed
-            log(f"long context skipped: {e}")
-            torch.cuda.empty_cache()
+    del flush
+    torch.cuda.empty_cache()
     vf = None
-    if not (args.no_verify_fold or args.prefill_only):
+    if want("verify_fold") and not args.no_verify_fold:
         log("verify+fold: generating inputs and timing")
         vf = bench_verify_fold(args, torch, kda, sg, synth)
         log(f"verify+fold: {vf['verify_ms'] * 1e3:.0f} + {vf['fold_ms'] * 1e3:.0f} us; fused {vf['fused_ms'] * 1e3:.0f} us")
@@ -559,63 +755,65 @@ def main():
         log("copy calibration: 3 x 1 GiB device copies (1 GiB read + 1 GiB written each)")
         del src, dst
     cpu = None
-    if not (args.no_cpu_baseline or args.prefill_only):
+    if only is None and not args.no_cpu_baseline:
         import oracle
 
         log("cpu baseline: fp64 oracle on host cores")
         cpu = cpu_baseline(synth, oracle)
-    traffic = PREFILL_TRAFFIC_BYTES
-    line = {
-        "metric": METRIC,
-        "value": pf["value"],
-        "unit": "tokens*heads/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": pf["ms"],
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "chunked prefill: 4 sequences x 2048 tokens, H=64, K=V=128, bf16 q/k/v, "
-                               "fp32 gk/beta/state, state_in N(0,0.1^2), chunk 32, one persistent launch",
-                   "n_seq": pf["N"], "seq_len": pf["L"], "heads": pf["H"], "head_dim": 128},
-        "roofline": {"bound": "hbm", "achieved": pf["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": pf["achieved"] / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "kda::prefill_kernel<false>", "algorithmic_bytes_per_launch": pf["bytes"]},
-        "cpu_baseline": cpu,
-    }
+
+    if head is not None:
+        line.update({
+            "value": head["tokens_heads_per_s"], "unit": "tokens*heads/s", "ms_per_step": head["ms"],
+            "config": {"workload": "long-context chunked prefill: 1 sequence x 1,048,576 tokens, H=96, K=V=128, "
+                                   "bf16 q/k/v, fp32 gk/beta/state, state_in zero, snapshots every 4096 tokens into "
+                                   "2 ping-pong slots, chunk 32, one persistent launch (two value blocks per head)",
+                       "n_seq": 1, "seq_len": 1048576, "heads": 96, "head_dim": 128},
+            "roofline": {"bound": "hbm", "achieved": head["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": head["hbm_frac"], "traffic": head["traffic"], "kernel": "kda::prefill_kernel<false>",
+                         "algorithmic_bytes_per_launch": head["algorithmic_bytes"], "mfma_frac": head["mfma_frac"],
+                         "median_ms": head["median_ms"], "min_ms": head["min_ms"]},
+        })
+        line["long_context"] = head
+    elif dense is not None:
+        line.update({
+            "value": dense["tokens_heads_per_s"], "unit": "tokens*heads/s", "ms_per_step": dense["ms"],
+            "config": {"workload": "chunked prefill: 4 sequences x 2048 tokens, H=64 (the long-context workload "
+                                   "did not run)", "n_seq": 4, "seq_len": 2048, "heads": 64, "head_dim": 128},
+            "roofline": {"bound": "hbm", "achieved": dense["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dense["hbm_frac"], "traffic": dense["traffic"], "kernel": "kda::prefill_kernel<false>",
+                         "algorithmic_bytes_per_launch": dense["algorithmic_bytes"]},
+        })
+    line["cpu_baseline"] = cpu
+    if dense is not None:
+        dense["workload"] = ("4 sequences x 2048 tokens, H=64, bf16 q/k/v, fp32 gk/beta/state, state_in N(0,0.1^2), "
+                             "no snapshots (one value block per head)")
+        line["prefill_4x2048_h64"] = dense
+    if varlen is not None:
+        varlen["workload"] = ("32 sequences, lengths log-uniform in [64, 24576] (seed 2), H=96, state_in zero, "
+                              "snapshots every 2048 tokens into 2 slots; the persistent kernel pulling (sequence, "
+                              "head) items longest-first (lpt) vs in input order (fifo)")
+        line["varlen_h96"] = varlen
+    if single is not None:
+        line["single_head_fp32"] = {
+            "verify_fp32_us": single["verify_fp32"]["median_ms"] * 1e3,
+            "prefill_bf16_us": single["prefill_bf16"]["median_ms"] * 1e3,
+            "workload": "1 head x 64 tokens, state zero: kda_verify on fp32 inputs (n_tok 64, commit after 64) and "
+                        "kda_chunk_prefill on bf16-rounded q/k/v (launch-bound; medians of 20 calls)"}
     if pg is not None:
         line["prefill_gated_norm"] = {
             "fused_us": pg["fused_ms"] * 1e3, "unfused_us": pg["unfused_ms"] * 1e3,
             "fused_tokens_heads_per_s": pg["tokens_heads"] / (pg["fused_ms"] * 1e-3),
             "fused_gbs": pg["fused_bytes"] / (pg["fused_ms"] * 1e-3) / 1e9,
             "fused_hbm_frac": pg["fused_bytes"] / (pg["fused_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "workload": "the headline prefill followed by the output gated RMSNorm (gate N(0,1) bf16, weights "
+            "workload": "the 4 x 2048, H64 prefill followed by the output gated RMSNorm (gate N(0,1) bf16, weights "
                         "1 + 0.1 N(0,1), eps 1e-6, bf16 y): kda_chunk_prefill_gated vs kda_chunk_prefill + "
-                        "kda_gated_rmsnorm",
+                        "kda_gated_rmsnorm (back-to-back launches)",
         }
     if pro is not None:
         line["prologue"] = {
             "us": pro["ms"] * 1e3, "gbs": pro["gbs"], "hbm_frac": pro["gbs"] / HBM_PEAK_GBS,
-            "workload": "kda_prologue over the headline prefill's 8,192 tokens x 64 heads: conv width 4 with the "
-                        "state carried in and out, SiLU, q/k L2 norm, beta sigmoid, gk = -softplus (2,568 B per "
-                        "token*head)",
-        }
-    if lc is not None:
-        line["long_context"] = {
-            "prefill_ms": lc["ms"], "prefill_tokens_heads_per_s": lc["T"] * lc["H"] / (lc["ms"] * 1e-3),
-            "prefill_gbs": lc["gbs"], "prefill_hbm_frac": lc["gbs"] / HBM_PEAK_GBS, "prefill_items": lc["items"],
-            "decode_us_per_step_eager": lc["eager_us"], "decode_us_per_step_graph": lc["graph_us"],
-            "decode_gbs_graph": lc["dec_gbs"], "decode_hbm_frac_graph": lc["dec_gbs"] / HBM_PEAK_GBS,
-            "decode_layer_us_per_step_three_launches": lc["layer_chain_us"],
-            "decode_layer_us_per_step_fused": lc["layer_fused_us"],
-            "workload": "1 x 1,048,576 tokens, H=96, snapshots every 4096 into 2 slots (automatic plan: two value "
-                        "blocks per head), then 128 single-token decode steps (kda_verify n_tok=1, in-place commit), "
-                        "one launch per step and as one replayed HIP graph; and a whole decode layer from the "
-                        "projections (conv width 4, gated output norm) as kda_prologue + kda_verify + "
-                        "kda_gated_rmsnorm per step vs one kda_decode per step, both replayed as graphs",
+            "workload": "kda_prologue over the 4 x 2048, H64 batch: conv width 4 with the state carried in and out, "
+                        "SiLU, q/k L2 norm, beta sigmoid, gk = -softplus (2,568 B per token*head)",
         }
     if mvs is not None:
         line["state_moves"] = {
@@ -628,6 +826,8 @@ def main():
             "us_per_step": (vf["verify_ms"] + vf["fold_ms"]) * 1e3,
             "verify_us": vf["verify_ms"] * 1e3, "fold_us": vf["fold_ms"] * 1e3,
             "verify_hbm_frac": vf["verify_gbs"] / HBM_PEAK_GBS, "fold_hbm_frac": vf["fold_gbs"] / HBM_PEAK_GBS,
+            "step_hbm_frac": (vf["verify_bytes"] + vf["fold_bytes"]) / ((vf["verify_ms"] + vf["fold_ms"]) * 1e-3)
+                             / 1e9 / HBM_PEAK_GBS,
             "verify_gbs": vf["verify_gbs"], "fold_gbs": vf["fold_gbs"], "accept_mean": vf["accept_mean"],
             "workload": "256 requests x 69 layers x 8 heads, gamma+1=8 bf16 draft tokens, fp32 committed state, "
                         "ring length 16, accepted lengths geometric mean 2.7 clipped to [1,8]; 69 verify + 1 fold",
