@@ -245,6 +245,29 @@ kda_status kda_chunk_prefill(const kda_plan* plan, const kda_inputs* in, const f
                              void* stream);
 
 /*
+ * kda_chunk_prefill for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * there is no workspace argument. The plan's work list and its counters go
+ * into a static device array inside the library, KDA_NOALLOC_SCRATCH_BYTES
+ * long, one per GPU, held until the process ends; each call copies the list
+ * there (from the plan's pinned buffer) before its launch. The call makes no
+ * allocation (no hipMalloc, hipFree or allocating library routine).
+ *  - Every other argument, every precondition and every result as
+ *    kda_chunk_prefill with flags = 0; the outputs are bit-identical to it.
+ *  - Limit: kda_plan_workspace_bytes(plan) <= KDA_NOALLOC_SCRATCH_BYTES
+ *    (65,520 work items); a larger plan is rejected (KDA_ERR_INVALID_ARG).
+ *  - All calls on one GPU share the array: two such calls in flight at the
+ *    same time on one GPU (on different streams) race. Calls ordered on one
+ *    stream are safe (the previous call's contents are overwritten).
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED (device index >= 64),
+ * KDA_ERR_DEVICE.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (1 << 20)
+kda_status kda_chunk_prefill_noalloc(const kda_plan* plan, const kda_inputs* in, const float* state_in,
+                                     float* state_out, float* o, float* snap, int snap_slots,
+                                     int32_t* snap_count, float scale, void* stream);
+
+/*
  * Chunked prefill with the output gated RMSNorm fused into its epilogue
  * [B200-NORM]: exactly kda_chunk_prefill, except that instead of o the kernel
  * writes

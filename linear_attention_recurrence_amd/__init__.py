@@ -10,5 +10,5 @@ from .kda import (  # noqa: F401
     KDA_F32, KDA_HEAD_DIM, KDA_OK, KDA_PLAN_FIFO, KDA_PLAN_LPT, KDA_PREFILL_PLAN_RESIDENT, EXPORTS, KdaError,
     Plan, Ring, kda_abi_version, kda_chunk_prefill, kda_chunk_prefill_gated, kda_gated_rmsnorm, kda_last_error, kda_prologue, kda_plan_create, kda_plan_items,
     kda_fold_verify, kda_plan_num_items, kda_plan_upload, kda_plan_v_blocks, kda_plan_workspace_bytes,
-    kda_host_release, kda_replay_fold, kda_verify, kda_verify_ragged, lib,
+    KDA_NOALLOC_SCRATCH_BYTES, kda_chunk_prefill_noalloc, kda_host_release, kda_replay_fold, kda_verify, kda_verify_ragged, lib,
 )

@@ -310,6 +310,60 @@ kda_status kda_chunk_prefill(const kda_plan* p, const kda_inputs* in, const floa
                       snap_slots, snap_count, workspace, scale, flags, stream);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The prefill without a caller workspace: the work list and its counters live in
+// `scratch`, a static device array of this library (one copy per GPU, kept until
+// the process ends). Host code never passes `scratch` itself to a kernel or a copy:
+// its name is a host-side stand-in. The device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the calling thread's current device and that device's address of `scratch`
+kda_status scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_fail("kda_chunk_prefill_noalloc: hipGetDevice", e);
+  if (dev < 0 || dev >= kMaxDevices) return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_prefill_noalloc: device index >= 64");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return device_fail("kda_chunk_prefill_noalloc: hipGetSymbolAddress(scratch)", e);
+    if (!ptr) return fail(KDA_ERR_DEVICE, "kda_chunk_prefill_noalloc: hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_prefill_noalloc(const kda_plan* p, const kda_inputs* in, const float* state_in,
+                                     float* state_out, float* o, float* snap, int snap_slots, int32_t* snap_count,
+                                     float scale, void* stream) {
+  if (!p) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill_noalloc: plan is NULL");
+  if (kda_plan_workspace_bytes(p) > (size_t)KDA_NOALLOC_SCRATCH_BYTES)
+    return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill_noalloc: the plan's work list (" +
+                                         std::to_string(kda_plan_workspace_bytes(p)) + " bytes) exceeds the " +
+                                         std::to_string(KDA_NOALLOC_SCRATCH_BYTES) + "-byte static scratch");
+  void* ws = nullptr;
+  const kda_status st = scratch_ptr(&ws);
+  if (st != KDA_OK) return st;
+  // the upload rewrites the whole list and zeroes the counters, so a previous call's contents never matter
+  return prefill_call("kda_chunk_prefill_noalloc", p, in, state_in, state_out, o, nullptr, nullptr, 0.f, nullptr, snap,
+                      snap_slots, snap_count, ws, scale, 0, stream);
+}
+
 kda_status kda_chunk_prefill_gated(const kda_plan* p, const kda_inputs* in, const void* gate, const float* norm_w,
                                    float eps, const float* state_in, float* state_out, void* y, float* snap,
                                    int snap_slots, int32_t* snap_count, void* workspace, float scale, int flags,

@@ -32,7 +32,7 @@ KDA_CHUNK = 32
 
 EXPORTS = ("kda_abi_version", "kda_last_error", "kda_plan_create", "kda_plan_create_ex", "kda_plan_v_blocks",
            "kda_plan_workspace_bytes", "kda_plan_num_items", "kda_plan_items", "kda_plan_upload", "kda_plan_destroy",
-           "kda_host_release",
+           "kda_host_release", "kda_chunk_prefill_noalloc",
            "kda_chunk_prefill", "kda_chunk_prefill_gated", "kda_gated_rmsnorm", "kda_prologue", "kda_verify",
            "kda_replay_fold", "kda_fold_verify", "kda_verify_ragged", "kda_state_move", "kda_chunk_split",
            "kda_slots_create", "kda_slots_destroy", "kda_slots_free_count", "kda_slots_owner", "kda_request_open",
@@ -92,6 +92,7 @@ def lib():
         L.kda_host_release.argtypes = []
         L.kda_host_release.restype = i32
         L.kda_chunk_prefill.argtypes = [vp, ctypes.POINTER(_Inputs), vp, vp, vp, vp, i32, vp, vp, f32, i32, vp]
+        L.kda_chunk_prefill_noalloc.argtypes = [vp, ctypes.POINTER(_Inputs), vp, vp, vp, vp, i32, vp, f32, vp]
         L.kda_chunk_prefill_gated.argtypes = [vp, ctypes.POINTER(_Inputs), vp, vp, f32, vp, vp, vp, vp, i32, vp, vp,
                                               f32, i32, vp]
         L.kda_gated_rmsnorm.argtypes = [ctypes.c_int64, vp, vp, vp, f32, vp, vp]
@@ -124,6 +125,7 @@ def lib():
                   "kda_request_donate", "kda_request_close", "kda_slot_release"):
             getattr(L, f).restype = i32
         for f in ("kda_plan_create", "kda_plan_create_ex", "kda_plan_items", "kda_plan_upload", "kda_chunk_prefill",
+                  "kda_chunk_prefill_noalloc",
                   "kda_chunk_prefill_gated", "kda_gated_rmsnorm", "kda_prologue", "kda_verify", "kda_replay_fold",
                   "kda_fold_verify", "kda_verify_ragged"):
             getattr(L, f).restype = i32
@@ -259,6 +261,30 @@ def kda_chunk_prefill(plan, q, k, v, gk, beta, state_out, o, workspace, state_in
     _check(lib().kda_chunk_prefill(plan.handle, ctypes.byref(ins), _ptr(state_in), _ptr(state_out), _ptr(o),
                                    _ptr(snap), int(snap_slots), _ptr(snap_count), _ptr(workspace), float(scale),
                                    int(flags), _stream(stream)))
+
+
+KDA_NOALLOC_SCRATCH_BYTES = 1 << 20
+
+
+def kda_chunk_prefill_noalloc(plan, q, k, v, gk, beta, state_out, o, state_in=None, snap=None, snap_slots=0,
+                              snap_count=None, scale=1.0, stream=None):
+    """kda_chunk_prefill without a workspace: the work list goes to the library's static device scratch
+    (see kda_chunk_prefill_noalloc in include/kda.h). Allocates nothing."""
+    T, H, N, Dh = plan.total_tokens, plan.n_heads, plan.n_seq, KDA_HEAD_DIM
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (T, H, Dh), _BF)
+    _need(gk, "gk", (T, H, Dh), _F32)
+    _need(beta, "beta", (T, H), _F32)
+    _need(o, "o", (T, H, Dh), _F32)
+    _need(state_out, "state_out", (N, H, Dh, Dh), _F32)
+    _need(state_in, "state_in", (N, H, Dh, Dh), _F32, allow_none=True)
+    if snap is not None:
+        _need(snap, "snap", (N, snap_slots, H, Dh, Dh), _F32)
+    _need(snap_count, "snap_count", (N,), _I32, allow_none=True)
+    ins = _Inputs(q.data_ptr(), k.data_ptr(), v.data_ptr(), gk.data_ptr(), beta.data_ptr())
+    _check(lib().kda_chunk_prefill_noalloc(plan.handle, ctypes.byref(ins), _ptr(state_in), _ptr(state_out), _ptr(o),
+                                           _ptr(snap), int(snap_slots), _ptr(snap_count), float(scale),
+                                           _stream(stream)))
 
 
 def kda_chunk_prefill_gated(plan, q, k, v, gk, beta, gate, norm_w, eps, state_out, y, workspace, state_in=None,

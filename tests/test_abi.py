@@ -50,6 +50,20 @@ def test_plan_destroy_and_release():
     kda.kda_host_release()
 
 
+def test_noalloc_prefill_rejects_oversize_plan():
+    """A work list longer than the static scratch (65,520 items) is refused before any device call."""
+    cu = np.array([0, 0], dtype=np.int32)
+    with kda.kda_plan_create(cu, n_heads=65535) as p:
+        assert kda.kda_plan_workspace_bytes(p) > kda.KDA_NOALLOC_SCRATCH_BYTES
+        ins = K._Inputs()
+        rc = kda.lib().kda_chunk_prefill_noalloc(p.handle, ctypes.byref(ins), None, ctypes.c_void_p(16), None, None, 0,
+                                                 None, 1.0, None)
+        assert rc == K.KDA_ERR_INVALID_ARG
+        assert "static scratch" in kda.kda_last_error()
+    with kda.kda_plan_create(cu, n_heads=65520) as p:
+        assert kda.kda_plan_workspace_bytes(p) == kda.KDA_NOALLOC_SCRATCH_BYTES
+
+
 def test_plan_lpt_order_and_ties():
     cu = [0, 5, 100, 100, 140, 235]  # lengths 5, 95, 0, 40, 95
     p = kda.kda_plan_create(cu, n_heads=3)
