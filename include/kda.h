@@ -208,13 +208,16 @@ typedef struct {
  * sequences, T = cu_seqlens[n_seq] tokens, H = plan heads.
  *
  *  in        : q, k, v bf16 [T, H, 128]; gk fp32 [T, H, 128]; beta fp32 [T, H].
- *              Chunked-form precondition: per key channel, the decay
- *              summed over each half of a 32-token chunk (tokens 32m..32m+15
- *              and 32m+16..32m+31 of a sequence) satisfies sum(-gk) <= 80,
- *              which keeps the intra-chunk factors exp(+-partial sums) in
- *              fp32/bf16 range; gk >= -5 everywhere is sufficient. Inputs
- *              outside it give non-finite results, not an error code. The
- *              recurrent entry points accept any gk <= 0.
+ *              Any gk <= 0 is exact, -inf (a full reset) included: a chunk
+ *              whose decay summed over a 16-token half exceeds 80 in some key
+ *              channel (where the fast factor form would leave fp32/bf16
+ *              range) is prepared on an exact path, about three chunk
+ *              periods slower. Range of the state products: the state, and
+ *              beta (v - k^T S) of every token, enter fp16 matrix products,
+ *              so their entries must stay below 2^15 in magnitude (fp16
+ *              overflows at 65504); beyond it o and the states become
+ *              non-finite (no error code: nothing is read back). Tested
+ *              with state_in ~ N(0, 300^2) and v ~ N(0, 30^2).
  *  state_in  : fp32 [n_seq, H, 128, 128] or NULL (= zeros).
  *  state_out : fp32 [n_seq, H, 128, 128]; may equal state_in (in place);
  *              any other overlap is rejected.
@@ -390,6 +393,13 @@ typedef struct {
  *                        commit_len = 1, commit_pool = state_pool).
  *  commit_pool         : like state_pool, or NULL; may equal state_pool, may
  *                        not overlap it otherwise.
+ * Arithmetic: with bf16 inputs, n_tok <= 16 and no commit, the window is one
+ * chunk of the chunked form on the matrix cores (the served path); otherwise
+ * the token-by-token recurrence (whose commit kda_replay_fold reproduces bit
+ * for bit). Both are exact for any gk <= 0 (-inf included): a window whose
+ * decay summed over it exceeds 80 in some key channel forms its intra-window
+ * products pairwise. On the chunked path the committed state and
+ * beta (v - k^T S0) enter fp16 products: their entries must stay below 2^15.
  * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_DEVICE.
  */
 kda_status kda_verify(int batch, int n_tok, int n_heads, int n_layers, int layer, int n_slots,

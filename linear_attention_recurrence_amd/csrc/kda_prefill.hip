@@ -182,6 +182,18 @@ __device__ __forceinline__ float row_scan_add(float v) {
   return v;
 }
 
+// row_shl:s with bound_ctrl: lane t reads lane t + s of its DPP row, 0 past the row's end
+#define KDA_ROW_SHL0(v, s) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x100 + (s), 0xf, 0xf, true))
+
+// exclusive suffix sum over the 16 lanes of a DPP row: lane t gets the sum of lanes t+1 .. 15
+__device__ __forceinline__ float row_suffix_excl(float v) {
+  v = v + KDA_ROW_SHL0(v, 1);
+  v = v + KDA_ROW_SHL0(v, 2);
+  v = v + KDA_ROW_SHL0(v, 4);
+  v = v + KDA_ROW_SHL0(v, 8);
+  return KDA_ROW_SHL0(v, 1);
+}
+
 __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float (&f)[8]) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -249,9 +261,18 @@ struct Keep {
 };
 
 // ---------------------------------------------------------------------------
+// The factor form below needs every factor in fp32/bf16 range: per key channel, the decay summed
+// over each 16-token half of the chunk must be at most 80 (log2: 116). It is checked on the whole
+// chunk's factor e^{G_31} (8 values per lane, less work than the 16 half sums, and sufficient: both
+// halves' factors are at most 1): a wave with a channel where e^{G_31} < 2^-116, or a decay of -inf,
+// runs stage1_exact after stage1, which rewrites everything stage1 wrote. The check costs the fast
+// path a minimum of 8 values and one branch at its end.
+constexpr float kMinChunkDecay = 0x1p-116f;  // e^{G_31} below this takes the exact path (e^-80.4)
+
 // producer, phase 1 of the period before chunk c: decay factors and partial A
-// and P tiles over this wave's 32 channels
-__device__ __forceinline__ void stage1(PrefillLds& L, const Raw& cur, int nc, int b, int pw, int g, int lr, Keep& kp_) {
+// and P tiles over this wave's 32 channels. Returns true when the wave's chunk is outside the
+// factor form's range (what it wrote is then to be replaced by stage1_exact).
+__device__ __forceinline__ bool stage1(PrefillLds& L, const Raw& cur, int nc, int b, int pw, int g, int lr, Keep& kp_) {
   const int co = 4 * pw + g;  // channel octet 8co..8co+7
   const int tl = lr;          // tokens tl (block 0) and 16+tl (block 1)
   const int c8 = 8 * co;
@@ -276,12 +297,10 @@ __device__ __forceinline__ void stage1(PrefillLds& L, const Raw& cur, int nc, in
   unpack_bf16x8(cur.k0, k0); unpack_bf16x8(cur.k1, k1);
   unpack_bf16x8(cur.q0, q0); unpack_bf16x8(cur.q1, q1);
   float xr0[8], xr1[8], yc0[8], yc1[8], e0[8], e1[8], f0[8], f1[8], dl[8];
-  // no branch inside this loop: its 16 prefix-sum chains and 32 exponentials are independent
-  // across channels and interleave only within one basic block
+  // the smallest prefix sum of this lane's channels: over a DPP row, the half totals (-inf included)
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    // prefix sums inside each 16-token block, then the four exponentials
-    const float s0 = row_scan_add(l0[i]), s1 = row_scan_add(l1[i]);  // log2 of e^{G_t - G_-1}, e^{G_t - G_15}
+    const float s0 = row_scan_add(l0[i]), s1 = row_scan_add(l1[i]);
     const float p0 = __builtin_amdgcn_exp2f(s0), r0 = __builtin_amdgcn_exp2f(-s0);
     const float p1 = __builtin_amdgcn_exp2f(s1), r1 = __builtin_amdgcn_exp2f(-s1);
     const float T0 = KDA_ROW_BCAST15(p0), T1 = KDA_ROW_BCAST15(p1);   // block totals
@@ -327,6 +346,118 @@ __device__ __forceinline__ void stage1(PrefillLds& L, const Raw& cur, int nc, in
 #pragma unroll
   for (int tl6 = 0; tl6 < 6; ++tl6)
     *reinterpret_cast<f32x4*>(&L.part[pw][tl6][lr][4 * g]) = acc[tl6];
+  const float m = __builtin_fminf(__builtin_fminf(__builtin_fminf(dl[0], dl[1]), __builtin_fminf(dl[2], dl[3])),
+                                  __builtin_fminf(__builtin_fminf(dl[4], dl[5]), __builtin_fminf(dl[6], dl[7])));
+  return __builtin_amdgcn_ballot_w64(m < kMinChunkDecay) != 0;  // (NaN breaks gk <= 0: not caught)
+}
+
+__device__ __forceinline__ void opaque(uint4& u) { asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w)); }
+__device__ __forceinline__ void opaque(float4& u) { asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w)); }
+
+// One diagonal 16-block of A and P, summed pairwise in fp32 over this wave's 32 channels: entry
+// (i, j), j <= i, is sum_c k_ic k_jc e^{G_ic - G_jc} (q_ic for P), e^{G_i - G_j} = 2^{ps_i - ps_j}
+// from the block's inclusive prefix sums ps (log2 units); entries j > i are 0. Lane (g, lr) holds
+// channel octet g of token i = lr; row j comes from lane j of the same 16-lane row (a lane shuffle),
+// the four octets are added across rows, and one row writes the tile in the partials' [j][i]
+// layout. A rolled loop: this path is rare, and its code should not crowd the fast path's.
+__device__ __forceinline__ void diag_pairwise(float (&part_a)[16][20], float (&part_p)[16][20], const float (&k)[8],
+                                              const float (&q)[8], const float (&ps)[8], int g, int lr) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll 1
+  for (int j = 0; j < 16; ++j) {
+    const int src = (lane & 48) | j;
+    float a = 0.f, pp = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float kj = __shfl(k[c], src), pj = __shfl(ps[c], src);
+      const float e = (j <= lr) ? __builtin_amdgcn_exp2f(ps[c] - pj) : 0.f;
+      const float kje = kj * e;
+      a = __builtin_fmaf(k[c], kje, a);
+      pp = __builtin_fmaf(q[c], kje, pp);
+    }
+    a += __shfl_xor(a, 16);
+    pp += __shfl_xor(pp, 16);
+    a += __shfl_xor(a, 32);
+    pp += __shfl_xor(pp, 32);
+    if (g == (j & 3)) {
+      part_a[j][lr] = a;
+      part_p[j][lr] = pp;
+    }
+  }
+}
+
+// producer, phase 1, exact for any decay gk <= 0 (including -inf), for a wave whose chunk is beyond
+// the factor form's range; it rewrites everything stage1 wrote (dlast, the operand rows, all six
+// partial tiles). The factors at most 1 (e^{G_t}, e^{G_31 - G_t}, e^{G_31}, and the
+// off-diagonal tiles' e^{G_t - G_15} of the second half and e^{G_15 - G_t} of the first) are each one
+// exponential of a prefix or suffix sum, never a product of a large and a small one; the diagonal
+// tiles A00, A11, P00, P11 are summed pairwise; A10 and P10 keep their MFMAs. Decays are clamped at
+// 2^-160 per token, which is 0 in fp32, so e^{-inf} = 0 exactly and no sum is infinite.
+__device__ __forceinline__ void stage1_exact(PrefillLds& L, const Raw& raw, int nc, int b, int pw, int g, int lr,
+                                             Keep& kp_) {
+  // a copy of the raw registers made opaque to the compiler, so that nothing stage1 derived from them
+  // is kept live for reuse here (that would cost the fast path registers)
+  Raw cur = raw;
+  opaque(cur.q0); opaque(cur.q1); opaque(cur.k0); opaque(cur.k1);
+  opaque(cur.g0a); opaque(cur.g0b); opaque(cur.g1a); opaque(cur.g1b);
+  const int co = 4 * pw + g, c8 = 8 * co, tl = lr;
+  const bool ok0 = tl < nc, ok1 = 16 + tl < nc;
+  constexpr float kLog2e = 1.4426950408889634f;
+  float p0[8], p1[8], x0[8], x1[8];  // inclusive prefix and exclusive suffix sums in each half (log2)
+  {
+    const float gx[8] = {cur.g0a.x, cur.g0a.y, cur.g0a.z, cur.g0a.w, cur.g0b.x, cur.g0b.y, cur.g0b.z, cur.g0b.w};
+    const float gy[8] = {cur.g1a.x, cur.g1a.y, cur.g1a.z, cur.g1a.w, cur.g1b.x, cur.g1b.y, cur.g1b.z, cur.g1b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float l0 = ok0 ? __builtin_fmaxf(gx[i] * kLog2e, -160.f) : 0.f;
+      const float l1 = ok1 ? __builtin_fmaxf(gy[i] * kLog2e, -160.f) : 0.f;
+      p0[i] = row_scan_add(l0);
+      p1[i] = row_scan_add(l1);
+      x0[i] = row_suffix_excl(l0);
+      x1[i] = row_suffix_excl(l1);
+    }
+  }
+  float k0[8], k1[8], q0[8], q1[8];
+  unpack_bf16x8(cur.k0, k0); unpack_bf16x8(cur.k1, k1);
+  unpack_bf16x8(cur.q0, q0); unpack_bf16x8(cur.q1, q1);
+  {
+    float e0[8], e1[8], f0[8], f1[8], dl[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float B0 = KDA_ROW_BCAST15(p0[i]), B1 = KDA_ROW_BCAST15(p1[i]);  // half totals
+      e0[i] = __builtin_amdgcn_exp2f(p0[i]);        // e^{G_t}, first half
+      e1[i] = __builtin_amdgcn_exp2f(B0 + p1[i]);   // e^{G_t}, second half
+      f0[i] = __builtin_amdgcn_exp2f(x0[i] + B1);   // e^{G_31 - G_t}, first half
+      f1[i] = __builtin_amdgcn_exp2f(x1[i]);        // e^{G_31 - G_t}, second half
+      dl[i] = __builtin_amdgcn_exp2f(B0 + B1);      // e^{G_31}
+    }
+    if (tl == 0) {
+      *reinterpret_cast<float4*>(&L.dlast[b][c8]) = make_float4(dl[0], dl[1], dl[2], dl[3]);
+      *reinterpret_cast<float4*>(&L.dlast[b][c8 + 4]) = make_float4(dl[4], dl[5], dl[6], dl[7]);
+    }
+    kp_.qt[0] = pk8_mul(q0, e0); kp_.qt[1] = pk8_mul(q1, e1);
+    kp_.kt[0] = pk8_mul(k0, e0); kp_.kt[1] = pk8_mul(k1, e1);
+    kp_.kp[0] = pk8_mul(k0, f0); kp_.kp[1] = pk8_mul(k1, f1);
+  }
+  {
+    // A10 and P10 as in stage1, from factors at most 1: e^{G_t - G_15} of the second half is 2^{p1},
+    // e^{G_15 - G_t} of the first half is 2^{x0}
+    bf16x8 rk1, rq1h, rq1l, ck0h, ck0l;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float xr1 = __builtin_amdgcn_exp2f(p1[i]), yc0 = __builtin_amdgcn_exp2f(x0[i]);
+      rk1[i] = (__bf16)(k1[i] * xr1);
+      float v = q1[i] * xr1; rq1h[i] = (__bf16)v; rq1l[i] = (__bf16)(v - (float)rq1h[i]);
+      v = k0[i] * yc0;       ck0h[i] = (__bf16)v; ck0l[i] = (__bf16)(v - (float)ck0h[i]);
+    }
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 a10 = mfma16(rk1, ck0l, mfma16(rk1, ck0h, z4));
+    const f32x4 p10 = mfma16(rq1l, ck0h, mfma16(rq1h, ck0l, mfma16(rq1h, ck0h, z4)));
+    *reinterpret_cast<f32x4*>(&L.part[pw][2][lr][4 * g]) = a10;
+    *reinterpret_cast<f32x4*>(&L.part[pw][5][lr][4 * g]) = p10;
+  }
+  diag_pairwise(L.part[pw][0], L.part[pw][3], k0, q0, p0, g, lr);  // A00, P00
+  diag_pairwise(L.part[pw][1], L.part[pw][4], k1, q1, p1, g, lr);  // A11, P11
 }
 
 // producer, phase 2: the fp16 operand rows formed in phase 1 go to LDS (token-major rows lr and 16+lr)
@@ -519,7 +650,10 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
         auto period = [&](int p, Raw& use) {
           const int c1 = p + 1, b1 = c1 & 1;
           Keep keep;
-          if (c1 < nch) stage1(L, use, min(C, len - C * c1), b1, pw, g, lr, keep);
+          if (c1 < nch) {
+            const int ncc = min(C, len - C * c1);
+            if (stage1(L, use, ncc, b1, pw, g, lr, keep)) stage1_exact(L, use, ncc, b1, pw, g, lr, keep);
+          }
           __syncthreads();
           issue(use, c1 + 2);
           asm volatile("" ::: "memory");

@@ -16,7 +16,10 @@
 //   R = diag(beta) (V - Kt S0),  W = (I + A)^-1 R,  O = scale (Qt S0 + P W)
 // with Kt = k e^G and Qt = q e^G. The factors e^{-G} grow with the decay
 // summed over the window, which stays in fp32/bf16 range while that sum is at
-// most 80 per key channel (gk >= -5 over 16 tokens suffices).
+// most 80 per key channel. A unit whose window decays more in some channel
+// (gk = -inf included) forms A and P pairwise instead, each entry in fp32 from
+// the exponential of the decay summed between its two tokens, so the path is
+// exact for any gk <= 0; decays are clamped at e^-110 per token (0 in fp32).
 //
 // Precision follows the prefill kernel: A and P from bf16 MFMAs with the
 // q e^G and k e^{-G} factors split into bf16 hi + lo (k e^G single); the state
@@ -37,6 +40,8 @@ namespace kda {
 namespace {
 
 constexpr int VT = 16;   // tokens per call on this path (padded)
+constexpr float kMinDecay = -110.f;        // per-token log-decay clamp: e^-110 is 0 in fp32
+constexpr float kMaxWindowDecay = 80.f;    // factor form's range: sum(-gk) over the window per channel
 constexpr int TV = 136;  // operand row stride (16-bit elements; 128 + 8 pad)
 constexpr int PS = 24;   // 16x16 fp16 rows (+8 pad)
 
@@ -70,6 +75,7 @@ struct alignas(16) VerifyLds {
   uint16_t ph[VT][PS];     // fp16 P, rows t
   float am[VT][20];        // A rows (fp32) for the solve
   float beta[VT];
+  int exact;               // this unit's window decays beyond the factor form's range
   uint16_t kin[NT][D];     // raw k, q (bf16) and gk rows of the window
   uint16_t qin[NT][D];
   float gin[NT][D];
@@ -266,6 +272,7 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     __syncthreads();                         // the previous unit's LDS readers are done
     float S[16][4];                          // fused fold: the state, in the recurrence step's ownership
     int fn = 0;                              // entries to fold
+    if (tid == 0) L.exact = 0;               // set below by any channel beyond the factor form's range
     if constexpr (FOLD) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) { S[i][0] = sv[i].x; S[i][1] = sv[i].y; S[i][2] = sv[i].z; S[i][3] = sv[i].w; }
@@ -362,14 +369,14 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
       float gs = 0.f;
       if (t0) {
 #pragma unroll
-        for (int j = 0; j < NH; ++j) gs += (j < tn) ? L.gin[j][c] : 0.f;
+        for (int j = 0; j < NH; ++j) gs += (j < tn) ? __builtin_fmaxf(L.gin[j][c], kMinDecay) : 0.f;
       }
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
         const int t = t0 + j;
         const bool ok_t = t < tn;
         const float kv = bf2f(L.kin[t][c]), qv = bf2f(L.qin[t][c]);
-        gs += ok_t ? L.gin[t][c] : 0.f;
+        gs += ok_t ? __builtin_fmaxf(L.gin[t][c], kMinDecay) : 0.f;
         const float e = __expf(gs), ie = __expf(-gs);
         const float ke = ok_t ? kv * e : 0.f, qe = ok_t ? qv * e : 0.f, ck = ok_t ? kv * ie : 0.f;
         L.kt[t][c] = h16(ke);
@@ -381,28 +388,50 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
         split_bf16(ck, hi, lo);
         L.ckh[t][c] = hi; L.ckl[t][c] = lo;
       }
+      if (gs < -kMaxWindowDecay) L.exact = 1;  // e^{-G} would leave the range
     }
     prefetch_state(unitn, kPiece1, kPiece2);
     __syncthreads();
 
     // ---- A, P and X = (I + A)^-1 (wave 0)
-    if (wave == 0) {
-      const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-      f32x4 am = z4, pm = z4;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 rk = perm_b(&L.rk[lr][32 * s], g);
-        const bf16x8 qh = perm_b(&L.rqh[lr][32 * s], g), ql = perm_b(&L.rql[lr][32 * s], g);
-        const bf16x8 ch = perm_b(&L.ckh[lr][32 * s], g), cl = perm_b(&L.ckl[lr][32 * s], g);
-        am = mfma16(rk, cl, mfma16(rk, ch, am));
-        pm = mfma16(ql, ch, mfma16(qh, cl, mfma16(qh, ch, pm)));
+    const bool exact = L.exact != 0;  // workgroup-uniform: written before the last barrier
+    if (exact) {
+      // pairwise: thread (i, j) forms its entry over the 128 channels, e^{G_ic - G_jc} from the decay
+      // summed over tokens j + 1 .. i (tokens past the window only reach rows whose beta is 0)
+      const int i = tid >> 4, j = tid & 15;
+      float a = 0.f, pp = 0.f;
+      if (i < NT && j <= i) {
+        for (int cc = 0; cc < D; ++cc) {
+          float d = 0.f;
+          for (int tt = j + 1; tt <= i; ++tt) d += __builtin_fmaxf(L.gin[tt][cc], kMinDecay);
+          const float kje = bf2f(L.kin[j][cc]) * __expf(d);
+          a = __builtin_fmaf(bf2f(L.kin[i][cc]), kje, a);
+          pp = __builtin_fmaf(bf2f(L.qin[i][cc]), kje, pp);
+        }
       }
-      // lane (g, lr) holds entries (4g + r, lr)
+      L.am[i][j] = (i < NT && j < i) ? a * L.beta[i] : 0.f;
+      L.ph[i][j] = (i < NT && j <= i) ? h16(pp) : (uint16_t)0;
+      __syncthreads();
+    }
+    if (wave == 0) {
+      if (!exact) {
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 am = z4, pm = z4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 4 * g + r, j = lr;
-        L.am[i][j] = (j < i) ? am[r] * L.beta[i] : 0.f;
-        L.ph[i][j] = (j <= i) ? h16(pm[r]) : (uint16_t)0;
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 rk = perm_b(&L.rk[lr][32 * s], g);
+          const bf16x8 qh = perm_b(&L.rqh[lr][32 * s], g), ql = perm_b(&L.rql[lr][32 * s], g);
+          const bf16x8 ch = perm_b(&L.ckh[lr][32 * s], g), cl = perm_b(&L.ckl[lr][32 * s], g);
+          am = mfma16(rk, cl, mfma16(rk, ch, am));
+          pm = mfma16(ql, ch, mfma16(qh, cl, mfma16(qh, ch, pm)));
+        }
+        // lane (g, lr) holds entries (4g + r, lr)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * g + r, j = lr;
+          L.am[i][j] = (j < i) ? am[r] * L.beta[i] : 0.f;
+          L.ph[i][j] = (j <= i) ? h16(pm[r]) : (uint16_t)0;
+        }
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
       __builtin_amdgcn_wave_barrier();
