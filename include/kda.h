@@ -78,7 +78,8 @@
  *    thread-local message for the last non-OK status. No C++ exception
  *    crosses the ABI. KDA_ERR_DEVICE carries the HIP runtime's error text.
  *  - Two calls in flight must not write the same state, snapshot, output or
- *    ring rows (the single forward stream of [LMSYS-MEM] gives this order).
+ *    ring rows (the single forward stream of [LMSYS-MEM] gives this order),
+ *    nor share a prefill workspace (it holds the launch's work counter).
  */
 #ifndef KDA_H
 #define KDA_H
@@ -230,7 +231,12 @@ typedef struct {
  *              buffer when snap_slots == 2). snap_slots >= 1.
  *  snap_count: int32 [n_seq] or NULL; receives floor(L_n / snap_interval)
  *              (0 without snapshots).
- *  workspace : device scratch of kda_plan_workspace_bytes(plan) bytes.
+ *  workspace : device scratch of kda_plan_workspace_bytes(plan) bytes. It
+ *              holds the work list and a counter that the launch increments
+ *              and its last workgroup resets to zero: two prefills in flight
+ *              at the same time (on two streams) must use two workspaces,
+ *              even with the same plan; calls ordered on one stream may share
+ *              one.
  *  scale     : readout scale.
  *  flags     : 0, or KDA_PREFILL_PLAN_RESIDENT when `workspace` already holds
  *              this plan's work list from kda_plan_upload or from an earlier

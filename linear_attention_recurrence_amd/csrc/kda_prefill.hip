@@ -48,9 +48,9 @@
 //     per-wave partial A and P tiles and the fp16 operand rows of the chain;
 //     raw v goes from global memory straight into LDS (global_load_lds) for
 //     the chain. Phase 2: the operand rows go to LDS and the loads of the
-//     chunk after next are issued; meanwhile, after their state update, three
-//     consumer waves turn the partials into the next chunk's X (wave 0 inverts
-//     the diagonal blocks of I + A), P (wave 1) and -A10 (wave 2).
+//     chunk after next are issued; meanwhile, after their state update, the
+//     consumer waves turn the partials into the next chunk's X (waves 0 and 3
+//     invert one diagonal block of I + A each), P (wave 1) and -A10 (wave 2).
 // Everything the two stages exchange is double-buffered by chunk parity, so
 // a period needs just its two barriers. Operands that a product needs
 // transposed are read with the transposing LDS load (ds_read_b64_tr_b16)
@@ -236,6 +236,34 @@ __device__ __forceinline__ void load_raw(Raw& r, const PrefillArgs& A, size_t ro
   r.b1 = *reinterpret_cast<const float*>(beta + t1 * H4);
 }
 
+// the two halves of load_raw: q and k (issued during phase 1, once the set's q and k are unpacked),
+// then gk and beta (issued in phase 2)
+__device__ __forceinline__ void load_raw_qk(Raw& r, const PrefillArgs& A, size_t row0, int nc, int co, int tl) {
+  const uint32_t HD2 = (uint32_t)A.n_heads * (D * 2);
+  const uint32_t t0 = (uint32_t)min(tl, nc - 1), t1 = (uint32_t)min(16 + tl, nc - 1);
+  const uint32_t b0 = t0 * HD2 + 16u * co, b1 = t1 * HD2 + 16u * co;
+  const char* q = reinterpret_cast<const char*>(A.q + row0 * D);
+  const char* k = reinterpret_cast<const char*>(A.k + row0 * D);
+  r.q0 = *reinterpret_cast<const uint4*>(q + b0);
+  r.q1 = *reinterpret_cast<const uint4*>(q + b1);
+  r.k0 = *reinterpret_cast<const uint4*>(k + b0);
+  r.k1 = *reinterpret_cast<const uint4*>(k + b1);
+}
+__device__ __forceinline__ void load_raw_gb(Raw& r, const PrefillArgs& A, size_t row0, int nc, int co, int tl) {
+  const uint32_t HD2 = (uint32_t)A.n_heads * (D * 2);
+  const uint32_t t0 = (uint32_t)min(tl, nc - 1), t1 = (uint32_t)min(16 + tl, nc - 1);
+  const uint32_t b0 = t0 * HD2 + 16u * co, b1 = t1 * HD2 + 16u * co;
+  const char* gk = reinterpret_cast<const char*>(A.gk + row0 * D);
+  const char* beta = reinterpret_cast<const char*>(A.beta + row0);
+  const uint32_t H4 = (uint32_t)A.n_heads * 4u;
+  r.g0a = *reinterpret_cast<const float4*>(gk + 2u * b0);
+  r.g0b = *reinterpret_cast<const float4*>(gk + 2u * b0 + 16u);
+  r.g1a = *reinterpret_cast<const float4*>(gk + 2u * b1);
+  r.g1b = *reinterpret_cast<const float4*>(gk + 2u * b1 + 16u);
+  r.b0 = *reinterpret_cast<const float*>(beta + t0 * H4);
+  r.b1 = *reinterpret_cast<const float*>(beta + t1 * H4);
+}
+
 // raw v rows of a chunk straight into LDS: 4 rows of 256 bytes per instruction, rows
 // 16r + 4w .. 16r + 4w + 3 (r < 2) from wave w of a role; 16-byte chunks land at chunk ^ (2 row & 15)
 __device__ __forceinline__ void issue_v(const uint16_t* src, const PrefillArgs& A, uint16_t (&dst)[C][D], size_t row0, int nc, int wu, int lane) {
@@ -272,7 +300,9 @@ constexpr float kMinChunkDecay = 0x1p-116f;  // e^{G_31} below this takes the ex
 // producer, phase 1 of the period before chunk c: decay factors and partial A
 // and P tiles over this wave's 32 channels. Returns true when the wave's chunk is outside the
 // factor form's range (what it wrote is then to be replaced by stage1_exact).
-__device__ __forceinline__ bool stage1(PrefillLds& L, const Raw& cur, int nc, int b, int pw, int g, int lr, Keep& kp_) {
+template <class Refill>
+__device__ __forceinline__ bool stage1(PrefillLds& L, const Raw& cur, int nc, int b, int pw, int g, int lr, Keep& kp_,
+                                       Refill refill) {
   const int co = 4 * pw + g;  // channel octet 8co..8co+7
   const int tl = lr;          // tokens tl (block 0) and 16+tl (block 1)
   const int c8 = 8 * co;
@@ -296,6 +326,13 @@ __device__ __forceinline__ bool stage1(PrefillLds& L, const Raw& cur, int nc, in
   float k0[8], k1[8], q0[8], q1[8];
   unpack_bf16x8(cur.k0, k0); unpack_bf16x8(cur.k1, k1);
   unpack_bf16x8(cur.q0, q0); unpack_bf16x8(cur.q1, q1);
+  // q and k are unpacked: their registers take a later chunk's q and k now, so that the address
+  // unit works through those loads during this phase's arithmetic (16 rows x 64 bytes per load
+  // instruction is slow to address; issued all at once in phase 2 they held the issuing waves for
+  // most of it)
+  asm volatile("" ::: "memory");
+  refill();
+  asm volatile("" ::: "memory");
   float xr0[8], xr1[8], yc0[8], yc1[8], e0[8], e1[8], f0[8], f1[8], dl[8];
   // the smallest prefix sum of this lane's channels: over a DPP row, the half totals (-inf included)
 #pragma unroll
@@ -351,9 +388,6 @@ __device__ __forceinline__ bool stage1(PrefillLds& L, const Raw& cur, int nc, in
   return __builtin_amdgcn_ballot_w64(m < kMinChunkDecay) != 0;  // (NaN breaks gk <= 0: not caught)
 }
 
-__device__ __forceinline__ void opaque(uint4& u) { asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w)); }
-__device__ __forceinline__ void opaque(float4& u) { asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w)); }
-
 // One diagonal 16-block of A and P, summed pairwise in fp32 over this wave's 32 channels: entry
 // (i, j), j <= i, is sum_c k_ic k_jc e^{G_ic - G_jc} (q_ic for P), e^{G_i - G_j} = 2^{ps_i - ps_j}
 // from the block's inclusive prefix sums ps (log2 units); entries j > i are 0. Lane (g, lr) holds
@@ -393,13 +427,12 @@ __device__ __forceinline__ void diag_pairwise(float (&part_a)[16][20], float (&p
 // exponential of a prefix or suffix sum, never a product of a large and a small one; the diagonal
 // tiles A00, A11, P00, P11 are summed pairwise; A10 and P10 keep their MFMAs. Decays are clamped at
 // 2^-160 per token, which is 0 in fp32, so e^{-inf} = 0 exactly and no sum is infinite.
-__device__ __forceinline__ void stage1_exact(PrefillLds& L, const Raw& raw, int nc, int b, int pw, int g, int lr,
-                                             Keep& kp_) {
-  // a copy of the raw registers made opaque to the compiler, so that nothing stage1 derived from them
-  // is kept live for reuse here (that would cost the fast path registers)
-  Raw cur = raw;
-  opaque(cur.q0); opaque(cur.q1); opaque(cur.k0); opaque(cur.k1);
-  opaque(cur.g0a); opaque(cur.g0b); opaque(cur.g1a); opaque(cur.g1b);
+__device__ __forceinline__ void stage1_exact(PrefillLds& L, const PrefillArgs& A, size_t row0, int nc, int b, int pw,
+                                             int g, int lr, Keep& kp_) {
+  // the raw registers already hold a later chunk's loads: read this chunk again (this path is rare)
+  Raw cur;
+  load_raw(cur, A, row0, nc, 4 * pw + g, lr);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   const int co = 4 * pw + g, c8 = 8 * co, tl = lr;
   const bool ok0 = tl < nc, ok1 = 16 + tl < nc;
   constexpr float kLog2e = 1.4426950408889634f;
@@ -491,45 +524,42 @@ __device__ __forceinline__ void reduce_tiles(const PrefillLds& L, int t0, int j,
   }
 }
 
-// producer wave 0, phase 2: the diagonal 16-blocks of A (beta-scaled strict lower parts of the
-// summed tiles) and of X = (I + A)^-1. The off-diagonal block of X is never formed: the chain
-// applies it as W1 = X11 (R1 - A10 W0).
-__device__ __forceinline__ void stage2_solve(PrefillLds& L, int b, int lane) {
+// phase 2, on one chain wave per block: diagonal 16-block blk of A (the beta-scaled strict lower part
+// of the summed tile) and of X = (I + A)^-1. The off-diagonal block of X is never formed: the chain
+// applies it as W1 = X11 (R1 - A10 W0). The two blocks are independent and go to two waves.
+__device__ __forceinline__ void stage2_solve(PrefillLds& L, int b, int lane, int blk) {
   const int g = lane >> 4, lr = lane & 15;
   {
     const int j = lane >> 2, i0 = 4 * (lane & 3);
-    f32x4 sums[2];
-    reduce_tiles<2>(L, 0, j, i0, sums);
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {  // A00, A11
-      const f32x4 s4 = sums[blk];
-      const float4 b4 = *reinterpret_cast<const float4*>(&L.beta[b][16 * blk + i0]);
-      const int jg = 16 * blk + j, ig = 16 * blk + i0;
-      L.ar[ig][jg] = (jg < ig) ? s4[0] * b4.x : 0.f;
-      L.ar[ig + 1][jg] = (jg < ig + 1) ? s4[1] * b4.y : 0.f;
-      L.ar[ig + 2][jg] = (jg < ig + 2) ? s4[2] * b4.z : 0.f;
-      L.ar[ig + 3][jg] = (jg < ig + 3) ? s4[3] * b4.w : 0.f;
-    }
+    f32x4 sums[1];
+    reduce_tiles<1>(L, blk, j, i0, sums);  // tile 0: A00, tile 1: A11
+    const f32x4 s4 = sums[0];
+    const float4 b4 = *reinterpret_cast<const float4*>(&L.beta[b][16 * blk + i0]);
+    const int jg = 16 * blk + j, ig = 16 * blk + i0;
+    L.ar[ig][jg] = (jg < ig) ? s4[0] * b4.x : 0.f;
+    L.ar[ig + 1][jg] = (jg < ig + 1) ? s4[1] * b4.y : 0.f;
+    L.ar[ig + 2][jg] = (jg < ig + 2) ? s4[2] * b4.z : 0.f;
+    L.ar[ig + 3][jg] = (jg < ig + 3) ? s4[3] * b4.w : 0.f;
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
   __builtin_amdgcn_wave_barrier();
-  // Forward substitution on rows. DPP row g of the wave (16 lanes) holds block
-  // blk = g & 1, lane lr = row i of it, and the columns of parity par = g >> 1:
-  // x[m] = X[i][2m + par]. Step kk subtracts A[i][kk] times row kk, which
-  // row_newbcast:kk reads from lane kk of the same DPP row; row kk has no
-  // entries right of column kk, so column pairs beyond kk are skipped.
-  const int blk = g & 1, par = g >> 1, i = lr;
+  // Forward substitution on rows. DPP row g of the wave (16 lanes) holds the columns q with
+  // q % 4 == g of the block, lane lr = row i: x[m] = X[i][4m + g]. Step kk subtracts A[i][kk]
+  // times row kk, which row_newbcast:kk reads from lane kk of the same DPP row; row kk has no
+  // entries right of column kk, so columns beyond kk are skipped. Every X[i][q] takes the same
+  // sequence of fused multiply-adds whichever lane holds it.
+  const int par = g, i = lr;
   float arow[16];
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     const float4 t4 = *reinterpret_cast<const float4*>(&L.ar[16 * blk + i][16 * blk + 4 * q4]);
     arow[4 * q4] = -t4.x; arow[4 * q4 + 1] = -t4.y; arow[4 * q4 + 2] = -t4.z; arow[4 * q4 + 3] = -t4.w;
   }
-  float x[8];
+  float x[4];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) x[m] = (2 * m + par == i) ? 1.f : 0.f;
+  for (int m = 0; m < 4; ++m) x[m] = (4 * m + par == i) ? 1.f : 0.f;
 #define KDA_SOLVE_STEP(kk)                                                                                  \
-  _Pragma("unroll") for (int m = 0; 2 * m <= (kk); ++m) {                                                   \
+  _Pragma("unroll") for (int m = 0; 4 * m <= (kk); ++m) {                                                   \
     const float xk_ = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[m]), 0x150 + (kk), 0xf, 0xf, true)); \
     x[m] = __builtin_fmaf(arow[kk], xk_, x[m]);                                                             \
   }
@@ -538,8 +568,8 @@ __device__ __forceinline__ void stage2_solve(PrefillLds& L, int b, int lane) {
   KDA_SOLVE_STEP(10) KDA_SOLVE_STEP(11) KDA_SOLVE_STEP(12) KDA_SOLVE_STEP(13) KDA_SOLVE_STEP(14)
 #undef KDA_SOLVE_STEP
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
-    L.xb[b][16 * blk + i][16 * blk + 2 * m + par] = __builtin_bit_cast(uint16_t, (_Float16)x[m]);
+  for (int m = 0; m < 4; ++m)
+    L.xb[b][16 * blk + i][16 * blk + 4 * m + par] = __builtin_bit_cast(uint16_t, (_Float16)x[m]);
 }
 
 // producer wave 2, phase 2: -A10 = -(beta-scaled summed tile), fp16, for the chain's W1
@@ -622,11 +652,12 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
       const int lane = lane_o, g = g_o, lr = lr_o;
       // Raw inputs are prefetched two periods ahead: q, k, gk, beta into registers, alternating
       // between two sets (chunk c lives in set c & 1 from the period that issues it, c - 3,
-      // until its stage 1 in period c - 1), and v straight into vr[c & 1] (issued in period
-      // c - 2, read by the chain in period c; with GATED the gate rows go into gr[c & 1] the same
-      // way). Every period issues the same 12 loads (14 with GATED; past the last chunk they re-read
-      // it), so the compiler's waits before each register use count exactly, and the wait that
-      // closes a period can leave just that period's loads in flight.
+      // until its stage 1 in period c - 1: its q and k in that period's phase 1, as soon as stage 1
+      // has unpacked the set's previous q and k, its gk and beta in phase 2), and v straight into
+      // vr[c & 1] (issued in period c - 2, read by the chain in period c; with GATED the gate rows
+      // go into gr[c & 1] the same way). Every period issues the same 12 loads (14 with GATED; past
+      // the last chunk they re-read it), so the compiler's waits before each register use count
+      // exactly, and the wait that closes a period can leave just that period's loads in flight.
       if (nch == 0) {
         __syncthreads();
         __syncthreads();
@@ -635,6 +666,14 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
         auto issue = [&](Raw& r, int c) {
           c = min(c, nch - 1);
           load_raw(r, A, (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), 4 * pw + g, lr);
+        };
+        auto issue_early = [&](Raw& r, int c) {
+          c = min(c, nch - 1);
+          load_raw_qk(r, A, (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), 4 * pw + g, lr);
+        };
+        auto issue_late = [&](Raw& r, int c) {
+          c = min(c, nch - 1);
+          load_raw_gb(r, A, (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), 4 * pw + g, lr);
         };
         auto issue_vc = [&](int c) {
           c = min(c, nch - 1);
@@ -652,10 +691,13 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
           Keep keep;
           if (c1 < nch) {
             const int ncc = min(C, len - C * c1);
-            if (stage1(L, use, ncc, b1, pw, g, lr, keep)) stage1_exact(L, use, ncc, b1, pw, g, lr, keep);
+            if (stage1(L, use, ncc, b1, pw, g, lr, keep, [&] { issue_early(use, c1 + 2); }))
+              stage1_exact(L, A, (size_t)(tok0 + C * c1) * H + h, ncc, b1, pw, g, lr, keep);
+          } else {
+            issue_early(use, c1 + 2);
           }
           __syncthreads();
-          issue(use, c1 + 2);
+          issue_late(use, c1 + 2);
           asm volatile("" ::: "memory");
           issue_vc(c1 + 1);  // into the buffer the chain read in this period's phase 1
           if (c1 < nch) stage1b(L, keep, b1, pw, g, lr);
@@ -877,11 +919,12 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
               L.rs[lane] = norm_rstd(ss, A.eps);
             }
           }
-          // the next chunk's X, P and -A10 from the partials the producers wrote in phase 1, on three
-          // of the chain waves (the producers' phase 2 is taken up by issuing the next loads)
-          if (cw == 0 && p + 1 < nch) stage2_solve(L, (p + 1) & 1, lane);
+          // the next chunk's X, P and -A10 from the partials the producers wrote in phase 1, on the
+          // chain waves (the producers' phase 2 is taken up by issuing the next loads)
+          if (cw == 0 && p + 1 < nch) stage2_solve(L, (p + 1) & 1, lane, 0);
           else if (cw == 1 && p + 1 < nch) stage2_p(L, (p + 1) & 1, lane);
           else if (cw == 2 && p + 1 < nch) stage2_a10(L, (p + 1) & 1, lane);
+          else if (cw == 3 && p + 1 < nch) stage2_solve(L, (p + 1) & 1, lane, 1);
           __syncthreads();
         }
 
