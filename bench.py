@@ -723,7 +723,7 @@ def main():
     varlen = None
     if want("varlen_h96"):
         log("varlen H96 prefill: longest-first and input order")
-        r = bench_prefill_workload("varlen_h96", [LPT, FIFO], 5, 1, torch, kda, sg, synth, flush)
+        r = bench_prefill_workload("varlen_h96", [LPT, FIFO], 10, 2, torch, kda, sg, synth, flush, short=True)
         varlen = {"lpt": prefill_leg(r, LPT, "varlen_h96"), "fifo": prefill_leg(r, FIFO, "varlen_h96"),
                   "total_tokens": int(sum(r["lens"])), "n_seq": r["N"], "heads": r["H"]}
         varlen["lpt_speedup"] = varlen["fifo"]["ms"] / varlen["lpt"]["ms"]
