@@ -52,7 +52,7 @@ METRIC = "KDA prefill tokens*heads/s and verify+fold us/step at 1 GPU; % of roof
 # HBM bytes per prefill launch measured by rocprofv3 PMC (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, the
 # factors that make a plain 1 GiB copy read 1 GiB and write 1 GiB), per workload; None for a workload
 # not measured with the current kernel (set to None whenever the kernel changes until it is measured again)
-PREFILL_TRAFFIC_BYTES = {"long_1m_h96": 233_037_035_296, "prefill_4x2048_h64": 980_575_923}
+PREFILL_TRAFFIC_BYTES = {"long_1m_h96": None, "prefill_4x2048_h64": None}
 FLUSH_BYTES = 1 << 30  # scratch written before every timed prefill rep: evicts the 256 MB Infinity Cache and L2s
 
 

@@ -871,7 +871,9 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
               if constexpr (GATED && NV == 2) L.ssq[t][4 * cw + g] = norm_slice_ssq(Og[mt][0], Og[mt][1]);
             }
           }
-          __syncthreads();
+          // The state update reads only this chunk's K' rows and e^{G_31} (written by the preparation
+          // waves in the previous period) and this wave's own W, so it runs before the barrier, in the
+          // time the chain would otherwise wait there for the preparation of the next chunk.
           if (p >= 0) {
             // ---------------- S = e^{G_31} S0 + K'^T W ----------------
   #pragma unroll
@@ -903,6 +905,7 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
                   for (int r = 0; r < 4; ++r) dst[(16 * mc + r) * D + 16 * nv] = S[mc][nv][r];
             }
           }
+          __syncthreads();
           // (GATED) 1 / rms of each of this chunk's token rows from the slice sums of phase 1, on the
           // chain wave with the most slack in phase 2; the next period's phase 1 uses them
           if constexpr (GATED && NV == 2) {
