@@ -209,8 +209,8 @@ typedef struct {
  * sequences, T = cu_seqlens[n_seq] tokens, H = plan heads.
  *
  *  in        : q, k, v bf16 [T, H, 128]; gk fp32 [T, H, 128]; beta fp32 [T, H].
- *              Any gk <= 0 is exact, -inf (a full reset) included: a chunk
- *              whose decay summed over a 16-token half exceeds 80 in some key
+ *              Any gk <= 0 is exact, -inf (a full reset) included: a 32-token
+ *              chunk whose decay summed over it exceeds 60 in some key
  *              channel (where the fast factor form would leave fp32/bf16
  *              range) is prepared on an exact path, about three chunk
  *              periods slower. Range of the state products: the state, and

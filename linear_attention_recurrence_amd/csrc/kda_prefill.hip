@@ -11,16 +11,16 @@
 //
 // Algebra (the chunked form of the token recurrence; C = 32 tokens, chunk
 // start state S0, G_t = sum_{tau<=t} gk_tau inside the chunk):
-//   A[i][j] = beta_i sum_c Rk_ic Ck_jc     (j < i)   Rk = k e^{G - G_15}, Ck = k e^{G_15 - G}
-//   P[t][i] =        sum_c Rq_tc Ck_ic     (i <= t)  Rq = q e^{G - G_15}
-//   X = (I + A)^-1,   R = diag(beta) (V - Kt S0),   W = X R       Kt = k e^G
-//   O = scale (Qt S0 + P W)                                       Qt = q e^G
+//   A[i][j] = beta_i sum_c Kt_ic Ck_jc     (j < i)   Kt = k e^G, Ck = k e^{-G}
+//   P[t][i] =        sum_c Qt_tc Ck_ic     (i <= t)  Qt = q e^G
+//   X = (I + A)^-1,   R = diag(beta) (V - Kt S0),   W = X R
+//   O = scale (Qt S0 + P W)
 //   S_end = e^{G_31} S0 + K'^T W                                  K' = k e^{G_31 - G}
-// The intra-chunk factors are anchored at token 15 so each spans at most 16
-// tokens of decay; every factor is a product of a = exp(gk) over such a span
-// or its reciprocal, which stays in fp32/bf16 range while the decay summed
-// over each 16-token half chunk is at most 80 (gk >= -5 suffices), the
-// documented precondition of this path. The factors of Kt, Qt, K' are <= 1.
+// Kt and Qt serve both as the chain's fp16 operands and, rounded to bf16, as
+// the row factors of A and P. The column factor e^{-G} grows with the decay
+// summed over the chunk; every factor stays in fp32/bf16 range, with its bf16
+// low part normal, while that sum is at most 60 per key channel. Beyond it
+// (or for gk = -inf) a wave takes the exact path below.
 //
 // Precision (chosen by measuring each operand's rounding against the fp64
 // oracle): the intra-chunk factors Rq and Ck enter their MFMAs as bf16 hi + lo
@@ -280,6 +280,9 @@ __device__ __forceinline__ void issue_v(const uint16_t* src, const PrefillArgs& 
 // What phase 2 of the producer needs from phase 1 to write the chain's operand rows: the
 // masked raw q and k (bf16) and the decay factors e^{G_t} and e^{G_31 - G_t} of both tokens.
 // eight fp16 products x[i] * y[i], packed
+__device__ __forceinline__ uint4 pk8(const float (&x)[8]) {
+  return make_uint4(pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]), pk_f16(x[6], x[7]));
+}
 __device__ __forceinline__ uint4 pk8_mul(const float (&x)[8], const float (&y)[8]) {
   return make_uint4(pk_f16(x[0] * y[0], x[1] * y[1]), pk_f16(x[2] * y[2], x[3] * y[3]), pk_f16(x[4] * y[4], x[5] * y[5]),
                     pk_f16(x[6] * y[6], x[7] * y[7]));
@@ -290,12 +293,11 @@ struct Keep {
 
 // ---------------------------------------------------------------------------
 // The factor form below needs every factor in fp32/bf16 range: per key channel, the decay summed
-// over each 16-token half of the chunk must be at most 80 (log2: 116). It is checked on the whole
-// chunk's factor e^{G_31} (8 values per lane, less work than the 16 half sums, and sufficient: both
-// halves' factors are at most 1): a wave with a channel where e^{G_31} < 2^-116, or a decay of -inf,
-// runs stage1_exact after stage1, which rewrites everything stage1 wrote. The check costs the fast
-// path a minimum of 8 values and one branch at its end.
-constexpr float kMinChunkDecay = 0x1p-116f;  // e^{G_31} below this takes the exact path (e^-80.4)
+// over the chunk must be at most 60 (log2: 86), so that e^{-G} <= 2^86 and the bf16 low parts of
+// q e^G stay normal. It is checked on the chunk's factor e^{G_31} (8 values per lane): a wave with a
+// channel where e^{G_31} < 2^-86, or a decay of -inf, runs stage1_exact after stage1, which rewrites
+// everything stage1 wrote. The check costs the fast path a minimum of 8 values and one branch.
+constexpr float kMinChunkDecay = 0x1p-86f;  // e^{G_31} below this takes the exact path (e^-59.6)
 
 // producer, phase 1 of the period before chunk c: decay factors and partial A
 // and P tiles over this wave's 32 channels. Returns true when the wave's chunk is outside the
@@ -333,31 +335,36 @@ __device__ __forceinline__ bool stage1(PrefillLds& L, const Raw& cur, int nc, in
   asm volatile("" ::: "memory");
   refill();
   asm volatile("" ::: "memory");
-  float xr0[8], xr1[8], yc0[8], yc1[8], e0[8], e1[8], f0[8], f1[8], dl[8];
-  // the smallest prefix sum of this lane's channels: over a DPP row, the half totals (-inf included)
+  float e0[8], e1[8], ie0[8], ie1[8], f0[8], f1[8], dl[8];
+  // no branch inside this loop: its 16 prefix-sum chains and 32 exponentials are independent
+  // across channels and interleave only within one basic block
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float s0 = row_scan_add(l0[i]), s1 = row_scan_add(l1[i]);
+    // prefix sums inside each 16-token half, then the four exponentials
+    const float s0 = row_scan_add(l0[i]), s1 = row_scan_add(l1[i]);  // log2 of e^{G_t}, e^{G_t - G_15}
     const float p0 = __builtin_amdgcn_exp2f(s0), r0 = __builtin_amdgcn_exp2f(-s0);
     const float p1 = __builtin_amdgcn_exp2f(s1), r1 = __builtin_amdgcn_exp2f(-s1);
-    const float T0 = KDA_ROW_BCAST15(p0), T1 = KDA_ROW_BCAST15(p1);   // block totals
-    xr0[i] = p0 * KDA_ROW_BCAST15(r0);       // e^{G_t - G_15}, block 0 (lane 15's r0 is 1 / T0)
-    xr1[i] = p1;
-    yc0[i] = T0 * r0;                         // e^{G_15 - G_t}, block 0
-    yc1[i] = r1;
+    const float T0 = KDA_ROW_BCAST15(p0), T1 = KDA_ROW_BCAST15(p1);   // e^{G_15}, e^{G_31 - G_15}
     e0[i] = p0;                               // e^{G_t}
     e1[i] = T0 * p1;
-    f0[i] = yc0[i] * T1;                      // e^{G_31 - G_t}
-    f1[i] = T1 * r1;
+    ie0[i] = r0;                              // e^{-G_t}
+    ie1[i] = KDA_ROW_BCAST15(r0) * r1;        // (lane 15's r0 is e^{-G_15})
     dl[i] = T0 * T1;                          // e^{G_31}
+    f0[i] = dl[i] * r0;                       // e^{G_31 - G_t}
+    f1[i] = T1 * r1;
   }
   if (tl == 0) {
     *reinterpret_cast<float4*>(&L.dlast[b][c8]) = make_float4(dl[0], dl[1], dl[2], dl[3]);
     *reinterpret_cast<float4*>(&L.dlast[b][c8 + 4]) = make_float4(dl[4], dl[5], dl[6], dl[7]);
   }
-  // fp16 operand rows of the chain, written to LDS in phase 2
-  kp_.qt[0] = pk8_mul(q0, e0); kp_.qt[1] = pk8_mul(q1, e1);
-  kp_.kt[0] = pk8_mul(k0, e0); kp_.kt[1] = pk8_mul(k1, e1);
+  // q e^G and k e^G serve twice: rounded to fp16 they are the chain's operand rows (written to LDS in
+  // phase 2), rounded to bf16 they are the row factors of A and P (anchored at the chunk start:
+  // A_ij = beta_i sum_c (k_ic e^{G_ic}) (k_jc e^{-G_jc}), P_ti = sum_c (q_tc e^{G_tc}) (k_ic e^{-G_ic}))
+  float qe0[8], qe1[8], ke0[8], ke1[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { qe0[i] = q0[i] * e0[i]; qe1[i] = q1[i] * e1[i]; ke0[i] = k0[i] * e0[i]; ke1[i] = k1[i] * e1[i]; }
+  kp_.qt[0] = pk8(qe0); kp_.qt[1] = pk8(qe1);
+  kp_.kt[0] = pk8(ke0); kp_.kt[1] = pk8(ke1);
   kp_.kp[0] = pk8_mul(k0, f0); kp_.kp[1] = pk8_mul(k1, f1);
   // A and P over this wave's 32 channels, straight from registers: lane (g, lr) holds
   // channels 32pw+8g..+7 of tokens lr (block 0) and 16+lr (block 1), which is the
@@ -365,12 +372,12 @@ __device__ __forceinline__ bool stage1(PrefillLds& L, const Raw& cur, int nc, in
   bf16x8 rk0, rk1, rq0h, rq0l, rq1h, rq1l, ck0h, ck0l, ck1h, ck1l;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    rk0[i] = (__bf16)(k0[i] * xr0[i]);
-    rk1[i] = (__bf16)(k1[i] * xr1[i]);
-    float v = q0[i] * xr0[i]; rq0h[i] = (__bf16)v; rq0l[i] = (__bf16)(v - (float)rq0h[i]);
-    v = q1[i] * xr1[i];       rq1h[i] = (__bf16)v; rq1l[i] = (__bf16)(v - (float)rq1h[i]);
-    v = k0[i] * yc0[i];       ck0h[i] = (__bf16)v; ck0l[i] = (__bf16)(v - (float)ck0h[i]);
-    v = k1[i] * yc1[i];       ck1h[i] = (__bf16)v; ck1l[i] = (__bf16)(v - (float)ck1h[i]);
+    rk0[i] = (__bf16)ke0[i];
+    rk1[i] = (__bf16)ke1[i];
+    float v = qe0[i];         rq0h[i] = (__bf16)v; rq0l[i] = (__bf16)(v - (float)rq0h[i]);
+    v = qe1[i];               rq1h[i] = (__bf16)v; rq1l[i] = (__bf16)(v - (float)rq1h[i]);
+    v = k0[i] * ie0[i];       ck0h[i] = (__bf16)v; ck0l[i] = (__bf16)(v - (float)ck0h[i]);
+    v = k1[i] * ie1[i];       ck1h[i] = (__bf16)v; ck1l[i] = (__bf16)(v - (float)ck1h[i]);
   }
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc[6];
@@ -473,8 +480,8 @@ __device__ __forceinline__ void stage1_exact(PrefillLds& L, const PrefillArgs& A
     kp_.kp[0] = pk8_mul(k0, f0); kp_.kp[1] = pk8_mul(k1, f1);
   }
   {
-    // A10 and P10 as in stage1, from factors at most 1: e^{G_t - G_15} of the second half is 2^{p1},
-    // e^{G_15 - G_t} of the first half is 2^{x0}
+    // A10 and P10 on the MFMAs, factored at token 15 into factors at most 1: e^{G_t - G_15} of the
+    // second half is 2^{p1}, e^{G_15 - G_t} of the first half is 2^{x0}
     bf16x8 rk1, rq1h, rq1l, ck0h, ck0l;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
