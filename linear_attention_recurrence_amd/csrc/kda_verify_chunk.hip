@@ -76,8 +76,8 @@ struct alignas(16) VerifyLds {
   float am[VT][20];        // A rows (fp32) for the solve
   float beta[VT];
   int exact;               // this unit's window decays beyond the factor form's range
-  uint16_t kin[NT][D];     // raw k, q (bf16) and gk rows of the window
-  uint16_t qin[NT][D];
+  alignas(16) uint16_t kin[NT][D];  // raw k, q (bf16) and gk rows of the window; after the decay factors,
+  uint16_t qin[NT][D];              // the four waves' A and P partials (8 KB) on the fast path
   float gin[NT][D];
 };
 
@@ -393,8 +393,16 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     prefetch_state(unitn, kPiece1, kPiece2);
     __syncthreads();
 
-    // ---- A, P and X = (I + A)^-1 (wave 0)
+    // ---- A, P and X = (I + A)^-1
     const bool exact = L.exact != 0;  // workgroup-uniform: written before the last barrier
+    // A and P partials of one reduction step (32 channels) per wave, kept in the raw rows' space
+    // (kin, qin, gin: read only by the decay factors above and by the exact path): [wave][A, P][lane]
+    f32x4* part = reinterpret_cast<f32x4*>(&L.kin[0][0]);
+    static_assert(offsetof(VerifyLds<NT>, qin) == offsetof(VerifyLds<NT>, kin) + sizeof(L.kin) &&
+                      offsetof(VerifyLds<NT>, gin) == offsetof(VerifyLds<NT>, qin) + sizeof(L.qin) &&
+                      offsetof(VerifyLds<NT>, kin) % 16 == 0 &&
+                      sizeof(L.kin) + sizeof(L.qin) + sizeof(L.gin) >= 4 * 2 * 64 * sizeof(f32x4),
+                  "the partials need 8 KB of contiguous, aligned raw-row space");
     if (exact) {
       // pairwise: thread (i, j) forms its entry over the 128 channels, e^{G_ic - G_jc} from the decay
       // summed over tokens j + 1 .. i (tokens past the window only reach rows whose beta is 0)
@@ -411,21 +419,26 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
       }
       L.am[i][j] = (i < NT && j < i) ? a * L.beta[i] : 0.f;
       L.ph[i][j] = (i < NT && j <= i) ? h16(pp) : (uint16_t)0;
-      __syncthreads();
+    } else {
+      const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+      const int s = wave;
+      const bf16x8 rk = perm_b(&L.rk[lr][32 * s], g);
+      const bf16x8 qh = perm_b(&L.rqh[lr][32 * s], g), ql = perm_b(&L.rql[lr][32 * s], g);
+      const bf16x8 ch = perm_b(&L.ckh[lr][32 * s], g), cl = perm_b(&L.ckl[lr][32 * s], g);
+      part[(2 * wave) * 64 + lane] = mfma16(rk, cl, mfma16(rk, ch, z4));
+      part[(2 * wave + 1) * 64 + lane] = mfma16(ql, ch, mfma16(qh, cl, mfma16(qh, ch, z4)));
     }
+    __syncthreads();
     if (wave == 0) {
       if (!exact) {
-        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-        f32x4 am = z4, pm = z4;
+        // the four waves' partials in wave order; lane (g, lr) holds entries (4g + r, lr)
+        f32x4 am = part[lane], pm = part[64 + lane];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 rk = perm_b(&L.rk[lr][32 * s], g);
-          const bf16x8 qh = perm_b(&L.rqh[lr][32 * s], g), ql = perm_b(&L.rql[lr][32 * s], g);
-          const bf16x8 ch = perm_b(&L.ckh[lr][32 * s], g), cl = perm_b(&L.ckl[lr][32 * s], g);
-          am = mfma16(rk, cl, mfma16(rk, ch, am));
-          pm = mfma16(ql, ch, mfma16(qh, cl, mfma16(qh, ch, pm)));
+        for (int w = 1; w < 4; ++w) {
+          const f32x4 a4 = part[(2 * w) * 64 + lane], p4 = part[(2 * w + 1) * 64 + lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) { am[r] += a4[r]; pm[r] += p4[r]; }
         }
-        // lane (g, lr) holds entries (4g + r, lr)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 4 * g + r, j = lr;
