@@ -82,6 +82,10 @@ struct alignas(16) VerifyLds {
 };
 
 __device__ __forceinline__ uint2 lds8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+// a range-checked buffer over `bytes` bytes at p, read only here (an empty range reads zeros)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t read_range(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kBufWord3);
+}
 // A wave-uniform 32-bit read through the scalar data cache. Plain loads of these
 // indices are emitted as vector loads, and waiting for one of those waits for every
 // older vector memory operation of the wave (prefetches and stores included).
@@ -185,18 +189,18 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
   // on the fused path). The next unit's slice is issued in three pieces, between the compute
   // phases: all 16 at once fill the memory queue and stall the issuing wave until most of them
   // have returned, with this unit's compute still to do.
-  auto prefetch_state = [&](size_t unit, int i0, int i1) {
-    if constexpr (FOLD) {
-      const float* sp = A.state_pool + unit * D * D + col0;
+  // The loads go through a buffer range over the unit's state, empty when there is no next unit:
+  // the same instructions are issued and return zeros without touching memory.
+  auto state_range = [&](size_t unit, bool live) {
+    return read_range(A.state_pool + unit * D * D, live ? D * D * 4 : 0);
+  };
+  auto prefetch_state = [&](__amdgpu_buffer_rsrc_t srs, int i0, int i1) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (i >= i0 && i < i1) sv[i] = *reinterpret_cast<const float4*>(sp + (size_t)(r0 + i) * D);
-    } else {
-      const float* sp = A.state_pool + unit * D * D + 32 * wave + 4 * (lane & 7);
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (i >= i0 && i < i1) sv[i] = *reinterpret_cast<const float4*>(sp + (size_t)(8 * i + (lane >> 3)) * D);
-    }
+    for (int i = 0; i < 16; ++i)
+      if (i >= i0 && i < i1) {
+        const int off = FOLD ? ((r0 + i) * D + col0) * 4 : ((8 * i + (lane >> 3)) * D + 32 * wave + 4 * (lane & 7)) * 4;
+        sv[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(srs, off, 0, 0));
+      }
   };
   constexpr int kPiece1 = 4, kPiece2 = 10;  // loads issued after staging, after the decay factors, after A and P
   // the window of request b: its first input row and its length tn <= T. Ragged bounds are
@@ -213,40 +217,56 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
       tn = T;
     }
   };
-  // the raw inputs of a unit (and the entries to fold on the fused path)
-  auto prefetch_inputs = [&](int b, int h, size_t unit) {
+  // the raw inputs of a unit (and the entries to fold on the fused path), through buffer ranges
+  // over the unit's rows that are empty when there is no such unit (live false) or no window:
+  // the loads are issued all the same and return zeros without touching memory
+  auto prefetch_inputs = [&](int b, int h, size_t unit, bool live) {
     if constexpr (FOLD) {
       // entries past the window re-read its last one (or its first, for an empty window)
       const int n = fold_n(b), fs = A.fold_start ? sload_i32(A.fold_start + b) : 0;
       const int pos = (fs + min(ti, max(n - 1, 0))) & (A.ring_len - 1);
-      const size_t re = (unit * A.ring_len + pos) * D + c4;
-      fk = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.ring_k) + re);
-      fv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.ring_v) + re);
-      fg = *reinterpret_cast<const float4*>(A.ring_gk + re);
-      fb = A.ring_beta[unit * A.ring_len + pos];
+      const int nrow = live ? A.ring_len : 0;
+      const size_t rbase = unit * A.ring_len;
+      const int re = pos * D + c4;
+      fk = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+               read_range(static_cast<const uint16_t*>(A.ring_k) + rbase * D, nrow * D * 2), 2 * re, 0, 0));
+      fv = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+               read_range(static_cast<const uint16_t*>(A.ring_v) + rbase * D, nrow * D * 2), 2 * re, 0, 0));
+      fg = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+               read_range(A.ring_gk + rbase * D, nrow * D * 4), 4 * re, 0, 0));
+      fb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+               read_range(A.ring_beta + rbase, nrow * 4), 4 * pos, 0, 0));
     }
     size_t first;
     int tn;
     window(b, first, tn);
+    // rows first .. first + tn - 1 of head h: row t at (first + t) * H + h
+    const size_t row0 = first * H + h;
+    const uint32_t span = (live && tn > 0) ? ((uint32_t)(tn - 1) * H + 1) * D : 0u;  // elements
+    const __amdgpu_buffer_rsrc_t krs = read_range(static_cast<const uint16_t*>(A.k) + row0 * D, 2 * span);
+    const __amdgpu_buffer_rsrc_t qrs = read_range(static_cast<const uint16_t*>(A.q) + row0 * D, 2 * span);
+    const __amdgpu_buffer_rsrc_t vrs = read_range(static_cast<const uint16_t*>(A.v) + row0 * D, 2 * span);
+    const __amdgpu_buffer_rsrc_t grs = read_range(A.gk + row0 * D, 4 * span);
+    const __amdgpu_buffer_rsrc_t brs = read_range(A.beta + row0, 4 * (span / D));
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
-      // tokens past the window re-read its last row (an empty window: a row that exists)
-      const size_t tr = first + (size_t)min(ti + 8 * n, max(tn - 1, 0));
-      const size_t r = (RAGGED ? min(tr, (size_t)A.total_tok - 1) : tr) * H + h;
-      pk[n] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.k) + r * D + c4);
-      pq[n] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.q) + r * D + c4);
-      pv[n] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(A.v) + r * D + c4);
-      pg[n] = *reinterpret_cast<const float4*>(A.gk + r * D + c4);
-      pb[n] = A.beta[r];
+      // tokens past the window re-read its last row
+      const int t = min(ti + 8 * n, max(tn - 1, 0));
+      const int e = t * H * D + c4;
+      pk[n] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(krs, 2 * e, 0, 0));
+      pq[n] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(qrs, 2 * e, 0, 0));
+      pv[n] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vrs, 2 * e, 0, 0));
+      pg[n] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(grs, 4 * e, 0, 0));
+      pb[n] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(brs, 4 * t * H, 0, 0));
     }
   };
   if (blockIdx.x < (unsigned)n_units) {
     int b, h;
     size_t unit;
     unit_of(blockIdx.x, b, h, unit);
-    if constexpr (!FOLD) prefetch_state(unit, 0, 16);
-    prefetch_inputs(b, h, unit);
-    if constexpr (FOLD) prefetch_state(unit, 0, 16);
+    if constexpr (!FOLD) prefetch_state(state_range(unit, true), 0, 16);
+    prefetch_inputs(b, h, unit, true);
+    if constexpr (FOLD) prefetch_state(state_range(unit, true), 0, 16);
     // The same stores as the end of an iteration, into empty ranges (dropped): the loop is
     // then entered with the same pattern of outstanding memory operations from both sides,
     // and the compiler's wait for the prefetched registers need not drain the stores.
@@ -269,6 +289,16 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     int b, h;
     size_t unit;
     const bool ok = unit_of(u, b, h, unit);  // wave-uniform
+    {
+      // the two workgroups sharing a CU drift apart (the older one's waves win the issue
+      // arbitration), and the one behind would run its last units alone: a wave's priority is the
+      // number of units its workgroup has left after this one, so the one behind issues first
+      const int left = (n_units - 1 - u) / (int)gridDim.x;
+      if (left >= 3) __builtin_amdgcn_s_setprio(3);
+      else if (left == 2) __builtin_amdgcn_s_setprio(2);
+      else if (left == 1) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     __syncthreads();                         // the previous unit's LDS readers are done
     float S[16][4];                          // fused fold: the state, in the recurrence step's ownership
     int fn = 0;                              // entries to fold
@@ -319,17 +349,17 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pb[n]), rb_rs, c4 == 0 ? 4 * pos : 0x7ffffff0, 0, kStream);
       }
     }
-    // the next unit streams in while this one computes (past the last unit: this one again,
-    // so that every iteration issues the same loads); the fused fold issues its state after the
-    // fold, whose state shares the registers
+    // the next unit streams in while this one computes (past the last unit, the same loads into
+    // empty ranges, so that every iteration issues the same instructions); the fused fold issues
+    // its state after the fold, whose state shares the registers
     int bn, hn;
     size_t unitn;
-    {
-      const int un = u + (int)gridDim.x;
-      unit_of(un < n_units ? un : u, bn, hn, unitn);
-    }
-    prefetch_inputs(bn, hn, unitn);
-    if constexpr (!FOLD) prefetch_state(unitn, 0, kPiece1);
+    const int un = u + (int)gridDim.x;
+    const bool more = un < n_units;  // wave-uniform
+    unit_of(more ? un : u, bn, hn, unitn);
+    prefetch_inputs(bn, hn, unitn, more);
+    const __amdgpu_buffer_rsrc_t srs = state_range(unitn, more);
+    if constexpr (!FOLD) prefetch_state(srs, 0, kPiece1);
     const size_t row0 = first * H + h;  // input row of token t: row0 + t * H
     __syncthreads();
     if constexpr (FOLD) {
@@ -347,7 +377,7 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
         const uint32_t lo = pack2(h16(S[i][0]), h16(S[i][1])), hi = pack2(h16(S[i][2]), h16(S[i][3]));
         *reinterpret_cast<uint2*>(&L.sh[wave][r0 + i][4 * (lane >> 3)]) = make_uint2(lo, hi);
       }
-      prefetch_state(unitn, 0, kPiece1);
+      prefetch_state(srs, 0, kPiece1);
       __syncthreads();
       // the fold's staging shares memory with the operand rows kt, qt, rk and rqh (FoldLds spans
       // 16.4 KB of them): their padding rows NT .. 15, which every MFMA tile reads, must be zero
@@ -390,7 +420,7 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
       }
       if (gs < -kMaxWindowDecay) L.exact = 1;  // e^{-G} would leave the range
     }
-    prefetch_state(unitn, kPiece1, kPiece2);
+    prefetch_state(srs, kPiece1, kPiece2);
     __syncthreads();
 
     // ---- A, P and X = (I + A)^-1
@@ -489,7 +519,7 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
         }
       }
     }
-    prefetch_state(unitn, kPiece2, 16);
+    prefetch_state(srs, kPiece2, 16);
     __syncthreads();  // X and P are complete
 
     // ---- R = diag(beta)(V - Kt S0), W = X R, O^T = scale (QT + W^T P^T)
