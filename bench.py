@@ -52,7 +52,10 @@ METRIC = "KDA prefill tokens*heads/s and verify+fold us/step at 1 GPU; % of roof
 # HBM bytes per prefill launch measured by rocprofv3 PMC (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, the
 # factors that make a plain 1 GiB copy read 1 GiB and write 1 GiB), per workload; None for a workload
 # not measured with the current kernel (set to None whenever the kernel changes until it is measured again)
-PREFILL_TRAFFIC_BYTES = {"long_1m_h96": None, "prefill_4x2048_h64": None}
+PREFILL_TRAFFIC_BYTES = {"long_1m_h96": 219_758_701_056, "prefill_4x2048_h64": 980_407_296}
+# the same for one launch of each kernel of the speculative step (256 x 69 x 8): kda_verify (chunked),
+# kda_replay_fold, kda_fold_verify, kda_verify_ragged
+VERIFY_TRAFFIC_BYTES = {"verify": 183_104_307, "fold": 18_942_231_654, "fused": 323_779_174, "ragged": 162_897_818}
 FLUSH_BYTES = 1 << 30  # scratch written before every timed prefill rep: evicts the 256 MB Infinity Cache and L2s
 
 
@@ -521,7 +524,7 @@ def bench_verify_fold(args, torch, kda, sg, synth):
                verify_gbs=v_bytes / (ver * 1e-3) / 1e9, fold_gbs=f_bytes / (fol * 1e-3) / 1e9,
                verify_bytes=v_bytes, fold_bytes=f_bytes, fused_ms=fus, fused_bytes=fv_bytes,
                fused_gbs=fv_bytes / (fus * 1e-3) / 1e9, ragged_ms=rag, ragged_bytes=r_bytes,
-               ragged_gbs=r_bytes / (rag * 1e-3) / 1e9, ragged_mean_window=float(win.mean()))
+               ragged_gbs=r_bytes / (rag * 1e-3) / 1e9, ragged_mean_window=float(win.mean()), layers=Lyr)
     del pool, pristine, ring, ins_r, o, o_r
     return res
 
@@ -829,6 +832,10 @@ def main():
             "step_hbm_frac": (vf["verify_bytes"] + vf["fold_bytes"]) / ((vf["verify_ms"] + vf["fold_ms"]) * 1e-3)
                              / 1e9 / HBM_PEAK_GBS,
             "verify_gbs": vf["verify_gbs"], "fold_gbs": vf["fold_gbs"], "accept_mean": vf["accept_mean"],
+            "algorithmic_bytes_per_launch": {"verify": vf["verify_bytes"] // vf["layers"], "fold": vf["fold_bytes"],
+                                             "fused": vf["fused_bytes"] // vf["layers"],
+                                             "ragged": vf["ragged_bytes"] // vf["layers"]},
+            "traffic_per_launch": VERIFY_TRAFFIC_BYTES,
             "workload": "256 requests x 69 layers x 8 heads, gamma+1=8 bf16 draft tokens, fp32 committed state, "
                         "ring length 16, accepted lengths geometric mean 2.7 clipped to [1,8]; 69 verify + 1 fold",
             "fused_us_per_step": vf["fused_ms"] * 1e3, "fused_gbs": vf["fused_gbs"],
