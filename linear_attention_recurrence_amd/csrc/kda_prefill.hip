@@ -277,6 +277,26 @@ __device__ __forceinline__ void issue_v(const uint16_t* src, const PrefillArgs& 
   }
 }
 
+// The decay rows of a register set turned, in place, into what stage 1 starts from: gk in log2
+// units (0 for tokens past the chunk end, so that G stops advancing there), summed over the tokens
+// of each 16-token half up to this lane's. Run in the phase 2 before the set's stage 1, where its
+// multiplies and DPP adds fill the time the address unit takes over that phase's loads.
+__device__ __forceinline__ void prescan(Raw& r, int nc, int tl) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  const bool ok0 = tl < nc, ok1 = 16 + tl < nc;
+  float gx[8] = {r.g0a.x, r.g0a.y, r.g0a.z, r.g0a.w, r.g0b.x, r.g0b.y, r.g0b.z, r.g0b.w};
+  float gy[8] = {r.g1a.x, r.g1a.y, r.g1a.z, r.g1a.w, r.g1b.x, r.g1b.y, r.g1b.z, r.g1b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    gx[i] = row_scan_add(ok0 ? gx[i] * kLog2e : 0.f);
+    gy[i] = row_scan_add(ok1 ? gy[i] * kLog2e : 0.f);
+  }
+  r.g0a = make_float4(gx[0], gx[1], gx[2], gx[3]);
+  r.g0b = make_float4(gx[4], gx[5], gx[6], gx[7]);
+  r.g1a = make_float4(gy[0], gy[1], gy[2], gy[3]);
+  r.g1b = make_float4(gy[4], gy[5], gy[6], gy[7]);
+}
+
 // What phase 2 of the producer needs from phase 1 to write the chain's operand rows: the
 // masked raw q and k (bf16) and the decay factors e^{G_t} and e^{G_31 - G_t} of both tokens.
 // eight fp16 products x[i] * y[i], packed
@@ -309,15 +329,9 @@ __device__ __forceinline__ bool stage1(PrefillLds& L, const Raw& cur, int nc, in
   const int tl = lr;          // tokens tl (block 0) and 16+tl (block 1)
   const int c8 = 8 * co;
   const bool ok0 = tl < nc, ok1 = 16 + tl < nc;
-  // gk in log2 units; tokens past the end decay by nothing
-  constexpr float kLog2e = 1.4426950408889634f;
-  float l0[8], l1[8];
-  {
-    const float gx[8] = {cur.g0a.x, cur.g0a.y, cur.g0a.z, cur.g0a.w, cur.g0b.x, cur.g0b.y, cur.g0b.z, cur.g0b.w};
-    const float gy[8] = {cur.g1a.x, cur.g1a.y, cur.g1a.z, cur.g1a.w, cur.g1b.x, cur.g1b.y, cur.g1b.z, cur.g1b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) { l0[i] = ok0 ? gx[i] * kLog2e : 0.f; l1[i] = ok1 ? gy[i] * kLog2e : 0.f; }
-  }
+  // the set's decay rows, already summed within each half by prescan (log2 units)
+  const float ps0[8] = {cur.g0a.x, cur.g0a.y, cur.g0a.z, cur.g0a.w, cur.g0b.x, cur.g0b.y, cur.g0b.z, cur.g0b.w};
+  const float ps1[8] = {cur.g1a.x, cur.g1a.y, cur.g1a.z, cur.g1a.w, cur.g1b.x, cur.g1b.y, cur.g1b.z, cur.g1b.w};
   if (pw == 0 && g == 0) {
     L.beta[b][tl] = ok0 ? cur.b0 : 0.f;
     L.beta[b][16 + tl] = ok1 ? cur.b1 : 0.f;
@@ -336,12 +350,12 @@ __device__ __forceinline__ bool stage1(PrefillLds& L, const Raw& cur, int nc, in
   refill();
   asm volatile("" ::: "memory");
   float e0[8], e1[8], ie0[8], ie1[8], f0[8], f1[8], dl[8];
-  // no branch inside this loop: its 16 prefix-sum chains and 32 exponentials are independent
-  // across channels and interleave only within one basic block
+  // no branch inside this loop: its 32 exponentials are independent across channels and
+  // interleave only within one basic block
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    // prefix sums inside each 16-token half, then the four exponentials
-    const float s0 = row_scan_add(l0[i]), s1 = row_scan_add(l1[i]);  // log2 of e^{G_t}, e^{G_t - G_15}
+    // the four exponentials of the prefix sums inside each 16-token half
+    const float s0 = ps0[i], s1 = ps1[i];  // log2 of e^{G_t}, e^{G_t - G_15}
     const float p0 = __builtin_amdgcn_exp2f(s0), r0 = __builtin_amdgcn_exp2f(-s0);
     const float p1 = __builtin_amdgcn_exp2f(s1), r1 = __builtin_amdgcn_exp2f(-s1);
     const float T0 = KDA_ROW_BCAST15(p0), T1 = KDA_ROW_BCAST15(p1);   // e^{G_15}, e^{G_31 - G_15}
@@ -693,7 +707,9 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
         asm volatile("" ::: "memory");
         issue(rb, 1);
         asm volatile("" ::: "memory");
-        auto period = [&](int p, Raw& use) {
+        auto nc_of = [&](int c) { c = min(c, nch - 1); return min(C, len - C * c); };
+        prescan(ra, nc_of(0), lr);
+        auto period = [&](int p, Raw& use, Raw& other) {
           const int c1 = p + 1, b1 = c1 & 1;
           Keep keep;
           if (c1 < nch) {
@@ -705,6 +721,8 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
           }
           __syncthreads();
           issue_late(use, c1 + 2);
+          asm volatile("" ::: "memory");
+          prescan(other, nc_of(c1 + 1), lr);  // the next period's set, while the loads above go out
           asm volatile("" ::: "memory");
           issue_vc(c1 + 1);  // into the buffer the chain read in this period's phase 1
           if (c1 < nch) stage1b(L, keep, b1, pw, g, lr);
@@ -718,10 +736,10 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
         // around the loop
         int p = -1;
         for (; p + 1 < nch; p += 2) {
-          period(p, ra);
-          period(p + 1, rb);
+          period(p, ra, rb);
+          period(p + 1, rb, ra);
         }
-        if (p < nch) period(p, ra);
+        if (p < nch) period(p, ra, rb);
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no LDS write may outlive the item
       }
     } else {
