@@ -281,6 +281,14 @@ __device__ __forceinline__ void issue_v(const uint16_t* src, const PrefillArgs& 
 // units (0 for tokens past the chunk end, so that G stops advancing there), summed over the tokens
 // of each 16-token half up to this lane's. Run in the phase 2 before the set's stage 1, where its
 // multiplies and DPP adds fill the time the address unit takes over that phase's loads.
+template <int S>
+__device__ __forceinline__ void scan_step(float (&x)[8], float (&y)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[i] = x[i] + KDA_ROW_SHR0(x[i], S);
+    y[i] = y[i] + KDA_ROW_SHR0(y[i], S);
+  }
+}
 __device__ __forceinline__ void prescan(Raw& r, int nc, int tl) {
   constexpr float kLog2e = 1.4426950408889634f;
   const bool ok0 = tl < nc, ok1 = 16 + tl < nc;
@@ -288,9 +296,15 @@ __device__ __forceinline__ void prescan(Raw& r, int nc, int tl) {
   float gy[8] = {r.g1a.x, r.g1a.y, r.g1a.z, r.g1a.w, r.g1b.x, r.g1b.y, r.g1b.z, r.g1b.w};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    gx[i] = row_scan_add(ok0 ? gx[i] * kLog2e : 0.f);
-    gy[i] = row_scan_add(ok1 ? gy[i] * kLog2e : 0.f);
+    gx[i] = ok0 ? gx[i] * kLog2e : 0.f;
+    gy[i] = ok1 ? gy[i] * kLog2e : 0.f;
   }
+  // the sixteen scans step by step, so that each step's adds are independent of one another
+  // (row_scan_add's steps, in its order)
+  scan_step<1>(gx, gy);
+  scan_step<2>(gx, gy);
+  scan_step<4>(gx, gy);
+  scan_step<8>(gx, gy);
   r.g0a = make_float4(gx[0], gx[1], gx[2], gx[3]);
   r.g0b = make_float4(gx[4], gx[5], gx[6], gx[7]);
   r.g1a = make_float4(gy[0], gy[1], gy[2], gy[3]);
@@ -721,9 +735,9 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
           }
           __syncthreads();
           issue_late(use, c1 + 2);
-          asm volatile("" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
           prescan(other, nc_of(c1 + 1), lr);  // the next period's set, while the loads above go out
-          asm volatile("" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
           issue_vc(c1 + 1);  // into the buffer the chain read in this period's phase 1
           if (c1 < nch) stage1b(L, keep, b1, pw, g, lr);
           // everything older than this period's 12 (14) loads has landed: the next chunk's
