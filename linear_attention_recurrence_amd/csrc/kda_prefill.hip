@@ -659,9 +659,16 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
     for (int i = tid; i < D; i += NT) L.nw[i] = A.norm_w[i];
   }
 
-  for (;;) {
+  // A workgroup's first item is fixed: within each 16 workgroups, b and b + 8 (the same XCD under
+  // the dispatcher's round-robin placement) take work-list positions 2j and 2j + 1, which a plan
+  // with two value blocks fills with the two halves of one chain, so that the second half's reads
+  // of q, k, gk and beta find the first half's in that XCD's L2. Later items come from the counter.
+  const int G = (int)gridDim.x, b0 = (int)blockIdx.x;
+  int first = b0;
+  if (b0 < G - G % 16) first = 2 * (8 * (b0 >> 4) + (b0 & 7)) + ((b0 >> 3) & 1);
+  for (int round = 0;; ++round) {
     __syncthreads();
-    if (tid == 0) L.item = atomicAdd(&A.ws->counter, 1);
+    if (tid == 0) L.item = round == 0 ? first : atomicAdd(&A.ws->counter, 1) + G;
     __syncthreads();
     const int it = L.item;
     if (it < 0 || it >= A.n_items) break;  // also ends a launch on a stale counter
