@@ -52,7 +52,7 @@ METRIC = "KDA prefill tokens*heads/s and verify+fold us/step at 1 GPU; % of roof
 # HBM bytes per prefill launch measured by rocprofv3 PMC (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, the
 # factors that make a plain 1 GiB copy read 1 GiB and write 1 GiB), per workload; None for a workload
 # not measured with the current kernel (set to None whenever the kernel changes until it is measured again)
-PREFILL_TRAFFIC_BYTES = {"long_1m_h96": None, "prefill_4x2048_h64": None}
+PREFILL_TRAFFIC_BYTES = {"long_1m_h96": 190_852_481_741, "prefill_4x2048_h64": 992_968_909}
 # the same for one launch of each kernel of the speculative step (256 x 69 x 8): kda_verify (chunked),
 # kda_replay_fold, kda_fold_verify, kda_verify_ragged
 VERIFY_TRAFFIC_BYTES = {"verify": 183_104_307, "fold": 18_942_231_654, "fused": 323_779_174, "ragged": 162_897_818}
