@@ -106,8 +106,10 @@ __device__ __forceinline__ uint2 lds8(const uint16_t* p) { return *reinterpret_c
 // 16 bytes per lane from global memory into LDS at lds_base + 16 * lane
 // (lds_base wave-uniform). Written as inline assembly on purpose: the compiler
 // would otherwise make every later LDS read wait for these asynchronous
-// writes. The kernel orders them itself: the issuing wave waits for vmcnt(0)
-// before the barrier that ends the period. M0 is used by nothing else here.
+// writes. The kernel orders them itself: before the barrier that ends a period
+// the issuing wave waits until only that period's loads are in flight (vmcnt),
+// so rows issued one period earlier have landed before the chain reads them in
+// the next period. M0 is used by nothing else here.
 __device__ __forceinline__ void g2l16(const void* src, void* lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_base);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory");
