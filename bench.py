@@ -34,6 +34,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import statistics
 import os
 import sys
 import time
@@ -529,6 +530,48 @@ def bench_verify_fold(args, torch, kda, sg, synth):
     return res
 
 
+def measure_peaks(torch, kda, reps=5):
+    """The rates this GPU attains on the simplest work, through the library's measurement probes in the
+    same run: a streaming copy of 1 GiB (2 GiB moved), a streaming read of the same 1 GiB, and a loop of
+    independent bf16 16x16x32 MFMAs over two workgroups per CU. Median of `reps` launches after one
+    untimed launch each, timed with HIP events on the launch stream."""
+    dev = "cuda:0"
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4096 * 256, device=dev)
+
+    def med(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        return statistics.median(ts)
+
+    t_copy = med(lambda: kda.kda_probe_copy(dst, src))
+    t_read = med(lambda: kda.kda_probe_read(src, sink))
+    flop = [0]
+    iters = 20000
+
+    def mf():
+        flop[0] = kda.kda_probe_mfma(iters, sink)
+
+    t_mfma = med(mf)
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return {"hbm_copy_gbs": 2 * nbytes / t_copy / 1e9, "hbm_read_gbs": nbytes / t_read / 1e9,
+            "mfma_bf16_tflops": flop[0] / t_mfma / 1e12,
+            "probes": "kda_probe_copy of 1 GiB (2 GiB moved) and kda_probe_read of 1 GiB, non-temporal float4 "
+                      "streams; kda_probe_mfma with "
+                      f"{iters} rounds of 8 independent 16x16x32 bf16 MFMAs per wave; medians of {reps}"}
+
+
 def host_cores():
     """(threads to use, nproc, CPUs this process may run on, CPU model). The oracle runs one unit per task
     on the CPUs this process may use, capped by OMP_NUM_THREADS when the environment sets it (the share of
@@ -757,6 +800,12 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 x 1 GiB device copies (1 GiB read + 1 GiB written each)")
         del src, dst
+    peaks = None
+    if only is None:
+        log("attained peaks: copy, read and MFMA probes")
+        peaks = measure_peaks(torch, kda)
+        log(f"attained peaks: copy {peaks['hbm_copy_gbs']:.0f} GB/s, read {peaks['hbm_read_gbs']:.0f} GB/s, "
+            f"bf16 MFMA {peaks['mfma_bf16_tflops']:.0f} TFLOP/s")
     cpu = None
     if only is None and not args.no_cpu_baseline:
         import oracle
@@ -776,6 +825,9 @@ def main():
                          "algorithmic_bytes_per_launch": head["algorithmic_bytes"], "mfma_frac": head["mfma_frac"],
                          "median_ms": head["median_ms"], "min_ms": head["min_ms"]},
         })
+        if peaks is not None:
+            line["roofline"]["frac_of_attained_copy"] = head["gbs"] / peaks["hbm_copy_gbs"]
+            line["roofline"]["frac_of_attained_read"] = head["gbs"] / peaks["hbm_read_gbs"]
         line["long_context"] = head
     elif dense is not None:
         line.update({
@@ -786,6 +838,7 @@ def main():
                          "frac": dense["hbm_frac"], "traffic": dense["traffic"], "kernel": "kda::prefill_kernel<false>",
                          "algorithmic_bytes_per_launch": dense["algorithmic_bytes"]},
         })
+    line["attained_peaks"] = peaks
     line["cpu_baseline"] = cpu
     if dense is not None:
         dense["workload"] = ("4 sequences x 2048 tokens, H=64, bf16 q/k/v, fp32 gk/beta/state, state_in N(0,0.1^2), "

@@ -629,6 +629,31 @@ kda_status kda_request_donate(kda_slots* slots, kda_request_slots* r, int32_t* s
 kda_status kda_request_close(kda_slots* slots, kda_request_slots* r);
 kda_status kda_slot_release(kda_slots* slots, int32_t slot);
 
+/* -------------------------------------------------------------------------
+ * Measurement probes (diagnostics, not part of the method). The rates the
+ * chip reaches on the simplest work -- a streaming copy, a streaming read and
+ * a loop of independent bf16 matrix-core products -- so that a benchmark can
+ * report its kernels against what this GPU attains in the same run beside the
+ * vendor peaks. Asynchronous on stream; they read or write only the buffers
+ * named. Errors: KDA_ERR_INVALID_ARG, KDA_ERR_DEVICE.
+ * ------------------------------------------------------------------------- */
+
+/* dst = src, bytes each (a positive multiple of 16), both DEVICE, 16-byte
+ * aligned, not overlapping. Moves 2 * bytes through HBM. */
+kda_status kda_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+/* Reads bytes (a positive multiple of 16) of DEVICE src (16-byte aligned)
+ * once and writes one partial sum per thread to DEVICE sink (sink_floats >=
+ * 256; the grid is at most sink_floats / 256 workgroups of 256 threads). */
+kda_status kda_probe_read(const void* src, int64_t bytes, float* sink, int64_t sink_floats, void* stream);
+
+/* Runs iters (1 .. 2^30, rounded up to a multiple of 32) rounds of eight
+ * independent 16x16x32 bf16 MFMAs per wave (operands derived from seed and
+ * the lane) and writes one sum per thread to
+ * DEVICE sink (sink_floats >= 256). *flop (HOST) receives the flops the
+ * launch performs. */
+kda_status kda_probe_mfma(int iters, float seed, float* sink, int64_t sink_floats, int64_t* flop, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

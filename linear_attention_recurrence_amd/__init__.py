@@ -11,4 +11,5 @@ from .kda import (  # noqa: F401
     Plan, Ring, kda_abi_version, kda_chunk_prefill, kda_chunk_prefill_gated, kda_gated_rmsnorm, kda_last_error, kda_prologue, kda_plan_create, kda_plan_items,
     kda_fold_verify, kda_plan_num_items, kda_plan_upload, kda_plan_v_blocks, kda_plan_workspace_bytes,
     KDA_NOALLOC_SCRATCH_BYTES, kda_chunk_prefill_noalloc, kda_host_release, kda_replay_fold, kda_verify, kda_verify_ragged, lib,
+    kda_probe_copy, kda_probe_mfma, kda_probe_read,
 )

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_prefill.hip", "kda_verify_chunk.hip", "kda_norm.hip", "kda_prologue.hip", "kda_move.hip", "kda_decode.hip",
-           "kda_slots.cpp"]
+           "kda_probe.hip", "kda_slots.cpp"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
 

@@ -669,6 +669,56 @@ kda_status kda_prologue(int n_seq, int64_t total_tokens, int n_heads, int conv_w
   return ok();
 }
 
+// ---------------------------------------------------------------------------------------------
+// Measurement probes: the rates the chip reaches on the simplest work, for comparison with the
+// kernels above in the same run. Grids of 256-thread workgroups: 32 per CU for the copy, 16 per CU
+// for the read (or as many as its sink holds), two per CU for the MFMA loop (two waves per SIMD).
+
+static int probe_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = 256;
+  }
+  return n;
+}
+
+kda_status kda_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (!src || !dst) return fail(KDA_ERR_INVALID_ARG, "kda_probe_copy: src and dst are required");
+  if (bytes <= 0 || bytes % 16 != 0) return fail(KDA_ERR_INVALID_ARG, "kda_probe_copy: bytes must be a positive multiple of 16");
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0)
+    return fail(KDA_ERR_INVALID_ARG, "kda_probe_copy: src and dst must be 16-byte aligned");
+  if (overlap(src, (size_t)bytes, dst, (size_t)bytes)) return fail(KDA_ERR_INVALID_ARG, "kda_probe_copy: src and dst overlap");
+  const hipError_t e = kda::launch_probe_copy(src, dst, bytes / 16, 32 * probe_cus(), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail("kda_probe_copy: launch", e);
+  return ok();
+}
+
+kda_status kda_probe_read(const void* src, int64_t bytes, float* sink, int64_t sink_floats, void* stream) {
+  if (!src || !sink) return fail(KDA_ERR_INVALID_ARG, "kda_probe_read: src and sink are required");
+  if (bytes <= 0 || bytes % 16 != 0) return fail(KDA_ERR_INVALID_ARG, "kda_probe_read: bytes must be a positive multiple of 16");
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0) return fail(KDA_ERR_INVALID_ARG, "kda_probe_read: src must be 16-byte aligned");
+  const int64_t grid = std::min<int64_t>(16LL * probe_cus(), sink_floats / 256);
+  if (grid < 1) return fail(KDA_ERR_INVALID_ARG, "kda_probe_read: the sink must hold at least 256 floats");
+  const hipError_t e = kda::launch_probe_read(src, bytes / 16, sink, (int)grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail("kda_probe_read: launch", e);
+  return ok();
+}
+
+kda_status kda_probe_mfma(int iters, float seed, float* sink, int64_t sink_floats, int64_t* flop, void* stream) {
+  if (iters < 1 || !sink || !flop) return fail(KDA_ERR_INVALID_ARG, "kda_probe_mfma: iters >= 1, sink and flop are required");
+  const int64_t grid = std::min<int64_t>(2LL * probe_cus(), sink_floats / 256);
+  if (grid < 1) return fail(KDA_ERR_INVALID_ARG, "kda_probe_mfma: the sink must hold at least 256 floats");
+  // per workgroup: 4 waves x 8 accumulators x iters MFMAs of 2 x 16 x 16 x 32 flop (rounds run in
+  // blocks of 32)
+  if (iters > (1 << 30)) return fail(KDA_ERR_INVALID_ARG, "kda_probe_mfma: iters too large");
+  iters = (iters + 31) / 32 * 32;
+  *flop = grid * 4 * 8 * (int64_t)iters * (2 * 16 * 16 * 32);
+  const hipError_t e = kda::launch_probe_mfma(iters, (int)grid, seed, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail("kda_probe_mfma: launch", e);
+  return ok();
+}
+
 kda_status kda_state_move(int n_moves, const kda_move* moves, int n_slots, int64_t slot_floats, float* pool,
                           void* stream) {
   if (n_moves < 0 || n_slots < 1 || slot_floats < 4 || slot_floats % 4 != 0)

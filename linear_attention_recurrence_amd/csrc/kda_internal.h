@@ -144,5 +144,9 @@ hipError_t launch_fold_verify(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_fold(const FoldArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int grid, hipStream_t stream);
 int prefill_max_grid(int device);
+// measurement probes (kda_probe.hip): streaming copy and read of n_f4 float4s, a loop of bf16 MFMAs
+hipError_t launch_probe_copy(const void* src, void* dst, int64_t n_f4, int grid, hipStream_t stream);
+hipError_t launch_probe_read(const void* src, int64_t n_f4, float* sink, int grid, hipStream_t stream);
+hipError_t launch_probe_mfma(int iters, int grid, float seed, float* sink, hipStream_t stream);
 
 }  // namespace kda

@@ -36,7 +36,8 @@ EXPORTS = ("kda_abi_version", "kda_last_error", "kda_plan_create", "kda_plan_cre
            "kda_chunk_prefill", "kda_chunk_prefill_gated", "kda_gated_rmsnorm", "kda_prologue", "kda_verify",
            "kda_replay_fold", "kda_fold_verify", "kda_verify_ragged", "kda_state_move", "kda_chunk_split",
            "kda_slots_create", "kda_slots_destroy", "kda_slots_free_count", "kda_slots_owner", "kda_request_open",
-           "kda_request_snapshot", "kda_request_donate", "kda_request_close", "kda_slot_release", "kda_decode")
+           "kda_request_snapshot", "kda_request_donate", "kda_request_close", "kda_slot_release", "kda_decode",
+           "kda_probe_copy", "kda_probe_read", "kda_probe_mfma")
 
 
 class KdaError(RuntimeError):
@@ -121,7 +122,10 @@ def lib():
         L.kda_request_close.argtypes = [vp, ctypes.POINTER(RequestSlots)]
         L.kda_slot_release.argtypes = [vp, i32]
         L.kda_decode.argtypes = [i32] * 6 + [vp] * 11 + [f32] * 3 + [vp] * 3
-        for f in ("kda_decode", "kda_state_move", "kda_chunk_split", "kda_slots_create", "kda_request_open", "kda_request_snapshot",
+        L.kda_probe_copy.argtypes = [vp, vp, i64, vp]
+        L.kda_probe_read.argtypes = [vp, i64, vp, i64, vp]
+        L.kda_probe_mfma.argtypes = [i32, f32, vp, i64, ctypes.POINTER(i64), vp]
+        for f in ("kda_probe_copy", "kda_probe_read", "kda_probe_mfma", "kda_decode", "kda_state_move", "kda_chunk_split", "kda_slots_create", "kda_request_open", "kda_request_snapshot",
                   "kda_request_donate", "kda_request_close", "kda_slot_release"):
             getattr(L, f).restype = i32
         for f in ("kda_plan_create", "kda_plan_create_ex", "kda_plan_items", "kda_plan_upload", "kda_chunk_prefill",
@@ -498,6 +502,34 @@ def kda_state_move(pool, moves, stream=None):
     _need(pool, "pool", tuple(pool.shape), _F32)
     _check(lib().kda_state_move(moves.shape[0], _ptr(moves), pool.shape[0], pool[0].numel(), _ptr(pool),
                                 _stream(stream)))
+
+
+# ---------------------------------------------------------------- measurement probes
+def kda_probe_copy(dst, src, stream=None):
+    """dst = src through the library's streaming copy probe (see include/kda.h). Both contiguous device
+    tensors of the same number of bytes (a multiple of 16)."""
+    nb = src.numel() * src.element_size()
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()) or dst.numel() * dst.element_size() != nb:
+        raise ValueError("src and dst must be contiguous device tensors of the same size in bytes")
+    _check(lib().kda_probe_copy(_ptr(src), _ptr(dst), nb, _stream(stream)))
+
+
+def kda_probe_read(src, sink, stream=None):
+    """Reads src once through the streaming read probe; sink: fp32 device tensor of >= 256 elements
+    receiving one partial sum per thread (their total is the sum of src's fp32 values)."""
+    if not (src.is_cuda and src.is_contiguous()):
+        raise ValueError("src must be a contiguous device tensor")
+    _need(sink, "sink", tuple(sink.shape), _F32)
+    _check(lib().kda_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), sink.numel(), _stream(stream)))
+
+
+def kda_probe_mfma(iters, sink, seed=1e-3, stream=None):
+    """Runs the bf16 MFMA loop probe; sink: fp32 device tensor of >= 256 elements. Returns the flops of
+    the launch."""
+    _need(sink, "sink", tuple(sink.shape), _F32)
+    flop = ctypes.c_int64(0)
+    _check(lib().kda_probe_mfma(int(iters), float(seed), _ptr(sink), sink.numel(), ctypes.byref(flop), _stream(stream)))
+    return int(flop.value)
 
 
 def kda_chunk_split(pos0, length, budget, align=256):

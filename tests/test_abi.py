@@ -350,3 +350,22 @@ def test_binding_checks_shapes_without_device():
     with pytest.raises(ValueError):
         kda.kda_chunk_prefill(p, x, x, x, x.float(), torch.zeros((64, 1)), torch.zeros((1, 1, 128, 128)),
                               torch.zeros((64, 1, 128)), torch.zeros(kda.kda_plan_workspace_bytes(p), dtype=torch.uint8))
+
+
+def test_probes_reject_bad_arguments():
+    """The measurement probes refuse bad sizes, alignment and overlap before any device call."""
+    L = kda.lib()
+    p16, p32 = ctypes.c_void_p(16), ctypes.c_void_p(32)
+    flop = ctypes.c_int64(0)
+    cases = [
+        L.kda_probe_copy(None, p32, 16, None),
+        L.kda_probe_copy(p16, p32, 15, None),     # not a multiple of 16
+        L.kda_probe_copy(ctypes.c_void_p(17), p32, 16, None),  # misaligned
+        L.kda_probe_copy(p16, p32, 32, None),     # overlapping
+        L.kda_probe_read(p16, 0, p32, 256, None),
+        L.kda_probe_read(p16, 16, p32, 255, None),  # sink too small for one workgroup
+        L.kda_probe_mfma(0, 1.0, p32, 256, ctypes.byref(flop), None),
+        L.kda_probe_mfma(1, 1.0, p32, 100, ctypes.byref(flop), None),
+        L.kda_probe_mfma(1, 1.0, p32, 256, None, None),
+    ]
+    assert all(rc == K.KDA_ERR_INVALID_ARG for rc in cases), cases

@@ -1087,3 +1087,42 @@ def test_decode_fused(gpu, W):
             worst_y = max(worst_y, float(np.max(np.abs(yv - y_ref[0])) / np.max(np.abs(y_ref[0]))))
     log(f"decode fused W={W}: worst state {worst_s:.2e}, y {worst_y:.2e}")
     assert worst_s <= TOL and worst_y <= 8e-3
+
+
+def test_probes(gpu):
+    """The measurement probes do the work they report: the copy reproduces its source bit for bit, the
+    read's per-thread sums add up to the source's sum, and every thread of the MFMA loop ends with
+    iters x 8 accumulators x the sum of its four entries of A B, where lane l holds A[l % 16][8 (l / 16) + i]
+    = bf16(seed (l + i)) and B[8 (l / 16) + i][l % 16] = bf16(seed (l - i)) and gets D[4 (l / 16) + r][l % 16]."""
+    n = 1 << 22
+    src = torch.randn(n, device=DEV)
+    dst = torch.empty_like(src)
+    kda.kda_probe_copy(dst, src)
+    sink = torch.zeros(2048 * 256, device=DEV)
+    kda.kda_probe_read(src, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    total, mag = float(src.double().sum()), float(src.abs().double().sum())
+    assert abs(float(sink.double().sum()) - total) <= 1e-5 * mag
+    # MFMA loop
+    iters, seed = 64, 1e-3  # a multiple of the probe's 32-round blocks (other counts round up)
+    assert kda.kda_probe_mfma(33, sink, seed=seed) == kda.kda_probe_mfma(64, sink, seed=seed)
+    sink.zero_()
+    flop = kda.kda_probe_mfma(iters, sink, seed=seed)
+    torch.cuda.synchronize()
+    grid = flop // (4 * 8 * iters * 2 * 16 * 16 * 32)
+    assert grid >= 1 and flop == grid * 4 * 8 * iters * 2 * 16 * 16 * 32
+    A = np.zeros((16, 32))
+    B = np.zeros((32, 16))
+    bf = lambda x: float(torch.tensor(np.float32(x)).to(torch.bfloat16).double())
+    for l in range(64):
+        g, lr = divmod(l, 16)
+        for i in range(8):
+            A[lr, 8 * g + i] = bf(np.float32(seed) * np.float32(l + i))
+            B[8 * g + i, lr] = bf(np.float32(seed) * np.float32(l - i))
+    Dm = A @ B
+    per_lane = np.array([iters * 8 * sum(Dm[4 * (l // 16) + r, l % 16] for r in range(4)) for l in range(64)])
+    got = np_(sink[: grid * 256]).reshape(grid * 4, 64).astype(np.float64)
+    err = np.abs(got - per_lane[None, :]).max() / np.abs(per_lane).max()
+    log(f"probes: mfma grid {grid}, worst relative error {err:.2e}")
+    assert err <= 1e-5
