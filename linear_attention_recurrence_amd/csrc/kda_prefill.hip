@@ -697,7 +697,8 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
       // Raw inputs are prefetched two periods ahead: q, k, gk, beta into registers, alternating
       // between two sets (chunk c lives in set c & 1 from the period that issues it, c - 3,
       // until its stage 1 in period c - 1: its q and k in that period's phase 1, as soon as stage 1
-      // has unpacked the set's previous q and k, its gk and beta in phase 2), and v straight into
+      // has unpacked the set's previous q and k, its gk and beta in phase 2; in phase 2 of period
+      // c - 2 prescan turns its gk into the prefix sums stage 1 starts from), and v straight into
       // vr[c & 1] (issued in period c - 2, read by the chain in period c; with GATED the gate rows
       // go into gr[c & 1] the same way). Every period issues the same 12 loads (14 with GATED; past
       // the last chunk they re-read it), so the compiler's waits before each register use count
