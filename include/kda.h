@@ -212,8 +212,10 @@ typedef struct {
  *              Any gk <= 0 is exact, -inf (a full reset) included: a 32-token
  *              chunk whose decay summed over it exceeds 60 in some key
  *              channel (where the fast factor form would leave fp32/bf16
- *              range) is prepared on an exact path, about three chunk
- *              periods slower. Range of the state products: the state, and
+ *              range) makes the kernel compute its work item (a sequence's
+ *              head, or one value block of it) a second time, in a form with
+ *              an exact path for such chunks: that item takes about twice as
+ *              long. Range of the state products: the state, and
  *              beta (v - k^T S) of every token, enter fp16 matrix products,
  *              so their entries must stay below 2^15 in magnitude (fp16
  *              overflows at 65504); beyond it o and the states become

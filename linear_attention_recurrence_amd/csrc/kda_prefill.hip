@@ -20,7 +20,8 @@
 // the row factors of A and P. The column factor e^{-G} grows with the decay
 // summed over the chunk; every factor stays in fp32/bf16 range, with its bf16
 // low part normal, while that sum is at most 60 per key channel. Beyond it
-// (or for gk = -inf) a wave takes the exact path below.
+// (or for gk = -inf) the item is computed again in a form with the exact path
+// below (see kMinChunkDecay).
 //
 // Precision (chosen by measuring each operand's rounding against the fp64
 // oracle): the intra-chunk factors Rq and Ck enter their MFMAs as bf16 hi + lo
@@ -93,6 +94,7 @@ struct alignas(16) PrefillLds {
   float part[4][6][16][20];            // per-wave partial A and P tiles over 32 channels, [col][row] (padded)
   float ar[C][ATS];                    // diagonal blocks of A, fp32, rows i
   int item;
+  int redo;                            // set when a chunk of the item is beyond the factor form's range
   // the fused output norm (kda_chunk_prefill_gated): raw gate rows (stored like vr), per-token slice
   // sums of squares of o, and the norm weights
   uint16_t gr[2][C][D];
@@ -330,9 +332,13 @@ struct Keep {
 // ---------------------------------------------------------------------------
 // The factor form below needs every factor in fp32/bf16 range: per key channel, the decay summed
 // over the chunk must be at most 60 (log2: 86), so that e^{-G} <= 2^86 and the bf16 low parts of
-// q e^G stay normal. It is checked on the chunk's factor e^{G_31} (8 values per lane): a wave with a
-// channel where e^{G_31} < 2^-86, or a decay of -inf, runs stage1_exact after stage1, which rewrites
-// everything stage1 wrote. The check costs the fast path a minimum of 8 values and one branch.
+// q e^G stay normal. It is checked on the chunk's factor e^{G_31} (8 values per lane). Each item
+// runs first in the fast form, where a wave with a channel where e^{G_31} < 2^-86, or a decay of
+// -inf, only flags the item (its outputs are then overwritten, and its final state is not written);
+// a flagged item then runs again in the exact form, where such a wave runs stage1_exact after stage1,
+// which rewrites everything stage1 wrote. With the exact path kept out of the fast form's loop, the
+// fast form keeps its register allocation and schedule; with it inlined there, a prefill of 1M tokens
+// x 96 heads ran 4 % slower although the path was never taken.
 constexpr float kMinChunkDecay = 0x1p-86f;  // e^{G_31} below this takes the exact path (e^-59.6)
 
 // producer, phase 1 of the period before chunk c: decay factors and partial A
@@ -670,7 +676,10 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
   if (b0 < G - G % 16) first = 2 * (8 * (b0 >> 4) + (b0 & 7)) + ((b0 >> 3) & 1);
   for (int round = 0;; ++round) {
     __syncthreads();
-    if (tid == 0) L.item = round == 0 ? first : atomicAdd(&A.ws->counter, 1) + G;
+    if (tid == 0) {
+      L.item = round == 0 ? first : atomicAdd(&A.ws->counter, 1) + G;
+      L.redo = 0;
+    }
     __syncthreads();
     const int it = L.item;
     if (it < 0 || it >= A.n_items) break;  // also ends a launch on a stale counter
@@ -683,6 +692,12 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
     const size_t unit = (size_t)n * H + h;
     const int nch = (len + C - 1) / C;
 
+    // pass 0 runs the item in the fast form; pass 1, only for an item that pass 0 flagged, runs it
+    // again in the exact form. The flag is set before some barrier of pass 0 and read by every wave
+    // after its last one, so all waves take the same decision.
+    for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1 && !L.redo) break;
+
     // Both roles run nch + 1 periods of two barriers each. Period p runs the
     // chain of chunk p (p >= 0) beside the preparation of chunk p + 1.
     // Inside each role the lane index is made opaque once per item, so that the compiler
@@ -694,6 +709,8 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
     if (producer) {
       const int pw = rw;
       const int lane = lane_o, g = g_o, lr = lr_o;
+      auto produce = [&](auto exact_form) {
+      constexpr bool EXACT = decltype(exact_form)::value;
       // Raw inputs are prefetched two periods ahead: q, k, gk, beta into registers, alternating
       // between two sets (chunk c lives in set c & 1 from the period that issues it, c - 3,
       // until its stage 1 in period c - 1: its q and k in that period's phase 1, as soon as stage 1
@@ -738,8 +755,10 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
           Keep keep;
           if (c1 < nch) {
             const int ncc = min(C, len - C * c1);
-            if (stage1(L, use, ncc, b1, pw, g, lr, keep, [&] { issue_early(use, c1 + 2); }))
-              stage1_exact(L, A, (size_t)(tok0 + C * c1) * H + h, ncc, b1, pw, g, lr, keep);
+            if (stage1(L, use, ncc, b1, pw, g, lr, keep, [&] { issue_early(use, c1 + 2); })) {
+              if constexpr (EXACT) stage1_exact(L, A, (size_t)(tok0 + C * c1) * H + h, ncc, b1, pw, g, lr, keep);
+              else L.redo = 1;
+            }
           } else {
             issue_early(use, c1 + 2);
           }
@@ -766,6 +785,9 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
         if (p < nch) period(p, ra, rb);
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no LDS write may outlive the item
       }
+      };
+      if (pass == 0) produce(std::false_type{});
+      else produce(std::true_type{});
     } else {
       const int lane = lane_o, g = g_o, lr = lr_o;
       // The chain on the item's value columns: all 128 (four waves of 32, NV = 2 tiles of 16), or
@@ -982,18 +1004,23 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
 
         if (nch >= 1) norm_epilogue(nch - 1);  // (GATED only) the last chunk's output
 
-        float* dst = A.state_out + unit * D * D + soff;
+        // a flagged fast pass leaves the final state unwritten, so that pass 1 still finds the
+        // initial state where the caller passed the same buffer for both
+        if (pass == 1 || !L.redo) {
+          float* dst = A.state_out + unit * D * D + soff;
   #pragma unroll
-        for (int mc = 0; mc < 8; ++mc)
+          for (int mc = 0; mc < 8; ++mc)
   #pragma unroll
-          for (int nv = 0; nv < NV; ++nv)
+            for (int nv = 0; nv < NV; ++nv)
   #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(16 * mc + r) * D + 16 * nv] = S[mc][nv][r];
+              for (int r = 0; r < 4; ++r) dst[(16 * mc + r) * D + 16 * nv] = S[mc][nv][r];
+        }
 
       };
       if (GATED || A.n_vblk == 1) chain(std::integral_constant<int, 2>{});
       else chain(std::integral_constant<int, 1>{});
       if (A.snap_count && h == 0 && vb == 0 && tid == 0) A.snap_count[n] = A.snap_interval > 0 ? len / A.snap_interval : 0;
+    }
     }
   }
 

@@ -18,6 +18,7 @@ import torch
 
 import oracle
 import synth
+import synth.gpu as sg
 import linear_attention_recurrence_amd as kda
 from kda_ref import TOL, block_err, log
 
@@ -122,6 +123,77 @@ def test_prefill_edge(gpu, case, v_blocks):
                 assert block_err(st_np[n, h].T.astype(np.float64) @ kl, vl) <= TOL
     log(f"prefill edge case {case}, value blocks {v_blocks}: worst {worst}")
     assert max(worst.values()) <= TOL, worst
+    plan.close()
+
+
+@pytest.mark.parametrize("v_blocks", [1, 2])
+def test_prefill_rerun(gpu, v_blocks):
+    """A batch where one sequence's chunks leave the factor form's range (the mixed case's gk) and the
+    others' do not: the kernel computes the flagged items a second time, in the form with the exact
+    path. With state_out == state_in (in place) that second pass must still read the initial state: o,
+    the final states and the snapshots equal the out-of-place call's bit for bit, and every (sequence,
+    head) agrees with the oracle. With one value block the fused gated call, which takes the same
+    second pass, gives y equal to kda_gated_rmsnorm of the plain call's o and the same states."""
+    rng = np.random.default_rng(4000 + v_blocks)
+    lens, H, flagged = [70, 97, 33], 2, 1
+    cu = synth.cu_seqlens(lens)
+    T, N = int(cu[-1]), len(lens)
+    q, k, v, gk, beta, _ = make_inputs("mixed", rng, T * H)
+    shp = (T, H, 128)
+    gk = gk.reshape(shp)
+    plain = (-np.logaddexp(0.0, rng.standard_normal(shp))).astype(np.float32)
+    for n in range(N):
+        if n != flagged:
+            gk[cu[n]:cu[n + 1]] = plain[cu[n]:cu[n + 1]]
+    S0 = (rng.standard_normal((N, H, 128, 128)) * 0.1).astype(np.float32)
+    ins = (bf16_dev(q.reshape(shp)), bf16_dev(k.reshape(shp)), bf16_dev(v.reshape(shp)), f32_dev(gk),
+           f32_dev(beta.reshape(T, H)))
+    plan = kda.kda_plan_create(cu, n_heads=H, snap_interval=32, v_blocks=v_blocks)
+    ws = torch.empty(kda.kda_plan_workspace_bytes(plan), dtype=torch.uint8, device=DEV)
+
+    def call(state_in, state_out):
+        o = torch.full(shp, float("nan"), device=DEV)
+        snap = torch.full((N, 2, H, 128, 128), float("nan"), device=DEV)
+        kda.kda_chunk_prefill(plan, *ins, state_out, o, ws, state_in=state_in, snap=snap, snap_slots=2)
+        return o, snap
+
+    log(f"prefill second pass, value blocks {v_blocks}: out of place, then in place")
+    st_a = torch.full((N, H, 128, 128), float("nan"), device=DEV)
+    o_a, sn_a = call(f32_dev(S0), st_a)
+    inplace = f32_dev(S0)
+    o_b, sn_b = call(inplace, inplace)
+    torch.cuda.synchronize()
+    o_np, st_np, sn_np = o_a.cpu().numpy(), st_a.cpu().numpy(), sn_a.cpu().numpy()
+    assert np.all(np.isfinite(o_np)) and np.all(np.isfinite(st_np))
+    bits = lambda t: t.view(torch.int32)  # noqa: E731 (unused snapshot slots stay NaN: compare bits)
+    assert torch.equal(bits(o_a), bits(o_b)) and torch.equal(bits(st_a), bits(inplace)) \
+        and torch.equal(bits(sn_a), bits(sn_b)), "the in-place call differs from the out-of-place one"
+    worst = {"o": 0.0, "state": 0.0, "snap": 0.0}
+    q3, k3, v3, b2 = q.reshape(shp), k.reshape(shp), v.reshape(shp), beta.reshape(T, H)
+    for n in range(N):
+        a, e = int(cu[n]), int(cu[n + 1])
+        for h in range(H):
+            o_ref, S_ref, snaps, cnt = oracle.recurrent(q3[a:e, h], k3[a:e, h], v3[a:e, h], gk[a:e, h], b2[a:e, h],
+                                                        S0[n, h], snap_interval=32, snap_slots=2)
+            worst["o"] = max(worst["o"], block_err(o_np[a:e, h], o_ref))
+            worst["state"] = max(worst["state"], block_err(st_np[n, h], S_ref))
+            sl = (cnt - 1) % 2
+            worst["snap"] = max(worst["snap"], block_err(sn_np[n, sl, h], snaps[sl]))
+    log(f"prefill second pass, value blocks {v_blocks}: worst {worst}")
+    assert max(worst.values()) <= TOL, worst
+    if v_blocks == 1:
+        gate = sg.gate(4000, T, H, DEV)
+        wd = torch.from_numpy(synth.norm_weight(4000)).to(DEV)
+        y_ref = torch.empty(shp, dtype=torch.bfloat16, device=DEV)
+        kda.kda_gated_rmsnorm(o_a, gate, wd, 1e-6, y_ref)
+        y = torch.full(shp, 7.0, dtype=torch.bfloat16, device=DEV)
+        st_g = f32_dev(S0)
+        sn_g = torch.full((N, 2, H, 128, 128), float("nan"), device=DEV)
+        log("prefill second pass, gated, in place")
+        kda.kda_chunk_prefill_gated(plan, *ins, gate, wd, 1e-6, st_g, y, ws, state_in=st_g, snap=sn_g, snap_slots=2)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), "fused norm differs from prefill + norm"
+        assert torch.equal(bits(st_g), bits(st_a)) and torch.equal(bits(sn_g), bits(sn_a))
     plan.close()
 
 
