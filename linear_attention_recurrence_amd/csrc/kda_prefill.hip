@@ -42,16 +42,19 @@
 //     in MFMA accumulator registers for the whole sequence and is fed back as
 //     the B operand of the next products by permuting the reduction index
 //     identically in both operands. Phase 1: Kt S0, Qt S0, R, W = X R and
-//     O = Qt S0 + P W (stored straight from the accumulators); phase 2: the
-//     state update, the snapshot, and the sums below.
+//     O = Qt S0 + P W (stored straight from the accumulators), then the
+//     state update and the snapshot (they read only this chunk's rows,
+//     written one period earlier); phase 2: the sums below.
 //   producer waves 4-7 prepare chunk c+1. Phase 1: raw q, k, gk, beta
-//     (prefetched into registers two periods ahead) become decay factors,
-//     per-wave partial A and P tiles and the fp16 operand rows of the chain;
-//     raw v goes from global memory straight into LDS (global_load_lds) for
-//     the chain. Phase 2: the operand rows go to LDS and the loads of the
-//     chunk after next are issued; meanwhile, after their state update, the
-//     consumer waves turn the partials into the next chunk's X (waves 0 and 3
-//     invert one diagonal block of I + A each), P (wave 1) and -A10 (wave 2).
+//     (prefetched into registers two periods ahead, the set's gk already
+//     turned into prefix sums) become decay factors, per-wave partial A and
+//     P tiles and the fp16 operand rows of the chain, and the q and k loads
+//     of chunk c+3 go out. Phase 2: the gk and beta loads of chunk c+3, the
+//     next set's prefix sums, raw v of chunk c+2 from global memory straight
+//     into LDS (global_load_lds) for the chain, and the operand rows to LDS;
+//     meanwhile the consumer waves turn the partials into the next chunk's X
+//     (waves 0 and 3 invert one diagonal block of I + A each), P (wave 1) and
+//     -A10 (wave 2).
 // Everything the two stages exchange is double-buffered by chunk parity, so
 // a period needs just its two barriers. Operands that a product needs
 // transposed are read with the transposing LDS load (ds_read_b64_tr_b16)
