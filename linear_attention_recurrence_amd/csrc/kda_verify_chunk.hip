@@ -186,9 +186,12 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     return n < 0 ? 0 : (n > nmax ? nmax : n);
   };
   // loads i0 .. i1 - 1 of the 16 that bring in the state slice of a unit (in the fold's ownership
-  // on the fused path). The next unit's slice is issued in three pieces, between the compute
-  // phases: all 16 at once fill the memory queue and stall the issuing wave until most of them
-  // have returned, with this unit's compute still to do.
+  // on the fused path). The plain path stages a unit's slice into LDS only when its state
+  // products need it, after the key side (decay factors, A, P, X), which does not: the first
+  // unit's slice arrives while that work runs, and the next unit's slice is issued at once into
+  // the registers the staging frees. The fused path folds the state first, so it stages early and
+  // issues the next slice in three pieces between its compute phases (all 16 at once there fill
+  // the memory queue and stall the issuing wave with this unit's compute still to do).
   // The loads go through a buffer range over the unit's state, empty when there is no next unit:
   // the same instructions are issued and return zeros without touching memory.
   auto state_range = [&](size_t unit, bool live) {
@@ -202,7 +205,7 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
         sv[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(srs, off, 0, 0));
       }
   };
-  constexpr int kPiece1 = 4, kPiece2 = 10;  // loads issued after staging, after the decay factors, after A and P
+  constexpr int kPiece1 = 4, kPiece2 = 10;  // fused path: loads issued after staging, after the decay factors, after A and P
   // the window of request b: its first input row and its length tn <= T. Ragged bounds are
   // clamped into [0, total_tok] (the host passes total_tok >= 1), so a row index never leaves
   // the tensors whatever cu_tok holds
@@ -264,9 +267,8 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     int b, h;
     size_t unit;
     unit_of(blockIdx.x, b, h, unit);
-    if constexpr (!FOLD) prefetch_state(state_range(unit, true), 0, 16);
     prefetch_inputs(b, h, unit, true);
-    if constexpr (FOLD) prefetch_state(state_range(unit, true), 0, 16);
+    prefetch_state(state_range(unit, true), 0, 16);
     // The same stores as the end of an iteration, into empty ranges (dropped): the loop is
     // then entered with the same pattern of outstanding memory operations from both sides,
     // and the compiler's wait for the prefetched registers need not drain the stores.
@@ -308,13 +310,6 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
       for (int i = 0; i < 16; ++i) { S[i][0] = sv[i].x; S[i][1] = sv[i].y; S[i][2] = sv[i].z; S[i][3] = sv[i].w; }
       fn = fold_n(b);
       if (ti < fn) stage_entry(L.fold, ti, c4, fk, fv, fg, fb);
-    } else {
-      // state slice to fp16 in LDS
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t lo = pack2(h16(sv[i].x), h16(sv[i].y)), hi = pack2(h16(sv[i].z), h16(sv[i].w));
-        *reinterpret_cast<uint2*>(&L.sh[wave][8 * i + (lane >> 3)][4 * (lane & 7)]) = make_uint2(lo, hi);
-      }
     }
     // raw inputs: staging rows, v and beta for the chain, and the ring (bit copies; tokens past
     // the window rewrite the last entry with the same bits)
@@ -359,7 +354,6 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     unit_of(more ? un : u, bn, hn, unitn);
     prefetch_inputs(bn, hn, unitn, more);
     const __amdgpu_buffer_rsrc_t srs = state_range(unitn, more);
-    if constexpr (!FOLD) prefetch_state(srs, 0, kPiece1);
     const size_t row0 = first * H + h;  // input row of token t: row0 + t * H
     __syncthreads();
     if constexpr (FOLD) {
@@ -420,7 +414,7 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
       }
       if (gs < -kMaxWindowDecay) L.exact = 1;  // e^{-G} would leave the range
     }
-    prefetch_state(srs, kPiece1, kPiece2);
+    if constexpr (FOLD) prefetch_state(srs, kPiece1, kPiece2);
     __syncthreads();
 
     // ---- A, P and X = (I + A)^-1
@@ -500,6 +494,16 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
       *reinterpret_cast<uint2*>(&L.xh[lr][4 * g]) = make_uint2(pack2(h16(x[0]), h16(x[1])), pack2(h16(x[2]), h16(x[3])));
     }
 
+    if constexpr (!FOLD) {
+      // state slice to fp16 in LDS (this wave's own slice of sh, which only this wave reads), then
+      // the whole next unit's slice into the registers it leaves
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t lo = pack2(h16(sv[i].x), h16(sv[i].y)), hi = pack2(h16(sv[i].z), h16(sv[i].w));
+        *reinterpret_cast<uint2*>(&L.sh[wave][8 * i + (lane >> 3)][4 * (lane & 7)]) = make_uint2(lo, hi);
+      }
+      prefetch_state(srs, 0, 16);
+    }
     // ---- Kt S0 (tokens x values) and (Qt S0)^T (values x tokens) on this wave's 32 columns
     f32x4 KS[2], QT[2];
     {
@@ -519,7 +523,7 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
         }
       }
     }
-    prefetch_state(srs, kPiece2, 16);
+    if constexpr (FOLD) prefetch_state(srs, kPiece2, 16);
     __syncthreads();  // X and P are complete
 
     // ---- R = diag(beta)(V - Kt S0), W = X R, O^T = scale (QT + W^T P^T)
