@@ -291,10 +291,12 @@ __global__ void __launch_bounds__(256, 2) verify_chunk_kernel(VerifyArgs A) {
     int b, h;
     size_t unit;
     const bool ok = unit_of(u, b, h, unit);  // wave-uniform
-    {
+    if constexpr (FOLD) {
       // the two workgroups sharing a CU drift apart (the older one's waves win the issue
       // arbitration), and the one behind would run its last units alone: a wave's priority is the
-      // number of units its workgroup has left after this one, so the one behind issues first
+      // number of units its workgroup has left after this one, so the one behind issues first.
+      // (Worth 1.8 % on the fused path; with the plain path's late state staging it no longer
+      // helps the plain verify and costs the trimmed one 0.8 %, so those keep one priority.)
       const int left = (n_units - 1 - u) / (int)gridDim.x;
       if (left >= 3) __builtin_amdgcn_s_setprio(3);
       else if (left == 2) __builtin_amdgcn_s_setprio(2);
