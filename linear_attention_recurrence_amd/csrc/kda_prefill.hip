@@ -699,331 +699,331 @@ __global__ void __launch_bounds__(NT) prefill_kernel(PrefillArgs A) {
     // again in the exact form. The flag is set before some barrier of pass 0 and read by every wave
     // after its last one, so all waves take the same decision.
     for (int pass = 0; pass < 2; ++pass) {
-    if (pass == 1 && !L.redo) break;
+      if (pass == 1 && !L.redo) break;
 
-    // Both roles run nch + 1 periods of two barriers each. Period p runs the
-    // chain of chunk p (p >= 0) beside the preparation of chunk p + 1.
-    // Inside each role the lane index is made opaque once per item, so that the compiler
-    // cannot hoist one role's lane-dependent addresses out of the item loop, where they would
-    // stay live (and spill) while the other role runs.
-    int lane_o = lane;
-    asm volatile("" : "+v"(lane_o));
-    const int g_o = lane_o >> 4, lr_o = lane_o & 15;
-    if (producer) {
-      const int pw = rw;
-      const int lane = lane_o, g = g_o, lr = lr_o;
-      auto produce = [&](auto exact_form) {
-      constexpr bool EXACT = decltype(exact_form)::value;
-      // Raw inputs are prefetched two periods ahead: q, k, gk, beta into registers, alternating
-      // between two sets (chunk c lives in set c & 1 from the period that issues it, c - 3,
-      // until its stage 1 in period c - 1: its q and k in that period's phase 1, as soon as stage 1
-      // has unpacked the set's previous q and k, its gk and beta in phase 2; in phase 2 of period
-      // c - 2 prescan turns its gk into the prefix sums stage 1 starts from), and v straight into
-      // vr[c & 1] (issued in period c - 2, read by the chain in period c; with GATED the gate rows
-      // go into gr[c & 1] the same way). Every period issues the same 12 loads (14 with GATED; past
-      // the last chunk they re-read it), so the compiler's waits before each register use count
-      // exactly, and the wait that closes a period can leave just that period's loads in flight.
-      if (nch == 0) {
-        __syncthreads();
-        __syncthreads();
-      } else {
-        Raw ra, rb;
-        auto issue = [&](Raw& r, int c) {
-          c = min(c, nch - 1);
-          load_raw(r, A, (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), 4 * pw + g, lr);
-        };
-        auto issue_early = [&](Raw& r, int c) {
-          c = min(c, nch - 1);
-          load_raw_qk(r, A, (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), 4 * pw + g, lr);
-        };
-        auto issue_late = [&](Raw& r, int c) {
-          c = min(c, nch - 1);
-          load_raw_gb(r, A, (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), 4 * pw + g, lr);
-        };
-        auto issue_vc = [&](int c) {
-          c = min(c, nch - 1);
-          issue_v(A.v, A, L.vr[c & 1], (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), pw, lane);
-          if constexpr (GATED) issue_v(A.gate, A, L.gr[c & 1], (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), pw, lane);
-        };
-        issue(ra, 0);
-        asm volatile("" ::: "memory");  // keep the issue order: set a, v of chunk 0, set b
-        issue_vc(0);
-        asm volatile("" ::: "memory");
-        issue(rb, 1);
-        asm volatile("" ::: "memory");
-        auto nc_of = [&](int c) { c = min(c, nch - 1); return min(C, len - C * c); };
-        prescan(ra, nc_of(0), lr);
-        auto period = [&](int p, Raw& use, Raw& other) {
-          const int c1 = p + 1, b1 = c1 & 1;
-          Keep keep;
-          if (c1 < nch) {
-            const int ncc = min(C, len - C * c1);
-            if (stage1(L, use, ncc, b1, pw, g, lr, keep, [&] { issue_early(use, c1 + 2); })) {
-              if constexpr (EXACT) stage1_exact(L, A, (size_t)(tok0 + C * c1) * H + h, ncc, b1, pw, g, lr, keep);
-              else L.redo = 1;
-            }
+      // Both roles run nch + 1 periods of two barriers each. Period p runs the
+      // chain of chunk p (p >= 0) beside the preparation of chunk p + 1.
+      // Inside each role the lane index is made opaque once per item, so that the compiler
+      // cannot hoist one role's lane-dependent addresses out of the item loop, where they would
+      // stay live (and spill) while the other role runs.
+      int lane_o = lane;
+      asm volatile("" : "+v"(lane_o));
+      const int g_o = lane_o >> 4, lr_o = lane_o & 15;
+      if (producer) {
+        const int pw = rw;
+        const int lane = lane_o, g = g_o, lr = lr_o;
+        auto produce = [&](auto exact_form) {
+          constexpr bool EXACT = decltype(exact_form)::value;
+          // Raw inputs are prefetched two periods ahead: q, k, gk, beta into registers, alternating
+          // between two sets (chunk c lives in set c & 1 from the period that issues it, c - 3,
+          // until its stage 1 in period c - 1: its q and k in that period's phase 1, as soon as stage 1
+          // has unpacked the set's previous q and k, its gk and beta in phase 2; in phase 2 of period
+          // c - 2 prescan turns its gk into the prefix sums stage 1 starts from), and v straight into
+          // vr[c & 1] (issued in period c - 2, read by the chain in period c; with GATED the gate rows
+          // go into gr[c & 1] the same way). Every period issues the same 12 loads (14 with GATED; past
+          // the last chunk they re-read it), so the compiler's waits before each register use count
+          // exactly, and the wait that closes a period can leave just that period's loads in flight.
+          if (nch == 0) {
+            __syncthreads();
+            __syncthreads();
           } else {
-            issue_early(use, c1 + 2);
-          }
-          __syncthreads();
-          issue_late(use, c1 + 2);
-          __builtin_amdgcn_sched_barrier(0);
-          prescan(other, nc_of(c1 + 1), lr);  // the next period's set, while the loads above go out
-          __builtin_amdgcn_sched_barrier(0);
-          issue_vc(c1 + 1);  // into the buffer the chain read in this period's phase 1
-          if (c1 < nch) stage1b(L, keep, b1, pw, g, lr);
-          // everything older than this period's 12 (14) loads has landed: the next chunk's
-          // register set and the v (and gate) rows the chain reads in the next period
-          if constexpr (GATED) __builtin_amdgcn_s_waitcnt(0x0f7e);  // vmcnt(14): the gate rows are 2 more loads
-          else __builtin_amdgcn_s_waitcnt(0x0f7c);                  // vmcnt(12)
-          __syncthreads();
-        };
-        // periods -1 .. nch-1 in pairs, so that both sets' loads are issued on every path
-        // around the loop
-        int p = -1;
-        for (; p + 1 < nch; p += 2) {
-          period(p, ra, rb);
-          period(p + 1, rb, ra);
-        }
-        if (p < nch) period(p, ra, rb);
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no LDS write may outlive the item
-      }
-      };
-      if (pass == 0) produce(std::false_type{});
-      else produce(std::true_type{});
-    } else {
-      const int lane = lane_o, g = g_o, lr = lr_o;
-      // The chain on the item's value columns: all 128 (four waves of 32, NV = 2 tiles of 16), or
-      // one of two halves of 64 (four waves of 16, NV = 1). Each 16-column tile runs the same
-      // instructions either way, so a split item gives the same bits as the whole one.
-      auto chain = [&](auto nv_tiles) {
-        constexpr int NV = decltype(nv_tiles)::value;
-        const int cw = rw;
-        const int cb = vb * (D / 2) * (2 - NV) + 16 * NV * cw;  // first value column of this wave
-        // This lane's element of a row-major [128][128] state tile is (16mc+4g+r, cb+16nv+lr), at
-        // tile + soff + (16mc+r)*D + 16nv. soff is made opaque here so that the compiler keeps one
-        // offset per lane instead of hoisting all the element offsets out of the item loop.
-        int soff = 4 * g * D + cb + lr;
-        asm volatile("" : "+v"(soff));
-        // state slice of this wave in accumulator layout: S[mc][nv] holds rows 16mc+4g+r, column cb+16nv+lr
-        f32x4 S[8][NV];
-        if (A.state_in) {
-          const float* src = A.state_in + unit * D * D + soff;
-  #pragma unroll
-          for (int mc = 0; mc < 8; ++mc)
-  #pragma unroll
-            for (int nv = 0; nv < NV; ++nv)
-  #pragma unroll
-              for (int r = 0; r < 4; ++r) S[mc][nv][r] = src[(16 * mc + r) * D + 16 * nv];
-        } else {
-  #pragma unroll
-          for (int mc = 0; mc < 8; ++mc)
-  #pragma unroll
-            for (int nv = 0; nv < NV; ++nv) S[mc][nv] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        f16x8 Wh[NV], Wl[NV];
-
-        // GATED: o of tokens lr and 16 + lr of the last chunk and their gate bits (columns c0 .. c0 + 3),
-        // kept in registers from the phase 1 that forms them to the next period's phase 1, where the
-        // output gated RMSNorm of that chunk runs just before the new o replaces them. Its stores then
-        // go out late in phase 1, as the plain path's stores of o do: in phase 2, or early in phase 1,
-        // they would wait behind the producers' burst of loads in a full memory queue
-        f32x4 Og[2][NV];
-        uint2 Gq[2][NV];
-        auto norm_epilogue = [&](int pc) {
-          if constexpr (GATED && NV == 2) {
-            // rows past the chunk end fall outside the buffer range and are dropped by the hardware
-            const int ncc = min(C, len - C * pc);
-            const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
-                A.y + ((size_t)(tok0 + C * pc) * H + h) * D, 0, (int)((((uint32_t)ncc - 1) * H * D + D) * 2), 0x00020000);
-  #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-              const uint32_t t = 16 * mt + lr;
-              const float rstd = L.rs[t];
-  #pragma unroll
-              for (int nv = 0; nv < 2; ++nv) {
-                const float4 w4 = *reinterpret_cast<const float4*>(&L.nw[cb + 16 * nv + 4 * g]);
-                const uint2 yv = norm_apply4(Og[mt][nv], Gq[mt][nv], w4, rstd);
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2v, yv), yrs,
-                                                      (int)((t * H * D + cb + 16 * nv + 4 * g) * 2), 0, 0);
+            Raw ra, rb;
+            auto issue = [&](Raw& r, int c) {
+              c = min(c, nch - 1);
+              load_raw(r, A, (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), 4 * pw + g, lr);
+            };
+            auto issue_early = [&](Raw& r, int c) {
+              c = min(c, nch - 1);
+              load_raw_qk(r, A, (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), 4 * pw + g, lr);
+            };
+            auto issue_late = [&](Raw& r, int c) {
+              c = min(c, nch - 1);
+              load_raw_gb(r, A, (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), 4 * pw + g, lr);
+            };
+            auto issue_vc = [&](int c) {
+              c = min(c, nch - 1);
+              issue_v(A.v, A, L.vr[c & 1], (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), pw, lane);
+              if constexpr (GATED) issue_v(A.gate, A, L.gr[c & 1], (size_t)(tok0 + C * c) * H + h, min(C, len - C * c), pw, lane);
+            };
+            issue(ra, 0);
+            asm volatile("" ::: "memory");  // keep the issue order: set a, v of chunk 0, set b
+            issue_vc(0);
+            asm volatile("" ::: "memory");
+            issue(rb, 1);
+            asm volatile("" ::: "memory");
+            auto nc_of = [&](int c) { c = min(c, nch - 1); return min(C, len - C * c); };
+            prescan(ra, nc_of(0), lr);
+            auto period = [&](int p, Raw& use, Raw& other) {
+              const int c1 = p + 1, b1 = c1 & 1;
+              Keep keep;
+              if (c1 < nch) {
+                const int ncc = min(C, len - C * c1);
+                if (stage1(L, use, ncc, b1, pw, g, lr, keep, [&] { issue_early(use, c1 + 2); })) {
+                  if constexpr (EXACT) stage1_exact(L, A, (size_t)(tok0 + C * c1) * H + h, ncc, b1, pw, g, lr, keep);
+                  else L.redo = 1;
+                }
+              } else {
+                issue_early(use, c1 + 2);
               }
+              __syncthreads();
+              issue_late(use, c1 + 2);
+              __builtin_amdgcn_sched_barrier(0);
+              prescan(other, nc_of(c1 + 1), lr);  // the next period's set, while the loads above go out
+              __builtin_amdgcn_sched_barrier(0);
+              issue_vc(c1 + 1);  // into the buffer the chain read in this period's phase 1
+              if (c1 < nch) stage1b(L, keep, b1, pw, g, lr);
+              // everything older than this period's 12 (14) loads has landed: the next chunk's
+              // register set and the v (and gate) rows the chain reads in the next period
+              if constexpr (GATED) __builtin_amdgcn_s_waitcnt(0x0f7e);  // vmcnt(14): the gate rows are 2 more loads
+              else __builtin_amdgcn_s_waitcnt(0x0f7c);                  // vmcnt(12)
+              __syncthreads();
+            };
+            // periods -1 .. nch-1 in pairs, so that both sets' loads are issued on every path
+            // around the loop
+            int p = -1;
+            for (; p + 1 < nch; p += 2) {
+              period(p, ra, rb);
+              period(p + 1, rb, ra);
             }
+            if (p < nch) period(p, ra, rb);
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no LDS write may outlive the item
           }
         };
+        if (pass == 0) produce(std::false_type{});
+        else produce(std::true_type{});
+      } else {
+        const int lane = lane_o, g = g_o, lr = lr_o;
+        // The chain on the item's value columns: all 128 (four waves of 32, NV = 2 tiles of 16), or
+        // one of two halves of 64 (four waves of 16, NV = 1). Each 16-column tile runs the same
+        // instructions either way, so a split item gives the same bits as the whole one.
+        auto chain = [&](auto nv_tiles) {
+          constexpr int NV = decltype(nv_tiles)::value;
+          const int cw = rw;
+          const int cb = vb * (D / 2) * (2 - NV) + 16 * NV * cw;  // first value column of this wave
+          // This lane's element of a row-major [128][128] state tile is (16mc+4g+r, cb+16nv+lr), at
+          // tile + soff + (16mc+r)*D + 16nv. soff is made opaque here so that the compiler keeps one
+          // offset per lane instead of hoisting all the element offsets out of the item loop.
+          int soff = 4 * g * D + cb + lr;
+          asm volatile("" : "+v"(soff));
+          // state slice of this wave in accumulator layout: S[mc][nv] holds rows 16mc+4g+r, column cb+16nv+lr
+          f32x4 S[8][NV];
+          if (A.state_in) {
+            const float* src = A.state_in + unit * D * D + soff;
+    #pragma unroll
+            for (int mc = 0; mc < 8; ++mc)
+    #pragma unroll
+              for (int nv = 0; nv < NV; ++nv)
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) S[mc][nv][r] = src[(16 * mc + r) * D + 16 * nv];
+          } else {
+    #pragma unroll
+            for (int mc = 0; mc < 8; ++mc)
+    #pragma unroll
+              for (int nv = 0; nv < NV; ++nv) S[mc][nv] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+          f16x8 Wh[NV], Wl[NV];
 
-        for (int p = -1; p < nch; ++p) {
-          const int b = p & 1;
-          const int nc = min(C, len - C * p);
-          if (p >= 0) {
-            // ---------------- Kt S0 and Qt S0 ----------------
-            // S enters as fp16 B operands: step s reduces over rows {16(2s)+4g+r} then {16(2s+1)+4g+r},
-            // and the A operands read the same permutation of their columns
-            // The same fragments serve as the A operand of S^T, so (Qt S0)^T = S0^T Qt^T comes out
-            // transposed: QT[nv][mt] holds rows = value columns, columns = tokens.
-            f32x4 KS[2][NV], QT[NV][2];
-  #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-  #pragma unroll
-              for (int nv = 0; nv < NV; ++nv) { KS[mt][nv] = f32x4{0.f, 0.f, 0.f, 0.f}; QT[nv][mt] = f32x4{0.f, 0.f, 0.f, 0.f}; }
-  #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              f16x8 sh[NV];
-  #pragma unroll
-              for (int nv = 0; nv < NV; ++nv) sh[nv] = to_h8(S[2 * s][nv], S[2 * s + 1][nv]);
-  #pragma unroll
+          // GATED: o of tokens lr and 16 + lr of the last chunk and their gate bits (columns c0 .. c0 + 3),
+          // kept in registers from the phase 1 that forms them to the next period's phase 1, where the
+          // output gated RMSNorm of that chunk runs just before the new o replaces them. Its stores then
+          // go out late in phase 1, as the plain path's stores of o do: in phase 2, or early in phase 1,
+          // they would wait behind the producers' burst of loads in a full memory queue
+          f32x4 Og[2][NV];
+          uint2 Gq[2][NV];
+          auto norm_epilogue = [&](int pc) {
+            if constexpr (GATED && NV == 2) {
+              // rows past the chunk end fall outside the buffer range and are dropped by the hardware
+              const int ncc = min(C, len - C * pc);
+              const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+                  A.y + ((size_t)(tok0 + C * pc) * H + h) * D, 0, (int)((((uint32_t)ncc - 1) * H * D + D) * 2), 0x00020000);
+    #pragma unroll
               for (int mt = 0; mt < 2; ++mt) {
-                const int m = 16 * mt + lr;
-                const f16x8 kr = perm_h(&L.kt[b][m][32 * s], g);
-                const f16x8 qr = perm_h(&L.qt[b][m][32 * s], g);
-  #pragma unroll
-                for (int nv = 0; nv < NV; ++nv) {
-                  KS[mt][nv] = mfma_h(kr, sh[nv], KS[mt][nv]);
-                  QT[nv][mt] = mfma_h(sh[nv], qr, QT[nv][mt]);
+                const uint32_t t = 16 * mt + lr;
+                const float rstd = L.rs[t];
+    #pragma unroll
+                for (int nv = 0; nv < 2; ++nv) {
+                  const float4 w4 = *reinterpret_cast<const float4*>(&L.nw[cb + 16 * nv + 4 * g]);
+                  const uint2 yv = norm_apply4(Og[mt][nv], Gq[mt][nv], w4, rstd);
+                  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2v, yv), yrs,
+                                                        (int)((t * H * D + cb + 16 * nv + 4 * g) * 2), 0, 0);
                 }
               }
             }
-            // ---------------- R = diag(beta)(V - Kt S0), W = X R ----------------
-            // by blocks: W0 = X00 R0, W1 = X11 (R1 - A10 W0), 16x16x16 MFMAs with fp16 hi + lo operands
-            f32x4 W[2][NV];
-            const float mone = minus_one();
-            {
-              const f16x4 x00 = __builtin_bit_cast(f16x4, lds8(&L.xb[b][lr][4 * g]));
-              const f16x4 x11 = __builtin_bit_cast(f16x4, lds8(&L.xb[b][16 + lr][16 + 4 * g]));
-              const f16x4 a10 = __builtin_bit_cast(f16x4, lds8(&L.an[b][lr][4 * g]));
-  #pragma unroll
-              for (int nv = 0; nv < NV; ++nv) {
-                f32x4 R[2];
-                const int c0 = cb + 16 * nv + 4 * (lr & 3);
-  #pragma unroll
+          };
+
+          for (int p = -1; p < nch; ++p) {
+            const int b = p & 1;
+            const int nc = min(C, len - C * p);
+            if (p >= 0) {
+              // ---------------- Kt S0 and Qt S0 ----------------
+              // S enters as fp16 B operands: step s reduces over rows {16(2s)+4g+r} then {16(2s+1)+4g+r},
+              // and the A operands read the same permutation of their columns
+              // The same fragments serve as the A operand of S^T, so (Qt S0)^T = S0^T Qt^T comes out
+              // transposed: QT[nv][mt] holds rows = value columns, columns = tokens.
+              f32x4 KS[2][NV], QT[NV][2];
+    #pragma unroll
+              for (int mt = 0; mt < 2; ++mt)
+    #pragma unroll
+                for (int nv = 0; nv < NV; ++nv) { KS[mt][nv] = f32x4{0.f, 0.f, 0.f, 0.f}; QT[nv][mt] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    #pragma unroll
+              for (int s = 0; s < 4; ++s) {
+                f16x8 sh[NV];
+    #pragma unroll
+                for (int nv = 0; nv < NV; ++nv) sh[nv] = to_h8(S[2 * s][nv], S[2 * s + 1][nv]);
+    #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) {
-                  // V[16mt+4g+r][32cw+16nv+lr] through the transposing read of the swizzled raw rows;
-                  // the four rows of one read land in four different 8-bank groups
-                  const int row = 16 * mt + 4 * g + (lr >> 2);
-                  const uint2 vv = lds_tr(&L.vr[b][row][8 * ((c0 >> 3) ^ ((2 * row) & 15)) + (c0 & 7)]);
-                  const float4 b4 = *reinterpret_cast<const float4*>(&L.beta[b][16 * mt + 4 * g]);
-                  R[mt][0] = b4.x * (bf2f(vv.x & 0xffffu) - KS[mt][nv][0]);
-                  R[mt][1] = b4.y * (bf2f(vv.x >> 16) - KS[mt][nv][1]);
-                  R[mt][2] = b4.z * (bf2f(vv.y & 0xffffu) - KS[mt][nv][2]);
-                  R[mt][3] = b4.w * (bf2f(vv.y >> 16) - KS[mt][nv][3]);
-                }
-                const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-                f16x4 hi, lo;
-                split_h4(R[0], hi, lo, mone);
-                f32x4 w0 = mfma_h16(x00, lo, mfma_h16(x00, hi, z4));
-                split_h4(w0, hi, lo, mone);
-                f32x4 r1 = mfma_h16(a10, lo, mfma_h16(a10, hi, R[1]));
-                split_h4(r1, hi, lo, mone);
-                W[0][nv] = w0;
-                W[1][nv] = mfma_h16(x11, lo, mfma_h16(x11, hi, z4));
-              }
-            }
-  #pragma unroll
-            for (int nv = 0; nv < NV; ++nv) split_h8(W[0][nv], W[1][nv], Wh[nv], Wl[nv], mone);
-            if (p >= 1) norm_epilogue(p - 1);  // (GATED only) the previous chunk's output, before its o is replaced
-
-            // ---------------- O^T = scale (S0^T Qt^T + W^T P^T), stored from the accumulators ----------------
-            // lane (g, lr) holds O[16mt + lr][cb + 16nv + 4g + r], r < 4: one 16-byte store per tile
-  #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-              const f16x8 pa = perm_h(&L.pm[b][16 * mt + lr][0], g);
-              const int t = 16 * mt + lr;
-              float* orow = A.o + ((size_t)(tok0 + C * p) * H + h) * D + ((uint32_t)t * H * D + cb + 4 * g);
-  #pragma unroll
-              for (int nv = 0; nv < NV; ++nv) {
-                f32x4 acc = QT[nv][mt];
-                acc = mfma_h(Wh[nv], pa, acc);
-                acc = mfma_h(Wl[nv], pa, acc);
-                if constexpr (GATED) {
-                  Og[mt][nv] = f32x4{A.scale * acc[0], A.scale * acc[1], A.scale * acc[2], A.scale * acc[3]};
-                  const int c0 = cb + 16 * nv + 4 * g;
-                  Gq[mt][nv] = *reinterpret_cast<const uint2*>(&L.gr[b][t][8 * ((c0 >> 3) ^ ((2 * t) & 15)) + (c0 & 7)]);
-                } else if (t < nc) {
-                  *reinterpret_cast<float4*>(orow + 16 * nv) = make_float4(A.scale * acc[0], A.scale * acc[1], A.scale * acc[2], A.scale * acc[3]);
+                  const int m = 16 * mt + lr;
+                  const f16x8 kr = perm_h(&L.kt[b][m][32 * s], g);
+                  const f16x8 qr = perm_h(&L.qt[b][m][32 * s], g);
+    #pragma unroll
+                  for (int nv = 0; nv < NV; ++nv) {
+                    KS[mt][nv] = mfma_h(kr, sh[nv], KS[mt][nv]);
+                    QT[nv][mt] = mfma_h(sh[nv], qr, QT[nv][mt]);
+                  }
                 }
               }
-              // this lane's slice (4 cw + g) of token t: columns 32 cw + 4 g + {0..3}, then + 16
-              if constexpr (GATED && NV == 2) L.ssq[t][4 * cw + g] = norm_slice_ssq(Og[mt][0], Og[mt][1]);
-            }
-          }
-          // The state update reads only this chunk's K' rows and e^{G_31} (written by the preparation
-          // waves in the previous period) and this wave's own W, so it runs before the barrier, in the
-          // time the chain would otherwise wait there for the preparation of the next chunk.
-          if (p >= 0) {
-            // ---------------- S = e^{G_31} S0 + K'^T W ----------------
-  #pragma unroll
-            for (int mc = 0; mc < 8; ++mc) {
-              const float4 d4 = *reinterpret_cast<const float4*>(&L.dlast[b][16 * mc + 4 * g]);
-              // K'^T rows 16mc+lr, reduction positions t = 4g+r and 16+4g+r, via the transposing read
-              const uint16_t* base = &L.kp[b][4 * g + (lr >> 2)][16 * mc + 4 * (lr & 3)];
-              const f16x8 ka = as_f16x8(lds_tr(base), lds_tr(base + 16 * TM));
-  #pragma unroll
-              for (int nv = 0; nv < NV; ++nv) {
-                f32x4 acc = S[mc][nv];
-                acc[0] *= d4.x; acc[1] *= d4.y; acc[2] *= d4.z; acc[3] *= d4.w;
-                acc = mfma_h(ka, Wh[nv], acc);
-                acc = mfma_h(ka, Wl[nv], acc);
-                S[mc][nv] = acc;
+              // ---------------- R = diag(beta)(V - Kt S0), W = X R ----------------
+              // by blocks: W0 = X00 R0, W1 = X11 (R1 - A10 W0), 16x16x16 MFMAs with fp16 hi + lo operands
+              f32x4 W[2][NV];
+              const float mone = minus_one();
+              {
+                const f16x4 x00 = __builtin_bit_cast(f16x4, lds8(&L.xb[b][lr][4 * g]));
+                const f16x4 x11 = __builtin_bit_cast(f16x4, lds8(&L.xb[b][16 + lr][16 + 4 * g]));
+                const f16x4 a10 = __builtin_bit_cast(f16x4, lds8(&L.an[b][lr][4 * g]));
+    #pragma unroll
+                for (int nv = 0; nv < NV; ++nv) {
+                  f32x4 R[2];
+                  const int c0 = cb + 16 * nv + 4 * (lr & 3);
+    #pragma unroll
+                  for (int mt = 0; mt < 2; ++mt) {
+                    // V[16mt+4g+r][32cw+16nv+lr] through the transposing read of the swizzled raw rows;
+                    // the four rows of one read land in four different 8-bank groups
+                    const int row = 16 * mt + 4 * g + (lr >> 2);
+                    const uint2 vv = lds_tr(&L.vr[b][row][8 * ((c0 >> 3) ^ ((2 * row) & 15)) + (c0 & 7)]);
+                    const float4 b4 = *reinterpret_cast<const float4*>(&L.beta[b][16 * mt + 4 * g]);
+                    R[mt][0] = b4.x * (bf2f(vv.x & 0xffffu) - KS[mt][nv][0]);
+                    R[mt][1] = b4.y * (bf2f(vv.x >> 16) - KS[mt][nv][1]);
+                    R[mt][2] = b4.z * (bf2f(vv.y & 0xffffu) - KS[mt][nv][2]);
+                    R[mt][3] = b4.w * (bf2f(vv.y >> 16) - KS[mt][nv][3]);
+                  }
+                  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+                  f16x4 hi, lo;
+                  split_h4(R[0], hi, lo, mone);
+                  f32x4 w0 = mfma_h16(x00, lo, mfma_h16(x00, hi, z4));
+                  split_h4(w0, hi, lo, mone);
+                  f32x4 r1 = mfma_h16(a10, lo, mfma_h16(a10, hi, R[1]));
+                  split_h4(r1, hi, lo, mone);
+                  W[0][nv] = w0;
+                  W[1][nv] = mfma_h16(x11, lo, mfma_h16(x11, hi, z4));
+                }
+              }
+    #pragma unroll
+              for (int nv = 0; nv < NV; ++nv) split_h8(W[0][nv], W[1][nv], Wh[nv], Wl[nv], mone);
+              if (p >= 1) norm_epilogue(p - 1);  // (GATED only) the previous chunk's output, before its o is replaced
+
+              // ---------------- O^T = scale (S0^T Qt^T + W^T P^T), stored from the accumulators ----------------
+              // lane (g, lr) holds O[16mt + lr][cb + 16nv + 4g + r], r < 4: one 16-byte store per tile
+    #pragma unroll
+              for (int mt = 0; mt < 2; ++mt) {
+                const f16x8 pa = perm_h(&L.pm[b][16 * mt + lr][0], g);
+                const int t = 16 * mt + lr;
+                float* orow = A.o + ((size_t)(tok0 + C * p) * H + h) * D + ((uint32_t)t * H * D + cb + 4 * g);
+    #pragma unroll
+                for (int nv = 0; nv < NV; ++nv) {
+                  f32x4 acc = QT[nv][mt];
+                  acc = mfma_h(Wh[nv], pa, acc);
+                  acc = mfma_h(Wl[nv], pa, acc);
+                  if constexpr (GATED) {
+                    Og[mt][nv] = f32x4{A.scale * acc[0], A.scale * acc[1], A.scale * acc[2], A.scale * acc[3]};
+                    const int c0 = cb + 16 * nv + 4 * g;
+                    Gq[mt][nv] = *reinterpret_cast<const uint2*>(&L.gr[b][t][8 * ((c0 >> 3) ^ ((2 * t) & 15)) + (c0 & 7)]);
+                  } else if (t < nc) {
+                    *reinterpret_cast<float4*>(orow + 16 * nv) = make_float4(A.scale * acc[0], A.scale * acc[1], A.scale * acc[2], A.scale * acc[3]);
+                  }
+                }
+                // this lane's slice (4 cw + g) of token t: columns 32 cw + 4 g + {0..3}, then + 16
+                if constexpr (GATED && NV == 2) L.ssq[t][4 * cw + g] = norm_slice_ssq(Og[mt][0], Og[mt][1]);
               }
             }
-
-            // ---------------- snapshot at chunk ends q with q % interval == 0 ----------------
-            const int q = C * p + nc;
-            if (A.snap_interval > 0 && q % A.snap_interval == 0) {
-              const int m = q / A.snap_interval;
-              float* dst = A.snap + (((size_t)n * A.snap_slots + (m - 1) % A.snap_slots) * H + h) * D * D + soff;
-  #pragma unroll
-              for (int mc = 0; mc < 8; ++mc)
-  #pragma unroll
-                for (int nv = 0; nv < NV; ++nv)
-  #pragma unroll
-                  for (int r = 0; r < 4; ++r) dst[(16 * mc + r) * D + 16 * nv] = S[mc][nv][r];
-            }
-          }
-          __syncthreads();
-          // (GATED) 1 / rms of each of this chunk's token rows from the slice sums of phase 1, on the
-          // chain wave with the most slack in phase 2; the next period's phase 1 uses them
-          if constexpr (GATED && NV == 2) {
-            if (cw == 3 && p >= 0 && lane < C) {
-              float ss = 0.f;  // the 16 slice sums, in slice order
-  #pragma unroll
-              for (int k4 = 0; k4 < 4; ++k4) {
-                const float4 s4 = *reinterpret_cast<const float4*>(&L.ssq[lane][4 * k4]);
-                ss = ss + s4.x;
-                ss = ss + s4.y;
-                ss = ss + s4.z;
-                ss = ss + s4.w;
+            // The state update reads only this chunk's K' rows and e^{G_31} (written by the preparation
+            // waves in the previous period) and this wave's own W, so it runs before the barrier, in the
+            // time the chain would otherwise wait there for the preparation of the next chunk.
+            if (p >= 0) {
+              // ---------------- S = e^{G_31} S0 + K'^T W ----------------
+    #pragma unroll
+              for (int mc = 0; mc < 8; ++mc) {
+                const float4 d4 = *reinterpret_cast<const float4*>(&L.dlast[b][16 * mc + 4 * g]);
+                // K'^T rows 16mc+lr, reduction positions t = 4g+r and 16+4g+r, via the transposing read
+                const uint16_t* base = &L.kp[b][4 * g + (lr >> 2)][16 * mc + 4 * (lr & 3)];
+                const f16x8 ka = as_f16x8(lds_tr(base), lds_tr(base + 16 * TM));
+    #pragma unroll
+                for (int nv = 0; nv < NV; ++nv) {
+                  f32x4 acc = S[mc][nv];
+                  acc[0] *= d4.x; acc[1] *= d4.y; acc[2] *= d4.z; acc[3] *= d4.w;
+                  acc = mfma_h(ka, Wh[nv], acc);
+                  acc = mfma_h(ka, Wl[nv], acc);
+                  S[mc][nv] = acc;
+                }
               }
-              L.rs[lane] = norm_rstd(ss, A.eps);
+
+              // ---------------- snapshot at chunk ends q with q % interval == 0 ----------------
+              const int q = C * p + nc;
+              if (A.snap_interval > 0 && q % A.snap_interval == 0) {
+                const int m = q / A.snap_interval;
+                float* dst = A.snap + (((size_t)n * A.snap_slots + (m - 1) % A.snap_slots) * H + h) * D * D + soff;
+    #pragma unroll
+                for (int mc = 0; mc < 8; ++mc)
+    #pragma unroll
+                  for (int nv = 0; nv < NV; ++nv)
+    #pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[(16 * mc + r) * D + 16 * nv] = S[mc][nv][r];
+              }
             }
+            __syncthreads();
+            // (GATED) 1 / rms of each of this chunk's token rows from the slice sums of phase 1, on the
+            // chain wave with the most slack in phase 2; the next period's phase 1 uses them
+            if constexpr (GATED && NV == 2) {
+              if (cw == 3 && p >= 0 && lane < C) {
+                float ss = 0.f;  // the 16 slice sums, in slice order
+    #pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4) {
+                  const float4 s4 = *reinterpret_cast<const float4*>(&L.ssq[lane][4 * k4]);
+                  ss = ss + s4.x;
+                  ss = ss + s4.y;
+                  ss = ss + s4.z;
+                  ss = ss + s4.w;
+                }
+                L.rs[lane] = norm_rstd(ss, A.eps);
+              }
+            }
+            // the next chunk's X, P and -A10 from the partials the producers wrote in phase 1, on the
+            // chain waves (the producers' phase 2 is taken up by issuing the next loads)
+            if (cw == 0 && p + 1 < nch) stage2_solve(L, (p + 1) & 1, lane, 0);
+            else if (cw == 1 && p + 1 < nch) stage2_p(L, (p + 1) & 1, lane);
+            else if (cw == 2 && p + 1 < nch) stage2_a10(L, (p + 1) & 1, lane);
+            else if (cw == 3 && p + 1 < nch) stage2_solve(L, (p + 1) & 1, lane, 1);
+            __syncthreads();
           }
-          // the next chunk's X, P and -A10 from the partials the producers wrote in phase 1, on the
-          // chain waves (the producers' phase 2 is taken up by issuing the next loads)
-          if (cw == 0 && p + 1 < nch) stage2_solve(L, (p + 1) & 1, lane, 0);
-          else if (cw == 1 && p + 1 < nch) stage2_p(L, (p + 1) & 1, lane);
-          else if (cw == 2 && p + 1 < nch) stage2_a10(L, (p + 1) & 1, lane);
-          else if (cw == 3 && p + 1 < nch) stage2_solve(L, (p + 1) & 1, lane, 1);
-          __syncthreads();
-        }
 
-        if (nch >= 1) norm_epilogue(nch - 1);  // (GATED only) the last chunk's output
+          if (nch >= 1) norm_epilogue(nch - 1);  // (GATED only) the last chunk's output
 
-        // a flagged fast pass leaves the final state unwritten, so that pass 1 still finds the
-        // initial state where the caller passed the same buffer for both
-        if (pass == 1 || !L.redo) {
-          float* dst = A.state_out + unit * D * D + soff;
-  #pragma unroll
-          for (int mc = 0; mc < 8; ++mc)
-  #pragma unroll
-            for (int nv = 0; nv < NV; ++nv)
-  #pragma unroll
-              for (int r = 0; r < 4; ++r) dst[(16 * mc + r) * D + 16 * nv] = S[mc][nv][r];
-        }
+          // a flagged fast pass leaves the final state unwritten, so that pass 1 still finds the
+          // initial state where the caller passed the same buffer for both
+          if (pass == 1 || !L.redo) {
+            float* dst = A.state_out + unit * D * D + soff;
+    #pragma unroll
+            for (int mc = 0; mc < 8; ++mc)
+    #pragma unroll
+              for (int nv = 0; nv < NV; ++nv)
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) dst[(16 * mc + r) * D + 16 * nv] = S[mc][nv][r];
+          }
 
-      };
-      if (GATED || A.n_vblk == 1) chain(std::integral_constant<int, 2>{});
-      else chain(std::integral_constant<int, 1>{});
-      if (A.snap_count && h == 0 && vb == 0 && tid == 0) A.snap_count[n] = A.snap_interval > 0 ? len / A.snap_interval : 0;
-    }
+        };
+        if (GATED || A.n_vblk == 1) chain(std::integral_constant<int, 2>{});
+        else chain(std::integral_constant<int, 1>{});
+        if (A.snap_count && h == 0 && vb == 0 && tid == 0) A.snap_count[n] = A.snap_interval > 0 ? len / A.snap_interval : 0;
+      }
     }
   }
 
