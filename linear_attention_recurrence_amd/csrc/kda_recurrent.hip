@@ -61,15 +61,17 @@ __global__ void __launch_bounds__(256) verify_kernel(VerifyArgs A) {
   const int slot = A.slot_idx[b];
   if (slot < 0 || slot >= A.n_slots) return;  // whole workgroup skips together
   const size_t unit = ((size_t)slot * A.n_layers + A.layer) * A.n_heads + h;
+
+  // the state slice first: the commit length and the ring start are read after its loads are
+  // issued, so that their memory latency is not paid before the state's
+  float S[16][4];
+  load_state(S, A.state_pool + unit * D * D, r0, col0);
   int commit_n = 0;
   if (A.commit_len && A.commit_pool) {
     commit_n = A.commit_len[b];
     commit_n = commit_n < 0 ? 0 : (commit_n > A.n_tok ? A.n_tok : commit_n);
   }
   const int rstart = (RING && A.ring_start) ? A.ring_start[b] : 0;
-
-  float S[16][4];
-  load_state(S, A.state_pool + unit * D * D, r0, col0);
 
   for (int t0 = 0; t0 < A.n_tok; t0 += TB) {
     const int nb = (A.n_tok - t0) < TB ? (A.n_tok - t0) : TB;
