@@ -23,6 +23,7 @@ evicts the caches. Beside it, in the same JSON line:
   geometric (mean 2.7, clipped to [1, 8])" = 69 kda_verify launches + one
   kda_replay_fold launch, in us/step (committed states restored from a
   pristine copy outside the timed region before every step); beside it the
+  69 verifies replayed as one captured HIP graph (``verify_us_graph``), the
   same step through kda_fold_verify, and the verify with trimmed windows;
 * ``prologue``, ``state_moves``: the adjacent steps;
 * ``cpu_baseline``: the fp64 oracle (token-by-token) on the host cores this
@@ -458,6 +459,27 @@ def bench_verify_fold(args, torch, kda, sg, synth):
     ver = sum(t[0] for t in times) / len(times)
     fol = sum(t[1] for t in times) / len(times)
 
+    # The 69 verifies again, captured once as a HIP graph and replayed, as a serving loop launches a
+    # step's kernels: the same launches with the host's per-call work and most of the gaps between
+    # kernels taken out. They only read the committed pool and rewrite the ring with the same bits.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for l in range(Lyr):
+            q, k, v, gk, beta = ins[l]
+            kda.kda_verify(q, k, v, gk, beta, pool, slot_idx, o, layer=l, n_tok=T, ring=ring, ring_start=ring_start)
+    graph.replay()
+    torch.cuda.synchronize()
+    gtimes = []
+    for _ in range(args.vf_steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        graph.replay()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        gtimes.append(ev[0].elapsed_time(ev[1]))
+    ver_graph = sum(gtimes) / len(gtimes)
+    del graph
+
     # The same step through the fused path: one kda_fold_verify per layer folds the window the
     # verifies above recorded (positions 0..T-1, the accepted lengths) into the committed state and
     # verifies the next window (positions T..2T-1) from it.
@@ -521,7 +543,8 @@ def bench_verify_fold(args, torch, kda, sg, synth):
     # fused: the state read once, written back, the folded entries read, the verify's inputs and outputs
     fv_bytes = units * (2 * 65536 + T * (768 + 512 + 4 + 512 + 1028)) + int(round(float(acc.float().sum()) * Lyr * H * 1028))
     r_bytes = units * 65536 + tot_r * Lyr * H * (768 + 512 + 4 + 512 + 1028)
-    res = dict(verify_ms=ver, fold_ms=fol, accept_mean=acc_mean,
+    res = dict(verify_ms=ver, fold_ms=fol, accept_mean=acc_mean, verify_graph_ms=ver_graph,
+               verify_graph_gbs=v_bytes / (ver_graph * 1e-3) / 1e9,
                verify_gbs=v_bytes / (ver * 1e-3) / 1e9, fold_gbs=f_bytes / (fol * 1e-3) / 1e9,
                verify_bytes=v_bytes, fold_bytes=f_bytes, fused_ms=fus, fused_bytes=fv_bytes,
                fused_gbs=fv_bytes / (fus * 1e-3) / 1e9, ragged_ms=rag, ragged_bytes=r_bytes,
@@ -893,6 +916,8 @@ def main():
             "step_hbm_frac": (vf["verify_bytes"] + vf["fold_bytes"]) / ((vf["verify_ms"] + vf["fold_ms"]) * 1e-3)
                              / 1e9 / HBM_PEAK_GBS,
             "verify_gbs": vf["verify_gbs"], "fold_gbs": vf["fold_gbs"], "accept_mean": vf["accept_mean"],
+            "verify_us_graph": vf["verify_graph_ms"] * 1e3,
+            "verify_hbm_frac_graph": vf["verify_graph_gbs"] / HBM_PEAK_GBS,
             "algorithmic_bytes_per_launch": {"verify": vf["verify_bytes"] // vf["layers"], "fold": vf["fold_bytes"],
                                              "fused": vf["fused_bytes"] // vf["layers"],
                                              "ragged": vf["ragged_bytes"] // vf["layers"]},
