@@ -27,10 +27,13 @@
 // A call that also asks for the recurrent commit takes the token-by-token
 // kernel instead, whose arithmetic the fold replays bit for bit.
 //
-// Work decomposition: one 256-thread workgroup per (request, head). Wave w
-// stages its 128 x 32 column slice of S0 as fp16 in LDS (coalesced 16-byte
-// loads) and reads it back transposed (ds_read_b64_tr_b16) as MFMA operands.
-// Two workgroups fit on a CU.
+// Work decomposition: a persistent grid of 256-thread workgroups, two per CU,
+// each taking (request, head) units in turn and prefetching the next unit's
+// state slice and inputs into registers while it computes the current one.
+// Wave w stages its 128 x 32 column slice of S0 as fp16 in LDS (coalesced
+// 16-byte loads; on the plain and trimmed paths after the unit's key side, on
+// the fused path after the fold) and reads it back transposed
+// (ds_read_b64_tr_b16) as MFMA operands.
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_step.h"
