@@ -21,7 +21,7 @@ namespace kda {
 
 constexpr int TB = 8;  // steps staged in LDS per batch
 
-struct StepLds {
+struct alignas(16) StepLds {
   float a[TB][D];     // exp(gk)
   float ak[TB][D];    // exp(gk) * k
   float k[TB][D];
@@ -31,7 +31,7 @@ struct StepLds {
 };
 
 // the same staging without q, for folds
-struct FoldLds {
+struct alignas(16) FoldLds {
   float a[TB][D];
   float ak[TB][D];
   float k[TB][D];
