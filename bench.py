@@ -57,7 +57,7 @@ METRIC = "KDA prefill tokens*heads/s and verify+fold us/step at 1 GPU; % of roof
 PREFILL_TRAFFIC_BYTES = {"long_1m_h96": 187_985_215_224, "prefill_4x2048_h64": 994_373_454}
 # the same for one launch of each kernel of the speculative step (256 x 69 x 8): kda_verify (chunked),
 # kda_replay_fold, kda_fold_verify, kda_verify_ragged
-VERIFY_TRAFFIC_BYTES = {"verify": 182_660_442, "fold": None, "fused": 323_764_716, "ragged": 162_462_854}
+VERIFY_TRAFFIC_BYTES = {"verify": 182_660_442, "fold": 18_941_977_265, "fused": 323_764_716, "ragged": 162_462_854}
 FLUSH_BYTES = 1 << 30  # scratch written before every timed prefill rep: evicts the 256 MB Infinity Cache and L2s
 
 
